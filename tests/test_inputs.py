@@ -1,0 +1,53 @@
+"""The seeded input generator: bf16 rounding, determinism and the workload recipe (CPU)."""
+import numpy as np
+import torch
+
+from megatron_tensor_transformer_mlp_amd import inputs
+
+
+def test_rne_matches_torch_bfloat16(rng):
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32) * 3,
+                        np.array([0.0, -0.0, 1.0, 65504.0, 1e-40, -1e-40, np.inf, -np.inf], np.float32),
+                        # exact ties: low 16 bits 0x8000, odd and even upper halves
+                        np.array([0x3F808000, 0x3F818000, 0xBF808000], np.uint32).view(np.float32)])
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(inputs.round_to_bf16_bits(x), want)
+    back = inputs.bf16_bits_to_f32(want)
+    np.testing.assert_array_equal(back, torch.from_numpy(want.view(np.int16)).view(torch.bfloat16).float().numpy())
+
+
+def test_inputs_deterministic_and_shaped():
+    a = inputs.make_inputs(300, 64, 128, 200, t=2, rank=1, v_global=400, bias=True)
+    b = inputs.make_inputs(300, 64, 128, 200, t=2, rank=1, v_global=400, bias=True)
+    for k in ("X", "A", "B", "E", "dZ", "targets", "b1"):
+        np.testing.assert_array_equal(a[k], b[k])
+    assert a["X"].shape == (300, 64) and a["A"].shape == (64, 128) and a["B"].shape == (128, 64)
+    assert a["E"].shape == (64, 200) and a["dZ"].shape == (300, 64) and a["b1"].shape == (128,)
+    assert a["X"].dtype == np.uint16 and a["targets"].dtype == np.int64
+    assert a["targets"].min() >= 0 and a["targets"].max() < 400 and int(a["vocab_start"]) == 200
+    c = inputs.make_inputs(300, 64, 128, 200, t=2, rank=0, v_global=400)
+    assert not np.array_equal(a["E"], c["E"])        # ranks draw different shards
+    np.testing.assert_array_equal(a["X"], c["X"])    # activations are replicated
+
+
+def test_inputs_distribution():
+    d = inputs.make_inputs(4096, 256, 512, 64, sigma_w=0.02, want=("X", "A"))
+    x = inputs.bf16_bits_to_f32(d["X"]).astype(np.float64)
+    a = inputs.bf16_bits_to_f32(d["A"]).astype(np.float64)
+    assert abs(x.mean()) < 0.01 and abs(x.std() - 1) < 0.01
+    assert abs(a.std() - 0.02) < 0.0005
+
+
+def test_config_table():
+    c = inputs.CONFIGS
+    assert [c[k].t for k in inputs.CONFIG_ORDER] == [1, 1, 8, 4, 4]
+    assert c["gpt_8p3b_t8"].v_i * 8 == c["gpt_8p3b_t8"].v_global
+    assert c["bert_3p9b_t4"].v_i * 4 == c["bert_3p9b_t4"].v_global
+    assert c["bloom_176b_t4"].v_i * 4 == c["bloom_176b_t4"].v_global
+    for k in inputs.CONFIG_ORDER:
+        assert c[k].h % 8 == 0 and c[k].f_i % 8 == 0 and c[k].v_i % 8 == 0
+
+
+def test_sample_indices_include_edges():
+    s = inputs.sample_indices(1000, 50, 7, [0, 255, 256, 999, 5000])
+    assert {0, 255, 256, 999} <= set(s.tolist()) and 5000 not in s and len(s) >= 50
