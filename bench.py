@@ -1,0 +1,192 @@
+"""Benchmark: one step = the whole per-rank hot path on one batch of synthetic input:
+mlp_shard_fwd + mlp_shard_bwd + vocab_ce_shard_fwd + ce_combine.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+Default workload: the GPT-2 1.5B-like full layer (t=1): T = 8*1024 tokens, h = 1600,
+FFN 6400, vocab 50304 (padded).  Inputs are seeded synthetic bf16 tensors, resident
+in HBM before the timed region.  Prints one JSON line.
+
+value = algorithmic TFLOP/s of the whole step: (12*T*h*f_i + 2*T*h*v_i) / step time.
+The MLP fwd+bwd TFLOP/s, the CE tokens/s and their fractions of the bf16 MFMA peak
+are reported alongside.  ``roofline`` covers the dominant kernel (the fused
+logits-GEMM + CE epilogue), timed with HIP events on the launch stream; the
+``cpu_baseline`` leg times the fp64 oracle on a bounded token sample of the same
+workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0
+
+
+def _args():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="gpt2_1p5b")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle CPU time")
+    return p.parse_args()
+
+
+def cpu_baseline(cfg, d, target_s: float):
+    """Time the fp64 oracle (as it stands) on the first Ts tokens of the same inputs:
+    MLP fwd + bwd on Ts tokens and the CE shard + combine on Ts tokens."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    cores = len(os.sched_getaffinity(0))
+
+    def run(Ts):
+        X, dZ, tg = d["X"][:Ts], d["dZ"][:Ts], d["targets"][:Ts]
+        t0 = time.perf_counter()
+        oracle.mlp_shard_fwd(X, d["A"], d["B"])
+        oracle.mlp_shard_bwd(X, d["A"], d["B"], dZ)
+        p = oracle.vocab_ce_shard(X, d["E"], tg, 0)
+        oracle.ce_combine(p["m"], p["s"], p["z"])
+        return time.perf_counter() - t0
+
+    ctx = threadpool_limits(limits=cores) if threadpool_limits else None
+    try:
+        Ts = 64
+        dt = run(Ts)
+        Ts = int(min(cfg.T, max(64, Ts * target_s / max(dt, 1e-3))))
+        Ts -= Ts % 64 if Ts > 64 else 0
+        dt = run(Ts)
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    flop = 12 * Ts * cfg.h * cfg.f_i + 2 * Ts * cfg.h * cfg.v_i
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"numpy fp64 oracle, MLP fwd+bwd + CE shard + combine on the first {Ts} of {cfg.T} "
+                      f"tokens ({flop / 1e9:.1f} GFLOP in {dt:.2f} s)",
+            "seconds": dt}
+
+
+def main():
+    a = _args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported (the multi-GPU exchange "
+              "is not part of this library)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from megatron_tensor_transformer_mlp_amd import build as _b, inputs
+    if not os.path.exists(os.path.join(ROOT, "megatron_tensor_transformer_mlp_amd", "libmshard.so")):
+        _b.build_library(verbose=False)
+    from megatron_tensor_transformer_mlp_amd import mshard
+
+    cfg = inputs.CONFIGS[a.workload]
+    T, h, f, v = cfg.T, cfg.h, cfg.f_i, cfg.v_i
+    d = inputs.make_config_inputs(cfg)
+    dev = torch.device("cuda:0")
+
+    def up(u):
+        return torch.from_numpy(np.ascontiguousarray(u).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    X, A, B, E, dZ = up(d["X"]), up(d["A"]), up(d["B"]), up(d["E"]), up(d["dZ"])
+    tg = torch.from_numpy(d["targets"]).to(dev)
+    bf = torch.bfloat16
+    H = torch.empty((T, f), dtype=bf, device=dev)
+    Y = torch.empty((T, f), dtype=bf, device=dev)
+    Z = torch.empty((T, h), dtype=torch.float32, device=dev)
+    dX = torch.empty((T, h), dtype=torch.float32, device=dev)
+    dA = torch.empty((h, f), dtype=bf, device=dev)
+    dB = torch.empty((f, h), dtype=bf, device=dev)
+    mlp_ws = torch.empty(max(mshard.mlp_shard_workspace_bytes(T, h, f), 1), dtype=torch.uint8, device=dev)
+    ce_ws = torch.empty(max(mshard.vocab_ce_workspace_bytes(T, h, v), 1), dtype=torch.uint8, device=dev)
+    m, s, z = (torch.empty((1, T), dtype=torch.float32, device=dev) for _ in range(3))
+    loss = torch.empty((T,), dtype=torch.float32, device=dev)
+    mean = torch.empty((1,), dtype=torch.float32, device=dev)
+    vstart = int(d["vocab_start"])
+
+    stream = torch.cuda.current_stream(dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def step(events=None):
+        if events is not None:
+            events[0].record(stream)
+        mshard.mlp_shard_fwd(X, A, B, None, out=(H, Y, Z))
+        mshard.mlp_shard_bwd(X, A, B, H, Y, dZ, workspace=mlp_ws, out=(dX, dA, dB, None))
+        if events is not None:
+            events[1].record(stream)
+        mshard.vocab_ce_shard_fwd(X, E, tg, vstart, workspace=ce_ws, out=(m[0], s[0], z[0]))
+        if events is not None:
+            events[2].record(stream)
+        mshard.ce_combine(m, s, z, out=(loss, mean))
+        if events is not None:
+            events[3].record(stream)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[ev() for _ in range(4)] for _ in range(a.steps)]
+    t0 = time.perf_counter()
+    for k in range(a.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms_step = wall * 1e3 / a.steps
+    mlp_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    ce_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    comb_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    mlp_flop, ce_flop = cfg.mlp_flop, cfg.ce_flop
+    value = (mlp_flop + ce_flop) / (ms_step * 1e-3) / 1e12
+    mlp_tflops = mlp_flop / (mlp_ms * 1e-3) / 1e12
+    ce_tflops = ce_flop / (ce_ms * 1e-3) / 1e12
+
+    out = {
+        "metric": "MLP-shard fwd+bwd TFLOP/s + fused vocab-CE tokens/s, % of bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: one rank's MLP shard fwd+bwd + vocab-parallel fused CE + combine, "
+                               f"t={cfg.t}, T={T} tokens, h={h}, f_i={f}, v_i={v}",
+                   "tokens": T, "h": h, "f_i": f, "v_i": v, "t": cfg.t},
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "mlp_fwd_bwd_tflops": round(mlp_tflops, 2),
+        "mlp_pct_of_peak": round(100 * mlp_tflops / PEAK_BF16_TFLOPS, 2),
+        "mlp_ms": round(mlp_ms, 4),
+        "ce_tokens_per_s": round(T / (ce_ms * 1e-3), 1),
+        "ce_tflops": round(ce_tflops, 2),
+        "ce_pct_of_peak": round(100 * ce_tflops / PEAK_BF16_TFLOPS, 2),
+        "ce_ms": round(ce_ms, 4),
+        "ce_combine_ms": round(comb_ms, 4),
+        "roofline": {"bound": "mfma", "kernel": "fused logits GEMM + CE epilogue (vocab_ce_shard_fwd)",
+                     "achieved": round(ce_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ce_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flop_per_launch": ce_flop},
+    }
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, d, a.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

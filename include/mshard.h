@@ -1,0 +1,156 @@
+/*
+ * mshard.h - C ABI of libmshard.so: one tensor-parallel rank's shard of the
+ * transformer MLP block (forward and backward) and of the vocab-parallel output
+ * layer fused with cross-entropy, as hand-written HIP kernels for gfx950.
+ *
+ * The operations are those of the Megatron-LM intra-layer split:
+ *   - Megatron-LM explainer (azimuth.plus/paper/megatron-lm), "core idea:
+ *     slicing the feed-forward network": Y = GeLU(XA), Z = Dropout(YB); A is
+ *     split by columns so each rank applies GeLU to X A_i with no
+ *     synchronisation, B by rows so Y_i B_i is this rank's partial of YB.
+ *   - same page, "the f and g operators": f (before the block) is the identity
+ *     forward and all-reduces the input gradient backward; g (after the block)
+ *     all-reduces the partial outputs forward and is the identity backward.
+ *     This library computes everything between f and g for one rank: it emits
+ *     the partials Z_i and dX_i that g and f would sum.
+ *   - Megatron-LM paper notes (notes.yuuk.io), "vocab-embedding parallelism":
+ *     E_{H x v} is split along the vocabulary, each rank computes its partial
+ *     GEMM X E_i, and the output GEMM is fused with the cross-entropy so only
+ *     b*s values per quantity leave the rank instead of b*s*v logits.
+ *   - Megatron Core bitwise-determinism news item (news.hamidun.com): every
+ *     reduction here runs in a fixed order with private per-writer workspace,
+ *     and no floating-point atomics are used, so repeated calls with the same
+ *     inputs give bitwise-identical outputs.
+ *
+ * Conventions shared by every entry point
+ *   - Matrices are row-major in the pages' math layout: X[T x h], A_i[h x f_i],
+ *     B_i[f_i x h], E_i[h x v_i], dZ[T x h]; T = b*s tokens (the order of b and
+ *     s does not matter: every operation is per token row).
+ *   - bf16 values are passed as raw 16-bit patterns (ms_bf16).  Every GEMM
+ *     multiplies bf16 inputs with fp32 accumulation; bf16 outputs are rounded
+ *     once, to nearest even.
+ *   - All pointers are DEVICE pointers on the current HIP device, except where
+ *     stated.  The caller owns every buffer and the stream; the library never
+ *     allocates, frees or synchronises.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = default stream).
+ *     MS_OK means "validated and enqueued"; device faults surface at the
+ *     caller's next synchronisation, as with any HIP launch.
+ *   - Validation runs first, on the host, without touching device memory.  On
+ *     any error nothing is enqueued, the status is returned, and
+ *     ms_last_error() gives a message.  Checks: required pointers non-NULL;
+ *     T >= 1 and h, f_i, v_i >= 8 and multiples of 8; every buffer and the
+ *     workspace 16-byte aligned; every buffer smaller than 2^31 bytes; no output
+ *     overlapping an input, another output or the workspace; workspace at least
+ *     the size the matching *_workspace_bytes function returns.
+ *   - Preconditions that are not checked: device pointers are valid for the
+ *     sizes given; 0 <= target < v_global; inputs are finite (NaN/Inf simply
+ *     propagate).  Calls that share a workspace must not overlap in time.
+ *   - Determinism: identical inputs, shapes, device model and library build give
+ *     bitwise-identical outputs, whatever the stream, buffer addresses or prior
+ *     workspace contents.
+ */
+#ifndef MSHARD_H
+#define MSHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t ms_bf16; /* raw bf16 bit pattern */
+
+typedef enum {
+  MS_OK = 0,
+  MS_ERR_NULL = 1,      /* a required pointer is NULL */
+  MS_ERR_SHAPE = 2,     /* a size is out of range or not a multiple of 8 */
+  MS_ERR_ALIGN = 3,     /* a buffer is not 16-byte aligned */
+  MS_ERR_ALIAS = 4,     /* an output overlaps an input, another output or the workspace */
+  MS_ERR_WORKSPACE = 5, /* workspace missing or too small */
+  MS_ERR_ENUM = 6,      /* unknown enum value */
+  MS_ERR_HIP = 7        /* a HIP call failed (no gfx950 device, launch failure, ...) */
+} ms_status;
+
+/* GeLU form.  The pages name GeLU without a formula: MS_GELU_ERF is the
+ * definition x * Phi(x); MS_GELU_TANH is the tanh approximation from the GELU
+ * paper (Hendrycks & Gimpel). */
+typedef enum { MS_GELU_ERF = 0, MS_GELU_TANH = 1 } ms_gelu;
+
+/* Bytes of device workspace that mlp_shard_fwd and mlp_shard_bwd need for these
+ * sizes (one number covers both).  Returns 0 for invalid sizes. */
+size_t mlp_shard_workspace_bytes(int64_t T, int64_t h, int64_t f_i);
+
+/* Forward of one rank's MLP shard (explainer, "core idea"; paper notes, "MLP
+ * block split"):
+ *     H_i = X A_i (+ b1_i),   Y_i = GeLU(H_i),   Z_i = Y_i B_i.
+ * Inputs : X[T x h], A_i[h x f_i], B_i[f_i x h] bf16; b1_i[f_i] bf16 or NULL
+ *          (column-sharded bias added before GeLU).
+ * Outputs: H_i[T x f_i] and Y_i[T x f_i] bf16 (saved for the backward; Y_i is
+ *          GeLU of the fp32 pre-activation, then rounded); Z_i[T x h] fp32,
+ *          this rank's partial of YB (g would sum it over ranks; the second
+ *          bias and dropout act after that sum and are not applied here). */
+ms_status mlp_shard_fwd(const ms_bf16* X, const ms_bf16* A_i, const ms_bf16* b1_i, const ms_bf16* B_i,
+                        int64_t T, int64_t h, int64_t f_i, ms_gelu gelu,
+                        ms_bf16* H_i, ms_bf16* Y_i, float* Z_i,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward of one rank's MLP shard, by the chain rule with dZ arriving
+ * unchanged through g's backward (explainer, "the f and g operators"):
+ *     dH_i = (dZ B_i^T) * GeLU'(H_i),   dB_i = Y_i^T dZ,   dA_i = X^T dH_i,
+ *     db1_i = sum over tokens of dH_i,  dX_i = dH_i A_i^T.
+ * Inputs : X[T x h], A_i[h x f_i], B_i[f_i x h], H_i and Y_i[T x f_i] (from the
+ *          forward), dZ[T x h], all bf16.
+ * Outputs: dX_i[T x h] fp32 (this rank's partial; f would all-reduce it);
+ *          dA_i[h x f_i], dB_i[f_i x h] bf16; db1_i[f_i] bf16 or NULL (skip).
+ * Weight-gradient GEMMs may split the token contraction; their partial sums go
+ * to private workspace slices and are added in ascending slice order. */
+ms_status mlp_shard_bwd(const ms_bf16* X, const ms_bf16* A_i, const ms_bf16* B_i,
+                        const ms_bf16* H_i, const ms_bf16* Y_i, const ms_bf16* dZ,
+                        int64_t T, int64_t h, int64_t f_i, ms_gelu gelu,
+                        float* dX_i, ms_bf16* dA_i, ms_bf16* dB_i, ms_bf16* db1_i,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace vocab_ce_shard_fwd needs.  Returns 0 for invalid sizes. */
+size_t vocab_ce_workspace_bytes(int64_t T, int64_t h, int64_t v_i);
+
+/* Vocab-parallel logits GEMM fused with the cross-entropy partials (paper
+ * notes, "vocab-embedding parallelism").  The logits L = X E_i (fp32) are
+ * never written to memory.  Per token t:
+ *     m_i[t] = max_j L[t,j],   s_i[t] = sum_j exp(L[t,j] - m_i[t]),
+ *     z_i[t] = L[t, target[t] - vocab_start] if vocab_start <= target[t] <
+ *              vocab_start + v_i (this rank owns the target), else 0.
+ * Inputs : X[T x h], E_i[h x v_i] bf16; target[T] int64 global vocabulary ids;
+ *          vocab_start = first global id of this shard (>= 0).
+ * Outputs: m_i, s_i, z_i [T] fp32.  Every column of E_i, padded ones included,
+ *          takes part in the softmax. */
+ms_status vocab_ce_shard_fwd(const ms_bf16* X, const ms_bf16* E_i, const int64_t* target,
+                             int64_t T, int64_t h, int64_t v_i, int64_t vocab_start,
+                             float* m_i, float* s_i, float* z_i,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace ce_combine needs (currently 0 for valid sizes). */
+size_t ce_combine_workspace_bytes(int32_t t, int64_t T);
+
+/* Merge the t vocab shards' partials into the loss, in ascending rank order:
+ *     M = max_r m[r][t],  S = sum_r s[r][t] exp(m[r][t] - M),
+ *     loss[t] = ln S + M - sum_r z[r][t],
+ *     loss_mean = (fixed-order pairwise sum of loss) / T.
+ * Inputs : m, s, z fp32, each [t x T] row-major (rank r's vector at offset r*T).
+ * Outputs: loss[T] fp32; loss_mean[1] fp32 or NULL (skip).  t >= 1. */
+ms_status ce_combine(const float* m, const float* s, const float* z, int32_t t, int64_t T,
+                     float* loss, float* loss_mean,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Text for the last non-OK status returned on the calling thread ("" if none).
+ * The pointer stays valid until the next library call on this thread. */
+const char* ms_last_error(void);
+
+/* Library version string (host pointer, static storage). */
+const char* ms_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSHARD_H */

@@ -1,0 +1,215 @@
+// abi.cpp - the extern "C" entry points of libmshard.so declared in mshard.h:
+// host-side validation (no device access), workspace sizing, a one-time check
+// that the current device is a gfx950, then the launch sequences.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "launch.hpp"
+#include "mshard.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ms_status fail(ms_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+struct Buf {
+  const void* p;
+  size_t bytes;
+  const char* name;
+  bool output;
+};
+
+constexpr int64_t kMaxBytes = (int64_t)1 << 31;  // every buffer must be smaller than 2^31 bytes
+
+// a * b * esize in bytes, saturated at 2^62 (dimensions are at most 2^31 - 1 each).
+size_t nbytes(int64_t a, int64_t b, int64_t esize) {
+  const int64_t cap = (int64_t)1 << 62;
+  if (a <= 0 || b <= 0) return 0;
+  if (a > cap / b) return (size_t)cap;
+  const int64_t ab = a * b;
+  if (ab > cap / esize) return (size_t)cap;
+  return (size_t)(ab * esize);
+}
+
+ms_status check_dims(int64_t T, std::initializer_list<std::pair<const char*, int64_t>> dims) {
+  if (T < 1) return fail(MS_ERR_SHAPE, "T must be >= 1 (got %lld)", (long long)T);
+  if (T > INT32_MAX) return fail(MS_ERR_SHAPE, "T too large (%lld)", (long long)T);
+  for (auto& d : dims) {
+    if (d.second < 8 || d.second % 8 != 0)
+      return fail(MS_ERR_SHAPE, "%s must be a positive multiple of 8 (got %lld)", d.first, (long long)d.second);
+    if (d.second > INT32_MAX) return fail(MS_ERR_SHAPE, "%s too large (%lld)", d.first, (long long)d.second);
+  }
+  return MS_OK;
+}
+
+ms_status check_bufs(const std::vector<Buf>& bufs) {
+  for (const Buf& b : bufs) {
+    if (!b.p) return fail(MS_ERR_NULL, "%s is NULL", b.name);
+    if ((int64_t)b.bytes >= kMaxBytes)
+      return fail(MS_ERR_SHAPE, "%s is %zu bytes; each buffer must be < 2^31 bytes", b.name, b.bytes);
+    if (((uintptr_t)b.p & 15) != 0) return fail(MS_ERR_ALIGN, "%s is not 16-byte aligned", b.name);
+  }
+  for (size_t i = 0; i < bufs.size(); ++i) {
+    for (size_t j = i + 1; j < bufs.size(); ++j) {
+      const Buf& a = bufs[i];
+      const Buf& b = bufs[j];
+      if (!a.output && !b.output) continue;  // inputs may share memory
+      const uintptr_t a0 = (uintptr_t)a.p, a1 = a0 + a.bytes;
+      const uintptr_t b0 = (uintptr_t)b.p, b1 = b0 + b.bytes;
+      if (a0 < b1 && b0 < a1) return fail(MS_ERR_ALIAS, "%s overlaps %s", a.name, b.name);
+    }
+  }
+  return MS_OK;
+}
+
+ms_status check_workspace(const void* ws, size_t have, size_t need, std::vector<Buf>& bufs) {
+  if (need == 0) return MS_OK;
+  if (!ws) return fail(MS_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", need);
+  if (have < need) return fail(MS_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", have, need);
+  bufs.push_back(Buf{ws, need, "workspace", true});
+  return MS_OK;
+}
+
+// One-time (per device) check that the current device is a gfx950.
+ms_status check_device() {
+  static std::mutex mu;
+  static std::vector<int> ok_devices;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MS_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(mu);
+  for (int d : ok_devices)
+    if (d == dev) return MS_OK;
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return fail(MS_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(MS_ERR_HIP, "device %d is %s; this library is built for gfx950 only", dev, prop.gcnArchName);
+  ok_devices.push_back(dev);
+  return MS_OK;
+}
+
+ms_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MS_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  g_last_error.clear();
+  return MS_OK;
+}
+
+#define MS_TRY(x)                   \
+  do {                              \
+    ms_status _st = (x);            \
+    if (_st != MS_OK) return _st;   \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+size_t mlp_shard_workspace_bytes(int64_t T, int64_t h, int64_t f_i) {
+  if (check_dims(T, {{"h", h}, {"f_i", f_i}}) != MS_OK) return 0;
+  return mshard::mlp_workspace_layout(T, h, f_i).bytes;
+}
+
+ms_status mlp_shard_fwd(const ms_bf16* X, const ms_bf16* A_i, const ms_bf16* b1_i, const ms_bf16* B_i,
+                        int64_t T, int64_t h, int64_t f_i, ms_gelu gelu, ms_bf16* H_i, ms_bf16* Y_i, float* Z_i,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;  // the forward needs no workspace
+  MS_TRY(check_dims(T, {{"h", h}, {"f_i", f_i}}));
+  if (gelu != MS_GELU_ERF && gelu != MS_GELU_TANH) return fail(MS_ERR_ENUM, "unknown gelu form %d", (int)gelu);
+  std::vector<Buf> bufs = {
+      {X, nbytes(T, h, 2), "X", false},         {A_i, nbytes(h, f_i, 2), "A_i", false},
+      {B_i, nbytes(f_i, h, 2), "B_i", false},   {H_i, nbytes(T, f_i, 2), "H_i", true},
+      {Y_i, nbytes(T, f_i, 2), "Y_i", true},    {Z_i, nbytes(T, h, 4), "Z_i", true}};
+  if (b1_i) bufs.push_back({b1_i, nbytes(f_i, 1, 2), "b1_i", false});
+  MS_TRY(check_bufs(bufs));
+  MS_TRY(check_device());
+  return launched(mshard::launch_mlp_fwd(X, A_i, b1_i, B_i, T, h, f_i, (int)gelu, H_i, Y_i, Z_i,
+                                         (hipStream_t)stream),
+                  "mlp_shard_fwd");
+}
+
+ms_status mlp_shard_bwd(const ms_bf16* X, const ms_bf16* A_i, const ms_bf16* B_i, const ms_bf16* H_i,
+                        const ms_bf16* Y_i, const ms_bf16* dZ, int64_t T, int64_t h, int64_t f_i, ms_gelu gelu,
+                        float* dX_i, ms_bf16* dA_i, ms_bf16* dB_i, ms_bf16* db1_i, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  MS_TRY(check_dims(T, {{"h", h}, {"f_i", f_i}}));
+  if (gelu != MS_GELU_ERF && gelu != MS_GELU_TANH) return fail(MS_ERR_ENUM, "unknown gelu form %d", (int)gelu);
+  std::vector<Buf> bufs = {
+      {X, nbytes(T, h, 2), "X", false},          {A_i, nbytes(h, f_i, 2), "A_i", false},
+      {B_i, nbytes(f_i, h, 2), "B_i", false},    {H_i, nbytes(T, f_i, 2), "H_i", false},
+      {Y_i, nbytes(T, f_i, 2), "Y_i", false},    {dZ, nbytes(T, h, 2), "dZ", false},
+      {dX_i, nbytes(T, h, 4), "dX_i", true},     {dA_i, nbytes(h, f_i, 2), "dA_i", true},
+      {dB_i, nbytes(f_i, h, 2), "dB_i", true}};
+  if (db1_i) bufs.push_back({db1_i, nbytes(f_i, 1, 2), "db1_i", true});
+  MS_TRY(check_workspace(workspace, workspace_bytes, mshard::mlp_workspace_layout(T, h, f_i).bytes, bufs));
+  MS_TRY(check_bufs(bufs));
+  MS_TRY(check_device());
+  return launched(mshard::launch_mlp_bwd(X, A_i, B_i, H_i, Y_i, dZ, T, h, f_i, (int)gelu, dX_i, dA_i, dB_i,
+                                         db1_i, workspace, (hipStream_t)stream),
+                  "mlp_shard_bwd");
+}
+
+size_t vocab_ce_workspace_bytes(int64_t T, int64_t h, int64_t v_i) {
+  if (check_dims(T, {{"h", h}, {"v_i", v_i}}) != MS_OK) return 0;
+  return mshard::ce_workspace_layout(T, v_i).bytes;
+}
+
+ms_status vocab_ce_shard_fwd(const ms_bf16* X, const ms_bf16* E_i, const int64_t* target, int64_t T, int64_t h,
+                             int64_t v_i, int64_t vocab_start, float* m_i, float* s_i, float* z_i,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  MS_TRY(check_dims(T, {{"h", h}, {"v_i", v_i}}));
+  if (vocab_start < 0) return fail(MS_ERR_SHAPE, "vocab_start must be >= 0 (got %lld)", (long long)vocab_start);
+  std::vector<Buf> bufs = {{X, nbytes(T, h, 2), "X", false},     {E_i, nbytes(h, v_i, 2), "E_i", false},
+                           {target, nbytes(T, 1, 8), "target", false}, {m_i, nbytes(T, 1, 4), "m_i", true},
+                           {s_i, nbytes(T, 1, 4), "s_i", true},       {z_i, nbytes(T, 1, 4), "z_i", true}};
+  MS_TRY(check_workspace(workspace, workspace_bytes, mshard::ce_workspace_layout(T, v_i).bytes, bufs));
+  MS_TRY(check_bufs(bufs));
+  MS_TRY(check_device());
+  return launched(mshard::launch_vocab_ce(X, E_i, target, T, h, v_i, vocab_start, m_i, s_i, z_i, workspace,
+                                          (hipStream_t)stream),
+                  "vocab_ce_shard_fwd");
+}
+
+size_t ce_combine_workspace_bytes(int32_t t, int64_t T) {
+  (void)t;
+  (void)T;
+  return 0;
+}
+
+ms_status ce_combine(const float* m, const float* s, const float* z, int32_t t, int64_t T, float* loss,
+                     float* loss_mean, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (t < 1) return fail(MS_ERR_SHAPE, "t must be >= 1 (got %d)", (int)t);
+  if (T < 1 || T > INT32_MAX) return fail(MS_ERR_SHAPE, "T out of range (%lld)", (long long)T);
+  std::vector<Buf> bufs = {{m, nbytes(t, T, 4), "m", false},
+                           {s, nbytes(t, T, 4), "s", false},
+                           {z, nbytes(t, T, 4), "z", false},
+                           {loss, nbytes(T, 1, 4), "loss", true}};
+  if (loss_mean) bufs.push_back({loss_mean, 4, "loss_mean", true});
+  MS_TRY(check_bufs(bufs));
+  MS_TRY(check_device());
+  return launched(mshard::launch_ce_combine(m, s, z, t, T, loss, loss_mean, (hipStream_t)stream), "ce_combine");
+}
+
+const char* ms_last_error(void) { return g_last_error.c_str(); }
+
+const char* ms_version(void) { return "mshard 0.1.0 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// launch.hpp - host-side interface between the C ABI layer (abi.cpp) and the
+// kernel launch sequences (kernels.hip).  Arguments reaching these functions
+// have been validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mshard {
+
+struct MlpWorkspace {
+  size_t off_dH;      // bf16 [T x f]: dH, consumed by the dA and dX GEMMs
+  size_t off_db1;     // fp32 [db1_parts x f]: per-writer bias-gradient column sums
+  size_t off_splitk;  // fp32 [S x h*f]: weight-gradient split-K slices
+  size_t bytes;
+  int db1_parts;
+  int splits_dA, splits_dB;
+};
+
+struct CeWorkspace {
+  size_t off_m, off_s, off_z;  // fp32 [parts x T] each
+  size_t bytes;
+  int parts;
+};
+
+int weight_grad_splits(int64_t M, int64_t N, int64_t K);
+MlpWorkspace mlp_workspace_layout(int64_t T, int64_t h, int64_t f);
+CeWorkspace ce_workspace_layout(int64_t T, int64_t v);
+
+hipError_t launch_mlp_fwd(const uint16_t* X, const uint16_t* A, const uint16_t* b1, const uint16_t* B,
+                          int64_t T, int64_t h, int64_t f, int gelu, uint16_t* H, uint16_t* Y, float* Z,
+                          hipStream_t st);
+hipError_t launch_mlp_bwd(const uint16_t* X, const uint16_t* A, const uint16_t* B, const uint16_t* H,
+                          const uint16_t* Y, const uint16_t* dZ, int64_t T, int64_t h, int64_t f, int gelu,
+                          float* dX, uint16_t* dA, uint16_t* dB, uint16_t* db1, void* ws, hipStream_t st);
+hipError_t launch_vocab_ce(const uint16_t* X, const uint16_t* E, const int64_t* target, int64_t T, int64_t h,
+                           int64_t v, int64_t vocab_start, float* m, float* s, float* z, void* ws,
+                           hipStream_t st);
+hipError_t launch_ce_combine(const float* m, const float* s, const float* z, int t, int64_t T, float* loss,
+                             float* loss_mean, hipStream_t st);
+
+}  // namespace mshard

@@ -27,18 +27,23 @@ from typing import Dict, List, Optional
 import numpy as np
 
 STREAMS = ("X", "A", "B", "E", "dZ", "targets", "b1")
-_ROWS_PER_BLOCK = 4096
+_ELEMS_PER_BLOCK = 1 << 24
 
 
 def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """float32 -> bf16 bit pattern (uint16), round-to-nearest-even; NaN kept quiet."""
+    """float32 -> bf16 bit pattern (uint16), round-to-nearest-even; NaN kept quiet.
+
+    For every non-NaN pattern u <= 0xFF800000, u + 0x7FFF + 1 fits in 32 bits.
+    """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    u = x.view(np.uint32)
+    r = u + np.uint32(0x7FFF)
+    r += (u >> np.uint32(16)) & np.uint32(1)
+    r >>= np.uint32(16)
+    r = r.astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
-        r[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)
+        r[nan] = ((u[nan] >> np.uint32(16)) | np.uint32(0x40)).astype(np.uint16)
     return r
 
 
@@ -96,8 +101,9 @@ def _normal_bf16(ss: np.random.SeedSequence, shape, sigma: float) -> np.ndarray:
     rows, cols = (shape[0], int(np.prod(shape[1:]))) if len(shape) > 1 else (1, shape[0])
     out = np.empty((rows, cols), dtype=np.uint16)
     s = np.float32(sigma)
-    for r0 in range(0, rows, _ROWS_PER_BLOCK):
-        r1 = min(rows, r0 + _ROWS_PER_BLOCK)
+    step = max(1, _ELEMS_PER_BLOCK // cols)
+    for r0 in range(0, rows, step):
+        r1 = min(rows, r0 + step)
         out[r0:r1] = round_to_bf16_bits(g.standard_normal((r1 - r0, cols), dtype=np.float32) * s)
     return out.reshape(shape)
 

@@ -1,0 +1,197 @@
+"""Thin ctypes binding over libmshard.so (argument marshalling only).
+
+Every computation runs in the library's HIP kernels; this module only checks
+tensor dtypes/devices, allocates outputs with ``torch.empty`` and passes raw
+device pointers plus the current HIP stream.  If the library is not built the
+import fails loudly; there is no fallback.
+
+Entry points mirror the C ABI in include/mshard.h:
+  mlp_shard_fwd, mlp_shard_bwd, vocab_ce_shard_fwd, ce_combine, plus the
+  workspace-size queries.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libmshard.so")
+
+MS_OK, MS_ERR_NULL, MS_ERR_SHAPE, MS_ERR_ALIGN, MS_ERR_ALIAS, MS_ERR_WORKSPACE, MS_ERR_ENUM, MS_ERR_HIP = range(8)
+STATUS_NAMES = ["MS_OK", "MS_ERR_NULL", "MS_ERR_SHAPE", "MS_ERR_ALIGN", "MS_ERR_ALIAS", "MS_ERR_WORKSPACE",
+                "MS_ERR_ENUM", "MS_ERR_HIP"]
+GELU = {"erf": 0, "tanh": 1}
+
+EXPORTED = ("mlp_shard_workspace_bytes", "mlp_shard_fwd", "mlp_shard_bwd", "vocab_ce_workspace_bytes",
+            "vocab_ce_shard_fwd", "ce_combine_workspace_bytes", "ce_combine", "ms_last_error", "ms_version")
+
+
+class MshardError(RuntimeError):
+    def __init__(self, status: int, func: str, msg: str):
+        name = STATUS_NAMES[status] if 0 <= status < len(STATUS_NAMES) else str(status)
+        super().__init__(f"{func}: {name}: {msg}")
+        self.status = status
+
+
+_vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m megatron_tensor_transformer_mlp_amd.build` "
+                          "(there is no fallback path)")
+    lib = ctypes.CDLL(LIB_PATH)
+    sig = {
+        "mlp_shard_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+        "mlp_shard_fwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_int, _vp, _vp, _vp, _vp,
+                                         _sz, _vp]),
+        "mlp_shard_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_int, _vp, _vp,
+                                         _vp, _vp, _vp, _sz, _vp]),
+        "vocab_ce_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+        "vocab_ce_shard_fwd": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
+        "ce_combine_workspace_bytes": (_sz, [_i32, _i64]),
+        "ce_combine": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i64, _vp, _vp, _vp, _sz, _vp]),
+        "ms_last_error": (ctypes.c_char_p, []),
+        "ms_version": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+LIB = _load()
+
+
+def version() -> str:
+    return LIB.ms_version().decode()
+
+
+def _check(status: int, func: str) -> None:
+    if status != MS_OK:
+        raise MshardError(status, func, LIB.ms_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, name: str, dtype, shape) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def mlp_shard_workspace_bytes(T: int, h: int, f_i: int) -> int:
+    return int(LIB.mlp_shard_workspace_bytes(T, h, f_i))
+
+
+def vocab_ce_workspace_bytes(T: int, h: int, v_i: int) -> int:
+    return int(LIB.vocab_ce_workspace_bytes(T, h, v_i))
+
+
+def ce_combine_workspace_bytes(t: int, T: int) -> int:
+    return int(LIB.ce_combine_workspace_bytes(t, T))
+
+
+def _workspace(nbytes: int, device, given: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return given
+    if given is not None:
+        if given.device != device or given.numel() * given.element_size() < nbytes:
+            raise ValueError(f"workspace must be >= {nbytes} bytes on {device}")
+        return given
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def mlp_shard_fwd(X: torch.Tensor, A_i: torch.Tensor, B_i: torch.Tensor, b1_i: Optional[torch.Tensor] = None,
+                  gelu: str = "erf", out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
+    """(H_i, Y_i, Z_i) = forward of one rank's MLP shard (bf16 H, Y; fp32 partial Z)."""
+    T, h = X.shape
+    f_i = A_i.shape[1]
+    bf = torch.bfloat16
+    _dev(X, "X", bf, (T, h)); _dev(A_i, "A_i", bf, (h, f_i)); _dev(B_i, "B_i", bf, (f_i, h))
+    if b1_i is not None:
+        _dev(b1_i, "b1_i", bf, (f_i,))
+    if out is None:
+        H = torch.empty((T, f_i), dtype=bf, device=X.device)
+        Y = torch.empty((T, f_i), dtype=bf, device=X.device)
+        Z = torch.empty((T, h), dtype=torch.float32, device=X.device)
+    else:
+        H, Y, Z = out
+    st = LIB.mlp_shard_fwd(_ptr(X), _ptr(A_i), _ptr(b1_i), _ptr(B_i), T, h, f_i, GELU[gelu],
+                           _ptr(H), _ptr(Y), _ptr(Z), None, 0, _stream(X.device))
+    _check(st, "mlp_shard_fwd")
+    return H, Y, Z
+
+
+def mlp_shard_bwd(X, A_i, B_i, H_i, Y_i, dZ, gelu: str = "erf", want_db1: bool = False,
+                  workspace: Optional[torch.Tensor] = None, out=None):
+    """(dX_i fp32, dA_i bf16, dB_i bf16, db1_i bf16 or None) = backward of one rank's MLP shard."""
+    T, h = X.shape
+    f_i = A_i.shape[1]
+    bf = torch.bfloat16
+    for t, n, s in ((X, "X", (T, h)), (A_i, "A_i", (h, f_i)), (B_i, "B_i", (f_i, h)), (H_i, "H_i", (T, f_i)),
+                    (Y_i, "Y_i", (T, f_i)), (dZ, "dZ", (T, h))):
+        _dev(t, n, bf, s)
+    if out is None:
+        dX = torch.empty((T, h), dtype=torch.float32, device=X.device)
+        dA = torch.empty((h, f_i), dtype=bf, device=X.device)
+        dB = torch.empty((f_i, h), dtype=bf, device=X.device)
+        db1 = torch.empty((f_i,), dtype=bf, device=X.device) if want_db1 else None
+    else:
+        dX, dA, dB, db1 = out
+    nbytes = mlp_shard_workspace_bytes(T, h, f_i)
+    ws = _workspace(nbytes, X.device, workspace)
+    st = LIB.mlp_shard_bwd(_ptr(X), _ptr(A_i), _ptr(B_i), _ptr(H_i), _ptr(Y_i), _ptr(dZ), T, h, f_i, GELU[gelu],
+                           _ptr(dX), _ptr(dA), _ptr(dB), _ptr(db1), _ptr(ws), nbytes, _stream(X.device))
+    _check(st, "mlp_shard_bwd")
+    return dX, dA, dB, db1
+
+
+def vocab_ce_shard_fwd(X, E_i, target, vocab_start: int, workspace: Optional[torch.Tensor] = None, out=None):
+    """(m_i, s_i, z_i) fp32 [T] = this rank's fused logits-GEMM + CE partials."""
+    T, h = X.shape
+    v_i = E_i.shape[1]
+    _dev(X, "X", torch.bfloat16, (T, h)); _dev(E_i, "E_i", torch.bfloat16, (h, v_i))
+    _dev(target, "target", torch.int64, (T,))
+    if out is None:
+        m, s, z = (torch.empty((T,), dtype=torch.float32, device=X.device) for _ in range(3))
+    else:
+        m, s, z = out
+    nbytes = vocab_ce_workspace_bytes(T, h, v_i)
+    ws = _workspace(nbytes, X.device, workspace)
+    st = LIB.vocab_ce_shard_fwd(_ptr(X), _ptr(E_i), _ptr(target), T, h, v_i, int(vocab_start), _ptr(m), _ptr(s),
+                                _ptr(z), _ptr(ws), nbytes, _stream(X.device))
+    _check(st, "vocab_ce_shard_fwd")
+    return m, s, z
+
+
+def ce_combine(m: torch.Tensor, s: torch.Tensor, z: torch.Tensor, want_mean: bool = True, out=None):
+    """(loss [T] fp32, mean [1] fp32 or None) from [t, T] shard partials in rank order."""
+    t, T = m.shape
+    for x, n in ((m, "m"), (s, "s"), (z, "z")):
+        _dev(x, n, torch.float32, (t, T))
+    if out is None:
+        loss = torch.empty((T,), dtype=torch.float32, device=m.device)
+        mean = torch.empty((1,), dtype=torch.float32, device=m.device) if want_mean else None
+    else:
+        loss, mean = out
+    st = LIB.ce_combine(_ptr(m), _ptr(s), _ptr(z), t, T, _ptr(loss), _ptr(mean), None, 0, _stream(m.device))
+    _check(st, "ce_combine")
+    return loss, mean

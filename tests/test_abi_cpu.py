@@ -1,0 +1,128 @@
+"""The C ABI on the host: the library loads, exports every symbol the header
+declares, sizes workspaces, and rejects bad arguments before touching a device.
+
+Every call here fails validation, which runs before any HIP call, so these
+tests never launch a kernel (fake pointers are never dereferenced).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mshard.h")
+
+
+@pytest.fixture(scope="module")
+def ms():
+    from megatron_tensor_transformer_mlp_amd import build, mshard
+    if not os.path.exists(mshard.LIB_PATH):
+        build.build_library(verbose=False)
+    return mshard
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined", "sizeof"})
+
+
+def test_exports_every_declared_symbol(ms):
+    declared = _declared_functions()
+    assert set(declared) == set(ms.EXPORTED)
+    lib = ctypes.CDLL(ms.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert "gfx950" in ms.version()
+
+
+def test_workspace_sizes(ms):
+    assert ms.mlp_shard_workspace_bytes(64, 64, 256) >= 64 * 256 * 2
+    assert ms.mlp_shard_workspace_bytes(0, 64, 256) == 0
+    assert ms.mlp_shard_workspace_bytes(64, 60, 256) == 0
+    assert ms.vocab_ce_workspace_bytes(8192, 1600, 50304) >= 3 * 8192 * 4
+    assert ms.vocab_ce_workspace_bytes(8192, 1600, 50300) == 0
+    assert ms.ce_combine_workspace_bytes(4, 8192) == 0
+    # weight-gradient split-K slices appear only for small tile grids
+    assert ms.mlp_shard_workspace_bytes(8192, 3072, 1536) > 8192 * 1536 * 2 + 3072 * 1536 * 4
+
+
+FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced
+
+
+def _fwd(ms, X=FAKE, A=FAKE + (1 << 30), b1=None, B=FAKE + (2 << 30), T=64, h=64, f=256, gelu=0,
+         H=FAKE + (3 << 30), Y=FAKE + (4 << 30), Z=FAKE + (5 << 30)):
+    return ms.LIB.mlp_shard_fwd(X, A, b1, B, T, h, f, gelu, H, Y, Z, None, 0, None)
+
+
+def test_fwd_validation(ms):
+    assert _fwd(ms, X=None) == ms.MS_ERR_NULL
+    assert "X is NULL" in ms.LIB.ms_last_error().decode()
+    assert _fwd(ms, h=60) == ms.MS_ERR_SHAPE
+    assert _fwd(ms, T=0) == ms.MS_ERR_SHAPE
+    assert _fwd(ms, f=0) == ms.MS_ERR_SHAPE
+    assert _fwd(ms, gelu=7) == ms.MS_ERR_ENUM
+    assert _fwd(ms, A=FAKE + (1 << 30) + 8) == ms.MS_ERR_ALIGN
+    assert _fwd(ms, Y=FAKE + (3 << 30) + 64) == ms.MS_ERR_ALIAS       # Y overlaps H
+    assert _fwd(ms, Z=FAKE + 16) == ms.MS_ERR_ALIAS                   # output overlaps input X
+    assert _fwd(ms, T=1 << 20, h=1 << 12) == ms.MS_ERR_SHAPE          # X would be >= 2^31 bytes... 8 GiB
+    assert "2^31" in ms.LIB.ms_last_error().decode()
+
+
+def test_bwd_validation(ms):
+    T, h, f = 64, 64, 256
+    need = ms.mlp_shard_workspace_bytes(T, h, f)
+    p = [FAKE + (i << 30) for i in range(12)]
+
+    def bwd(ws=p[10], nbytes=need, dA=p[7], db1=None, gelu=0):
+        return ms.LIB.mlp_shard_bwd(p[0], p[1], p[2], p[3], p[4], p[5], T, h, f, gelu, p[6], dA, p[8], db1,
+                                    ws, nbytes, None)
+
+    assert bwd(ws=None) == ms.MS_ERR_WORKSPACE
+    assert bwd(nbytes=need - 1) == ms.MS_ERR_WORKSPACE
+    assert bwd(dA=p[3]) == ms.MS_ERR_ALIAS            # dA_i on top of the saved H_i
+    assert bwd(db1=p[10] + 256) == ms.MS_ERR_ALIAS    # db1 inside the workspace
+    assert bwd(gelu=-1) == ms.MS_ERR_ENUM
+
+
+def test_ce_validation(ms):
+    T, h, v = 128, 64, 512
+    need = ms.vocab_ce_workspace_bytes(T, h, v)
+    p = [FAKE + (i << 30) for i in range(8)]
+
+    def ce(v_=v, start=0, ws=p[6], nbytes=need, tgt=p[2], z=p[5]):
+        return ms.LIB.vocab_ce_shard_fwd(p[0], p[1], tgt, T, h, v_, start, p[3], p[4], z, ws, nbytes, None)
+
+    assert ce(v_=500) == ms.MS_ERR_SHAPE
+    assert ce(start=-1) == ms.MS_ERR_SHAPE
+    assert ce(ws=None) == ms.MS_ERR_WORKSPACE
+    assert ce(tgt=None) == ms.MS_ERR_NULL
+    assert ce(z=p[4] + 16) == ms.MS_ERR_ALIAS
+
+
+def test_combine_validation(ms):
+    p = [FAKE + (i << 30) for i in range(5)]
+    assert ms.LIB.ce_combine(p[0], p[1], p[2], 0, 16, p[3], p[4], None, 0, None) == ms.MS_ERR_SHAPE
+    assert ms.LIB.ce_combine(p[0], p[1], p[2], 2, 0, p[3], p[4], None, 0, None) == ms.MS_ERR_SHAPE
+    assert ms.LIB.ce_combine(p[0], p[1], p[2], 2, 16, p[0] + 64, p[4], None, 0, None) == ms.MS_ERR_ALIAS
+    assert ms.LIB.ce_combine(p[0], None, p[2], 2, 16, p[3], p[4], None, 0, None) == ms.MS_ERR_NULL
+
+
+def test_no_float_atomics_in_kernel_sources():
+    """Determinism by construction: no atomics anywhere in the kernel sources."""
+    csrc = os.path.join(ROOT, "megatron_tensor_transformer_mlp_amd", "csrc")
+    for fn in os.listdir(csrc):
+        text = open(os.path.join(csrc, fn)).read()
+        code = re.sub(r"//[^\n]*|/\*.*?\*/", "", text, flags=re.S)   # comments may say "no atomics"
+        assert not re.search(r"atomic", code, flags=re.I), fn
+
+
+def test_binding_has_no_fallback():
+    """The product path imports the HIP library and nothing from the oracle."""
+    pkg = os.path.join(ROOT, "megatron_tensor_transformer_mlp_amd")
+    for fn in os.listdir(pkg):
+        if fn.endswith(".py"):
+            text = open(os.path.join(pkg, fn)).read()
+            assert not re.search(r"^\s*(from|import)\s+oracle", text, flags=re.M), fn
+            assert "sys.path" not in text, fn
