@@ -1,9 +1,18 @@
 // epilogues.hpp - what each GEMM does with its fp32 accumulators.
 //
-// Accumulator element acc[mi][ni][r] of wave (wm, wn) in the tile at (m0, n0)
-// is C[m0 + wm*128 + mi*16 + (lane & 15)][n0 + wn*128 + ni*16 + (lane >> 4)*4 + r].
-// N is a multiple of 8, so each lane's 4-column group is entirely inside or
-// entirely outside the matrix; rows are masked one by one.
+// Accumulator element acc[mi][ni][4g + r] of wave (wm, wn) in the tile at
+// (m0, n0) is C[m0 + wm*128 + mi*32 + (lane & 31)]
+//              [n0 + wn*128 + ni*32 + 8g + 4*(lane >> 5) + r],   g, r = 0..3.
+//
+// Epilogues hand the accumulators over through LDS: each wave writes its
+// 128 x 128 fp32 sub-tile, 64 rows at a time, into a private 32 KiB region
+// (row pitch 512 bytes, 16-byte chunk q of row r at slot q ^ (r & 7), so 8
+// consecutive rows of one chunk hit distinct banks), then reads it back in a
+// row-major lane order.  The accumulators are therefore only ever stored,
+// which keeps them in the accumulation registers through the main loop, and
+// global stores become full 256/512-byte row segments.  N is a multiple of 8,
+// so every 4-column group is entirely inside or outside the matrix; rows are
+// masked one by one.
 #pragma once
 
 #include "gemm_core.hpp"
@@ -44,8 +53,60 @@ __device__ __forceinline__ float gelu_grad_f(float x) {
   }
 }
 
-__device__ __forceinline__ int epi_row(const EpiCtx& c, int mi) { return c.wm * kWaveM + mi * 16 + (c.lane & 15); }
-__device__ __forceinline__ int epi_col(const EpiCtx& c, int ni) { return c.wn * kWaveN + ni * 16 + (c.lane >> 4) * 4; }
+// ---------------------------------------------------------------------------
+// LDS hand-over of the accumulators
+
+__device__ __forceinline__ char* epi_region(const EpiCtx& c) {
+  const int wave = c.wm * 2 + c.wn;
+  return (wave < 2 ? c.lds0 : c.lds1) + (wave & 1) * 32768;
+}
+
+__device__ __forceinline__ int epi_slot(int lr, int q) { return lr * 512 + ((q ^ (lr & 7)) << 4); }
+
+// Write rows [64h, 64h + 64) of the wave's sub-tile (row blocks mi = 2h, 2h+1).
+__device__ __forceinline__ void epi_stage_half(const f32x16_t (&acc)[kSubM][kSubN], char* region, int h,
+                                               int lane) {
+  if (h == 0) acc_settle();
+#pragma unroll
+  for (int m2 = 0; m2 < 2; ++m2) {
+    const int lr = m2 * 32 + (lane & 31);
+#pragma unroll
+    for (int ni = 0; ni < kSubN; ++ni)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int q = ni * 8 + 2 * g + (lane >> 5);
+        const f32x16_t& a = acc[2 * h + m2][ni];
+        acc_store_lds(region + epi_slot(lr, q), f32x4_t{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]});
+      }
+  }
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Local row lr (0..63) of the staged half, columns 4q .. 4q+3 (q = 0..31).
+__device__ __forceinline__ f32x4_t epi_read(const char* region, int lr, int q) {
+  return *(const f32x4_t*)(region + epi_slot(lr, q));
+}
+
+// Row-major walk of the staged sub-tile: calls f(row, col, v) with tile-local
+// row/col of 4 consecutive values; 32 lanes cover one 128-column row.
+template <class F>
+__device__ __forceinline__ void epi_rows(const f32x16_t (&acc)[kSubM][kSubN], const EpiCtx& c, F&& f) {
+  char* region = epi_region(c);
+  const int q = c.lane & 31;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    epi_stage_half(acc, region, h, c.lane);  // h must be a constant: acc is indexed by it
+#pragma unroll 1
+    for (int it = 0; it < 32; ++it) {
+      const int lr = it * 2 + (c.lane >> 5);
+      f(c.wm * kWaveM + h * 64 + lr, c.wn * kWaveN + q * 4, epi_read(region, lr, q));
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// ---------------------------------------------------------------------------
 
 // fp32 store of C (optionally into split slice `split` of a workspace).
 struct EpiStoreF32 {
@@ -53,21 +114,14 @@ struct EpiStoreF32 {
   int64_t ld;
   int M, N;
   int64_t split_stride;  // elements between split slices (0 when splits == 1)
-  __device__ void operator()(f32x4_t (&acc)[kSubM][kSubN], const EpiCtx& c) const {
+  __device__ void operator()(f32x16_t (&acc)[kSubM][kSubN], const EpiCtx& c) const {
     const int64_t base = (int64_t)c.split * split_stride + (int64_t)c.m0 * ld + c.n0;
     const rsrc_t rs = make_rsrc(C + base, ((int64_t)c.split * split_stride + (int64_t)M * ld - base) * 4);
-#pragma unroll
-    for (int ni = 0; ni < kSubN; ++ni) {
-      const int cl = epi_col(c, ni);
-      const bool cok = c.n0 + cl < N;
-#pragma unroll
-      for (int mi = 0; mi < kSubM; ++mi) {
-        const int rl = epi_row(c, mi);
-        const bool ok = cok && (c.m0 + rl) < M;
-        const uint32_t off = ok ? (uint32_t)(((int64_t)rl * ld + cl) * 4) : kOOB;
-        buf_store16(__builtin_bit_cast(u32x4_t, acc[mi][ni]), rs, off);
-      }
-    }
+    const int mrem = M - c.m0, nrem = N - c.n0;
+    epi_rows(acc, c, [&](int rl, int cl, f32x4_t v) {
+      const bool ok = rl < mrem && cl < nrem;
+      buf_store16(__builtin_bit_cast(u32x4_t, v), rs, ok ? (uint32_t)(((int64_t)rl * ld + cl) * 4) : kOOB);
+    });
   }
 };
 
@@ -76,22 +130,15 @@ struct EpiStoreBF16 {
   uint16_t* C;
   int64_t ld;
   int M, N;
-  __device__ void operator()(f32x4_t (&acc)[kSubM][kSubN], const EpiCtx& c) const {
+  __device__ void operator()(f32x16_t (&acc)[kSubM][kSubN], const EpiCtx& c) const {
     const int64_t base = (int64_t)c.m0 * ld + c.n0;
     const rsrc_t rs = make_rsrc(C + base, ((int64_t)M * ld - base) * 2);
-#pragma unroll
-    for (int ni = 0; ni < kSubN; ++ni) {
-      const int cl = epi_col(c, ni);
-      const bool cok = c.n0 + cl < N;
-#pragma unroll
-      for (int mi = 0; mi < kSubM; ++mi) {
-        const int rl = epi_row(c, mi);
-        const bool ok = cok && (c.m0 + rl) < M;
-        const uint32_t off = ok ? (uint32_t)(((int64_t)rl * ld + cl) * 2) : kOOB;
-        const f32x4_t v = acc[mi][ni];
-        buf_store8(u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}, rs, off);
-      }
-    }
+    const int mrem = M - c.m0, nrem = N - c.n0;
+    epi_rows(acc, c, [&](int rl, int cl, f32x4_t v) {
+      const bool ok = rl < mrem && cl < nrem;
+      buf_store8(u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}, rs,
+                 ok ? (uint32_t)(((int64_t)rl * ld + cl) * 2) : kOOB);
+    });
   }
 };
 
@@ -104,33 +151,29 @@ struct EpiGeluFwd {
   const uint16_t* b1;  // may be null: its resource is then empty and reads give 0
   int64_t ld;
   int M, N;
-  __device__ void operator()(f32x4_t (&acc)[kSubM][kSubN], const EpiCtx& c) const {
+  __device__ void operator()(f32x16_t (&acc)[kSubM][kSubN], const EpiCtx& c) const {
     const int64_t base = (int64_t)c.m0 * ld + c.n0;
     const int64_t bytes = ((int64_t)M * ld - base) * 2;
     const rsrc_t rh = make_rsrc(H + base, bytes);
     const rsrc_t ry = make_rsrc(Y + base, bytes);
+    const int mrem = M - c.m0, nrem = N - c.n0;
+    // this lane always owns the same 4 columns: load their bias once
+    const int col = c.n0 + c.wn * kWaveN + (c.lane & 31) * 4;
     const rsrc_t rb = make_rsrc(b1, b1 ? (int64_t)N * 2 : 0);
+    const u32x2_t bb = buf_load8(rb, col < N ? (uint32_t)col * 2u : kOOB);
+    const float bv[4] = {bf16_lo(bb[0]), bf16_hi(bb[0]), bf16_lo(bb[1]), bf16_hi(bb[1])};
+    epi_rows(acc, c, [&](int rl, int cl, f32x4_t v) {
+      const bool ok = rl < mrem && cl < nrem;
+      const uint32_t off = ok ? (uint32_t)(((int64_t)rl * ld + cl) * 2) : kOOB;
+      float hv[4], yv[4];
 #pragma unroll
-    for (int ni = 0; ni < kSubN; ++ni) {
-      const int cl = epi_col(c, ni);
-      const bool cok = c.n0 + cl < N;
-      const u32x2_t bb = buf_load8(rb, cok ? (uint32_t)((c.n0 + cl) * 2) : kOOB);
-      const float bias[4] = {bf16_lo(bb[0]), bf16_hi(bb[0]), bf16_lo(bb[1]), bf16_hi(bb[1])};
-#pragma unroll
-      for (int mi = 0; mi < kSubM; ++mi) {
-        const int rl = epi_row(c, mi);
-        const bool ok = cok && (c.m0 + rl) < M;
-        const uint32_t off = ok ? (uint32_t)(((int64_t)rl * ld + cl) * 2) : kOOB;
-        float hv[4], yv[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          hv[r] = acc[mi][ni][r] + bias[r];
-          yv[r] = gelu_f<FORM>(hv[r]);
-        }
-        buf_store8(u32x2_t{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])}, rh, off);
-        buf_store8(u32x2_t{pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3])}, ry, off);
+      for (int r = 0; r < 4; ++r) {
+        hv[r] = v[r] + bv[r];
+        yv[r] = gelu_f<FORM>(hv[r]);
       }
-    }
+      buf_store8(u32x2_t{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])}, rh, off);
+      buf_store8(u32x2_t{pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3])}, ry, off);
+    });
   }
 };
 
@@ -144,51 +187,66 @@ struct EpiDGelu {
   float* db1_part;
   int64_t ld;
   int M, N;
-  __device__ void operator()(f32x4_t (&acc)[kSubM][kSubN], const EpiCtx& c) const {
+  __device__ void operator()(f32x16_t (&acc)[kSubM][kSubN], const EpiCtx& c) const {
     const int64_t base = (int64_t)c.m0 * ld + c.n0;
     const int64_t bytes = ((int64_t)M * ld - base) * 2;
     const rsrc_t rh = make_rsrc(H + base, bytes);
     const rsrc_t rd = make_rsrc(dH + base, bytes);
+    const int mrem = M - c.m0, nrem = N - c.n0;
+    char* region = epi_region(c);
+    const int q = c.lane & 31;
+    const int cl = c.wn * kWaveN + q * 4;
+    float csum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ni = 0; ni < kSubN; ++ni) {
-      const int cl = epi_col(c, ni);
-      const bool cok = c.n0 + cl < N;
-      float csum[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < 2; ++h) {
+      epi_stage_half(acc, region, h, c.lane);  // h must be a constant: acc is indexed by it
+#pragma unroll 1
+      for (int it0 = 0; it0 < 32; it0 += 8) {
+        // 8 rows' H values first (independent loads in flight together)
+        u32x2_t hh[8];
 #pragma unroll
-      for (int mi = 0; mi < kSubM; ++mi) {
-        const int rl = epi_row(c, mi);
-        const bool ok = cok && (c.m0 + rl) < M;
-        const uint32_t off = ok ? (uint32_t)(((int64_t)rl * ld + cl) * 2) : kOOB;
-        const u32x2_t hh = buf_load8(rh, off);
-        const float hv[4] = {bf16_lo(hh[0]), bf16_hi(hh[0]), bf16_lo(hh[1]), bf16_hi(hh[1])};
-        float dv[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          dv[r] = ok ? acc[mi][ni][r] * gelu_grad_f<FORM>(hv[r]) : 0.0f;
-          csum[r] += dv[r];
+        for (int u = 0; u < 8; ++u) {
+          const int rl = c.wm * kWaveM + h * 64 + (it0 + u) * 2 + (c.lane >> 5);
+          const bool ok = rl < mrem && cl < nrem;
+          hh[u] = buf_load8(rh, ok ? (uint32_t)(((int64_t)rl * ld + cl) * 2) : kOOB);
         }
-        buf_store8(u32x2_t{pack_bf16x2(dv[0], dv[1]), pack_bf16x2(dv[2], dv[3])}, rd, off);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int lr = (it0 + u) * 2 + (c.lane >> 5);
+          const int rl = c.wm * kWaveM + h * 64 + lr;
+          const bool ok = rl < mrem && cl < nrem;
+          const f32x4_t v = epi_read(region, lr, q);
+          const float hv[4] = {bf16_lo(hh[u][0]), bf16_hi(hh[u][0]), bf16_lo(hh[u][1]), bf16_hi(hh[u][1])};
+          float dv[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            dv[r] = ok ? v[r] * gelu_grad_f<FORM>(hv[r]) : 0.0f;
+            csum[r] += dv[r];
+          }
+          buf_store8(u32x2_t{pack_bf16x2(dv[0], dv[1]), pack_bf16x2(dv[2], dv[3])}, rd,
+                     ok ? (uint32_t)(((int64_t)rl * ld + cl) * 2) : kOOB);
+        }
       }
-      if (db1_part) {
+      __builtin_amdgcn_wave_barrier();
+    }
+    if (db1_part) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-#pragma unroll
-          for (int sh = 1; sh < 16; sh <<= 1) csum[r] += __shfl_xor(csum[r], sh, 64);
-        }
-        if ((c.lane & 15) == 0 && cok) {
-          const int64_t slot = (int64_t)(c.tm * 2 + c.wm) * N + c.n0 + cl;
-          *(f32x4_t*)(db1_part + slot) = f32x4_t{csum[0], csum[1], csum[2], csum[3]};
-        }
+      for (int r = 0; r < 4; ++r) csum[r] += __shfl_xor(csum[r], 32, 64);
+      if ((c.lane >> 5) == 0 && cl < nrem) {
+        const int64_t slot = (int64_t)(c.tm * 2 + c.wm) * N + c.n0 + cl;
+        *(f32x4_t*)(db1_part + slot) = f32x4_t{csum[0], csum[1], csum[2], csum[3]};
       }
     }
   }
 };
 
-// Fused cross-entropy epilogue of the logits GEMM L = X E_i.  Per token row and
-// per wave (128 columns), writes the partial triple
-//   pm = max over the wave's valid columns, ps = sum exp(L - pm),
-//   pz = L at the target column if it lies in these columns, else 0
-// to partial slot p = tile_n*2 + wn of arrays laid out [P][T].
+// Fused cross-entropy epilogue of the logits GEMM L = X E_i.  Per token row of
+// the tile, computes over the tile's valid columns
+//   pm = max L,  ps = sum exp(L - pm),  pz = L at the target column if it lies
+//   in this tile, else 0,
+// each wave over its 128 columns with one row per lane (no cross-lane
+// reduction), then the two column-waves are merged in LDS in fixed order; the
+// triple goes to partial slot tile_n of arrays laid out [tiles_n][T].
 struct EpiCE {
   const int64_t* target;
   int64_t vocab_start;
@@ -196,46 +254,87 @@ struct EpiCE {
   float* ps;
   float* pz;
   int M, N;  // M = T tokens, N = v_i
-  __device__ void operator()(f32x4_t (&acc)[kSubM][kSubN], const EpiCtx& c) const {
-    const int p = c.tn * 2 + c.wn;
+  __device__ void operator()(f32x16_t (&acc)[kSubM][kSubN], const EpiCtx& c) const {
     const rsrc_t rt = make_rsrc(target, (int64_t)M * 8);
+    char* region = epi_region(c);
+    const int ncol = min(N - c.n0 - c.wn * kWaveN, kWaveN);  // valid columns of this wave (may be <= 0)
+    float rm[2], rs[2], rz[2];
 #pragma unroll
-    for (int mi = 0; mi < kSubM; ++mi) {
-      const int row = c.m0 + epi_row(c, mi);
-      const bool rok = row < M;
-      const u32x2_t tw = buf_load8(rt, rok ? (uint32_t)row * 8u : kOOB);
-      const int64_t tgt = (int64_t)(((uint64_t)tw[1] << 32) | tw[0]) - vocab_start;
-      float mx = -INFINITY;
+    for (int h = 0; h < 2; ++h) {
+      const int row = c.m0 + c.wm * kWaveM + h * 64 + c.lane;
+      const u32x2_t tw = buf_load8(rt, row < M ? (uint32_t)row * 8u : kOOB);
+      const int64_t tgt = (int64_t)(((uint64_t)tw[1] << 32) | tw[0]) - vocab_start - (c.n0 + c.wn * kWaveN);
+      epi_stage_half(acc, region, h, c.lane);
+      // the row in two 64-column chunks, merged by log-sum-exp in fixed order
+      float mx = -INFINITY, sm = 0.f, zz = 0.f;
+#pragma unroll 1
+      for (int ch = 0; ch < 2; ++ch) {
+        float v[64];
 #pragma unroll
-      for (int ni = 0; ni < kSubN; ++ni) {
-        const bool cok = c.n0 + epi_col(c, ni) < N;
+        for (int q = 0; q < 16; ++q) {
+          const f32x4_t x = epi_read(region, c.lane, ch * 16 + q);
+          v[4 * q] = x[0];
+          v[4 * q + 1] = x[1];
+          v[4 * q + 2] = x[2];
+          v[4 * q + 3] = x[3];
+        }
+        const int nv = ncol - ch * 64;  // valid columns in this chunk (may be <= 0)
+        float cm = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) mx = cok ? fmaxf(mx, acc[mi][ni][r]) : mx;
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mxl = mx * kLog2e;
-      float sm = 0.f, zz = 0.f;
+        for (int j2 = 0; j2 < 64; ++j2) cm = j2 < nv ? fmaxf(cm, v[j2]) : cm;
+        const float cml = cm * kLog2e;
+        float cs = 0.f;
 #pragma unroll
-      for (int ni = 0; ni < kSubN; ++ni) {
-        const int col = c.n0 + epi_col(c, ni);
-        const bool cok = col < N;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float v = acc[mi][ni][r];
-          sm += cok ? __builtin_amdgcn_exp2f(__builtin_fmaf(v, kLog2e, -mxl)) : 0.f;
-          zz = ((int64_t)(col + r) == tgt) ? v : zz;
+        for (int j2 = 0; j2 < 64; ++j2) {
+          cs += j2 < nv ? __builtin_amdgcn_exp2f(__builtin_fmaf(v[j2], kLog2e, -cml)) : 0.f;
+          zz = (j2 < nv && (int64_t)(ch * 64 + j2) == tgt) ? v[j2] : zz;
+        }
+        if (cs > 0.f) {
+          if (!(sm > 0.f)) {
+            mx = cm;
+            sm = cs;
+          } else {
+            const float mm = fmaxf(mx, cm);
+            sm = sm * __builtin_amdgcn_exp2f((mx - mm) * kLog2e) + cs * __builtin_amdgcn_exp2f((cm - mm) * kLog2e);
+            mx = mm;
+          }
         }
       }
-      sm += __shfl_xor(sm, 16, 64);
-      sm += __shfl_xor(sm, 32, 64);
-      zz += __shfl_xor(zz, 16, 64);
-      zz += __shfl_xor(zz, 32, 64);
-      if ((c.lane >> 4) == 0 && rok) {
-        const int64_t o = (int64_t)p * M + row;
-        pm[o] = mx;
-        ps[o] = sm;
-        pz[o] = zz;
+      rm[h] = mx;
+      rs[h] = sm;
+      rz[h] = zz;
+      __builtin_amdgcn_wave_barrier();
+    }
+    // merge the two column-waves of each row: wn = 1 hands its triples to
+    // wn = 0 through LDS (1.5 KiB per row block, after every wave is done
+    // with its staging region).
+    __syncthreads();
+    float* xch = (float*)c.lds0;  // [wm][h][64 lanes][3]
+    if (c.wn == 1) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float* e = xch + ((c.wm * 2 + h) * 64 + c.lane) * 3;
+        e[0] = rm[h];
+        e[1] = rs[h];
+        e[2] = rz[h];
+      }
+    }
+    __syncthreads();
+    if (c.wn == 0) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int row = c.m0 + c.wm * kWaveM + h * 64 + c.lane;
+        if (row < M) {
+          const float* e = xch + ((c.wm * 2 + h) * 64 + c.lane) * 3;
+          const float m1 = e[0], s1 = e[1], z1 = e[2];
+          const float mm = fmaxf(rm[h], m1);
+          const float s0 = rs[h] > 0.f ? rs[h] * __builtin_amdgcn_exp2f((rm[h] - mm) * kLog2e) : 0.f;
+          const float s1m = s1 > 0.f ? s1 * __builtin_amdgcn_exp2f((m1 - mm) * kLog2e) : 0.f;
+          const int64_t o = (int64_t)c.tn * M + row;
+          pm[o] = mm;
+          ps[o] = s0 + s1m;
+          pz[o] = rz[h] + z1;
+        }
       }
     }
   }

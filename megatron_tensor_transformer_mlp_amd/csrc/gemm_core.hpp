@@ -14,7 +14,7 @@
 // Work decomposition
 //   * One workgroup = 256 threads = 4 wave64s computes a 256 x 256 tile of C.
 //     The waves form a 2 x 2 grid, each owning a 128 x 128 sub-tile held as
-//     8 x 8 fp32 16x16 MFMA accumulators (256 VGPRs per lane).
+//     4 x 4 fp32 32x32 MFMA accumulators (256 accumulation registers per lane).
 //   * K advances in steps of 64.  Each step's A and B tiles are staged in LDS
 //     (2 x 32 KiB), double buffered (128 KiB total), one barrier per step.
 //     Global loads of step k+1 are issued before the MFMAs of step k.
@@ -24,11 +24,14 @@
 //     (and the 16-byte tile writes) hit distinct bank groups.
 //   * M/N-major operands are loaded as 8 x 8 bf16 blocks (8 k rows of 16 bytes)
 //     and transposed in registers with v_perm before the LDS write.
-//   * MFMA v_mfma_f32_16x16x32_bf16 is issued with the B fragment as its first
-//     operand and the A fragment as its second, so each lane ends up holding
-//     C[row = l%16][4 consecutive columns (l/16)*4 .. +3] of every 16x16
-//     block: row-contiguous 16-byte (fp32) or 8-byte (bf16) output vectors,
-//     and per-row reductions need only lanes l, l^16, l^32, l^48.
+//   * MFMA v_mfma_f32_32x32x16_bf16 (16 k per instruction; 4 k steps per LDS
+//     stage).  The fragments of k step s+1 are read from LDS while the 16
+//     MFMAs of step s run (two fragment register sets of 32 VGPRs).
+//   * The MFMA is issued with the B fragment as its first operand and the A
+//     fragment as its second, so each lane ends up holding, for every 32x32
+//     block, row l%32 and the four 4-column groups 8g + 4*(l/32) .. +3
+//     (g = 0..3): row-contiguous 16-byte (fp32) or 8-byte (bf16) output
+//     vectors, and per-row reductions need only lanes l and l^32.
 //   * All global accesses use buffer instructions on per-tile resources:
 //     masked-off lanes get an offset beyond the resource, so edge tiles read
 //     zeros and drop their stores without branches.
@@ -42,10 +45,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace mshard {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -53,9 +59,8 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kBM = 256, kBN = 256, kBK = 64;
 constexpr int kThreads = 256;
 constexpr int kWaveM = 128, kWaveN = 128;
-constexpr int kSubM = kWaveM / 16, kSubN = kWaveN / 16;
+constexpr int kSubM = kWaveM / 32, kSubN = kWaveN / 32;  // 32x32 MFMA blocks per wave
 constexpr int kStageBytes = (kBM + kBN) * kBK * 2;  // 64 KiB
-constexpr int kLdsBytes = 2 * kStageBytes;          // 128 KiB
 constexpr int kGroupM = 8;
 constexpr int kNumXcd = 8;
 constexpr uint32_t kOOB = 0x80000000u;  // any offset >= every resource size
@@ -125,131 +130,164 @@ __device__ __forceinline__ void map_tile(const GemmGeom& g, int& tm, int& tn, in
 }
 
 // ---------------------------------------------------------------------------
-// Tile loaders: global -> registers (16-byte buffer loads) and registers -> LDS.
-// LDS row r (of m or n) holds 64 k values; chunk c (k = 8c .. 8c+7) sits at
-// byte r*128 + ((c ^ (r & 7)) << 4).
+// Global -> LDS: direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds), no
+// staging registers.  One instruction moves 64 x 16 bytes into 1 KiB of
+// contiguous LDS (lane l -> byte 16*l); each lane chooses which 16-byte global
+// chunk lands in its slot, so the LDS layout is free at 16-byte granularity.
+// Out-of-range lanes (edge tiles) get an offset beyond the resource and write
+// zeros.  A 32 KiB operand tile = 2048 slots = 32 instructions, 8 per wave.
+//
+// Layouts (16-byte slots; a K-major tile is [256 m/n rows][64 k], an
+// M/N-major tile is [64 k rows][256 m/n columns]):
+//   K-major : slot(r, c)  = (r/8)*64 + c*8 + r%8          c = k/8 (8 k values)
+//   MN-major: slot(k, j)  = (k/4)*128 + j*4 + k%4         j = col/8 (8 columns)
+// The K-major layout puts 8 consecutive rows of one k chunk in 128 contiguous
+// bytes (a ds_read_b128 fragment read of 8 lanes is conflict-free); the
+// MN-major layout puts 4 consecutive k rows of a chunk pair in 128 contiguous
+// bytes (a 16-lane ds_read_b64_tr_b16 read is conflict-free).  In both, the
+// fragment address is one per-lane base plus compile-time offsets.
 
-// K-major tile: 256 stored rows (row0 ..), 64 k values from k0.
-// Thread t loads chunk c = t & 7 of rows (t >> 3) + 32 i, i = 0..7.
-__device__ __forceinline__ void load_kmajor(u32x4_t (&v)[8], const Operand& op, int row0, int nrows,
-                                            int k0, int K) {
-  const int t = threadIdx.x;
-  const int c = t & 7, r = t >> 3;
-  const int64_t base_elem = (int64_t)row0 * op.ld + k0;
-  const rsrc_t rs = make_rsrc(op.ptr + base_elem, (op.elems - base_elem) * 2);
-  const bool kok = (k0 + c * 8) < K;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = r + 32 * i;
-    const bool ok = kok && (row0 + row) < nrows;
-    const uint32_t off = ok ? (uint32_t)(((int64_t)row * op.ld + c * 8) * 2) : kOOB;
-    v[i] = buf_load16(rs, off);
-  }
-}
-
-__device__ __forceinline__ void store_kmajor(const u32x4_t (&v)[8], char* lds) {
-  const int t = threadIdx.x;
-  const int c = t & 7, r = t >> 3;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = r + 32 * i;
-    *(u32x4_t*)(lds + row * 128 + ((c ^ (row & 7)) << 4)) = v[i];
-  }
-}
-
-// M/N-major tile: 64 stored rows (k = k0 ..), 256 contiguous columns from col0.
-// Thread t owns the 8 x 8 block k = 8*(t & 7) .. +7, col = 8*(t >> 3) .. +7.
-__device__ __forceinline__ void load_mnmajor(u32x4_t (&v)[8], const Operand& op, int col0, int ncols,
-                                             int k0, int K) {
-  const int t = threadIdx.x;
-  const int kb = t & 7, mb = t >> 3;
-  const int64_t base_elem = (int64_t)k0 * op.ld + col0;
-  const rsrc_t rs = make_rsrc(op.ptr + base_elem, (op.elems - base_elem) * 2);
-  const bool cok = (col0 + mb * 8) < ncols;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int k = kb * 8 + i;
-    const bool ok = cok && (k0 + k) < K;
-    const uint32_t off = ok ? (uint32_t)(((int64_t)k * op.ld + mb * 8) * 2) : kOOB;
-    v[i] = buf_load16(rs, off);
-  }
-}
-
-// in[i] = 8 columns of k row i; out[j] = 8 k values of column j.
-__device__ __forceinline__ void transpose8x8(const u32x4_t (&in)[8], u32x4_t (&out)[8]) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      out[j][p] = __builtin_amdgcn_perm(in[2 * p + 1][j >> 1], in[2 * p][j >> 1], sel);
-    }
-  }
-}
-
-__device__ __forceinline__ void store_mnmajor(const u32x4_t (&v)[8], char* lds) {
-  const int t = threadIdx.x;
-  const int kb = t & 7, mb = t >> 3;
-  u32x4_t tr[8];
-  transpose8x8(v, tr);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int row = mb * 8 + j;
-    *(u32x4_t*)(lds + row * 128 + ((kb ^ j) << 4)) = tr[j];
-  }
-}
+typedef __attribute__((address_space(3))) char lds_char;
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
+constexpr int kTileBytes = kBM * kBK * 2;  // 32 KiB per operand tile
 
 template <bool KMAJOR>
-__device__ __forceinline__ void load_tile(u32x4_t (&v)[8], const Operand& op, int mn0, int nmn, int k0, int K) {
-  if constexpr (KMAJOR) load_kmajor(v, op, mn0, nmn, k0, K);
-  else load_mnmajor(v, op, mn0, nmn, k0, K);
-}
-template <bool KMAJOR>
-__device__ __forceinline__ void store_tile(const u32x4_t (&v)[8], char* lds) {
-  if constexpr (KMAJOR) store_kmajor(v, lds);
-  else store_mnmajor(v, lds);
-}
-
-// One 64-deep K step from an LDS stage into the wave's 8 x 8 accumulators.
-__device__ __forceinline__ void mfma_stage(f32x4_t (&acc)[kSubM][kSubN], const char* As, const char* Bs,
-                                           int wm, int wn, int lane) {
+__device__ __forceinline__ void dma_tile(const Operand& op, int mn0, int nmn, int k0, int K, lds_char* tile,
+                                         int wave, int lane) {
+  // Recompute the per-lane offsets every k tile (a few VALU ops) instead of
+  // letting them be hoisted out of the main loop, where 16+ long-lived
+  // registers would compete with the fragment registers.
+  asm volatile("" : "+v"(lane));
+  int64_t base_elem;
+  if constexpr (KMAJOR) base_elem = (int64_t)mn0 * op.ld + k0;
+  else base_elem = (int64_t)k0 * op.ld + mn0;
+  const rsrc_t rs = make_rsrc(op.ptr + base_elem, (op.elems - base_elem) * 2);
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const int c = ks * 4 + (lane >> 4);
-    bf16x8_t af[kSubM], bfr[kSubN];
-#pragma unroll
-    for (int mi = 0; mi < kSubM; ++mi) {
-      const int row = wm * kWaveM + mi * 16 + (lane & 15);
-      af[mi] = *(const bf16x8_t*)(As + row * 128 + ((c ^ (row & 7)) << 4));
+  for (int i = 0; i < 8; ++i) {
+    const int inst = wave * 8 + i;
+    uint32_t off;
+    if constexpr (KMAJOR) {
+      const int r = inst * 8 + (lane & 7), c = lane >> 3;
+      const bool ok = (mn0 + r) < nmn && (k0 + c * 8) < K;
+      off = ok ? (uint32_t)(((int64_t)r * op.ld + c * 8) * 2) : kOOB;
+    } else {
+      const int k = (inst >> 1) * 4 + (lane & 3), j = (inst & 1) * 16 + (lane >> 2);
+      const bool ok = (k0 + k) < K && (mn0 + j * 8) < nmn;
+      off = ok ? (uint32_t)(((int64_t)k * op.ld + j * 8) * 2) : kOOB;
     }
-#pragma unroll
-    for (int ni = 0; ni < kSubN; ++ni) {
-      const int row = wn * kWaveN + ni * 16 + (lane & 15);
-      bfr[ni] = *(const bf16x8_t*)(Bs + row * 128 + ((c ^ (row & 7)) << 4));
-    }
-#pragma unroll
-    for (int mi = 0; mi < kSubM; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < kSubN; ++ni)
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(tile + inst * 1024), 16,
+                                             off, 0, 0, 0);
   }
 }
 
-// Position of accumulator element acc[mi][ni][r] inside the 256 x 256 tile:
-//   row = wm*128 + mi*16 + (lane & 15),  col = wn*128 + ni*16 + (lane >> 4)*4 + r.
+// Per-lane byte offset of this lane's fragment piece inside a tile (k step 0,
+// block 0, wave coordinate 0); the rest of the address is compile-time.
+template <bool KMAJOR>
+__device__ __forceinline__ int frag_lane_base(int lane) {
+  if constexpr (KMAJOR) {
+    // row = blk*32 + l%32, chunk = 2*ks + l/32
+    return ((lane & 31) >> 3) * 1024 + (lane >> 5) * 128 + (lane & 7) * 16;
+  } else {
+    // group g = l/16 (k half g/2, column half g%2); in-group i: q = i%4 (column quad), e = i/4 (k row)
+    const int g = lane >> 4, i = lane & 15, q = i & 3, e = i >> 2;
+    return e * 16 + (q >> 1) * 64 + (q & 1) * 8 + (g & 1) * 128 + (g >> 1) * 4096;
+  }
+}
+
+// Fragment of k step ks (16 k) of block blk (32 rows/columns) for wave
+// coordinate w: 8 bf16 k values of row/column l%32 at k = 16ks + 8(l/32) + e.
+template <bool KMAJOR>
+__device__ __forceinline__ bf16x8_t load_frag(const lds_char* tile, int lane_base, int w, int blk, int ks) {
+  if constexpr (KMAJOR) {
+    return *(const bf16x8_t*)(tile + lane_base + w * 16384 + blk * 4096 + ks * 256);
+  } else {
+    const lds_char* p = tile + lane_base + w * 1024 + blk * 256 + ks * 8192;
+    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p);
+    const s16x4_t hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p + 2048));
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+}
+
+struct Frags {
+  bf16x8_t a[kSubM];
+  bf16x8_t b[kSubN];
+};
+
+template <bool AK, bool BK>
+__device__ __forceinline__ void load_frags(Frags& f, const lds_char* stage, int ks, int wm, int wn, int la, int lb) {
+#pragma unroll
+  for (int mi = 0; mi < kSubM; ++mi) f.a[mi] = load_frag<AK>(stage, la, wm, mi, ks);
+#pragma unroll
+  for (int ni = 0; ni < kSubN; ++ni) f.b[ni] = load_frag<BK>(stage + kTileBytes, lb, wn, ni, ks);
+}
+
+// The MFMA is written as inline assembly with accumulation-register operands so
+// that the 256 accumulators are pinned to the accumulation registers for their
+// whole life (compiler-selected forms end up copying them between register
+// files every iteration).  Hazards: a given accumulator is re-used only after
+// the 15 other MFMAs of the k step; fragment registers come from LDS loads,
+// which the wait-count pass tracks through the asm operands; the first read
+// after the loop is fenced with explicit wait states.
+template <bool FIRST>
+__device__ __forceinline__ void mfma_32x32x16(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  if constexpr (FIRST)  // the first k step starts from C = 0 (inline constant): no zero fill
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+template <bool FIRST>
+__device__ __forceinline__ void mfma_frags(f32x16_t (&acc)[kSubM][kSubN], const Frags& f) {
+#pragma unroll
+  for (int mi = 0; mi < kSubM; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < kSubN; ++ni) mfma_32x32x16<FIRST>(acc[mi][ni], f.b[ni], f.a[mi]);
+}
+
+// Position of accumulator element acc[mi][ni][4g + r] inside the 256 x 256 tile:
+//   row = wm*128 + mi*32 + (lane & 31),
+//   col = wn*128 + ni*32 + 8g + 4*(lane >> 5) + r        (g, r = 0..3).
+// LDS store of 4 accumulators straight from their accumulation registers.
+// Every non-MFMA use of the accumulators is this or a buffer store, so they
+// stay in the accumulation registers for the whole main loop.  LDS operations
+// of a wave complete in order, so later LDS reads of the same bytes see the data.
+__device__ __forceinline__ void acc_store_lds(char* p, f32x4_t a) {
+  // generic (flat) pointer the compiler cannot narrow to LDS: a flat store, whose
+  // data operand may be an accumulation register, like a buffer store's
+  asm volatile("" : "+v"(p));
+  *(f32x4_t*)p = a;
+}
+
+// Wait states between the last MFMA and the first explicit accumulator read
+// (covers the longest MFMA result latency).
+__device__ __forceinline__ void acc_settle() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n s_nop 7\n s_nop 7" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 struct EpiCtx {
   int m0, n0;   // tile origin in C
   int tm, tn;   // tile coordinates
   int split;    // K split index
   int wm, wn;   // wave coordinates in the tile
   int lane;
-  char* lds;    // 128 KiB, free for the epilogue after the main loop
+  char* lds0;   // the two 64 KiB LDS stages, free for the epilogue after the main loop
+  char* lds1;
 };
 
 template <bool A_KMAJOR, bool B_KMAJOR, class Epi>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 gemm_kernel(GemmGeom g, Operand a, Operand b, Epi epi) {
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  // Two LDS stages (A tile then B tile in each), kept as separate objects so
+  // that the direct-to-LDS writes into one stage are known not to alias the
+  // fragment reads of the other.
+  __shared__ __attribute__((aligned(1024))) char lds0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char lds1[kStageBytes];
+  lds_char* st0 = (lds_char*)lds0;
+  lds_char* st1 = (lds_char*)lds1;
   int tm, tn, split;
   map_tile(g, tm, tn, split);
   const int m0 = tm * kBM, n0 = tn * kBN;
@@ -258,38 +296,44 @@ gemm_kernel(GemmGeom g, Operand a, Operand b, Epi epi) {
   const int kt_end = (int)(((int64_t)(split + 1) * nk) / g.splits);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+  const int la = frag_lane_base<A_KMAJOR>(lane), lb = frag_lane_base<B_KMAJOR>(lane);
 
-  f32x4_t acc[kSubM][kSubN];
-#pragma unroll
-  for (int mi = 0; mi < kSubM; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < kSubN; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x16_t acc[kSubM][kSubN];
 
-  if (kt_beg < kt_end) {
-    u32x4_t ra[8], rb[8];
-    load_tile<A_KMAJOR>(ra, a, m0, g.M, kt_beg * kBK, g.K);
-    load_tile<B_KMAJOR>(rb, b, n0, g.N, kt_beg * kBK, g.K);
-    store_tile<A_KMAJOR>(ra, lds);
-    store_tile<B_KMAJOR>(rb, lds + kBM * 128);
-    __syncthreads();
-    for (int kt = kt_beg; kt < kt_end; ++kt) {
-      const int stage = (kt - kt_beg) & 1;
-      const bool more = kt + 1 < kt_end;
-      if (more) {
-        load_tile<A_KMAJOR>(ra, a, m0, g.M, (kt + 1) * kBK, g.K);
-        load_tile<B_KMAJOR>(rb, b, n0, g.N, (kt + 1) * kBK, g.K);
-      }
-      const char* As = lds + stage * kStageBytes;
-      mfma_stage(acc, As, As + kBM * 128, wm, wn, lane);
-      if (more) {
-        char* nxt = lds + (stage ^ 1) * kStageBytes;
-        store_tile<A_KMAJOR>(ra, nxt);
-        store_tile<B_KMAJOR>(rb, nxt + kBM * 128);
-      }
-      __syncthreads();
+  // One k tile: DMA of tile kt+1 into `nxt` in flight under the 4 k steps of
+  // tile kt from `cur`; the fragments of k step s+1 are read while the MFMAs of
+  // step s run.  The barrier (which waits for this wave's DMA) publishes `nxt`.
+  // The host guarantees kt_beg < kt_end, so the first tile always runs.
+  auto step = [&](auto first, const lds_char* cur, lds_char* nxt, int kt, Frags (&f)[2]) {
+    constexpr bool kFirst = decltype(first)::value;
+    const bool more = kt + 1 < kt_end;
+    if (more) {
+      dma_tile<A_KMAJOR>(a, m0, g.M, (kt + 1) * kBK, g.K, nxt, wave, lane);
+      dma_tile<B_KMAJOR>(b, n0, g.N, (kt + 1) * kBK, g.K, nxt + kTileBytes, wave, lane);
     }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks < 3) load_frags<A_KMAJOR, B_KMAJOR>(f[(ks + 1) & 1], cur, ks + 1, wm, wn, la, lb);
+      if (kFirst && ks == 0) mfma_frags<true>(acc, f[0]);
+      else mfma_frags<false>(acc, f[ks & 1]);
+    }
+    __syncthreads();
+    if (more) load_frags<A_KMAJOR, B_KMAJOR>(f[0], nxt, 0, wm, wn, la, lb);
+  };
+  using True = std::integral_constant<bool, true>;
+  using False = std::integral_constant<bool, false>;
+
+  dma_tile<A_KMAJOR>(a, m0, g.M, kt_beg * kBK, g.K, st0, wave, lane);
+  dma_tile<B_KMAJOR>(b, n0, g.N, kt_beg * kBK, g.K, st0 + kTileBytes, wave, lane);
+  __syncthreads();
+  Frags f[2];
+  load_frags<A_KMAJOR, B_KMAJOR>(f[0], st0, 0, wm, wn, la, lb);
+  step(True{}, st0, st1, kt_beg, f);
+  for (int kt = kt_beg + 1; kt < kt_end; kt += 2) {
+    step(False{}, st1, st0, kt, f);
+    if (kt + 1 < kt_end) step(False{}, st0, st1, kt + 1, f);
   }
-  EpiCtx ctx{m0, n0, tm, tn, split, wm, wn, lane, lds};
+  EpiCtx ctx{m0, n0, tm, tn, split, wm, wn, lane, lds0, lds1};
   epi(acc, ctx);
 }
 

@@ -46,26 +46,54 @@ __global__ void __launch_bounds__(256) colsum_reduce_bf16(const float* __restric
   out[j] = __builtin_bit_cast(uint16_t, (__bf16)acc);
 }
 
-// Per token row: merge the P partial triples of the logits tiles in ascending
-// column order into the shard's (m, s, z).
-__global__ void __launch_bounds__(256) ce_tile_combine(const float* __restrict__ pm, const float* __restrict__ ps,
+// Log-sum-exp merge of (m2, s2) into (M, S): afterwards S = sum exp(. - M) over
+// both parts and M = the larger max.  Parts with s <= 0 are empty.
+__device__ __forceinline__ void lse_merge(float& M, float& S, float m2, float s2) {
+  if (!(s2 > 0.f)) return;
+  if (!(S > 0.f)) {
+    M = m2;
+    S = s2;
+  } else if (m2 > M) {
+    S = S * expf(M - m2) + s2;
+    M = m2;
+  } else {
+    S += s2 * expf(m2 - M);
+  }
+}
+
+// Per token row: merge the P tile partials of the logits GEMM into the shard's
+// (m, s, z).  A block covers 64 rows with 8 waves; wave w merges partials
+// [w*P/8, (w+1)*P/8) in ascending order (one row per lane, coalesced over
+// rows), then wave 0 merges the 8 wave results in ascending wave order.
+__global__ void __launch_bounds__(512) ce_tile_combine(const float* __restrict__ pm, const float* __restrict__ ps,
                                                        const float* __restrict__ pz, int P, int T,
                                                        float* __restrict__ m, float* __restrict__ s,
                                                        float* __restrict__ z) {
-  const int row = blockIdx.x * 256 + threadIdx.x;
-  if (row >= T) return;
-  float M = -INFINITY;
-  for (int p = 0; p < P; ++p) M = fmaxf(M, pm[(int64_t)p * T + row]);
-  float S = 0.f, Z = 0.f;
-  for (int p = 0; p < P; ++p) {
-    const int64_t o = (int64_t)p * T + row;
-    const float sp = ps[o];
-    S += sp > 0.f ? sp * expf(pm[o] - M) : 0.f;
-    Z += pz[o];
+  __shared__ float xm[8][64], xs[8][64], xz[8][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int row = blockIdx.x * 64 + lane;
+  const int p0 = (int)(((int64_t)w * P) / 8), p1 = (int)(((int64_t)(w + 1) * P) / 8);
+  float M = -INFINITY, S = 0.f, Z = 0.f;
+  if (row < T) {
+    for (int p = p0; p < p1; ++p) {
+      const int64_t o = (int64_t)p * T + row;
+      lse_merge(M, S, pm[o], ps[o]);
+      Z += pz[o];
+    }
   }
-  m[row] = M;
-  s[row] = S;
-  z[row] = Z;
+  xm[w][lane] = M;
+  xs[w][lane] = S;
+  xz[w][lane] = Z;
+  __syncthreads();
+  if (w == 0 && row < T) {
+    for (int q = 1; q < 8; ++q) {
+      lse_merge(M, S, xm[q][lane], xs[q][lane]);
+      Z += xz[q][lane];
+    }
+    m[row] = M;
+    s[row] = S;
+    z[row] = Z;
+  }
 }
 
 // Per token: merge t shards' partials in ascending rank order into the loss.
@@ -74,13 +102,10 @@ __global__ void __launch_bounds__(256) ce_combine_tokens(const float* __restrict
                                                          float* __restrict__ loss) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= T) return;
-  float M = -INFINITY;
-  for (int r = 0; r < t; ++r) M = fmaxf(M, m[(int64_t)r * T + i]);
-  float S = 0.f, Z = 0.f;
+  float M = -INFINITY, S = 0.f, Z = 0.f;
   for (int r = 0; r < t; ++r) {
     const int64_t o = (int64_t)r * T + i;
-    const float sr = s[o];
-    S += sr > 0.f ? sr * expf(m[o] - M) : 0.f;
+    lse_merge(M, S, m[o], s[o]);
     Z += z[o];
   }
   loss[i] = logf(S) + M - Z;
@@ -112,7 +137,9 @@ static GemmGeom make_geom(int64_t M, int64_t N, int64_t K, int splits) {
   g.K = (int)K;
   g.tiles_m = (int)((M + kBM - 1) / kBM);
   g.tiles_n = (int)((N + kBN - 1) / kBN);
-  g.splits = splits;
+  // every K split must own at least one k tile (the kernel always runs its first tile)
+  const int64_t nk = (K + kBK - 1) / kBK;
+  g.splits = (int)(splits < nk ? splits : nk);
   return g;
 }
 
@@ -152,7 +179,7 @@ MlpWorkspace mlp_workspace_layout(int64_t T, int64_t h, int64_t f) {
 CeWorkspace ce_workspace_layout(int64_t T, int64_t v) {
   CeWorkspace w;
   auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  w.parts = (int)(((v + kBN - 1) / kBN) * 2);
+  w.parts = (int)((v + kBN - 1) / kBN);
   const size_t one = align((size_t)w.parts * T * 4);
   w.off_m = 0;
   w.off_s = one;
@@ -197,6 +224,7 @@ hipError_t launch_mlp_fwd(const uint16_t* X, const uint16_t* A, const uint16_t* 
 static hipError_t weight_grad(const uint16_t* P, int64_t ldp, const uint16_t* Q, int64_t ldq, int64_t Kt,
                               int64_t M, int64_t N, int S, uint16_t* C, float* splitk, hipStream_t st) {
   GemmGeom g = make_geom(M, N, Kt, S);
+  S = g.splits;
   Operand a{P, ldp, Kt * ldp}, b{Q, ldq, Kt * ldq};
   if (S == 1) {
     EpiStoreBF16 e{C, N, (int)M, (int)N};
@@ -270,7 +298,7 @@ hipError_t launch_vocab_ce(const uint16_t* X, const uint16_t* E, const int64_t* 
   EpiCE e{target, vocab_start, pm, ps, pz, (int)T, (int)v};
   hipError_t err = launch_gemm<true, false>(g, a, b, e, st);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(ce_tile_combine, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, st, pm, ps, pz, w.parts,
+  hipLaunchKernelGGL(ce_tile_combine, dim3((unsigned)((T + 63) / 64)), dim3(512), 0, st, pm, ps, pz, w.parts,
                      (int)T, m, s, z);
   return hipGetLastError();
 }
