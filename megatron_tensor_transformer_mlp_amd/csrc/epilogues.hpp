@@ -58,7 +58,7 @@ __device__ __forceinline__ float gelu_grad_f(float x) {
 
 __device__ __forceinline__ char* epi_region(const EpiCtx& c) {
   const int wave = c.wm * 2 + c.wn;
-  return (wave < 2 ? c.lds0 : c.lds1) + (wave & 1) * 32768;
+  return wave == 0 ? c.lds0 : (wave == 1 ? c.lds1 : (wave == 2 ? c.lds2 : c.lds3));
 }
 
 __device__ __forceinline__ int epi_slot(int lr, int q) { return lr * 512 + ((q ^ (lr & 7)) << 4); }
@@ -250,10 +250,10 @@ struct EpiDGelu {
 struct EpiCE {
   const int64_t* target;
   int64_t vocab_start;
-  float* pm;
-  float* ps;
-  float* pz;
-  int M, N;  // M = T tokens, N = v_i
+  float* part;  // pm at part, ps at part + stride, pz at part + 2*stride (floats)
+  int stride;
+  int M, N;     // M = T tokens, N = v_i
+  int pad_;
   __device__ void operator()(f32x16_t (&acc)[kSubM][kSubN], const EpiCtx& c) const {
     const rsrc_t rt = make_rsrc(target, (int64_t)M * 8);
     char* region = epi_region(c);
@@ -279,15 +279,23 @@ struct EpiCE {
           v[4 * q + 3] = x[3];
         }
         const int nv = ncol - ch * 64;  // valid columns in this chunk (may be <= 0)
+        if (nv <= 0) continue;           // uniform: this wave's columns end before the chunk
+        // invalid (padding beyond v_i) columns become -inf with per-lane selects,
+        // so no per-column uniform masks stay live
+        int nvv = nv;
+        asm volatile("" : "+v"(nvv));
+        const int tl = (tgt >= ch * 64 && tgt < ch * 64 + nv) ? (int)(tgt - ch * 64) : -1;
+#pragma unroll
+        for (int j2 = 0; j2 < 64; ++j2) v[j2] = j2 < nvv ? v[j2] : -INFINITY;
         float cm = -INFINITY;
 #pragma unroll
-        for (int j2 = 0; j2 < 64; ++j2) cm = j2 < nv ? fmaxf(cm, v[j2]) : cm;
+        for (int j2 = 0; j2 < 64; ++j2) cm = fmaxf(cm, v[j2]);
         const float cml = cm * kLog2e;
         float cs = 0.f;
 #pragma unroll
         for (int j2 = 0; j2 < 64; ++j2) {
-          cs += j2 < nv ? __builtin_amdgcn_exp2f(__builtin_fmaf(v[j2], kLog2e, -cml)) : 0.f;
-          zz = (j2 < nv && (int64_t)(ch * 64 + j2) == tgt) ? v[j2] : zz;
+          cs += __builtin_amdgcn_exp2f(__builtin_fmaf(v[j2], kLog2e, -cml));
+          zz = j2 == tl ? v[j2] : zz;
         }
         if (cs > 0.f) {
           if (!(sm > 0.f)) {
@@ -330,10 +338,10 @@ struct EpiCE {
           const float mm = fmaxf(rm[h], m1);
           const float s0 = rs[h] > 0.f ? rs[h] * __builtin_amdgcn_exp2f((rm[h] - mm) * kLog2e) : 0.f;
           const float s1m = s1 > 0.f ? s1 * __builtin_amdgcn_exp2f((m1 - mm) * kLog2e) : 0.f;
-          const int64_t o = (int64_t)c.tn * M + row;
-          pm[o] = mm;
-          ps[o] = s0 + s1m;
-          pz[o] = rz[h] + z1;
+          float* o = part + (int64_t)c.tn * M + row;
+          o[0] = mm;
+          o[stride] = s0 + s1m;
+          o[2 * (int64_t)stride] = rz[h] + z1;
         }
       }
     }

@@ -56,11 +56,12 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
-constexpr int kBM = 256, kBN = 256, kBK = 64;
+constexpr int kBM = 256, kBN = 256, kBK = 32;
+constexpr int kStages = 4;  // LDS ring: tiles kt+1..kt+3 in flight while kt is consumed
 constexpr int kThreads = 256;
 constexpr int kWaveM = 128, kWaveN = 128;
 constexpr int kSubM = kWaveM / 32, kSubN = kWaveN / 32;  // 32x32 MFMA blocks per wave
-constexpr int kStageBytes = (kBM + kBN) * kBK * 2;  // 64 KiB
+constexpr int kStageBytes = (kBM + kBN) * kBK * 2;  // 32 KiB
 constexpr int kGroupM = 8;
 constexpr int kNumXcd = 8;
 constexpr uint32_t kOOB = 0x80000000u;  // any offset >= every resource size
@@ -135,50 +136,83 @@ __device__ __forceinline__ void map_tile(const GemmGeom& g, int& tm, int& tn, in
 // contiguous LDS (lane l -> byte 16*l); each lane chooses which 16-byte global
 // chunk lands in its slot, so the LDS layout is free at 16-byte granularity.
 // Out-of-range lanes (edge tiles) get an offset beyond the resource and write
-// zeros.  A 32 KiB operand tile = 2048 slots = 32 instructions, 8 per wave.
+// zeros.  A 16 KiB operand tile = 1024 slots = 16 instructions, 4 per wave.
 //
-// Layouts (16-byte slots; a K-major tile is [256 m/n rows][64 k], an
-// M/N-major tile is [64 k rows][256 m/n columns]):
-//   K-major : slot(r, c)  = (r/8)*64 + c*8 + r%8          c = k/8 (8 k values)
-//   MN-major: slot(k, j)  = (k/4)*128 + j*4 + k%4         j = col/8 (8 columns)
-// The K-major layout puts 8 consecutive rows of one k chunk in 128 contiguous
-// bytes (a ds_read_b128 fragment read of 8 lanes is conflict-free); the
-// MN-major layout puts 4 consecutive k rows of a chunk pair in 128 contiguous
-// bytes (a 16-lane ds_read_b64_tr_b16 read is conflict-free).  In both, the
-// fragment address is one per-lane base plus compile-time offsets.
+// Layouts (16-byte slots; a K-major tile is [256 m/n rows][32 k], an
+// M/N-major tile is [32 k rows][256 m/n columns]):
+//   K-major : slot(r, c) = (r/16)*64 + c*16 + r%16       c = k/8 (8 k values)
+//   MN-major: slot(k, j) = (k/4)*128 + j*4 + k%4         j = col/8 (8 columns)
+// LDS serves 16 lanes x 16 bytes (all 64 banks) per cycle.  The K-major layout
+// puts 16 consecutive rows of one k chunk in 256 contiguous bytes, so a 16-lane
+// ds_read_b128 fragment read is conflict-free; the MN-major layout puts 4
+// consecutive k rows of a chunk pair in 128 contiguous bytes (a 16-lane
+// ds_read_b64_tr_b16 read is conflict-free).  In both, the fragment address is
+// one per-lane base plus compile-time offsets.
 
 typedef __attribute__((address_space(3))) char lds_char;
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x8_t __attribute__((ext_vector_type(8)));
-constexpr int kTileBytes = kBM * kBK * 2;  // 32 KiB per operand tile
+constexpr int kTileBytes = kBM * kBK * 2;  // 16 KiB per operand tile
+constexpr int kDmaPerWave = kTileBytes / 1024 / 4;
 
+// One buffer_load_dwordx4 ... lds: 64 lanes x 16 bytes from the buffer
+// described by `desc` at per-lane byte offsets `off` into 1 KiB of LDS at
+// `lds_addr` (wave-uniform; passed in M0).  Issued as inline assembly so the
+// compiler's wait-count pass neither tracks nor waits for it: the main loop
+// accounts for these loads itself with explicit vmcnt waits (vector-memory
+// operations retire in issue order, so the compiler's own waits stay correct).
+__device__ __forceinline__ void dma16(u32x4_t desc, uint32_t off, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(off), "s"(desc), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+// Buffer descriptor over [base, base + bytes_left), size clamped below 2^31.
+__device__ __forceinline__ u32x4_t make_desc(const void* base, int64_t bytes_left) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint32_t n = bytes_left < 0 ? 0u : (bytes_left > 0x7fffffff ? 0x7fffffffu : (uint32_t)bytes_left);
+  return u32x4_t{(uint32_t)b, (uint32_t)(b >> 32) & 0xffffu, n, kRsrcWord3};
+}
+
+// Descriptor of the k tile at k0 of an operand (scalar work, once per tile).
 template <bool KMAJOR>
-__device__ __forceinline__ void dma_tile(const Operand& op, int mn0, int nmn, int k0, int K, lds_char* tile,
-                                         int wave, int lane) {
-  // Recompute the per-lane offsets every k tile (a few VALU ops) instead of
-  // letting them be hoisted out of the main loop, where 16+ long-lived
-  // registers would compete with the fragment registers.
-  asm volatile("" : "+v"(lane));
+__device__ __forceinline__ u32x4_t tile_desc(const Operand& op, int mn0, int k0) {
   int64_t base_elem;
   if constexpr (KMAJOR) base_elem = (int64_t)mn0 * op.ld + k0;
   else base_elem = (int64_t)k0 * op.ld + mn0;
-  const rsrc_t rs = make_rsrc(op.ptr + base_elem, (op.elems - base_elem) * 2);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int inst = wave * 8 + i;
-    uint32_t off;
-    if constexpr (KMAJOR) {
-      const int r = inst * 8 + (lane & 7), c = lane >> 3;
-      const bool ok = (mn0 + r) < nmn && (k0 + c * 8) < K;
-      off = ok ? (uint32_t)(((int64_t)r * op.ld + c * 8) * 2) : kOOB;
-    } else {
-      const int k = (inst >> 1) * 4 + (lane & 3), j = (inst & 1) * 16 + (lane >> 2);
-      const bool ok = (k0 + k) < K && (mn0 + j * 8) < nmn;
-      off = ok ? (uint32_t)(((int64_t)k * op.ld + j * 8) * 2) : kOOB;
-    }
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(tile + inst * 1024), 16,
-                                             off, 0, 0, 0);
+  return make_desc(op.ptr + base_elem, (op.elems - base_elem) * 2);
+}
+
+// Direct-to-LDS instruction i (0 .. kDmaPerWave-1) of this wave's share of one
+// operand tile.  The per-lane offset is recomputed each time (a few VALU ops
+// that co-issue with the MFMAs) rather than hoisted into long-lived registers.
+template <bool KMAJOR>
+__device__ __forceinline__ void dma_one(const Operand& op, u32x4_t desc, int mn0, int nmn, int k0, int K,
+                                        lds_char* tile, int wave, int lane, int i) {
+  asm volatile("" : "+v"(lane));
+  const int inst = wave * kDmaPerWave + i;
+  uint32_t off;
+  if constexpr (KMAJOR) {
+    // one 16-row group per instruction: slot l -> row l%16, chunk l/16
+    const int r = inst * 16 + (lane & 15), c = lane >> 4;
+    const bool ok = (mn0 + r) < nmn && (k0 + c * 8) < K;
+    off = ok ? (uint32_t)(((int64_t)r * op.ld + c * 8) * 2) : kOOB;
+  } else {
+    const int k = (inst >> 1) * 4 + (lane & 3), j = (inst & 1) * 16 + (lane >> 2);
+    const bool ok = (k0 + k) < K && (mn0 + j * 8) < nmn;
+    off = ok ? (uint32_t)(((int64_t)k * op.ld + j * 8) * 2) : kOOB;
   }
+  dma16(desc, off, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(tile + inst * 1024)));
+}
+
+// Direct-to-LDS copy of this wave's share of one operand tile.
+template <bool KMAJOR>
+__device__ __forceinline__ void dma_tile(const Operand& op, int mn0, int nmn, int k0, int K, lds_char* tile,
+                                         int wave, int lane) {
+  const u32x4_t desc = tile_desc<KMAJOR>(op, mn0, k0);
+#pragma unroll
+  for (int i = 0; i < kDmaPerWave; ++i) dma_one<KMAJOR>(op, desc, mn0, nmn, k0, K, tile, wave, lane, i);
 }
 
 // Per-lane byte offset of this lane's fragment piece inside a tile (k step 0,
@@ -186,8 +220,8 @@ __device__ __forceinline__ void dma_tile(const Operand& op, int mn0, int nmn, in
 template <bool KMAJOR>
 __device__ __forceinline__ int frag_lane_base(int lane) {
   if constexpr (KMAJOR) {
-    // row = blk*32 + l%32, chunk = 2*ks + l/32
-    return ((lane & 31) >> 3) * 1024 + (lane >> 5) * 128 + (lane & 7) * 16;
+    // row = blk*32 + l%32 -> (row/16)*1024 + (row%16)*16; chunk = 2*ks + l/32 -> chunk*256
+    return ((lane & 31) >> 4) * 1024 + (lane >> 5) * 256 + (lane & 15) * 16;
   } else {
     // group g = l/16 (k half g/2, column half g%2); in-group i: q = i%4 (column quad), e = i/4 (k row)
     const int g = lane >> 4, i = lane & 15, q = i & 3, e = i >> 2;
@@ -200,7 +234,7 @@ __device__ __forceinline__ int frag_lane_base(int lane) {
 template <bool KMAJOR>
 __device__ __forceinline__ bf16x8_t load_frag(const lds_char* tile, int lane_base, int w, int blk, int ks) {
   if constexpr (KMAJOR) {
-    return *(const bf16x8_t*)(tile + lane_base + w * 16384 + blk * 4096 + ks * 256);
+    return *(const bf16x8_t*)(tile + lane_base + w * 8192 + blk * 2048 + ks * 512);
   } else {
     const lds_char* p = tile + lane_base + w * 1024 + blk * 256 + ks * 8192;
     const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p);
@@ -238,12 +272,16 @@ __device__ __forceinline__ void mfma_32x32x16(f32x16_t& acc, const bf16x8_t& a, 
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
-template <bool FIRST>
-__device__ __forceinline__ void mfma_frags(f32x16_t (&acc)[kSubM][kSubN], const Frags& f) {
+// The 16 MFMAs of one k step; after each group of 4 (one A row block), calls
+// between(mi) so that other work (direct-to-LDS issue) interleaves with them.
+template <bool FIRST, class Between>
+__device__ __forceinline__ void mfma_frags(f32x16_t (&acc)[kSubM][kSubN], const Frags& f, Between&& between) {
 #pragma unroll
-  for (int mi = 0; mi < kSubM; ++mi)
+  for (int mi = 0; mi < kSubM; ++mi) {
 #pragma unroll
     for (int ni = 0; ni < kSubN; ++ni) mfma_32x32x16<FIRST>(acc[mi][ni], f.b[ni], f.a[mi]);
+    between(mi);
+  }
 }
 
 // Position of accumulator element acc[mi][ni][4g + r] inside the 256 x 256 tile:
@@ -274,20 +312,48 @@ struct EpiCtx {
   int split;    // K split index
   int wm, wn;   // wave coordinates in the tile
   int lane;
-  char* lds0;   // the two 64 KiB LDS stages, free for the epilogue after the main loop
+  char* lds0;   // the four 32 KiB LDS stages, free for the epilogue after the main loop
   char* lds1;
+  char* lds2;
+  char* lds3;
 };
+
+// s_waitcnt with only the vector-memory count: wait until at most n of this
+// wave's vector memory operations (here: direct-to-LDS loads) are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  static_assert(kDmaPerWave == kSubM, "one DMA instruction per A row block of MFMAs");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Make every 32-bit word of a kernel-argument struct live in scalar registers
+// here.  Scalar memory loads complete out of order, so one left outstanding
+// across the main loop (the compiler likes to hoist the epilogue's argument
+// loads) would turn every LDS wait in the loop into a full drain.
+template <class T>
+__device__ __forceinline__ void args_to_sgprs(const T& t) {
+  static_assert(sizeof(T) % 4 == 0, "word-sized argument struct");
+  const uint32_t* w = (const uint32_t*)&t;
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 4); ++i) asm volatile("" ::"s"(w[i]));
+}
 
 template <bool A_KMAJOR, bool B_KMAJOR, class Epi>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 gemm_kernel(GemmGeom g, Operand a, Operand b, Epi epi) {
-  // Two LDS stages (A tile then B tile in each), kept as separate objects so
+  args_to_sgprs(g);
+  args_to_sgprs(a);
+  args_to_sgprs(b);
+  args_to_sgprs(epi);
+  // Four LDS stages (A tile then B tile in each), kept as separate objects so
   // that the direct-to-LDS writes into one stage are known not to alias the
-  // fragment reads of the other.
+  // fragment reads of another.
   __shared__ __attribute__((aligned(1024))) char lds0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) char lds1[kStageBytes];
-  lds_char* st0 = (lds_char*)lds0;
-  lds_char* st1 = (lds_char*)lds1;
+  __shared__ __attribute__((aligned(1024))) char lds2[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char lds3[kStageBytes];
+  lds_char* st[kStages] = {(lds_char*)lds0, (lds_char*)lds1, (lds_char*)lds2, (lds_char*)lds3};
   int tm, tn, split;
   map_tile(g, tm, tn, split);
   const int m0 = tm * kBM, n0 = tn * kBN;
@@ -300,40 +366,63 @@ gemm_kernel(GemmGeom g, Operand a, Operand b, Epi epi) {
 
   f32x16_t acc[kSubM][kSubN];
 
-  // One k tile: DMA of tile kt+1 into `nxt` in flight under the 4 k steps of
-  // tile kt from `cur`; the fragments of k step s+1 are read while the MFMAs of
-  // step s run.  The barrier (which waits for this wave's DMA) publishes `nxt`.
-  // The host guarantees kt_beg < kt_end, so the first tile always runs.
-  auto step = [&](auto first, const lds_char* cur, lds_char* nxt, int kt, Frags (&f)[2]) {
+  auto dma = [&](int kt, lds_char* stage) {
+    dma_tile<A_KMAJOR>(a, m0, g.M, kt * kBK, g.K, stage, wave, lane);
+    dma_tile<B_KMAJOR>(b, n0, g.N, kt * kBK, g.K, stage + kTileBytes, wave, lane);
+  };
+  constexpr int kPerTile = 2 * kDmaPerWave;  // direct-to-LDS instructions per wave per tile
+
+  // One k tile from stage `cur` (2 k steps of 16).  Invariant at entry: tiles
+  // kt and kt+1 are published (complete in LDS for every wave) and the first
+  // k step's fragments of tile kt are in f[0].  The DMA of tile kt+3 goes into
+  // the stage consumed at kt-1; the second k step's fragments of tile kt are
+  // read under the first step's MFMAs, and the first step's fragments of tile
+  // kt+1 under the second step's.  Then this wave waits for its share of tile
+  // kt+2 (tile kt+3 may stay in flight) and the barrier publishes it; that
+  // barrier also orders every read of stage kt before its reuse at kt+1.
+  // The host guarantees kt_beg < kt_end.
+  auto step = [&](auto first, const lds_char* cur, const lds_char* nxt, lds_char* far, int kt, Frags (&f)[2]) {
     constexpr bool kFirst = decltype(first)::value;
-    const bool more = kt + 1 < kt_end;
-    if (more) {
-      dma_tile<A_KMAJOR>(a, m0, g.M, (kt + 1) * kBK, g.K, nxt, wave, lane);
-      dma_tile<B_KMAJOR>(b, n0, g.N, (kt + 1) * kBK, g.K, nxt + kTileBytes, wave, lane);
-    }
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if (ks < 3) load_frags<A_KMAJOR, B_KMAJOR>(f[(ks + 1) & 1], cur, ks + 1, wm, wn, la, lb);
-      if (kFirst && ks == 0) mfma_frags<true>(acc, f[0]);
-      else mfma_frags<false>(acc, f[ks & 1]);
-    }
-    __syncthreads();
-    if (more) load_frags<A_KMAJOR, B_KMAJOR>(f[0], nxt, 0, wm, wn, la, lb);
+    const bool issue = kt + 3 < kt_end;
+    const int k3 = (kt + 3) * kBK;
+    const u32x4_t da = tile_desc<A_KMAJOR>(a, m0, k3);
+    const u32x4_t db = tile_desc<B_KMAJOR>(b, n0, k3);
+    // one direct-to-LDS instruction after every 4 MFMAs: A's share under the
+    // first k step, B's under the second
+    auto dma_a = [&](int q) {
+      if (issue) dma_one<A_KMAJOR>(a, da, m0, g.M, k3, g.K, far, wave, lane, q);
+    };
+    auto dma_b = [&](int q) {
+      if (issue) dma_one<B_KMAJOR>(b, db, n0, g.N, k3, g.K, far + kTileBytes, wave, lane, q);
+    };
+    load_frags<A_KMAJOR, B_KMAJOR>(f[1], cur, 1, wm, wn, la, lb);
+    if constexpr (kFirst) mfma_frags<true>(acc, f[0], dma_a);
+    else mfma_frags<false>(acc, f[0], dma_a);
+    if (kt + 1 < kt_end) load_frags<A_KMAJOR, B_KMAJOR>(f[0], nxt, 0, wm, wn, la, lb);
+    mfma_frags<false>(acc, f[1], dma_b);
+    if (issue) wait_vmcnt<kPerTile>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
   };
   using True = std::integral_constant<bool, true>;
   using False = std::integral_constant<bool, false>;
 
-  dma_tile<A_KMAJOR>(a, m0, g.M, kt_beg * kBK, g.K, st0, wave, lane);
-  dma_tile<B_KMAJOR>(b, n0, g.N, kt_beg * kBK, g.K, st0 + kTileBytes, wave, lane);
-  __syncthreads();
+  dma(kt_beg, st[0]);
+  if (kt_beg + 1 < kt_end) dma(kt_beg + 1, st[1]);
+  if (kt_beg + 2 < kt_end) dma(kt_beg + 2, st[2]);
+  if (kt_beg + 2 < kt_end) wait_vmcnt<kPerTile>();  // tiles kt_beg, kt_beg+1 done
+  else wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
   Frags f[2];
-  load_frags<A_KMAJOR, B_KMAJOR>(f[0], st0, 0, wm, wn, la, lb);
-  step(True{}, st0, st1, kt_beg, f);
-  for (int kt = kt_beg + 1; kt < kt_end; kt += 2) {
-    step(False{}, st1, st0, kt, f);
-    if (kt + 1 < kt_end) step(False{}, st0, st1, kt + 1, f);
+  load_frags<A_KMAJOR, B_KMAJOR>(f[0], st[0], 0, wm, wn, la, lb);
+  step(True{}, st[0], st[1], st[3], kt_beg, f);
+  for (int kt = kt_beg + 1; kt < kt_end; kt += 4) {
+    step(False{}, st[1], st[2], st[0], kt, f);
+    if (kt + 1 < kt_end) step(False{}, st[2], st[3], st[1], kt + 1, f);
+    if (kt + 2 < kt_end) step(False{}, st[3], st[0], st[2], kt + 2, f);
+    if (kt + 3 < kt_end) step(False{}, st[0], st[1], st[3], kt + 3, f);
   }
-  EpiCtx ctx{m0, n0, tm, tn, split, wm, wn, lane, lds0, lds1};
+  EpiCtx ctx{m0, n0, tm, tn, split, wm, wn, lane, lds0, lds1, lds2, lds3};
   epi(acc, ctx);
 }
 

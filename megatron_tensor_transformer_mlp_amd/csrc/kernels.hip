@@ -295,7 +295,7 @@ hipError_t launch_vocab_ce(const uint16_t* X, const uint16_t* E, const int64_t* 
   float* pz = (float*)((char*)ws + w.off_z);
   GemmGeom g = make_geom(T, v, h, 1);
   Operand a{X, h, T * h}, b{E, v, h * v};
-  EpiCE e{target, vocab_start, pm, ps, pz, (int)T, (int)v};
+  EpiCE e{target, vocab_start, pm, (int)((w.off_s - w.off_m) / 4), (int)T, (int)v, 0};
   hipError_t err = launch_gemm<true, false>(g, a, b, e, st);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(ce_tile_combine, dim3((unsigned)((T + 63) / 64)), dim3(512), 0, st, pm, ps, pz, w.parts,
