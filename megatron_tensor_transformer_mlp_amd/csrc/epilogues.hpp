@@ -27,29 +27,59 @@ constexpr float kSqrt2OverPi = 0.79788456080286535588f;
 constexpr float kTanhC = 0.044715f;
 constexpr float kLog2e = 1.44269504088896340736f;
 
-// GeLU and its derivative in fp32.  Erf form: x*Phi(x) with Phi from erff;
-// tanh form: the GELU paper's approximation 0.5x(1 + tanh(sqrt(2/pi)(x + c x^3))).
+// GeLU and its derivative in fp32.
+//
+// Erf form, GeLU(x) = x Phi(x) = x (1 + erf(x / sqrt 2)) / 2.  erf is evaluated
+// with Abramowitz & Stegun, Handbook of Mathematical Functions, formula
+// 7.1.26: for z >= 0, erf(z) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5))))
+// exp(-z^2), t = 1 / (1 + p z), with absolute error below 1.5e-7 (far below the
+// bf16 rounding of the outputs); erf(-z) = -erf(z).  The derivative
+// Phi(x) + x phi(x) reuses the same exp(-x^2 / 2) for phi.  One reciprocal and
+// one exp2 per element (hardware v_rcp_f32 / v_exp_f32).
+// Tanh form: the GELU paper's approximation 0.5 x (1 + tanh(u)),
+// u = sqrt(2/pi) (x + 0.044715 x^3), written as x * sigmoid(2u).
+constexpr float kAsP = 0.3275911f;
+constexpr float kAs1 = 0.254829592f, kAs2 = -0.284496736f, kAs3 = 1.421413741f, kAs4 = -1.453152027f,
+                kAs5 = 1.061405429f;
+
+struct ErfParts {
+  float phi_cdf;  // Phi(x)
+  float pdf;      // phi(x) = exp(-x^2/2) / sqrt(2 pi)
+};
+
+__device__ __forceinline__ ErfParts erf_parts(float x) {
+  const float z = fabsf(x) * kInvSqrt2;
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(kAsP, z, 1.0f));
+  const float poly = t * __builtin_fmaf(t, __builtin_fmaf(t, __builtin_fmaf(t, __builtin_fmaf(t, kAs5, kAs4), kAs3), kAs2), kAs1);
+  const float e = __builtin_amdgcn_exp2f(-0.5f * kLog2e * x * x);  // exp(-z^2) = exp(-x^2/2)
+  const float tail = 0.5f * poly * e;                                 // (1 - erf(z)) / 2
+  ErfParts r;
+  r.phi_cdf = x >= 0.0f ? 1.0f - tail : tail;
+  r.pdf = kInvSqrt2Pi * e;
+  return r;
+}
+
 template <int FORM>
 __device__ __forceinline__ float gelu_f(float x) {
   if constexpr (FORM == kGeluErf) {
-    return 0.5f * x * (1.0f + erff(x * kInvSqrt2));
+    return x * erf_parts(x).phi_cdf;
   } else {
-    const float u = kSqrt2OverPi * x * (1.0f + kTanhC * x * x);
-    return 0.5f * x * (1.0f + tanhf(u));
+    const float u2 = 2.0f * kSqrt2OverPi * x * __builtin_fmaf(kTanhC * x, x, 1.0f);
+    return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-u2 * kLog2e));
   }
 }
 
 template <int FORM>
 __device__ __forceinline__ float gelu_grad_f(float x) {
   if constexpr (FORM == kGeluErf) {
-    const float cdf = 0.5f * (1.0f + erff(x * kInvSqrt2));
-    const float pdf = kInvSqrt2Pi * expf(-0.5f * x * x);
-    return cdf + x * pdf;
+    const ErfParts p = erf_parts(x);
+    return __builtin_fmaf(x, p.pdf, p.phi_cdf);
   } else {
-    const float u = kSqrt2OverPi * x * (1.0f + kTanhC * x * x);
-    const float th = tanhf(u);
-    const float du = kSqrt2OverPi * (1.0f + 3.0f * kTanhC * x * x);
-    return 0.5f * (1.0f + th) + 0.5f * x * (1.0f - th * th) * du;
+    // d/dx [x s(2u)] = s + x s (1 - s) 2u',  s = sigmoid(2u),  u' = sqrt(2/pi)(1 + 3c x^2)
+    const float u2 = 2.0f * kSqrt2OverPi * x * __builtin_fmaf(kTanhC * x, x, 1.0f);
+    const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-u2 * kLog2e));
+    const float du2 = 2.0f * kSqrt2OverPi * __builtin_fmaf(3.0f * kTanhC * x, x, 1.0f);
+    return __builtin_fmaf(x * sg * (1.0f - sg), du2, sg);
   }
 }
 
