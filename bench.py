@@ -9,14 +9,23 @@ in HBM before the timed region.  Prints one JSON line.
 
 value = algorithmic TFLOP/s of the whole step: (12*T*h*f_i + 2*T*h*v_i) / step time.
 The MLP fwd+bwd TFLOP/s, the CE tokens/s and their fractions of the bf16 MFMA peak
-are reported alongside.  ``roofline`` covers the dominant kernel (the fused
-logits-GEMM + CE epilogue), timed with HIP events on the launch stream; the
+are reported alongside.  ``roofline`` covers the dominant kernel, the logits GEMM
+with the fused CE epilogue: the library records a pair of HIP events on its launch
+stream around that one launch in every timed step (ms_arm_kernel_events), and
+``achieved`` = 2*T*h*v_i / the mean of those durations.  ``traffic`` is the HBM
+bytes per launch that the committed counter summary for this workload gives
+(FETCH_SIZE + WRITE_SIZE, scaled by the copy calibration), or null when the
+kernel sources have changed since the counters were taken.  ``kernels_us`` is a
+per-GEMM breakdown from a separate pass after the timed region.  The
 ``cpu_baseline`` leg times the fp64 oracle on a bounded token sample of the same
 workload on the host cores.
+
+    python bench.py --copy-calibration   # only a plain 1 GiB device copy, for counter scaling
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -30,6 +39,9 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0
+# sources that define the GEMM kernels; counter-derived traffic is trusted only for these exact bytes
+KERNEL_SOURCES = ("gemm_core.hpp", "epilogues.hpp", "kernels.hip", "launch.hpp")
+TRAFFIC_MARK = "TRAFFIC_JSON "
 
 
 def _args():
@@ -40,7 +52,48 @@ def _args():
     p.add_argument("--workload", default="gpt2_1p5b")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle CPU time")
+    p.add_argument("--no-breakdown", action="store_true", help="skip the per-GEMM breakdown pass")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run only a plain device copy of 1 GiB (5 launches) and exit")
     return p.parse_args()
+
+
+def kernel_sources_sha256() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "megatron_tensor_transformer_mlp_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def committed_traffic(workload: str):
+    """HBM bytes per launch of the CE GEMM from profiles/, if taken on the current sources."""
+    path = os.path.join(ROOT, "profiles", f"ce_gemm_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None, "no counter summary for this workload"
+    rec = None
+    with open(path) as f:
+        for line in f:
+            if line.startswith(TRAFFIC_MARK):
+                rec = json.loads(line[len(TRAFFIC_MARK):])
+    if rec is None:
+        return None, "counter summary has no traffic record"
+    if rec.get("source_sha256") != kernel_sources_sha256():
+        return None, "kernel sources changed since the counters were taken"
+    return int(rec["hbm_bytes_per_launch"]), os.path.relpath(path, ROOT)
+
+
+def copy_calibration():
+    """A plain streaming copy of known size: 1 GiB read + 1 GiB written per launch."""
+    import torch
+    n = 1 << 28  # fp32 elements = 1 GiB
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)  # elementwise: reads n*4 bytes, writes n*4 bytes
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"read_bytes": n * 4, "write_bytes": n * 4, "launches": 5,
+                                           "kernel": "torch.neg elementwise (fp32, 1 GiB)"}}), flush=True)
 
 
 def cpu_baseline(cfg, d, target_s: float):
@@ -64,18 +117,20 @@ def cpu_baseline(cfg, d, target_s: float):
 
     ctx = threadpool_limits(limits=cores) if threadpool_limits else None
     try:
-        Ts = 64
+        # the weight conversions are a fixed cost per call, so grow the sample by doubling
+        # until one run takes target_s (or the sample is the whole batch)
+        Ts = min(cfg.T, 256)
         dt = run(Ts)
-        Ts = int(min(cfg.T, max(64, Ts * target_s / max(dt, 1e-3))))
-        Ts -= Ts % 64 if Ts > 64 else 0
-        dt = run(Ts)
+        while dt < target_s and Ts < cfg.T:
+            Ts = min(cfg.T, 2 * Ts)
+            dt = run(Ts)
     finally:
         if ctx is not None:
             ctx.__exit__(None, None, None)
     flop = 12 * Ts * cfg.h * cfg.f_i + 2 * Ts * cfg.h * cfg.v_i
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"numpy fp64 oracle, MLP fwd+bwd + CE shard + combine on the first {Ts} of {cfg.T} "
-                      f"tokens ({flop / 1e9:.1f} GFLOP in {dt:.2f} s)",
+                      f"tokens ({flop / 1e9:.1f} GFLOP in {dt:.2f} s, weight conversions included)",
             "seconds": dt}
 
 
@@ -85,6 +140,9 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported (the multi-GPU exchange "
               "is not part of this library)", file=sys.stderr)
         sys.exit(2)
+    if a.copy_calibration:
+        copy_calibration()
+        return
 
     import torch
 
@@ -118,41 +176,60 @@ def main():
     vstart = int(d["vocab_start"])
 
     stream = torch.cuda.current_stream(dev)
-    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
-    def step(events=None):
-        if events is not None:
-            events[0].record(stream)
+    def ev():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)  # creates the device event so its handle can be handed to the library
+        return e
+
+    def step(phase=None, arm=()):
+        for name, (e0, e1) in arm:
+            mshard.arm_kernel_events(name, e0, e1)
+        if phase is not None:
+            phase[0].record(stream)
         mshard.mlp_shard_fwd(X, A, B, None, out=(H, Y, Z))
         mshard.mlp_shard_bwd(X, A, B, H, Y, dZ, workspace=mlp_ws, out=(dX, dA, dB, None))
-        if events is not None:
-            events[1].record(stream)
+        if phase is not None:
+            phase[1].record(stream)
         mshard.vocab_ce_shard_fwd(X, E, tg, vstart, workspace=ce_ws, out=(m[0], s[0], z[0]))
-        if events is not None:
-            events[2].record(stream)
         mshard.ce_combine(m, s, z, out=(loss, mean))
-        if events is not None:
-            events[3].record(stream)
+        if phase is not None:
+            phase[2].record(stream)
 
     for _ in range(a.warmup):
         step()
+    phases = [[ev() for _ in range(3)] for _ in range(a.steps)]
+    gemm_ev = [(ev(), ev()) for _ in range(a.steps)]
     torch.cuda.synchronize()
-    evs = [[ev() for _ in range(4)] for _ in range(a.steps)]
     t0 = time.perf_counter()
     for k in range(a.steps):
-        step(evs[k])
+        step(phases[k], arm=[("ce_gemm", gemm_ev[k])])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
     ms_step = wall * 1e3 / a.steps
-    mlp_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    ce_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    comb_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    mlp_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in phases]))
+    ce_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in phases]))
+    gemm_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in gemm_ev]))
     mlp_flop, ce_flop = cfg.mlp_flop, cfg.ce_flop
     value = (mlp_flop + ce_flop) / (ms_step * 1e-3) / 1e12
     mlp_tflops = mlp_flop / (mlp_ms * 1e-3) / 1e12
     ce_tflops = ce_flop / (ce_ms * 1e-3) / 1e12
+    gemm_tflops = ce_flop / (gemm_ms * 1e-3) / 1e12
 
+    kernels_us = None
+    if not a.no_breakdown:
+        names = list(mshard.KERNELS)
+        reps = 5
+        kev = [[(ev(), ev()) for _ in names] for _ in range(reps)]
+        torch.cuda.synchronize()
+        for r in range(reps):
+            step(arm=list(zip(names, kev[r])))
+        torch.cuda.synchronize()
+        kernels_us = {n: round(1e3 * float(np.mean([kev[r][i][0].elapsed_time(kev[r][i][1]) for r in range(reps)])), 1)
+                      for i, n in enumerate(names)}
+
+    traffic, traffic_src = committed_traffic(cfg.name)
     out = {
         "metric": "MLP-shard fwd+bwd TFLOP/s + fused vocab-CE tokens/s, % of bf16 MFMA peak",
         "value": round(value, 2),
@@ -177,11 +254,12 @@ def main():
         "ce_tflops": round(ce_tflops, 2),
         "ce_pct_of_peak": round(100 * ce_tflops / PEAK_BF16_TFLOPS, 2),
         "ce_ms": round(ce_ms, 4),
-        "ce_combine_ms": round(comb_ms, 4),
-        "roofline": {"bound": "mfma", "kernel": "fused logits GEMM + CE epilogue (vocab_ce_shard_fwd)",
-                     "achieved": round(ce_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(ce_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+        "roofline": {"bound": "mfma", "kernel": "logits GEMM X E_i with fused CE epilogue (gemm_kernel<EpiCE>)",
+                     "achieved": round(gemm_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "traffic_source": traffic_src, "launch_us": round(gemm_ms * 1e3, 1),
                      "algorithmic_flop_per_launch": ce_flop},
+        "kernels_us": kernels_us,
     }
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, d, a.cpu_seconds)

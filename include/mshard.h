@@ -142,6 +142,29 @@ ms_status ce_combine(const float* m, const float* s, const float* z, int32_t t, 
                      float* loss, float* loss_mean,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* Kernels that ms_arm_kernel_events can bracket (one GEMM launch each; the
+ * split-K reductions and CE tile-combine kernels are not included). */
+typedef enum {
+  MS_K_CE_GEMM = 0, /* vocab_ce_shard_fwd: X E_i with the fused CE epilogue     */
+  MS_K_FWD_H = 1,   /* mlp_shard_fwd:  X A_i (+ b1) with the GeLU epilogue      */
+  MS_K_FWD_Z = 2,   /* mlp_shard_fwd:  Y_i B_i -> Z_i                           */
+  MS_K_BWD_DH = 3,  /* mlp_shard_bwd:  dZ B_i^T with the GeLU' epilogue -> dH   */
+  MS_K_BWD_DB = 4,  /* mlp_shard_bwd:  Y_i^T dZ                                 */
+  MS_K_BWD_DA = 5,  /* mlp_shard_bwd:  X^T dH                                   */
+  MS_K_BWD_DX = 6,  /* mlp_shard_bwd:  dH A_i^T -> dX_i                         */
+  MS_K_COUNT = 7
+} ms_kernel;
+
+/* Measurement hook, no effect on results.  Arms two caller-created HIP events
+ * (hipEvent_t passed as void*, created with timing enabled) for kernel k: the
+ * next call on this host thread of the entry point that launches k records
+ * `before` on its stream immediately before that launch and `after`
+ * immediately after it, so hipEventElapsedTime(before, after) is that one
+ * kernel's device time.  The entry point disarms k when it returns (also on
+ * error).  before == after == NULL disarms k.  Errors: MS_ERR_ENUM for an
+ * unknown k, MS_ERR_NULL if exactly one event is NULL. */
+ms_status ms_arm_kernel_events(ms_kernel k, void* before, void* after);
+
 /* Text for the last non-OK status returned on the calling thread ("" if none).
  * The pointer stays valid until the next library call on this thread. */
 const char* ms_last_error(void);

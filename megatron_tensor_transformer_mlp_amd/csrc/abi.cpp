@@ -17,6 +17,20 @@ namespace {
 
 thread_local std::string g_last_error;
 
+// Events armed by ms_arm_kernel_events, per kernel id, on this thread.
+struct ArmedPair {
+  hipEvent_t before = nullptr, after = nullptr;
+};
+thread_local ArmedPair g_armed[mshard::kTkCount];
+
+// Disarms the listed kernels when an entry point returns, whatever the path.
+struct DisarmOnReturn {
+  int first, last;  // kernel ids [first, last] belong to one entry point
+  ~DisarmOnReturn() {
+    for (int id = first; id <= last; ++id) g_armed[id] = ArmedPair{};
+  }
+};
+
 ms_status fail(ms_status st, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -118,6 +132,13 @@ ms_status launched(hipError_t e, const char* what) {
 
 }  // namespace
 
+namespace mshard {
+void record_armed_event(int id, bool after, hipStream_t st) {
+  const hipEvent_t ev = after ? g_armed[id].after : g_armed[id].before;
+  if (ev) (void)hipEventRecord(ev, st);
+}
+}  // namespace mshard
+
 extern "C" {
 
 size_t mlp_shard_workspace_bytes(int64_t T, int64_t h, int64_t f_i) {
@@ -128,6 +149,7 @@ size_t mlp_shard_workspace_bytes(int64_t T, int64_t h, int64_t f_i) {
 ms_status mlp_shard_fwd(const ms_bf16* X, const ms_bf16* A_i, const ms_bf16* b1_i, const ms_bf16* B_i,
                         int64_t T, int64_t h, int64_t f_i, ms_gelu gelu, ms_bf16* H_i, ms_bf16* Y_i, float* Z_i,
                         void* workspace, size_t workspace_bytes, void* stream) {
+  const DisarmOnReturn disarm{mshard::kTkFwdH, mshard::kTkFwdZ};
   (void)workspace;
   (void)workspace_bytes;  // the forward needs no workspace
   MS_TRY(check_dims(T, {{"h", h}, {"f_i", f_i}}));
@@ -148,6 +170,7 @@ ms_status mlp_shard_bwd(const ms_bf16* X, const ms_bf16* A_i, const ms_bf16* B_i
                         const ms_bf16* Y_i, const ms_bf16* dZ, int64_t T, int64_t h, int64_t f_i, ms_gelu gelu,
                         float* dX_i, ms_bf16* dA_i, ms_bf16* dB_i, ms_bf16* db1_i, void* workspace,
                         size_t workspace_bytes, void* stream) {
+  const DisarmOnReturn disarm{mshard::kTkBwdDH, mshard::kTkBwdDX};
   MS_TRY(check_dims(T, {{"h", h}, {"f_i", f_i}}));
   if (gelu != MS_GELU_ERF && gelu != MS_GELU_TANH) return fail(MS_ERR_ENUM, "unknown gelu form %d", (int)gelu);
   std::vector<Buf> bufs = {
@@ -173,6 +196,7 @@ size_t vocab_ce_workspace_bytes(int64_t T, int64_t h, int64_t v_i) {
 ms_status vocab_ce_shard_fwd(const ms_bf16* X, const ms_bf16* E_i, const int64_t* target, int64_t T, int64_t h,
                              int64_t v_i, int64_t vocab_start, float* m_i, float* s_i, float* z_i,
                              void* workspace, size_t workspace_bytes, void* stream) {
+  const DisarmOnReturn disarm{mshard::kTkCeGemm, mshard::kTkCeGemm};
   MS_TRY(check_dims(T, {{"h", h}, {"v_i", v_i}}));
   if (vocab_start < 0) return fail(MS_ERR_SHAPE, "vocab_start must be >= 0 (got %lld)", (long long)vocab_start);
   std::vector<Buf> bufs = {{X, nbytes(T, h, 2), "X", false},     {E_i, nbytes(h, v_i, 2), "E_i", false},
@@ -206,6 +230,15 @@ ms_status ce_combine(const float* m, const float* s, const float* z, int32_t t, 
   MS_TRY(check_bufs(bufs));
   MS_TRY(check_device());
   return launched(mshard::launch_ce_combine(m, s, z, t, T, loss, loss_mean, (hipStream_t)stream), "ce_combine");
+}
+
+ms_status ms_arm_kernel_events(ms_kernel k, void* before, void* after) {
+  if ((int)k < 0 || (int)k >= mshard::kTkCount) return fail(MS_ERR_ENUM, "unknown kernel id %d", (int)k);
+  if ((before == nullptr) != (after == nullptr))
+    return fail(MS_ERR_NULL, "ms_arm_kernel_events: give both events or neither");
+  g_armed[k].before = (hipEvent_t)before;
+  g_armed[k].after = (hipEvent_t)after;
+  return MS_OK;
 }
 
 const char* ms_last_error(void) { return g_last_error.c_str(); }

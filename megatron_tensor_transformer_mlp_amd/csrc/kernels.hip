@@ -144,11 +144,14 @@ static GemmGeom make_geom(int64_t M, int64_t N, int64_t K, int splits) {
 }
 
 template <bool AK, bool BK, class Epi>
-static hipError_t launch_gemm(const GemmGeom& g, const Operand& a, const Operand& b, const Epi& epi,
+static hipError_t launch_gemm(int id, const GemmGeom& g, const Operand& a, const Operand& b, const Epi& epi,
                               hipStream_t stream) {
   const int blocks = g.tiles_m * g.tiles_n * g.splits;
+  record_armed_event(id, false, stream);
   hipLaunchKernelGGL((gemm_kernel<AK, BK, Epi>), dim3(blocks), dim3(kThreads), 0, stream, g, a, b, epi);
-  return hipGetLastError();
+  const hipError_t err = hipGetLastError();
+  record_armed_event(id, true, stream);
+  return err;
 }
 
 int weight_grad_splits(int64_t M, int64_t N, int64_t K) {
@@ -200,7 +203,7 @@ static hipError_t mlp_fwd_impl(const uint16_t* X, const uint16_t* A, const uint1
     GemmGeom g = make_geom(T, f, h, 1);
     Operand a{X, h, T * h}, b{A, f, h * f};
     EpiGeluFwd<FORM> e{H, Y, b1, f, (int)T, (int)f};
-    hipError_t err = launch_gemm<true, false>(g, a, b, e, st);
+    hipError_t err = launch_gemm<true, false>(kTkFwdH, g, a, b, e, st);
     if (err != hipSuccess) return err;
   }
   // Z = Y B:  NN, M = T, N = h, K = f
@@ -208,7 +211,7 @@ static hipError_t mlp_fwd_impl(const uint16_t* X, const uint16_t* A, const uint1
     GemmGeom g = make_geom(T, h, f, 1);
     Operand a{Y, f, T * f}, b{B, h, f * h};
     EpiStoreF32 e{Z, h, (int)T, (int)h, 0};
-    return launch_gemm<true, false>(g, a, b, e, st);
+    return launch_gemm<true, false>(kTkFwdZ, g, a, b, e, st);
   }
 }
 
@@ -221,17 +224,17 @@ hipError_t launch_mlp_fwd(const uint16_t* X, const uint16_t* A, const uint16_t* 
 
 // Weight gradient C[M x N] = sum_t P[t, m] Q[t, n] (TN), bf16 result, with an
 // optional deterministic K split through fp32 workspace slices.
-static hipError_t weight_grad(const uint16_t* P, int64_t ldp, const uint16_t* Q, int64_t ldq, int64_t Kt,
+static hipError_t weight_grad(int id, const uint16_t* P, int64_t ldp, const uint16_t* Q, int64_t ldq, int64_t Kt,
                               int64_t M, int64_t N, int S, uint16_t* C, float* splitk, hipStream_t st) {
   GemmGeom g = make_geom(M, N, Kt, S);
   S = g.splits;
   Operand a{P, ldp, Kt * ldp}, b{Q, ldq, Kt * ldq};
   if (S == 1) {
     EpiStoreBF16 e{C, N, (int)M, (int)N};
-    return launch_gemm<false, false>(g, a, b, e, st);
+    return launch_gemm<false, false>(id, g, a, b, e, st);
   }
   EpiStoreF32 e{splitk, N, (int)M, (int)N, M * N};
-  hipError_t err = launch_gemm<false, false>(g, a, b, e, st);
+  hipError_t err = launch_gemm<false, false>(id, g, a, b, e, st);
   if (err != hipSuccess) return err;
   const int64_t n = M * N;  // multiple of 8
   const int64_t blocks = (n / 8 + 255) / 256;
@@ -253,21 +256,21 @@ static hipError_t mlp_bwd_impl(const uint16_t* X, const uint16_t* A, const uint1
     GemmGeom g = make_geom(T, f, h, 1);
     Operand a{dZ, h, T * h}, b{B, h, f * h};
     EpiDGelu<FORM> e{H, dH, db1_part, f, (int)T, (int)f};
-    err = launch_gemm<true, true>(g, a, b, e, st);
+    err = launch_gemm<true, true>(kTkBwdDH, g, a, b, e, st);
     if (err != hipSuccess) return err;
   }
   // dB = Y^T dZ:  [f x h], contraction over tokens
-  err = weight_grad(Y, f, dZ, h, T, f, h, w.splits_dB, dB, splitk, st);
+  err = weight_grad(kTkBwdDB, Y, f, dZ, h, T, f, h, w.splits_dB, dB, splitk, st);
   if (err != hipSuccess) return err;
   // dA = X^T dH:  [h x f]
-  err = weight_grad(X, h, dH, f, T, h, f, w.splits_dA, dA, splitk, st);
+  err = weight_grad(kTkBwdDA, X, h, dH, f, T, h, f, w.splits_dA, dA, splitk, st);
   if (err != hipSuccess) return err;
   // dX = dH A^T:  NT, M = T, N = h, K = f; A stored [h x f] = [N x K]
   {
     GemmGeom g = make_geom(T, h, f, 1);
     Operand a{dH, f, T * f}, b{A, f, h * f};
     EpiStoreF32 e{dX, h, (int)T, (int)h, 0};
-    err = launch_gemm<true, true>(g, a, b, e, st);
+    err = launch_gemm<true, true>(kTkBwdDX, g, a, b, e, st);
     if (err != hipSuccess) return err;
   }
   if (db1) {
@@ -296,7 +299,7 @@ hipError_t launch_vocab_ce(const uint16_t* X, const uint16_t* E, const int64_t* 
   GemmGeom g = make_geom(T, v, h, 1);
   Operand a{X, h, T * h}, b{E, v, h * v};
   EpiCE e{target, vocab_start, pm, (int)((w.off_s - w.off_m) / 4), (int)T, (int)v, 0};
-  hipError_t err = launch_gemm<true, false>(g, a, b, e, st);
+  hipError_t err = launch_gemm<true, false>(kTkCeGemm, g, a, b, e, st);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(ce_tile_combine, dim3((unsigned)((T + 63) / 64)), dim3(512), 0, st, pm, ps, pz, w.parts,
                      (int)T, m, s, z);

@@ -24,6 +24,13 @@ struct CeWorkspace {
   int parts;
 };
 
+// Kernel ids for the measurement hook (same values as ms_kernel in mshard.h).
+enum TimedKernel { kTkCeGemm = 0, kTkFwdH, kTkFwdZ, kTkBwdDH, kTkBwdDB, kTkBwdDA, kTkBwdDX, kTkCount };
+
+// Records the armed event (if any) of kernel `id` on `st`; `after` picks which
+// of the pair.  Defined by the ABI layer, which owns the per-thread arming.
+void record_armed_event(int id, bool after, hipStream_t st);
+
 int weight_grad_splits(int64_t M, int64_t N, int64_t K);
 MlpWorkspace mlp_workspace_layout(int64_t T, int64_t h, int64_t f);
 CeWorkspace ce_workspace_layout(int64_t T, int64_t v);

@@ -26,7 +26,11 @@ STATUS_NAMES = ["MS_OK", "MS_ERR_NULL", "MS_ERR_SHAPE", "MS_ERR_ALIGN", "MS_ERR_
 GELU = {"erf": 0, "tanh": 1}
 
 EXPORTED = ("mlp_shard_workspace_bytes", "mlp_shard_fwd", "mlp_shard_bwd", "vocab_ce_workspace_bytes",
-            "vocab_ce_shard_fwd", "ce_combine_workspace_bytes", "ce_combine", "ms_last_error", "ms_version")
+            "vocab_ce_shard_fwd", "ce_combine_workspace_bytes", "ce_combine", "ms_arm_kernel_events",
+            "ms_last_error", "ms_version")
+
+# ms_kernel ids: the single GEMM launches ms_arm_kernel_events can bracket
+KERNELS = {"ce_gemm": 0, "fwd_h": 1, "fwd_z": 2, "bwd_dh": 3, "bwd_db": 4, "bwd_da": 5, "bwd_dx": 6}
 
 
 class MshardError(RuntimeError):
@@ -54,6 +58,7 @@ def _load() -> ctypes.CDLL:
         "vocab_ce_shard_fwd": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
         "ce_combine_workspace_bytes": (_sz, [_i32, _i64]),
         "ce_combine": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i64, _vp, _vp, _vp, _sz, _vp]),
+        "ms_arm_kernel_events": (ctypes.c_int, [ctypes.c_int, _vp, _vp]),
         "ms_last_error": (ctypes.c_char_p, []),
         "ms_version": (ctypes.c_char_p, []),
     }
@@ -69,6 +74,18 @@ LIB = _load()
 
 def version() -> str:
     return LIB.ms_version().decode()
+
+
+def arm_kernel_events(kernel: str, before: Optional[torch.cuda.Event], after: Optional[torch.cuda.Event]) -> None:
+    """Have the next call (on this thread) of the entry point that launches `kernel`
+    record `before`/`after` on its stream around that one GEMM launch; None, None
+    disarms.  The events must already exist on the device (record them once)."""
+    if (before is None) != (after is None):
+        raise ValueError("give both events or neither")
+    handles = (None, None) if before is None else (before.cuda_event, after.cuda_event)
+    if before is not None and not (handles[0] and handles[1]):
+        raise ValueError("events have no device handle yet; record them once first")
+    _check(LIB.ms_arm_kernel_events(KERNELS[kernel], *handles), "ms_arm_kernel_events")
 
 
 def _check(status: int, func: str) -> None:

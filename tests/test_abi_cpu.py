@@ -126,3 +126,15 @@ def test_binding_has_no_fallback():
             text = open(os.path.join(pkg, fn)).read()
             assert not re.search(r"^\s*(from|import)\s+oracle", text, flags=re.M), fn
             assert "sys.path" not in text, fn
+
+
+def test_arm_kernel_events_validation(ms):
+    fake_ev = FAKE  # never recorded: the arming is cleared again below without a launch
+    assert ms.LIB.ms_arm_kernel_events(7, None, None) == ms.MS_ERR_ENUM
+    assert ms.LIB.ms_arm_kernel_events(-1, None, None) == ms.MS_ERR_ENUM
+    assert ms.LIB.ms_arm_kernel_events(0, fake_ev, None) == ms.MS_ERR_NULL
+    assert "both events" in ms.LIB.ms_last_error().decode()
+    assert ms.LIB.ms_arm_kernel_events(0, None, None) == ms.MS_OK
+    for k in range(7):
+        assert ms.LIB.ms_arm_kernel_events(k, None, None) == ms.MS_OK
+    assert set(ms.KERNELS.values()) == set(range(7))
