@@ -59,10 +59,17 @@ def _args():
 
 
 def kernel_sources_sha256() -> str:
+    """SHA-256 over the GEMM sources with comments and blank lines removed, so that
+    only a change to the code itself invalidates counters taken on it."""
+    import re
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "megatron_tensor_transformer_mlp_amd", "csrc", name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(ROOT, "megatron_tensor_transformer_mlp_amd", "csrc", name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        code = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+        h.update(name.encode() + b"\0" + code.encode())
     return h.hexdigest()
 
 

@@ -15,18 +15,17 @@
 //   * One workgroup = 256 threads = 4 wave64s computes a 256 x 256 tile of C.
 //     The waves form a 2 x 2 grid, each owning a 128 x 128 sub-tile held as
 //     4 x 4 fp32 32x32 MFMA accumulators (256 accumulation registers per lane).
-//   * K advances in steps of 64.  Each step's A and B tiles are staged in LDS
-//     (2 x 32 KiB), double buffered (128 KiB total), one barrier per step.
-//     Global loads of step k+1 are issued before the MFMAs of step k.
-//   * LDS holds both operands K-contiguous: one 128-byte row per m (or n), split
-//     into eight 16-byte chunks of 8 k values.  Chunk c of row r is stored at
-//     slot c ^ (r & 7), so the 16-byte fragment reads of 8 consecutive rows
-//     (and the 16-byte tile writes) hit distinct bank groups.
-//   * M/N-major operands are loaded as 8 x 8 bf16 blocks (8 k rows of 16 bytes)
-//     and transposed in registers with v_perm before the LDS write.
-//   * MFMA v_mfma_f32_32x32x16_bf16 (16 k per instruction; 4 k steps per LDS
+//   * K advances in steps of 32.  A ring of 4 LDS stages (32 KiB each: the A
+//     and B tiles of one step) holds step kt being consumed, kt+1 and kt+2
+//     resident or landing, and kt+3 being loaded; the loads of kt+3 are
+//     interleaved with the MFMAs of kt.  One barrier per step.
+//   * Global -> LDS moves use direct-to-LDS buffer loads (no staging
+//     registers); the layouts (see below) make every fragment read
+//     conflict-free: K-major tiles are read with ds_read_b128, M/N-major tiles
+//     with the transposing ds_read_b64_tr_b16.
+//   * MFMA v_mfma_f32_32x32x16_bf16 (16 k per instruction; 2 k steps per LDS
 //     stage).  The fragments of k step s+1 are read from LDS while the 16
-//     MFMAs of step s run (two fragment register sets of 32 VGPRs).
+//     MFMAs of step s run (two fragment register sets).
 //   * The MFMA is issued with the B fragment as its first operand and the A
 //     fragment as its second, so each lane ends up holding, for every 32x32
 //     block, row l%32 and the four 4-column groups 8g + 4*(l/32) .. +3
