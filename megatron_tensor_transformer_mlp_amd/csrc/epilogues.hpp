@@ -1,14 +1,13 @@
 // epilogues.hpp - what each GEMM does with its fp32 accumulators.
 //
-// Accumulator element acc[mi][ni][4g + r] of wave (wm, wn) in the tile at
-// (m0, n0) is C[m0 + wm*128 + mi*32 + (lane & 31)]
-//              [n0 + wn*128 + ni*32 + 8g + 4*(lane >> 5) + r],   g, r = 0..3.
+// Accumulator element acc[mi][ni][r] of wave (wm, wn) in the tile at (m0, n0)
+// is C[m0 + wm*128 + mi*16 + (lane & 15)][n0 + wn*128 + ni*16 + 4*(lane >> 4) + r].
 //
 // Epilogues hand the accumulators over through LDS: each wave writes its
 // 128 x 128 fp32 sub-tile, 64 rows at a time, into a private 32 KiB region
-// (row pitch 512 bytes, 16-byte chunk q of row r at slot q ^ (r & 7), so 8
-// consecutive rows of one chunk hit distinct banks), then reads it back in a
-// row-major lane order.  The accumulators are therefore only ever stored,
+// (row pitch 512 bytes, 16-byte chunk q of row r at slot q ^ (r & 15), so the
+// 16 rows written or read together hit distinct banks), then reads it back in
+// a row-major lane order.  The accumulators are therefore only ever stored,
 // which keeps them in the accumulation registers through the main loop, and
 // global stores become full 256/512-byte row segments.  N is a multiple of 8,
 // so every 4-column group is entirely inside or outside the matrix; rows are
@@ -91,23 +90,16 @@ __device__ __forceinline__ char* epi_region(const EpiCtx& c) {
   return wave == 0 ? c.lds0 : (wave == 1 ? c.lds1 : (wave == 2 ? c.lds2 : c.lds3));
 }
 
-__device__ __forceinline__ int epi_slot(int lr, int q) { return lr * 512 + ((q ^ (lr & 7)) << 4); }
+__device__ __forceinline__ int epi_slot(int lr, int q) { return lr * 512 + ((q ^ (lr & 15)) << 4); }
 
-// Write rows [64h, 64h + 64) of the wave's sub-tile (row blocks mi = 2h, 2h+1).
-__device__ __forceinline__ void epi_stage_half(const f32x16_t (&acc)[kSubM][kSubN], char* region, int h,
-                                               int lane) {
+// Write rows [64h, 64h + 64) of the wave's sub-tile (row blocks mi = 4h .. 4h+3).
+__device__ __forceinline__ void epi_stage_half(const AccTile& acc, char* region, int h, int lane) {
   if (h == 0) acc_settle();
 #pragma unroll
-  for (int m2 = 0; m2 < 2; ++m2) {
-    const int lr = m2 * 32 + (lane & 31);
+  for (int m4 = 0; m4 < 4; ++m4) {
+    const int lr = m4 * 16 + (lane & 15);
 #pragma unroll
-    for (int ni = 0; ni < kSubN; ++ni)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int q = ni * 8 + 2 * g + (lane >> 5);
-        const f32x16_t& a = acc[2 * h + m2][ni];
-        acc_store_lds(region + epi_slot(lr, q), f32x4_t{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]});
-      }
+    for (int ni = 0; ni < kSubN; ++ni) acc_store_lds(region + epi_slot(lr, ni * 4 + (lane >> 4)), acc[4 * h + m4][ni]);
   }
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_wave_barrier();
@@ -121,7 +113,7 @@ __device__ __forceinline__ f32x4_t epi_read(const char* region, int lr, int q) {
 // Row-major walk of the staged sub-tile: calls f(row, col, v) with tile-local
 // row/col of 4 consecutive values; 32 lanes cover one 128-column row.
 template <class F>
-__device__ __forceinline__ void epi_rows(const f32x16_t (&acc)[kSubM][kSubN], const EpiCtx& c, F&& f) {
+__device__ __forceinline__ void epi_rows(const AccTile& acc, const EpiCtx& c, F&& f) {
   char* region = epi_region(c);
   const int q = c.lane & 31;
 #pragma unroll
@@ -144,7 +136,7 @@ struct EpiStoreF32 {
   int64_t ld;
   int M, N;
   int64_t split_stride;  // elements between split slices (0 when splits == 1)
-  __device__ void operator()(f32x16_t (&acc)[kSubM][kSubN], const EpiCtx& c) const {
+  __device__ void operator()(AccTile& acc, const EpiCtx& c) const {
     const int64_t base = (int64_t)c.split * split_stride + (int64_t)c.m0 * ld + c.n0;
     const rsrc_t rs = make_rsrc(C + base, ((int64_t)c.split * split_stride + (int64_t)M * ld - base) * 4);
     const int mrem = M - c.m0, nrem = N - c.n0;
@@ -160,7 +152,7 @@ struct EpiStoreBF16 {
   uint16_t* C;
   int64_t ld;
   int M, N;
-  __device__ void operator()(f32x16_t (&acc)[kSubM][kSubN], const EpiCtx& c) const {
+  __device__ void operator()(AccTile& acc, const EpiCtx& c) const {
     const int64_t base = (int64_t)c.m0 * ld + c.n0;
     const rsrc_t rs = make_rsrc(C + base, ((int64_t)M * ld - base) * 2);
     const int mrem = M - c.m0, nrem = N - c.n0;
@@ -181,7 +173,7 @@ struct EpiGeluFwd {
   const uint16_t* b1;  // may be null: its resource is then empty and reads give 0
   int64_t ld;
   int M, N;
-  __device__ void operator()(f32x16_t (&acc)[kSubM][kSubN], const EpiCtx& c) const {
+  __device__ void operator()(AccTile& acc, const EpiCtx& c) const {
     const int64_t base = (int64_t)c.m0 * ld + c.n0;
     const int64_t bytes = ((int64_t)M * ld - base) * 2;
     const rsrc_t rh = make_rsrc(H + base, bytes);
@@ -217,7 +209,7 @@ struct EpiDGelu {
   float* db1_part;
   int64_t ld;
   int M, N;
-  __device__ void operator()(f32x16_t (&acc)[kSubM][kSubN], const EpiCtx& c) const {
+  __device__ void operator()(AccTile& acc, const EpiCtx& c) const {
     const int64_t base = (int64_t)c.m0 * ld + c.n0;
     const int64_t bytes = ((int64_t)M * ld - base) * 2;
     const rsrc_t rh = make_rsrc(H + base, bytes);
@@ -284,7 +276,7 @@ struct EpiCE {
   int stride;
   int M, N;     // M = T tokens, N = v_i
   int pad_;
-  __device__ void operator()(f32x16_t (&acc)[kSubM][kSubN], const EpiCtx& c) const {
+  __device__ void operator()(AccTile& acc, const EpiCtx& c) const {
     const rsrc_t rt = make_rsrc(target, (int64_t)M * 8);
     char* region = epi_region(c);
     const int ncol = min(N - c.n0 - c.wn * kWaveN, kWaveN);  // valid columns of this wave (may be <= 0)

@@ -45,6 +45,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 namespace mshard {
 
@@ -59,7 +60,7 @@ constexpr int kBM = 256, kBN = 256, kBK = 32;
 constexpr int kStages = 4;  // LDS ring: tiles kt+1..kt+3 in flight while kt is consumed
 constexpr int kThreads = 256;
 constexpr int kWaveM = 128, kWaveN = 128;
-constexpr int kSubM = kWaveM / 32, kSubN = kWaveN / 32;  // 32x32 MFMA blocks per wave
+constexpr int kSubM = kWaveM / 16, kSubN = kWaveN / 16;  // 16x16 MFMA blocks per wave
 constexpr int kStageBytes = (kBM + kBN) * kBK * 2;  // 32 KiB
 constexpr int kGroupM = 8;
 constexpr int kNumXcd = 8;
@@ -139,14 +140,19 @@ __device__ __forceinline__ void map_tile(const GemmGeom& g, int& tm, int& tn, in
 //
 // Layouts (16-byte slots; a K-major tile is [256 m/n rows][32 k], an
 // M/N-major tile is [32 k rows][256 m/n columns]):
-//   K-major : slot(r, c) = (r/16)*64 + c*16 + r%16       c = k/8 (8 k values)
-//   MN-major: slot(k, j) = (k/4)*128 + j*4 + k%4         j = col/8 (8 columns)
-// LDS serves 16 lanes x 16 bytes (all 64 banks) per cycle.  The K-major layout
-// puts 16 consecutive rows of one k chunk in 256 contiguous bytes, so a 16-lane
-// ds_read_b128 fragment read is conflict-free; the MN-major layout puts 4
-// consecutive k rows of a chunk pair in 128 contiguous bytes (a 16-lane
-// ds_read_b64_tr_b16 read is conflict-free).  In both, the fragment address is
-// one per-lane base plus compile-time offsets.
+//   K-major : slot(r, c) = (r/16)*64 + (r%16)*4 + (c ^ ((r%16)/4 % 4))
+//                                                   c = k/8 (8 k values)
+//   MN-major: slot(k, j) = k*32 + (j ^ 2*((k%4) | 4*((k/8)%2)))
+//                                                   j = col/8 (8 columns)
+// Rows (K-major) and k rows (M/N-major) are contiguous, so each load
+// instruction's 64 lanes read whole 64-byte row segments or 512-byte k rows:
+// neighbouring lanes read neighbouring 16 bytes and the memory pipeline merges
+// them into full cache-line requests.  The XOR terms only permute slots
+// within a row; they make the fragment reads conflict-free (LDS serves 16
+// lanes x 16 bytes or 32 lanes x 8 bytes, all 64 banks, per cycle): a K-major
+// fragment's 16 rows of one chunk fall in 16 different 4-bank groups, and the
+// 8 k rows x 32 bytes that 32 lanes of an M/N-major transposing read touch
+// fall in 8 different 32-byte windows.
 
 typedef __attribute__((address_space(3))) char lds_char;
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -175,117 +181,219 @@ __device__ __forceinline__ u32x4_t make_desc(const void* base, int64_t bytes_lef
 }
 
 // Descriptor of the k tile at k0 of an operand (scalar work, once per tile).
+// Resource for one operand tile whose origin is (mn0, k0): it starts at the
+// tile origin and ends at the end of the stored matrix.  A K-major tile's rows
+// past M and an M/N-major tile's k rows past K therefore lie beyond the end and
+// read as zeros without any lane mask.
 template <bool KMAJOR>
 __device__ __forceinline__ u32x4_t tile_desc(const Operand& op, int mn0, int k0) {
   int64_t base_elem;
   if constexpr (KMAJOR) base_elem = (int64_t)mn0 * op.ld + k0;
   else base_elem = (int64_t)k0 * op.ld + mn0;
-  return make_desc(op.ptr + base_elem, (op.elems - base_elem) * 2);
+  // every operand is smaller than 2^31 bytes and the origin lies inside it
+  const uint64_t p = (uint64_t)(uintptr_t)(op.ptr + base_elem);
+  return u32x4_t{(uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, (uint32_t)((op.elems - base_elem) * 2), kRsrcWord3};
 }
 
-// Direct-to-LDS instruction i (0 .. kDmaPerWave-1) of this wave's share of one
-// operand tile.  The per-lane offset is recomputed each time (a few VALU ops
-// that co-issue with the MFMAs) rather than hoisted into long-lived registers.
+// Loop-invariant per-lane byte offsets of one operand's direct-to-LDS loads,
+// relative to the tile origin, for this wave's kDmaPerWave instructions
+// (which rows, k rows and chunks each lane loads is fixed by the LDS layout):
+//   K-major:   offset = v[0 or 1] + i * step    (v[1]: k chunks past K masked)
+//   M/N-major: offset = v[i % 2] + i * step     (columns past M/N masked)
+// The host keeps every leading dimension below 2^22 elements, so no offset of
+// a 256-row tile wraps 32 bits and a masked offset (kOOB + up to 3 steps)
+// stays out of range.
+struct DmaLanes {
+  uint32_t v[2];
+  uint32_t step;
+};
+
 template <bool KMAJOR>
-__device__ __forceinline__ void dma_one(const Operand& op, u32x4_t desc, int mn0, int nmn, int k0, int K,
-                                        lds_char* tile, int wave, int lane, int i) {
-  asm volatile("" : "+v"(lane));
-  const int inst = wave * kDmaPerWave + i;
-  uint32_t off;
+__device__ __forceinline__ DmaLanes dma_lanes(const Operand& op, int mn0, int nmn, int K, int wave, int lane) {
+  DmaLanes d;
+  const uint32_t ldb = (uint32_t)op.ld * 2u;
   if constexpr (KMAJOR) {
-    // one 16-row group per instruction: slot l -> row l%16, chunk l/16
-    const int r = inst * 16 + (lane & 15), c = lane >> 4;
-    const bool ok = (mn0 + r) < nmn && (k0 + c * 8) < K;
-    off = ok ? (uint32_t)(((int64_t)r * op.ld + c * 8) * 2) : kOOB;
+    // instruction 4w + i writes slots (4w + i)*64 + l: row (4w + i)*16 + l/4,
+    // chunk (l%4) ^ (l/16 % 4)
+    const uint32_t r = (uint32_t)wave * 64u + (uint32_t)(lane >> 2);
+    const int c = (lane & 3) ^ ((lane >> 4) & 3);
+    d.v[0] = r * ldb + (uint32_t)c * 16u;
+    const int tail = K & (kBK - 1);
+    d.v[1] = (c * 8 < tail) ? d.v[0] : kOOB;
+    d.step = 16u * ldb;
   } else {
-    const int k = (inst >> 1) * 4 + (lane & 3), j = (inst & 1) * 16 + (lane >> 2);
-    const bool ok = (k0 + k) < K && (mn0 + j * 8) < nmn;
-    off = ok ? (uint32_t)(((int64_t)k * op.ld + j * 8) * 2) : kOOB;
-  }
-  dma16(desc, off, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(tile + inst * 1024)));
-}
-
-// Direct-to-LDS copy of this wave's share of one operand tile.
-template <bool KMAJOR>
-__device__ __forceinline__ void dma_tile(const Operand& op, int mn0, int nmn, int k0, int K, lds_char* tile,
-                                         int wave, int lane) {
-  const u32x4_t desc = tile_desc<KMAJOR>(op, mn0, k0);
+    // instruction 4w + i writes slots (4w + i)*64 + l: k row 8w + 2i + l/32 and
+    // column group (l%32) ^ 2F with F = ((2i + l/32) % 4) | 4*(w%2); F depends
+    // on i only through i%2
+    const uint32_t k = (uint32_t)wave * 8u + (uint32_t)(lane >> 5);
 #pragma unroll
-  for (int i = 0; i < kDmaPerWave; ++i) dma_one<KMAJOR>(op, desc, mn0, nmn, k0, K, tile, wave, lane, i);
-}
-
-// Per-lane byte offset of this lane's fragment piece inside a tile (k step 0,
-// block 0, wave coordinate 0); the rest of the address is compile-time.
-template <bool KMAJOR>
-__device__ __forceinline__ int frag_lane_base(int lane) {
-  if constexpr (KMAJOR) {
-    // row = blk*32 + l%32 -> (row/16)*1024 + (row%16)*16; chunk = 2*ks + l/32 -> chunk*256
-    return ((lane & 31) >> 4) * 1024 + (lane >> 5) * 256 + (lane & 15) * 16;
-  } else {
-    // group g = l/16 (k half g/2, column half g%2); in-group i: q = i%4 (column quad), e = i/4 (k row)
-    const int g = lane >> 4, i = lane & 15, q = i & 3, e = i >> 2;
-    return e * 16 + (q >> 1) * 64 + (q & 1) * 8 + (g & 1) * 128 + (g >> 1) * 4096;
+    for (int par = 0; par < 2; ++par) {
+      const int F = ((2 * par + (lane >> 5)) & 3) | ((wave & 1) << 2);
+      const int j = (lane & 31) ^ (2 * F);
+      d.v[par] = (mn0 + j * 8 < nmn) ? k * ldb + (uint32_t)j * 16u : kOOB;
+    }
+    d.step = 2u * ldb;
   }
+  return d;
 }
 
-// Fragment of k step ks (16 k) of block blk (32 rows/columns) for wave
-// coordinate w: 8 bf16 k values of row/column l%32 at k = 16ks + 8(l/32) + e.
+// Direct-to-LDS instruction i of this wave's share of one operand tile.
+// `ktail` (K-major only): the tile is the last one and K is not a multiple of
+// 32.  `tile` is the tile's LDS address; `wave_s` the wave index (uniform).
 template <bool KMAJOR>
-__device__ __forceinline__ bf16x8_t load_frag(const lds_char* tile, int lane_base, int w, int blk, int ks) {
+__device__ __forceinline__ void dma_one(const DmaLanes& d, u32x4_t desc, bool ktail, uint32_t tile, int wave_s,
+                                        int i) {
+  uint32_t off;
+  if constexpr (KMAJOR) off = (ktail ? d.v[1] : d.v[0]) + (uint32_t)i * d.step;
+  else off = d.v[i & 1] + (uint32_t)i * d.step;
+  dma16(desc, off, tile + (uint32_t)wave_s * (kDmaPerWave * 1024u) + (uint32_t)i * 1024u);
+}
+
+template <bool KMAJOR>
+__device__ __forceinline__ void dma_tile(const Operand& op, const DmaLanes& d, int mn0, int k0, int K,
+                                         uint32_t tile, int wave_s) {
+  const u32x4_t desc = tile_desc<KMAJOR>(op, mn0, k0);
+  const bool ktail = k0 + kBK > K;
+#pragma unroll
+  for (int i = 0; i < kDmaPerWave; ++i) dma_one<KMAJOR>(d, desc, ktail, tile, wave_s, i);
+}
+
+// Fragments for v_mfma_f32_16x16x32_bf16.  Lane l holds 8 bf16 values of one
+// row (A) or column (B) of a 16-wide block: row/column l%16, k = 8*(l/16) + e
+// for e = 0..7, as two 4-value halves (k 8g..8g+3 and 8g+4..8g+7, g = l/16).
+// Both operands use the same lane -> k assignment, which is all the product
+// over k requires.
+//   K-major tile: a block's fragment is 1 KiB of contiguous slots (its 16 rows
+//     x 4 chunks): one ds_read_b128 per fragment.
+//   M/N-major tile: each half is one ds_read_b64_tr_b16.  Within a 16-lane
+//     group, lane x = 4e + q supplies the address of k row 8g + 4h + e,
+//     columns 4q..4q+3 of the block, and the instruction hands lane i the
+//     values of column i for the four k rows.
+struct Frag {
+  s16x4_t lo, hi;
+};
+
+__device__ __forceinline__ bf16x8_t frag_value(const Frag& f) {
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(f.lo, f.hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <bool KMAJOR>
+struct FragBase {
+  int x[KMAJOR ? 1 : kSubN];  // K-major: one lane base; M/N-major: one per 16-column block
+};
+
+template <bool KMAJOR>
+__device__ __forceinline__ FragBase<KMAJOR> frag_lane_base(int lane) {
+  FragBase<KMAJOR> fb;
   if constexpr (KMAJOR) {
-    return *(const bf16x8_t*)(tile + lane_base + w * 8192 + blk * 2048 + ks * 512);
+    // row l%16 of the block, chunk l/16
+    fb.x[0] = ((lane & 15) * 4 + ((lane >> 4) ^ ((lane >> 2) & 3))) * 16;
   } else {
-    const lds_char* p = tile + lane_base + w * 1024 + blk * 256 + ks * 8192;
-    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p);
-    const s16x4_t hi =
-        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p + 2048));
-    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    // lane x = 4e + q of group g: k row 8g + e (+ 4h), columns 4q..4q+3 of the
+    // block; the layout's XOR moves block b to position b ^ F within the row
+    const int g = lane >> 4, x = lane & 15, e = x >> 2, q = x & 3;
+    const int F = e | ((g & 1) << 2);
+    const int base = (8 * g + e) * 512 + F * 32 + (q >> 1) * 16 + (q & 1) * 8;
+#pragma unroll
+    for (int blk = 0; blk < kSubN; ++blk) fb.x[blk] = base ^ (blk * 32);
+  }
+  return fb;
+}
+
+// Pieces (LDS read instructions) per fragment.
+template <bool KMAJOR>
+constexpr int kPieces = KMAJOR ? 1 : 2;
+
+// Read piece h of the fragment of block blk (0..7) for wave coordinate w.
+template <bool KMAJOR>
+__device__ __forceinline__ void read_piece(Frag& f, const lds_char* tile, const FragBase<KMAJOR>& fb, int w, int blk,
+                                           int h) {
+  if constexpr (KMAJOR) {
+    const s16x8_t v = *(const s16x8_t*)(tile + fb.x[0] + (w * 8 + blk) * 1024);
+    f.lo = __builtin_shufflevector(v, v, 0, 1, 2, 3);
+    f.hi = __builtin_shufflevector(v, v, 4, 5, 6, 7);
+  } else {
+    const lds_char* p = tile + fb.x[blk] + h * 2048 + w * 256;
+    const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p);
+    if (h == 0) f.lo = v;
+    else f.hi = v;
   }
 }
 
 struct Frags {
-  bf16x8_t a[kSubM];
-  bf16x8_t b[kSubN];
+  Frag a[kSubM];
+  Frag b[kSubN];
 };
 
+// Order in which the fragments of a tile are read: A block 0, then every B
+// block, then A blocks 1..7 -- the order in which the MFMA sequence (A block
+// outer, B block inner) first needs them.  Piece p of PA + 8*PB + 7*PA pieces.
 template <bool AK, bool BK>
-__device__ __forceinline__ void load_frags(Frags& f, const lds_char* stage, int ks, int wm, int wn, int la, int lb) {
-#pragma unroll
-  for (int mi = 0; mi < kSubM; ++mi) f.a[mi] = load_frag<AK>(stage, la, wm, mi, ks);
-#pragma unroll
-  for (int ni = 0; ni < kSubN; ++ni) f.b[ni] = load_frag<BK>(stage + kTileBytes, lb, wn, ni, ks);
+struct ReadOrder {
+  static constexpr int PA = kPieces<AK>, PB = kPieces<BK>;
+  static constexpr int P = PA * kSubM + PB * kSubN;
+  // piece p is issued right after MFMA number slot(p) of the 64 (spread over the first 48)
+  static constexpr int slot(int p) { return (p * 48) / P; }
+  static constexpr int piece_at(int j) {
+    for (int p = 0; p < P; ++p)
+      if (slot(p) == j) return p;
+    return -1;
+  }
+};
+
+template <bool AK, bool BK, int p>
+__device__ __forceinline__ void read_piece_p(Frags& f, const lds_char* stage, const FragBase<AK>& fa,
+                                             const FragBase<BK>& fb, int wm, int wn) {
+  using R = ReadOrder<AK, BK>;
+  if constexpr (p < R::PA) {
+    read_piece<AK>(f.a[0], stage, fa, wm, 0, p);
+  } else if constexpr (p < R::PA + kSubN * R::PB) {
+    constexpr int q = p - R::PA;
+    read_piece<BK>(f.b[q / R::PB], stage + kTileBytes, fb, wn, q / R::PB, q % R::PB);
+  } else {
+    constexpr int q = p - R::PA - kSubN * R::PB;
+    read_piece<AK>(f.a[1 + q / R::PA], stage, fa, wm, 1 + q / R::PA, q % R::PA);
+  }
+}
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i = 0 .. N-1.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+template <bool AK, bool BK>
+__device__ __forceinline__ void read_all(Frags& f, const lds_char* stage, const FragBase<AK>& fa,
+                                         const FragBase<BK>& fb, int wm, int wn) {
+  static_for<ReadOrder<AK, BK>::P>([&](auto pc) { read_piece_p<AK, BK, decltype(pc)::value>(f, stage, fa, fb, wm, wn); });
 }
 
 // The MFMA is written as inline assembly with accumulation-register operands so
 // that the 256 accumulators are pinned to the accumulation registers for their
 // whole life (compiler-selected forms end up copying them between register
-// files every iteration).  Hazards: a given accumulator is re-used only after
-// the 15 other MFMAs of the k step; fragment registers come from LDS loads,
-// which the wait-count pass tracks through the asm operands; the first read
-// after the loop is fenced with explicit wait states.
+// files every iteration).  A given accumulator is re-used only after the 63
+// other MFMAs of the tile; fragment registers come from LDS loads, which the
+// wait-count pass tracks through the asm operands; the first read of the
+// accumulators after the loop is fenced with explicit wait states.
 template <bool FIRST>
-__device__ __forceinline__ void mfma_32x32x16(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
-  if constexpr (FIRST)  // the first k step starts from C = 0 (inline constant): no zero fill
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
+__device__ __forceinline__ void mfma_16x16x32(f32x4_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  if constexpr (FIRST)  // the first k tile starts from C = 0 (inline constant): no zero fill
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
   else
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
-// The 16 MFMAs of one k step; after each group of 4 (one A row block), calls
-// between(mi) so that other work (direct-to-LDS issue) interleaves with them.
-template <bool FIRST, class Between>
-__device__ __forceinline__ void mfma_frags(f32x16_t (&acc)[kSubM][kSubN], const Frags& f, Between&& between) {
-#pragma unroll
-  for (int mi = 0; mi < kSubM; ++mi) {
-#pragma unroll
-    for (int ni = 0; ni < kSubN; ++ni) mfma_32x32x16<FIRST>(acc[mi][ni], f.b[ni], f.a[mi]);
-    between(mi);
-  }
-}
+typedef f32x4_t AccTile[kSubM][kSubN];
 
-// Position of accumulator element acc[mi][ni][4g + r] inside the 256 x 256 tile:
-//   row = wm*128 + mi*32 + (lane & 31),
-//   col = wn*128 + ni*32 + 8g + 4*(lane >> 5) + r        (g, r = 0..3).
+// Position of accumulator element acc[mi][ni][r] inside the 256 x 256 tile
+// (the MFMA takes the B fragment as its first operand, so the hardware's row
+// index is the tile's column):
+//   row = wm*128 + mi*16 + (lane & 15),
+//   col = wn*128 + ni*16 + 4*(lane >> 4) + r        (r = 0..3).
 // LDS store of 4 accumulators straight from their accumulation registers.
 // Every non-MFMA use of the accumulators is this or a buffer store, so they
 // stay in the accumulation registers for the whole main loop.  LDS operations
@@ -322,7 +430,6 @@ struct EpiCtx {
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
-  static_assert(kDmaPerWave == kSubM, "one DMA instruction per A row block of MFMAs");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
@@ -360,45 +467,61 @@ gemm_kernel(GemmGeom g, Operand a, Operand b, Epi epi) {
   const int kt_beg = (int)(((int64_t)split * nk) / g.splits);
   const int kt_end = (int)(((int64_t)(split + 1) * nk) / g.splits);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // uniform copy for scalar address math
   const int wm = wave >> 1, wn = wave & 1;
-  const int la = frag_lane_base<A_KMAJOR>(lane), lb = frag_lane_base<B_KMAJOR>(lane);
+  const FragBase<A_KMAJOR> fra = frag_lane_base<A_KMAJOR>(lane);
+  const FragBase<B_KMAJOR> frb = frag_lane_base<B_KMAJOR>(lane);
+  const DmaLanes dla = dma_lanes<A_KMAJOR>(a, m0, g.M, g.K, wave_s, lane);
+  const DmaLanes dlb = dma_lanes<B_KMAJOR>(b, n0, g.N, g.K, wave_s, lane);
+  auto lds_addr = [](const lds_char* p) { return (uint32_t)(uintptr_t)p; };
 
-  f32x16_t acc[kSubM][kSubN];
+  AccTile acc;
 
   auto dma = [&](int kt, lds_char* stage) {
-    dma_tile<A_KMAJOR>(a, m0, g.M, kt * kBK, g.K, stage, wave, lane);
-    dma_tile<B_KMAJOR>(b, n0, g.N, kt * kBK, g.K, stage + kTileBytes, wave, lane);
+    dma_tile<A_KMAJOR>(a, dla, m0, kt * kBK, g.K, lds_addr(stage), wave_s);
+    dma_tile<B_KMAJOR>(b, dlb, n0, kt * kBK, g.K, lds_addr(stage + kTileBytes), wave_s);
   };
   constexpr int kPerTile = 2 * kDmaPerWave;  // direct-to-LDS instructions per wave per tile
+  using RO = ReadOrder<A_KMAJOR, B_KMAJOR>;
 
-  // One k tile from stage `cur` (2 k steps of 16).  Invariant at entry: tiles
-  // kt and kt+1 are published (complete in LDS for every wave) and the first
-  // k step's fragments of tile kt are in f[0].  The DMA of tile kt+3 goes into
-  // the stage consumed at kt-1; the second k step's fragments of tile kt are
-  // read under the first step's MFMAs, and the first step's fragments of tile
-  // kt+1 under the second step's.  Then this wave waits for its share of tile
-  // kt+2 (tile kt+3 may stay in flight) and the barrier publishes it; that
-  // barrier also orders every read of stage kt before its reuse at kt+1.
-  // The host guarantees kt_beg < kt_end.
-  auto step = [&](auto first, const lds_char* cur, const lds_char* nxt, lds_char* far, int kt, Frags (&f)[2]) {
+  // The 64 MFMAs of k tile kt on fragments fc.  Invariant at entry: tiles kt
+  // and kt+1 are published (complete in LDS for every wave) and fc holds tile
+  // kt's fragments.  Interleaved with the MFMAs, in a fixed order: the
+  // fragments of tile kt+1 are read from stage `nxt` into fn (when NEXT,
+  // i.e. kt+1 < kt_end), one LDS read every 1.5-3 MFMAs over the first 48, in
+  // the order the next tile's MFMAs need them; and the loads of tile kt+3 go
+  // into the stage consumed at kt-1 (when ISSUE, i.e. kt+3 < kt_end), one after
+  // every 8 MFMAs.  NEXT/ISSUE are compile-time in the steady-state loop.
+  // Then this wave waits for its share of tile kt+2 (tile kt+3 may stay in
+  // flight) and the barrier publishes it; that barrier also orders every read
+  // of stage kt+1 before its reuse at kt+2.  The host guarantees kt_beg < kt_end.
+  auto step = [&](auto first, auto checked, const lds_char* nxt, lds_char* far, int kt, Frags& fc, Frags& fn) {
     constexpr bool kFirst = decltype(first)::value;
-    const bool issue = kt + 3 < kt_end;
+    constexpr bool kChecked = decltype(checked)::value;
+    const bool issue = !kChecked || kt + 3 < kt_end;
+    const bool next = !kChecked || kt + 1 < kt_end;
     const int k3 = (kt + 3) * kBK;
     const u32x4_t da = tile_desc<A_KMAJOR>(a, m0, k3);
     const u32x4_t db = tile_desc<B_KMAJOR>(b, n0, k3);
-    // one direct-to-LDS instruction after every 4 MFMAs: A's share under the
-    // first k step, B's under the second
-    auto dma_a = [&](int q) {
-      if (issue) dma_one<A_KMAJOR>(a, da, m0, g.M, k3, g.K, far, wave, lane, q);
-    };
-    auto dma_b = [&](int q) {
-      if (issue) dma_one<B_KMAJOR>(b, db, n0, g.N, k3, g.K, far + kTileBytes, wave, lane, q);
-    };
-    load_frags<A_KMAJOR, B_KMAJOR>(f[1], cur, 1, wm, wn, la, lb);
-    if constexpr (kFirst) mfma_frags<true>(acc, f[0], dma_a);
-    else mfma_frags<false>(acc, f[0], dma_a);
-    if (kt + 1 < kt_end) load_frags<A_KMAJOR, B_KMAJOR>(f[0], nxt, 0, wm, wn, la, lb);
-    mfma_frags<false>(acc, f[1], dma_b);
+    const bool ktail = k3 + kBK > g.K;
+    const uint32_t fa = lds_addr(far), fb = lds_addr(far + kTileBytes);
+    static_for<kSubM * kSubN>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      constexpr int mi = j / kSubN, ni = j % kSubN;
+      mfma_16x16x32<kFirst>(acc[mi][ni], frag_value(fc.b[ni]), frag_value(fc.a[mi]));
+      constexpr int p = RO::piece_at(j);
+      if constexpr (p >= 0) {
+        if (next) read_piece_p<A_KMAJOR, B_KMAJOR, p>(fn, nxt, fra, frb, wm, wn);
+      }
+      if constexpr (j % 8 == 7) {
+        constexpr int q = j / 8;
+        if (issue) {
+          if constexpr (q < kDmaPerWave) dma_one<A_KMAJOR>(dla, da, ktail, fa, wave_s, q);
+          else dma_one<B_KMAJOR>(dlb, db, ktail, fb, wave_s, q - kDmaPerWave);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
     if (issue) wait_vmcnt<kPerTile>();
     else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
@@ -412,14 +535,22 @@ gemm_kernel(GemmGeom g, Operand a, Operand b, Epi epi) {
   if (kt_beg + 2 < kt_end) wait_vmcnt<kPerTile>();  // tiles kt_beg, kt_beg+1 done
   else wait_vmcnt<0>();
   __builtin_amdgcn_s_barrier();
-  Frags f[2];
-  load_frags<A_KMAJOR, B_KMAJOR>(f[0], st[0], 0, wm, wn, la, lb);
-  step(True{}, st[0], st[1], st[3], kt_beg, f);
-  for (int kt = kt_beg + 1; kt < kt_end; kt += 4) {
-    step(False{}, st[1], st[2], st[0], kt, f);
-    if (kt + 1 < kt_end) step(False{}, st[2], st[3], st[1], kt + 1, f);
-    if (kt + 2 < kt_end) step(False{}, st[3], st[0], st[2], kt + 2, f);
-    if (kt + 3 < kt_end) step(False{}, st[0], st[1], st[3], kt + 3, f);
+  Frags f0, f1;
+  read_all<A_KMAJOR, B_KMAJOR>(f0, st[0], fra, frb, wm, wn);
+  step(True{}, True{}, st[1], st[3], kt_beg, f0, f1);
+  int kt = kt_beg + 1;
+  // steady state: every step of the group reads its next tile and issues the loads of tile kt+3
+  for (; kt + 6 < kt_end; kt += 4) {
+    step(False{}, False{}, st[2], st[0], kt, f1, f0);
+    step(False{}, False{}, st[3], st[1], kt + 1, f0, f1);
+    step(False{}, False{}, st[0], st[2], kt + 2, f1, f0);
+    step(False{}, False{}, st[1], st[3], kt + 3, f0, f1);
+  }
+  for (; kt < kt_end; kt += 4) {
+    step(False{}, True{}, st[2], st[0], kt, f1, f0);
+    if (kt + 1 < kt_end) step(False{}, True{}, st[3], st[1], kt + 1, f0, f1);
+    if (kt + 2 < kt_end) step(False{}, True{}, st[0], st[2], kt + 2, f1, f0);
+    if (kt + 3 < kt_end) step(False{}, True{}, st[1], st[3], kt + 3, f0, f1);
   }
   EpiCtx ctx{m0, n0, tm, tn, split, wm, wn, lane, lds0, lds1, lds2, lds3};
   epi(acc, ctx);
