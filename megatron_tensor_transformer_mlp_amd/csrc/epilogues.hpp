@@ -32,36 +32,37 @@ constexpr float kLog2e = 1.44269504088896340736f;
 // with Abramowitz & Stegun, Handbook of Mathematical Functions, formula
 // 7.1.26: for z >= 0, erf(z) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5))))
 // exp(-z^2), t = 1 / (1 + p z), with absolute error below 1.5e-7 (far below the
-// bf16 rounding of the outputs); erf(-z) = -erf(z).  The derivative
-// Phi(x) + x phi(x) reuses the same exp(-x^2 / 2) for phi.  One reciprocal and
-// one exp2 per element (hardware v_rcp_f32 / v_exp_f32).
+// bf16 rounding of the outputs); erf(-z) = -erf(z).  With z = |x|/sqrt 2 and
+// tail = (1 - erf(z)) / 2 = q(t) exp(-x^2/2), q = t (a1/2 + ... ) (the 1/2
+// folded into the coefficients):
+//   GeLU(x)  = max(x, 0) - |x| tail                (x Phi(x) for either sign)
+//   GeLU'(x) = Phi(x) + x phi(x),  Phi(x) = 1/2 + sign(x) (1/2 - tail),
+//              phi(x) = exp(-x^2/2) / sqrt(2 pi)  (the same exponential).
+// One reciprocal and one exp2 per element (hardware v_rcp_f32 / v_exp_f32).
 // Tanh form: the GELU paper's approximation 0.5 x (1 + tanh(u)),
 // u = sqrt(2/pi) (x + 0.044715 x^3), written as x * sigmoid(2u).
 constexpr float kAsP = 0.3275911f;
-constexpr float kAs1 = 0.254829592f, kAs2 = -0.284496736f, kAs3 = 1.421413741f, kAs4 = -1.453152027f,
-                kAs5 = 1.061405429f;
+constexpr float kAsH1 = 0.5f * 0.254829592f, kAsH2 = 0.5f * -0.284496736f, kAsH3 = 0.5f * 1.421413741f,
+                kAsH4 = 0.5f * -1.453152027f, kAsH5 = 0.5f * 1.061405429f;
 
-struct ErfParts {
-  float phi_cdf;  // Phi(x)
-  float pdf;      // phi(x) = exp(-x^2/2) / sqrt(2 pi)
+struct ErfTail {
+  float tail;  // (1 - erf(|x|/sqrt 2)) / 2
+  float e;     // exp(-x^2/2)
 };
 
-__device__ __forceinline__ ErfParts erf_parts(float x) {
+__device__ __forceinline__ ErfTail erf_tail(float x) {
   const float z = fabsf(x) * kInvSqrt2;
   const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(kAsP, z, 1.0f));
-  const float poly = t * __builtin_fmaf(t, __builtin_fmaf(t, __builtin_fmaf(t, __builtin_fmaf(t, kAs5, kAs4), kAs3), kAs2), kAs1);
-  const float e = __builtin_amdgcn_exp2f(-0.5f * kLog2e * x * x);  // exp(-z^2) = exp(-x^2/2)
-  const float tail = 0.5f * poly * e;                                 // (1 - erf(z)) / 2
-  ErfParts r;
-  r.phi_cdf = x >= 0.0f ? 1.0f - tail : tail;
-  r.pdf = kInvSqrt2Pi * e;
-  return r;
+  const float q = t * __builtin_fmaf(t, __builtin_fmaf(t, __builtin_fmaf(t, __builtin_fmaf(t, kAsH5, kAsH4), kAsH3), kAsH2), kAsH1);
+  const float e = __builtin_amdgcn_exp2f(z * z * -kLog2e);  // exp(-z^2) = exp(-x^2/2)
+  return ErfTail{q * e, e};
 }
 
 template <int FORM>
 __device__ __forceinline__ float gelu_f(float x) {
   if constexpr (FORM == kGeluErf) {
-    return x * erf_parts(x).phi_cdf;
+    const ErfTail r = erf_tail(x);
+    return __builtin_fmaf(-fabsf(x), r.tail, fmaxf(x, 0.0f));
   } else {
     const float u2 = 2.0f * kSqrt2OverPi * x * __builtin_fmaf(kTanhC * x, x, 1.0f);
     return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-u2 * kLog2e));
@@ -71,8 +72,9 @@ __device__ __forceinline__ float gelu_f(float x) {
 template <int FORM>
 __device__ __forceinline__ float gelu_grad_f(float x) {
   if constexpr (FORM == kGeluErf) {
-    const ErfParts p = erf_parts(x);
-    return __builtin_fmaf(x, p.pdf, p.phi_cdf);
+    const ErfTail r = erf_tail(x);
+    const float phi_cdf = 0.5f + __builtin_copysignf(0.5f - r.tail, x);
+    return __builtin_fmaf(x * kInvSqrt2Pi, r.e, phi_cdf);
   } else {
     // d/dx [x s(2u)] = s + x s (1 - s) 2u',  s = sigmoid(2u),  u' = sqrt(2/pi)(1 + 3c x^2)
     const float u2 = 2.0f * kSqrt2OverPi * x * __builtin_fmaf(kTanhC * x, x, 1.0f);
@@ -101,7 +103,7 @@ __device__ __forceinline__ void epi_stage_half(const AccTile& acc, char* region,
 #pragma unroll
     for (int ni = 0; ni < kSubN; ++ni) acc_store_lds(region + epi_slot(lr, ni * 4 + (lane >> 4)), acc[4 * h + m4][ni]);
   }
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_wave_barrier();
 }
 
@@ -111,7 +113,9 @@ __device__ __forceinline__ f32x4_t epi_read(const char* region, int lr, int q) {
 }
 
 // Row-major walk of the staged sub-tile: calls f(row, col, v) with tile-local
-// row/col of 4 consecutive values; 32 lanes cover one 128-column row.
+// row/col of 4 consecutive values; 32 lanes cover one 128-column row.  Rows
+// are taken 4 at a time with their LDS reads issued together, so the read
+// latency is paid once per group.
 template <class F>
 __device__ __forceinline__ void epi_rows(const AccTile& acc, const EpiCtx& c, F&& f) {
   char* region = epi_region(c);
@@ -120,9 +124,15 @@ __device__ __forceinline__ void epi_rows(const AccTile& acc, const EpiCtx& c, F&
   for (int h = 0; h < 2; ++h) {
     epi_stage_half(acc, region, h, c.lane);  // h must be a constant: acc is indexed by it
 #pragma unroll 1
-    for (int it = 0; it < 32; ++it) {
-      const int lr = it * 2 + (c.lane >> 5);
-      f(c.wm * kWaveM + h * 64 + lr, c.wn * kWaveN + q * 4, epi_read(region, lr, q));
+    for (int it0 = 0; it0 < 32; it0 += 4) {
+      f32x4_t v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = epi_read(region, (it0 + u) * 2 + (c.lane >> 5), q);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int lr = (it0 + u) * 2 + (c.lane >> 5);
+        f(c.wm * kWaveM + h * 64 + lr, c.wn * kWaveN + q * 4, v[u]);
+      }
     }
     __builtin_amdgcn_wave_barrier();
   }

@@ -93,10 +93,12 @@ __device__ __forceinline__ void buf_store4(uint32_t v, rsrc_t r, uint32_t off) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
-// Two fp32 -> packed bf16 pair (lo in bits 0..15), round to nearest even.
+// Two fp32 -> packed bf16 pair (lo in bits 0..15), round to nearest even
+// (one v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
 struct Operand {
@@ -394,15 +396,15 @@ typedef f32x4_t AccTile[kSubM][kSubN];
 // index is the tile's column):
 //   row = wm*128 + mi*16 + (lane & 15),
 //   col = wn*128 + ni*16 + 4*(lane >> 4) + r        (r = 0..3).
-// LDS store of 4 accumulators straight from their accumulation registers.
-// Every non-MFMA use of the accumulators is this or a buffer store, so they
-// stay in the accumulation registers for the whole main loop.  LDS operations
-// of a wave complete in order, so later LDS reads of the same bytes see the data.
-__device__ __forceinline__ void acc_store_lds(char* p, f32x4_t a) {
-  // generic (flat) pointer the compiler cannot narrow to LDS: a flat store, whose
-  // data operand may be an accumulation register, like a buffer store's
-  asm volatile("" : "+v"(p));
-  *(f32x4_t*)p = a;
+// LDS store of 4 accumulators straight from their accumulation registers: a
+// ds_write_b128 whose data operand is the accumulation-register quad, so the
+// accumulators stay in the accumulation registers for the whole main loop and
+// no copy to ordinary registers is made.  Written as inline assembly, it is
+// not tracked by the compiler's wait-count pass: callers wait for lgkmcnt(0)
+// before the staged bytes are read.
+__device__ __forceinline__ void acc_store_lds(char* p, const f32x4_t& a) {
+  const uint32_t addr = (uint32_t)(uintptr_t)(lds_char*)p;
+  asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "a"(a) : "memory");
 }
 
 // Wait states between the last MFMA and the first explicit accumulator read
