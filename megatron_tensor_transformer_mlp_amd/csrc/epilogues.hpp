@@ -276,9 +276,41 @@ struct EpiDGelu {
 // the tile, computes over the tile's valid columns
 //   pm = max L,  ps = sum exp(L - pm),  pz = L at the target column if it lies
 //   in this tile, else 0,
-// each wave over its 128 columns with one row per lane (no cross-lane
-// reduction), then the two column-waves are merged in LDS in fixed order; the
-// triple goes to partial slot tile_n of arrays laid out [tiles_n][T].
+// straight from the accumulators.  Lane l holds 32 columns of each of its 8
+// rows and 4 lanes (l, l^16, l^32, l^48) share a row: each lane reduces its
+// 32 values to (max, sum of exp(L - max)), then the four are merged by
+// log-sum-exp over two lane-pair exchanges (v_permlane16_swap, then
+// v_permlane32_swap).  Each exchange hands every lane the pair's two values
+// in the same order, so all four lanes end with bitwise-equal results.  The
+// two column-waves of each row are merged in LDS in fixed order (wn = 0
+// first) and the triple goes to partial slot tile_n of arrays laid out
+// [tiles_n][T].
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// Both lanes of each exchanged pair receive (value of the lower lane, value of the upper lane).
+__device__ __forceinline__ void xswap16(float x, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void xswap32(float x, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+
+// (m, s) pairs -> merged pair; m = -inf means an empty set (s = 0).
+__device__ __forceinline__ void lse_pair(float ma, float sa, float mb, float sb, float& m, float& s) {
+  m = fmaxf(ma, mb);
+  const float ml = m == -INFINITY ? 0.f : m * kLog2e;
+  s = sa * __builtin_amdgcn_exp2f(__builtin_fmaf(ma, kLog2e, -ml)) +
+      sb * __builtin_amdgcn_exp2f(__builtin_fmaf(mb, kLog2e, -ml));
+}
+
 struct EpiCE {
   const int64_t* target;
   int64_t vocab_start;
@@ -288,92 +320,122 @@ struct EpiCE {
   int pad_;
   __device__ void operator()(AccTile& acc, const EpiCtx& c) const {
     const rsrc_t rt = make_rsrc(target, (int64_t)M * 8);
-    char* region = epi_region(c);
-    const int ncol = min(N - c.n0 - c.wn * kWaveN, kWaveN);  // valid columns of this wave (may be <= 0)
-    float rm[2], rs[2], rz[2];
+    const int l16 = c.lane & 15, g = c.lane >> 4;
+    const int col0 = c.n0 + c.wn * kWaveN;                // first column of this wave
+    const int ncol = min(N - col0, kWaveN);               // valid columns (may be <= 0)
+    const int row0 = c.m0 + c.wm * kWaveM + l16;          // row of block mi is row0 + 16 mi
+    u32x2_t tw[kSubM];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int row = c.m0 + c.wm * kWaveM + h * 64 + c.lane;
-      const u32x2_t tw = buf_load8(rt, row < M ? (uint32_t)row * 8u : kOOB);
-      const int64_t tgt = (int64_t)(((uint64_t)tw[1] << 32) | tw[0]) - vocab_start - (c.n0 + c.wn * kWaveN);
-      epi_stage_half(acc, region, h, c.lane);
-      // the row in two 64-column chunks, merged by log-sum-exp in fixed order
-      float mx = -INFINITY, sm = 0.f, zz = 0.f;
-#pragma unroll 1
-      for (int ch = 0; ch < 2; ++ch) {
-        float v[64];
+    for (int mi = 0; mi < kSubM; ++mi) {
+      const int row = row0 + mi * 16;
+      tw[mi] = buf_load8(rt, row < M ? (uint32_t)row * 8u : kOOB);
+    }
+    acc_settle();
+    // A 4-column group is entirely valid or entirely padding (N % 8 == 0);
+    // padding is added as -inf, and waves with no padding take a branch without it.
+    float rm[kSubM], rs[kSubM], rz[kSubM];
+    auto rows = [&](auto masked) {
+      constexpr bool kMasked = decltype(masked)::value;
+      float pad[kSubN];
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const f32x4_t x = epi_read(region, c.lane, ch * 16 + q);
-          v[4 * q] = x[0];
-          v[4 * q + 1] = x[1];
-          v[4 * q + 2] = x[2];
-          v[4 * q + 3] = x[3];
+      for (int ni = 0; ni < kSubN; ++ni) pad[ni] = (!kMasked || ni * 16 + 4 * g < ncol) ? 0.f : -INFINITY;
+#pragma unroll
+      for (int mi = 0; mi < kSubM; ++mi) {
+        float v[kSubN * 4];
+#pragma unroll
+        for (int ni = 0; ni < kSubN; ++ni)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[ni * 4 + r] = kMasked ? acc[mi][ni][r] + pad[ni] : acc[mi][ni][r];
+        float t[11];
+#pragma unroll
+        for (int k = 0; k < 10; ++k) t[k] = max3f(v[3 * k], v[3 * k + 1], v[3 * k + 2]);
+        t[10] = fmaxf(v[30], v[31]);
+        const float mx = max3f(max3f(t[0], t[1], t[2]), max3f(t[3], t[4], t[5]),
+                               max3f(max3f(t[6], t[7], t[8]), t[9], t[10]));
+        const float ml = mx == -INFINITY ? 0.f : mx * kLog2e;  // no valid column: every term is 0
+        float e[kSubN];
+#pragma unroll
+        for (int ni = 0; ni < kSubN; ++ni) {
+          float q[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) q[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[ni * 4 + r], kLog2e, -ml));
+          e[ni] = (q[0] + q[1]) + (q[2] + q[3]);
         }
-        const int nv = ncol - ch * 64;  // valid columns in this chunk (may be <= 0)
-        if (nv <= 0) continue;           // uniform: this wave's columns end before the chunk
-        // invalid (padding beyond v_i) columns become -inf with per-lane selects,
-        // so no per-column uniform masks stay live
-        int nvv = nv;
-        asm volatile("" : "+v"(nvv));
-        const int tl = (tgt >= ch * 64 && tgt < ch * 64 + nv) ? (int)(tgt - ch * 64) : -1;
-#pragma unroll
-        for (int j2 = 0; j2 < 64; ++j2) v[j2] = j2 < nvv ? v[j2] : -INFINITY;
-        float cm = -INFINITY;
-#pragma unroll
-        for (int j2 = 0; j2 < 64; ++j2) cm = fmaxf(cm, v[j2]);
-        const float cml = cm * kLog2e;
-        float cs = 0.f;
-#pragma unroll
-        for (int j2 = 0; j2 < 64; ++j2) {
-          cs += __builtin_amdgcn_exp2f(__builtin_fmaf(v[j2], kLog2e, -cml));
-          zz = j2 == tl ? v[j2] : zz;
-        }
-        if (cs > 0.f) {
-          if (!(sm > 0.f)) {
-            mx = cm;
-            sm = cs;
-          } else {
-            const float mm = fmaxf(mx, cm);
-            sm = sm * __builtin_amdgcn_exp2f((mx - mm) * kLog2e) + cs * __builtin_amdgcn_exp2f((cm - mm) * kLog2e);
-            mx = mm;
-          }
-        }
+        rm[mi] = mx;
+        rs[mi] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
       }
-      rm[h] = mx;
-      rs[h] = sm;
-      rz[h] = zz;
-      __builtin_amdgcn_wave_barrier();
+    };
+    if (ncol >= kWaveN) rows(std::false_type{});
+    else rows(std::true_type{});
+#pragma unroll
+    for (int mi = 0; mi < kSubM; ++mi) {
+      float ma, mb, sa, sb;
+      xswap16(rm[mi], ma, mb);
+      xswap16(rs[mi], sa, sb);
+      lse_pair(ma, sa, mb, sb, rm[mi], rs[mi]);
+    }
+#pragma unroll
+    for (int mi = 0; mi < kSubM; ++mi) {
+      float ma, mb, sa, sb;
+      xswap32(rm[mi], ma, mb);
+      xswap32(rs[mi], sa, sb);
+      lse_pair(ma, sa, mb, sb, rm[mi], rs[mi]);
+    }
+    // the target logit: only in the tiles that hold some row's target (about
+    // one in N/256); at most one lane of a row's four holds it
+    int tl[kSubM];
+    bool any = false;
+#pragma unroll
+    for (int mi = 0; mi < kSubM; ++mi) {
+      const int64_t t = (int64_t)(((uint64_t)tw[mi][1] << 32) | tw[mi][0]) - vocab_start - col0;
+      tl[mi] = (t >= 0 && t < ncol) ? (int)t : -1;
+      any |= tl[mi] >= 0;
+      rz[mi] = 0.f;
+    }
+    if (__any(any)) {
+#pragma unroll
+      for (int mi = 0; mi < kSubM; ++mi) {
+        float zz = 0.f;
+#pragma unroll
+        for (int ni = 0; ni < kSubN; ++ni)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float x;
+            asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x) : "a"(acc[mi][ni][r]));
+            zz = (ni * 16 + 4 * g + r) == tl[mi] ? x : zz;
+          }
+        float za, zb;
+        xswap16(zz, za, zb);
+        zz = za + zb;
+        xswap32(zz, za, zb);
+        rz[mi] = za + zb;
+      }
     }
     // merge the two column-waves of each row: wn = 1 hands its triples to
-    // wn = 0 through LDS (1.5 KiB per row block, after every wave is done
-    // with its staging region).
-    __syncthreads();
-    float* xch = (float*)c.lds0;  // [wm][h][64 lanes][3]
-    if (c.wn == 1) {
+    // wn = 0 through LDS (the stages are free: the main loop ended with a barrier)
+    float* xch = (float*)c.lds0;  // [wm][128 rows][3]
+    if (c.wn == 1 && g == 0) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        float* e = xch + ((c.wm * 2 + h) * 64 + c.lane) * 3;
-        e[0] = rm[h];
-        e[1] = rs[h];
-        e[2] = rz[h];
+      for (int mi = 0; mi < kSubM; ++mi) {
+        float* e = xch + (c.wm * kWaveM + mi * 16 + l16) * 3;
+        e[0] = rm[mi];
+        e[1] = rs[mi];
+        e[2] = rz[mi];
       }
     }
     __syncthreads();
-    if (c.wn == 0) {
+    if (c.wn == 0 && g == 0) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int row = c.m0 + c.wm * kWaveM + h * 64 + c.lane;
+      for (int mi = 0; mi < kSubM; ++mi) {
+        const int row = row0 + mi * 16;
         if (row < M) {
-          const float* e = xch + ((c.wm * 2 + h) * 64 + c.lane) * 3;
-          const float m1 = e[0], s1 = e[1], z1 = e[2];
-          const float mm = fmaxf(rm[h], m1);
-          const float s0 = rs[h] > 0.f ? rs[h] * __builtin_amdgcn_exp2f((rm[h] - mm) * kLog2e) : 0.f;
-          const float s1m = s1 > 0.f ? s1 * __builtin_amdgcn_exp2f((m1 - mm) * kLog2e) : 0.f;
+          const float* e = xch + (c.wm * kWaveM + mi * 16 + l16) * 3;
+          float mm, ss;
+          lse_pair(rm[mi], rs[mi], e[0], e[1], mm, ss);
           float* o = part + (int64_t)c.tn * M + row;
           o[0] = mm;
-          o[stride] = s0 + s1m;
-          o[2 * (int64_t)stride] = rz[h] + z1;
+          o[stride] = ss;
+          o[2 * (int64_t)stride] = rz[mi] + e[2];
         }
       }
     }
