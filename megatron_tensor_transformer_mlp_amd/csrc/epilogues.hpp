@@ -174,6 +174,23 @@ struct EpiStoreBF16 {
   }
 };
 
+// Weight-gradient store for the paired launches: the bf16 result when the
+// contraction is not split (slice_stride == 0), else this split's fp32 slice
+// of the workspace (summed in fixed order by the split-K reduction).
+struct EpiStoreWGrad {
+  void* C;
+  int64_t ld;
+  int M, N;
+  int64_t slice_stride;  // elements between fp32 slices; 0: bf16 output
+  __device__ void operator()(AccTile& acc, const EpiCtx& c) const {
+    if (slice_stride == 0) {
+      EpiStoreBF16{(uint16_t*)C, ld, M, N}(acc, c);
+    } else {
+      EpiStoreF32{(float*)C, ld, M, N, slice_stride}(acc, c);
+    }
+  }
+};
+
 // Forward column-parallel epilogue: H = acc (+ b1), Y = GeLU(H) from the fp32
 // value; both stored as bf16.
 template <int FORM>
@@ -232,23 +249,28 @@ struct EpiDGelu {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       epi_stage_half(acc, region, h, c.lane);  // h must be a constant: acc is indexed by it
-#pragma unroll 1
-      for (int it0 = 0; it0 < 32; it0 += 8) {
-        // 8 rows' H values first (independent loads in flight together)
-        u32x2_t hh[8];
+      // H of 8 rows per batch; the next batch's loads are issued before the
+      // current batch is processed, so their latency overlaps the arithmetic
+      auto load_h = [&](int it0, u32x2_t (&hh)[8]) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int rl = c.wm * kWaveM + h * 64 + (it0 + u) * 2 + (c.lane >> 5);
           const bool ok = rl < mrem && cl < nrem;
           hh[u] = buf_load8(rh, ok ? (uint32_t)(((int64_t)rl * ld + cl) * 2) : kOOB);
         }
+      };
+      u32x2_t hcur[8], hnext[8];
+      load_h(0, hcur);
+#pragma unroll 2
+      for (int it0 = 0; it0 < 32; it0 += 8) {
+        if (it0 + 8 < 32) load_h(it0 + 8, hnext);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int lr = (it0 + u) * 2 + (c.lane >> 5);
           const int rl = c.wm * kWaveM + h * 64 + lr;
           const bool ok = rl < mrem && cl < nrem;
           const f32x4_t v = epi_read(region, lr, q);
-          const float hv[4] = {bf16_lo(hh[u][0]), bf16_hi(hh[u][0]), bf16_lo(hh[u][1]), bf16_hi(hh[u][1])};
+          const float hv[4] = {bf16_lo(hcur[u][0]), bf16_hi(hcur[u][0]), bf16_lo(hcur[u][1]), bf16_hi(hcur[u][1])};
           float dv[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -258,6 +280,8 @@ struct EpiDGelu {
           buf_store8(u32x2_t{pack_bf16x2(dv[0], dv[1]), pack_bf16x2(dv[2], dv[3])}, rd,
                      ok ? (uint32_t)(((int64_t)rl * ld + cl) * 2) : kOOB);
         }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) hcur[u] = hnext[u];
       }
       __builtin_amdgcn_wave_barrier();
     }

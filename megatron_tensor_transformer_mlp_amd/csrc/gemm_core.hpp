@@ -114,9 +114,10 @@ struct GemmGeom {
 };
 
 // Block id -> (tile_m, tile_n, split), XCD-aware and grouped along M.
-__device__ __forceinline__ void map_tile(const GemmGeom& g, int& tm, int& tn, int& split) {
-  const int G = gridDim.x;
-  const int b = blockIdx.x;
+// `b` and `G` are the block's index and the block count of this GEMM within
+// the launch; the first block of each GEMM sits on XCD 0 (callers keep every
+// GEMM's first block index a multiple of 8).
+__device__ __forceinline__ void map_tile(const GemmGeom& g, int b, int G, int& tm, int& tn, int& split) {
   const int q = G / kNumXcd, r = G % kNumXcd;
   const int xcd = b % kNumXcd, idx = b / kNumXcd;
   const int lin = (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
@@ -447,23 +448,19 @@ __device__ __forceinline__ void args_to_sgprs(const T& t) {
   for (int i = 0; i < (int)(sizeof(T) / 4); ++i) asm volatile("" ::"s"(w[i]));
 }
 
+// One 256 x 256 output tile (or one K split of it): block `vb` of the `vg`
+// blocks this GEMM has in the launch.  lds0..lds3 are the kernel's four LDS
+// stages (A tile then B tile in each).
 template <bool A_KMAJOR, bool B_KMAJOR, class Epi>
-__global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
-gemm_kernel(GemmGeom g, Operand a, Operand b, Epi epi) {
+__device__ __forceinline__ void gemm_tile(const GemmGeom& g, const Operand& a, const Operand& b, const Epi& epi,
+                                          int vb, int vg, char* lds0, char* lds1, char* lds2, char* lds3) {
   args_to_sgprs(g);
   args_to_sgprs(a);
   args_to_sgprs(b);
   args_to_sgprs(epi);
-  // Four LDS stages (A tile then B tile in each), kept as separate objects so
-  // that the direct-to-LDS writes into one stage are known not to alias the
-  // fragment reads of another.
-  __shared__ __attribute__((aligned(1024))) char lds0[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) char lds1[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) char lds2[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) char lds3[kStageBytes];
   lds_char* st[kStages] = {(lds_char*)lds0, (lds_char*)lds1, (lds_char*)lds2, (lds_char*)lds3};
   int tm, tn, split;
-  map_tile(g, tm, tn, split);
+  map_tile(g, vb, vg, tm, tn, split);
   const int m0 = tm * kBM, n0 = tn * kBN;
   const int nk = (g.K + kBK - 1) / kBK;
   const int kt_beg = (int)(((int64_t)split * nk) / g.splits);
@@ -556,6 +553,43 @@ gemm_kernel(GemmGeom g, Operand a, Operand b, Epi epi) {
   }
   EpiCtx ctx{m0, n0, tm, tn, split, wm, wn, lane, lds0, lds1, lds2, lds3};
   epi(acc, ctx);
+}
+
+#define MS_DECLARE_LDS_STAGES                                 \
+  __shared__ __attribute__((aligned(1024))) char lds0[kStageBytes]; \
+  __shared__ __attribute__((aligned(1024))) char lds1[kStageBytes]; \
+  __shared__ __attribute__((aligned(1024))) char lds2[kStageBytes]; \
+  __shared__ __attribute__((aligned(1024))) char lds3[kStageBytes]
+
+template <bool A_KMAJOR, bool B_KMAJOR, class Epi>
+__global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+gemm_kernel(GemmGeom g, Operand a, Operand b, Epi epi) {
+  MS_DECLARE_LDS_STAGES;
+  gemm_tile<A_KMAJOR, B_KMAJOR, Epi>(g, a, b, epi, (int)blockIdx.x, (int)gridDim.x, lds0, lds1, lds2, lds3);
+}
+
+// Two independent GEMMs in one launch, so that the blocks of one fill the CUs
+// the other leaves idle.  The hardware hands blocks to free CUs in index
+// order, and the host puts the GEMM with the longer blocks first: when
+// `second_first` is set, GEMM 2 takes the leading block range.  The leading
+// GEMM's range is its block count rounded up to a multiple of 8 (the extra
+// blocks exit at once), which keeps the trailing GEMM's first block on XCD 0.
+template <bool AK1, bool BK1, class E1, bool AK2, bool BK2, class E2>
+__global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+gemm_pair_kernel(GemmGeom g1, Operand a1, Operand b1, E1 e1, int blocks1, GemmGeom g2, Operand a2, Operand b2,
+                 E2 e2, int blocks2, int second_first) {
+  MS_DECLARE_LDS_STAGES;
+  const int bid = (int)blockIdx.x;
+  const int lead = second_first ? blocks2 : blocks1;
+  const int lead_pad = (lead + 7) & ~7;
+  const bool in_lead = bid < lead_pad;
+  if (in_lead && bid >= lead) return;
+  const int vb = in_lead ? bid : bid - lead_pad;
+  if (in_lead != (second_first != 0)) {
+    gemm_tile<AK1, BK1, E1>(g1, a1, b1, e1, vb, blocks1, lds0, lds1, lds2, lds3);
+  } else {
+    gemm_tile<AK2, BK2, E2>(g2, a2, b2, e2, vb, blocks2, lds0, lds1, lds2, lds3);
+  }
 }
 
 }  // namespace mshard

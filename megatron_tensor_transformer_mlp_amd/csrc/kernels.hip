@@ -7,6 +7,13 @@
 // private per-writer output space).
 #include "launch.hpp"
 
+#include <array>
+#include <functional>
+#include <map>
+#include <mutex>
+#include <queue>
+#include <vector>
+
 #include "epilogues.hpp"
 
 namespace mshard {
@@ -154,27 +161,108 @@ static hipError_t launch_gemm(int id, const GemmGeom& g, const Operand& a, const
   return err;
 }
 
-int weight_grad_splits(int64_t M, int64_t N, int64_t K) {
-  const int64_t tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+// ---------------------------------------------------------------------------
+// Backward schedule.  For each independent pair of backward GEMMs -- (dB, dH)
+// and (dA, dX) -- the host chooses two launches or one paired launch, and the
+// weight gradient's K split, by a list-scheduling model of the 256 CUs:
+// blocks are handed in order to the earliest free CU, each costing ~1400
+// cycles per 32-k step + ~4000 to fill the pipeline + an epilogue cost by
+// kind (measured on this kernel at ~2 GHz), and a split-K reduction costs its
+// bytes at ~4 TB/s.  Only launch shapes and the (fixed) order of the fp32
+// additions depend on the plan, and equal shapes always get equal plans.
+namespace {
+constexpr int kModelCUs = 256;
+constexpr double kCyclesPerKStep = 1400.0, kFillCycles = 4000.0, kCyclesPerUs = 2000.0;
+constexpr double kEpiDGelu = 40000.0, kEpiF32 = 12000.0, kEpiBF16 = 10000.0;
+
+struct BlockList {
+  int64_t n;
+  double cost;  // cycles per block
+};
+
+double block_cost(int64_t K, int S, double epi) {
   const int64_t nk = (K + kBK - 1) / kBK;
-  int S = 1;
-  while (tiles * S < 256 && nk / (S * 2) >= 16 && S < 8) S *= 2;
-  return S;
+  return kCyclesPerKStep * (double)((nk + S - 1) / S) + kFillCycles + epi;
+}
+
+int64_t tile_count(int64_t M, int64_t N) { return ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN); }
+
+// Completion time (us) of the block lists dispatched in order to the earliest free CU.
+double makespan_us(std::initializer_list<BlockList> lists) {
+  std::priority_queue<double, std::vector<double>, std::greater<double>> q;
+  for (int i = 0; i < kModelCUs; ++i) q.push(0.0);
+  double end = 0.0;
+  for (const BlockList& l : lists)
+    for (int64_t i = 0; i < l.n; ++i) {
+      const double t = q.top() + l.cost;
+      q.pop();
+      q.push(t);
+      end = t > end ? t : end;
+    }
+  return end / kCyclesPerUs;
+}
+
+double reduce_us(int64_t M, int64_t N, int S) {
+  return S == 1 ? 0.0 : (double)(4 * S + 2) * (double)M * (double)N / 4e6 + 3.0;
+}
+
+// Weight gradient [M x N] (contraction over T) with partner GEMM blocks `p`.
+void plan_pair(int64_t M, int64_t N, int64_t T, BlockList p, int& S_out, bool& paired, bool& partner_first) {
+  const int64_t nk = (T + kBK - 1) / kBK;
+  const double alone = makespan_us({p});
+  double best = 1e300;
+  for (int S = 1; S <= 8; S *= 2) {
+    if (S > 1 && nk / S < 8) break;
+    const BlockList w{tile_count(M, N) * S, block_cost(T, S, S == 1 ? kEpiBF16 : kEpiF32)};
+    const double seq = makespan_us({w}) + alone + reduce_us(M, N, S);
+    const bool pf = p.cost > w.cost;
+    const double par = (pf ? makespan_us({p, w}) : makespan_us({w, p})) + reduce_us(M, N, S);
+    if (seq < best) {
+      best = seq;
+      S_out = S;
+      paired = false;
+      partner_first = false;
+    }
+    if (par < best) {
+      best = par;
+      S_out = S;
+      paired = true;
+      partner_first = pf;
+    }
+  }
+}
+}  // namespace
+
+BwdPlan plan_backward(int64_t T, int64_t h, int64_t f) {
+  // plans are cached per shape: the model simulates up to tens of thousands of blocks
+  static std::mutex mu;
+  static std::map<std::array<int64_t, 3>, BwdPlan> cache;
+  const std::array<int64_t, 3> key{T, h, f};
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+  }
+  BwdPlan pl;
+  const BlockList dh{tile_count(T, f), block_cost(h, 1, kEpiDGelu)};
+  const BlockList dx{tile_count(T, h), block_cost(f, 1, kEpiF32)};
+  plan_pair(f, h, T, dh, pl.splits_dB, pl.pair_bh, pl.dh_first);
+  plan_pair(h, f, T, dx, pl.splits_dA, pl.pair_ax, pl.dx_first);
+  std::lock_guard<std::mutex> lock(mu);
+  cache.emplace(key, pl);
+  return pl;
 }
 
 MlpWorkspace mlp_workspace_layout(int64_t T, int64_t h, int64_t f) {
   MlpWorkspace w;
   auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const int64_t tiles_m = (T + kBM - 1) / kBM;
-  const int Sb = weight_grad_splits(f, h, T);
-  const int Sa = weight_grad_splits(h, f, T);
-  w.splits_dB = Sb;
-  w.splits_dA = Sa;
+  w.plan = plan_backward(T, h, f);
   w.off_dH = 0;
   w.off_db1 = align((size_t)T * f * 2);
   w.db1_parts = (int)(tiles_m * 2);
   w.off_splitk = w.off_db1 + align((size_t)w.db1_parts * f * 4);
-  const int S = Sb > Sa ? Sb : Sa;
+  const int S = w.plan.splits_dB > w.plan.splits_dA ? w.plan.splits_dB : w.plan.splits_dA;
   w.bytes = w.off_splitk + (S > 1 ? align((size_t)S * h * f * 4) : 0);
   return w;
 }
@@ -222,24 +310,51 @@ hipError_t launch_mlp_fwd(const uint16_t* X, const uint16_t* A, const uint16_t* 
                           : mlp_fwd_impl<kGeluTanh>(X, A, b1, B, T, h, f, H, Y, Z, st);
 }
 
-// Weight gradient C[M x N] = sum_t P[t, m] Q[t, n] (TN), bf16 result, with an
-// optional deterministic K split through fp32 workspace slices.
-static hipError_t weight_grad(int id, const uint16_t* P, int64_t ldp, const uint16_t* Q, int64_t ldq, int64_t Kt,
-                              int64_t M, int64_t N, int S, uint16_t* C, float* splitk, hipStream_t st) {
-  GemmGeom g = make_geom(M, N, Kt, S);
-  S = g.splits;
-  Operand a{P, ldp, Kt * ldp}, b{Q, ldq, Kt * ldq};
-  if (S == 1) {
-    EpiStoreBF16 e{C, N, (int)M, (int)N};
-    return launch_gemm<false, false>(id, g, a, b, e, st);
-  }
-  EpiStoreF32 e{splitk, N, (int)M, (int)N, M * N};
-  hipError_t err = launch_gemm<false, false>(id, g, a, b, e, st);
-  if (err != hipSuccess) return err;
+// Two independent GEMMs as one launch (see gemm_pair_kernel); both kernel ids'
+// armed events bracket the shared launch.
+template <bool AK1, bool BK1, bool AK2, bool BK2, class E1, class E2>
+static hipError_t launch_gemm_pair(int id1, const GemmGeom& g1, const Operand& a1, const Operand& b1, const E1& e1,
+                                   int id2, const GemmGeom& g2, const Operand& a2, const Operand& b2, const E2& e2,
+                                   bool second_first, hipStream_t stream) {
+  const int n1 = g1.tiles_m * g1.tiles_n * g1.splits, n2 = g2.tiles_m * g2.tiles_n * g2.splits;
+  const int lead = second_first ? n2 : n1, trail = second_first ? n1 : n2;
+  const int blocks = ((lead + 7) & ~7) + trail;
+  record_armed_event(id1, false, stream);
+  record_armed_event(id2, false, stream);
+  hipLaunchKernelGGL((gemm_pair_kernel<AK1, BK1, E1, AK2, BK2, E2>), dim3(blocks), dim3(kThreads), 0, stream, g1, a1,
+                     b1, e1, n1, g2, a2, b2, e2, n2, second_first ? 1 : 0);
+  const hipError_t err = hipGetLastError();
+  record_armed_event(id1, true, stream);
+  record_armed_event(id2, true, stream);
+  return err;
+}
+
+static hipError_t launch_splitk_reduce(const float* splitk, int64_t M, int64_t N, int S, uint16_t* C, hipStream_t st) {
   const int64_t n = M * N;  // multiple of 8
   const int64_t blocks = (n / 8 + 255) / 256;
   hipLaunchKernelGGL(splitk_reduce_bf16, dim3((unsigned)blocks), dim3(256), 0, st, splitk, M * N, S, n, C);
   return hipGetLastError();
+}
+
+// Weight gradient C[M x N] = sum_t P[t, m] Q[t, n] (TN): its GEMM geometry,
+// operands and epilogue -- the bf16 result, or with a K split the fp32
+// workspace slices that splitk_reduce_bf16 sums in fixed order.
+struct WeightGrad {
+  GemmGeom g;
+  Operand a, b;
+  EpiStoreWGrad e;
+  int S;
+};
+
+static WeightGrad weight_grad_setup(const uint16_t* P, int64_t ldp, const uint16_t* Q, int64_t ldq, int64_t Kt,
+                                    int64_t M, int64_t N, int S, uint16_t* C, float* splitk) {
+  WeightGrad w;
+  w.g = make_geom(M, N, Kt, S);
+  w.S = w.g.splits;
+  w.a = Operand{P, ldp, Kt * ldp};
+  w.b = Operand{Q, ldq, Kt * ldq};
+  w.e = w.S == 1 ? EpiStoreWGrad{C, N, (int)M, (int)N, 0} : EpiStoreWGrad{splitk, N, (int)M, (int)N, M * N};
+  return w;
 }
 
 template <int FORM>
@@ -247,32 +362,40 @@ static hipError_t mlp_bwd_impl(const uint16_t* X, const uint16_t* A, const uint1
                                const uint16_t* Y, const uint16_t* dZ, int64_t T, int64_t h, int64_t f,
                                float* dX, uint16_t* dA, uint16_t* dB, uint16_t* db1, char* ws, hipStream_t st) {
   const MlpWorkspace w = mlp_workspace_layout(T, h, f);
+  const BwdPlan& pl = w.plan;
   uint16_t* dH = (uint16_t*)(ws + w.off_dH);
   float* db1_part = db1 ? (float*)(ws + w.off_db1) : nullptr;
   float* splitk = (float*)(ws + w.off_splitk);
   hipError_t err;
   // dH = (dZ B^T) * GeLU'(H):  NT, M = T, N = f, K = h; B stored [f x h] = [N x K]
-  {
-    GemmGeom g = make_geom(T, f, h, 1);
-    Operand a{dZ, h, T * h}, b{B, h, f * h};
-    EpiDGelu<FORM> e{H, dH, db1_part, f, (int)T, (int)f};
-    err = launch_gemm<true, true>(kTkBwdDH, g, a, b, e, st);
-    if (err != hipSuccess) return err;
+  const GemmGeom gh = make_geom(T, f, h, 1);
+  const Operand ah{dZ, h, T * h}, bh{B, h, f * h};
+  const EpiDGelu<FORM> eh{H, dH, db1_part, f, (int)T, (int)f};
+  // dB = Y^T dZ:  [f x h], contraction over tokens (independent of dH)
+  const WeightGrad wb = weight_grad_setup(Y, f, dZ, h, T, f, h, pl.splits_dB, dB, splitk);
+  if (pl.pair_bh) {
+    err = launch_gemm_pair<false, false, true, true>(kTkBwdDB, wb.g, wb.a, wb.b, wb.e, kTkBwdDH, gh, ah, bh, eh,
+                                                     pl.dh_first, st);
+  } else {
+    err = launch_gemm<true, true>(kTkBwdDH, gh, ah, bh, eh, st);
+    if (err == hipSuccess) err = launch_gemm<false, false>(kTkBwdDB, wb.g, wb.a, wb.b, wb.e, st);
   }
-  // dB = Y^T dZ:  [f x h], contraction over tokens
-  err = weight_grad(kTkBwdDB, Y, f, dZ, h, T, f, h, w.splits_dB, dB, splitk, st);
   if (err != hipSuccess) return err;
-  // dA = X^T dH:  [h x f]
-  err = weight_grad(kTkBwdDA, X, h, dH, f, T, h, f, w.splits_dA, dA, splitk, st);
-  if (err != hipSuccess) return err;
-  // dX = dH A^T:  NT, M = T, N = h, K = f; A stored [h x f] = [N x K]
-  {
-    GemmGeom g = make_geom(T, h, f, 1);
-    Operand a{dH, f, T * f}, b{A, f, h * f};
-    EpiStoreF32 e{dX, h, (int)T, (int)h, 0};
-    err = launch_gemm<true, true>(kTkBwdDX, g, a, b, e, st);
-    if (err != hipSuccess) return err;
+  if (wb.S > 1 && (err = launch_splitk_reduce(splitk, f, h, wb.S, dB, st)) != hipSuccess) return err;
+  // dA = X^T dH:  [h x f];  dX = dH A^T:  NT, M = T, N = h, K = f; A stored [h x f] = [N x K]
+  const WeightGrad wa = weight_grad_setup(X, h, dH, f, T, h, f, pl.splits_dA, dA, splitk);
+  const GemmGeom gx = make_geom(T, h, f, 1);
+  const Operand ax{dH, f, T * f}, bx{A, f, h * f};
+  const EpiStoreF32 ex{dX, h, (int)T, (int)h, 0};
+  if (pl.pair_ax) {
+    err = launch_gemm_pair<false, false, true, true>(kTkBwdDA, wa.g, wa.a, wa.b, wa.e, kTkBwdDX, gx, ax, bx, ex,
+                                                     pl.dx_first, st);
+  } else {
+    err = launch_gemm<false, false>(kTkBwdDA, wa.g, wa.a, wa.b, wa.e, st);
+    if (err == hipSuccess) err = launch_gemm<true, true>(kTkBwdDX, gx, ax, bx, ex, st);
   }
+  if (err != hipSuccess) return err;
+  if (wa.S > 1 && (err = launch_splitk_reduce(splitk, h, f, wa.S, dA, st)) != hipSuccess) return err;
   if (db1) {
     hipLaunchKernelGGL(colsum_reduce_bf16, dim3((unsigned)((f + 255) / 256)), dim3(256), 0, st, db1_part,
                        w.db1_parts, (int)f, db1);

@@ -9,13 +9,21 @@
 
 namespace mshard {
 
+// Launch plan of the backward: the four GEMMs form two independent pairs,
+// (dB, dH) and (dA, dX); each pair runs as two launches or one paired launch.
+struct BwdPlan {
+  int splits_dB, splits_dA;  // K splits of the weight gradients (1 = none)
+  bool pair_bh, pair_ax;     // (dB, dH) / (dA, dX) share one launch
+  bool dh_first, dx_first;   // in a paired launch, the partner's blocks lead
+};
+
 struct MlpWorkspace {
   size_t off_dH;      // bf16 [T x f]: dH, consumed by the dA and dX GEMMs
   size_t off_db1;     // fp32 [db1_parts x f]: per-writer bias-gradient column sums
   size_t off_splitk;  // fp32 [S x h*f]: weight-gradient split-K slices
   size_t bytes;
   int db1_parts;
-  int splits_dA, splits_dB;
+  BwdPlan plan;
 };
 
 struct CeWorkspace {
@@ -31,7 +39,7 @@ enum TimedKernel { kTkCeGemm = 0, kTkFwdH, kTkFwdZ, kTkBwdDH, kTkBwdDB, kTkBwdDA
 // of the pair.  Defined by the ABI layer, which owns the per-thread arming.
 void record_armed_event(int id, bool after, hipStream_t st);
 
-int weight_grad_splits(int64_t M, int64_t N, int64_t K);
+BwdPlan plan_backward(int64_t T, int64_t h, int64_t f);
 MlpWorkspace mlp_workspace_layout(int64_t T, int64_t h, int64_t f);
 CeWorkspace ce_workspace_layout(int64_t T, int64_t v);
 
