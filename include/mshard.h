@@ -160,7 +160,9 @@ typedef enum {
  * next call on this host thread of the entry point that launches k records
  * `before` on its stream immediately before that launch and `after`
  * immediately after it, so hipEventElapsedTime(before, after) is that one
- * kernel's device time.  The entry point disarms k when it returns (also on
+ * kernel's device time.  mlp_shard_bwd may run two independent GEMMs, (dB, dH)
+ * or (dA, dX), as one paired launch; both ids then bracket that one launch
+ * and time it together.  The entry point disarms k when it returns (also on
  * error).  before == after == NULL disarms k.  Errors: MS_ERR_ENUM for an
  * unknown k, MS_ERR_NULL if exactly one event is NULL. */
 ms_status ms_arm_kernel_events(ms_kernel k, void* before, void* after);
