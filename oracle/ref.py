@@ -29,6 +29,12 @@ Readings where the pages are silent (each one is also listed in the design notes
   * Combine: M = max_r m_r, S = sum_r s_r exp(m_r - M), loss = ln S + M - sum_r z_r;
     the reported loss is the mean over tokens.
   * Padded vocabulary columns take part in the softmax like any other column.
+  * CE backward (the pages give only the forward fusion): the objective is
+    sum_t coef[t] * loss[t] (coef = 1/T for the mean); the derivative of a
+    token's loss with respect to its logits is the textbook softmax minus the
+    one-hot target, with the softmax taken over the whole vocabulary through
+    the combined (M, S) of the token.  dX_i is a partial over this rank's
+    vocab columns (the ranks' partials sum); dE_i is this rank's own slice.
 """
 from __future__ import annotations
 
@@ -200,3 +206,60 @@ def full_vocab_ce(X, E, targets, rows: Optional[Sequence[int]] = None, block: in
         L = X[rb] @ E
         out[b0:b0 + block] = special.logsumexp(L, axis=1) - L[np.arange(len(rb)), targets[rb]]
     return out
+
+
+# ----------------------------------------------------------------------------- vocab CE backward
+def ce_row_stats(m, s) -> Dict[str, np.ndarray]:
+    """Combined softmax statistics of each token from t shards' partials [t, T]:
+    M = max_r m_r and S = sum_r s_r exp(m_r - M), so that the sum over the whole
+    vocabulary of exp(L[t, j] - M[t]) is S[t] ([NOTES vocab-embedding parallelism]:
+    only these b*s-sized values cross ranks)."""
+    m = np.atleast_2d(np.asarray(m, dtype=np.float64))
+    s = np.atleast_2d(np.asarray(s, dtype=np.float64))
+    M = m.max(axis=0)
+    return {"M": M, "S": (s * np.exp(m - M[None, :])).sum(axis=0)}
+
+
+def _ce_grad_block(L, M, S, coef, targets, vocab_start, cols):
+    """dL on a block of logits L[rows, cols]: coef * (softmax - one-hot of the target).
+
+    ``cols`` are the block's column indices within the shard; the target of a row
+    sits in this block iff its global id equals vocab_start + a column index."""
+    P = np.exp(L - M[:, None]) / S[:, None]
+    onehot = ((np.asarray(targets, dtype=np.int64)[:, None] - vocab_start) == np.asarray(cols)[None, :])
+    return coef[:, None] * (P - onehot)
+
+
+def vocab_ce_shard_bwd(X, E_i, targets, vocab_start: int, m, s, coef,
+                       rows: Optional[Sequence[int]] = None,
+                       cols: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
+    """Backward of the fused output GEMM + cross-entropy on one vocab shard.
+
+    Inputs: the shard's X [T, h] and E_i [h, v_i], global target ids, the shard's
+    first global column ``vocab_start``, the gathered partials m, s [t, T] of
+    every rank (rank order), and the per-token weight coef [T] of the objective
+    sum_t coef[t] * loss[t].
+
+        P[t, j]    = exp(L[t, j] - M[t]) / S[t]            (L = X E_i, M, S from ce_row_stats)
+        dL_i[t, j] = coef[t] * (P[t, j] - [vocab_start + j == y_t])
+        dX_i       = dL_i E_i^T    (this rank's partial; summed over ranks)
+        dE_i       = X^T dL_i      (this rank's slice of dE)
+
+    Without rows/cols every output is returned in full.  With them: dX on token
+    rows R (each needs only that token's logit row) and dE on shard columns C
+    (each needs only that column's logits over all tokens).
+    """
+    X, E_i = _f64(X), _f64(E_i)
+    st = ce_row_stats(m, s)
+    M, S = st["M"], st["S"]
+    coef = np.broadcast_to(np.asarray(coef, dtype=np.float64), M.shape)
+    targets = np.asarray(targets, dtype=np.int64)
+    v_i = E_i.shape[1]
+    if rows is None and cols is None:
+        dL = _ce_grad_block(X @ E_i, M, S, coef, targets, vocab_start, np.arange(v_i))
+        return {"dL": dL, "dX": dL @ E_i.T, "dE": X.T @ dL}
+    R = np.arange(X.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    C = np.arange(v_i) if cols is None else np.asarray(cols, dtype=np.int64)
+    dLR = _ce_grad_block(X[R] @ E_i, M[R], S[R], coef[R], targets[R], vocab_start, np.arange(v_i))
+    dLC = _ce_grad_block(X @ E_i[:, C], M, S, coef, targets, vocab_start, C)
+    return {"rows": R, "cols": C, "dL_rows": dLR, "dX_rows": dLR @ E_i.T, "dE_cols": X.T @ dLC}
