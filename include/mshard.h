@@ -142,6 +142,37 @@ ms_status ce_combine(const float* m, const float* s, const float* z, int32_t t, 
                      float* loss, float* loss_mean,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace vocab_ce_shard_bwd needs: the per-token records,
+ * the bf16 logit gradient [T x v_i] and, when the token contraction of dE_i
+ * is split, its fp32 slices.  Returns 0 for invalid sizes. */
+size_t vocab_ce_bwd_workspace_bytes(int64_t T, int64_t h, int64_t v_i);
+
+/* Backward of the vocab-parallel logits GEMM fused with cross-entropy (paper
+ * notes, "vocab-embedding parallelism", which gives the forward; the backward
+ * is the derivative of softmax cross-entropy through L = X E_i).  For the
+ * objective sum_t coef[t] loss[t], with coef[t] = grad_scale * dloss[t]
+ * (grad_scale alone when dloss is NULL; grad_scale = 1/T gives the mean):
+ *     M, S   = the token's statistics over the whole vocabulary, merged from
+ *              the ranks' partials in ascending rank order as ce_combine does,
+ *     dL[t,j] = coef[t] (exp(L[t,j] - M[t]) / S[t] - [vocab_start + j == target[t]]),
+ *     dX_i   = dL E_i^T,   dE_i = X^T dL.
+ * L is recomputed (same GEMM as vocab_ce_shard_fwd); dL is rounded to bf16 in
+ * the workspace between the GEMMs.
+ * Inputs : X[T x h], E_i[h x v_i] bf16; target[T] int64 global ids;
+ *          m, s fp32 [t x T] row-major: every rank's vocab_ce_shard_fwd
+ *          outputs m_i, s_i, rank r's at offset r*T (the same buffers
+ *          ce_combine takes); dloss[T] fp32 or NULL; vocab_start >= 0; t >= 1.
+ * Outputs: dX_i[T x h] fp32 (this rank's partial over its vocab columns; the
+ *          ranks' partials sum to dX); dE_i[h x v_i] bf16 (this rank's slice).
+ * Errors : as the other entry points; MS_ERR_SHAPE also when the workspace
+ *          would reach 2^31 bytes (T * v_i * 2 plus records and slices). */
+ms_status vocab_ce_shard_bwd(const ms_bf16* X, const ms_bf16* E_i, const int64_t* target,
+                             const float* m, const float* s, int32_t t,
+                             const float* dloss, float grad_scale,
+                             int64_t T, int64_t h, int64_t v_i, int64_t vocab_start,
+                             float* dX_i, ms_bf16* dE_i,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* Kernels that ms_arm_kernel_events can bracket (one GEMM launch each; the
  * split-K reductions and CE tile-combine kernels are not included). */
 typedef enum {
@@ -152,7 +183,10 @@ typedef enum {
   MS_K_BWD_DB = 4,  /* mlp_shard_bwd:  Y_i^T dZ                                 */
   MS_K_BWD_DA = 5,  /* mlp_shard_bwd:  X^T dH                                   */
   MS_K_BWD_DX = 6,  /* mlp_shard_bwd:  dH A_i^T -> dX_i                         */
-  MS_K_COUNT = 7
+  MS_K_CE_BWD_L = 7,  /* vocab_ce_shard_bwd: X E_i recomputed -> dL             */
+  MS_K_CE_BWD_DX = 8, /* vocab_ce_shard_bwd: dL E_i^T -> dX_i                   */
+  MS_K_CE_BWD_DE = 9, /* vocab_ce_shard_bwd: X^T dL -> dE_i                     */
+  MS_K_COUNT = 10
 } ms_kernel;
 
 /* Measurement hook, no effect on results.  Arms two caller-created HIP events
@@ -161,8 +195,8 @@ typedef enum {
  * `before` on its stream immediately before that launch and `after`
  * immediately after it, so hipEventElapsedTime(before, after) is that one
  * kernel's device time.  mlp_shard_bwd may run two independent GEMMs, (dB, dH)
- * or (dA, dX), as one paired launch; both ids then bracket that one launch
- * and time it together.  The entry point disarms k when it returns (also on
+ * or (dA, dX), as one paired launch, and vocab_ce_shard_bwd likewise (dE, dX);
+ * both ids then bracket that one launch and time it together.  The entry point disarms k when it returns (also on
  * error).  before == after == NULL disarms k.  Errors: MS_ERR_ENUM for an
  * unknown k, MS_ERR_NULL if exactly one event is NULL. */
 ms_status ms_arm_kernel_events(ms_kernel k, void* before, void* after);

@@ -210,6 +210,32 @@ ms_status vocab_ce_shard_fwd(const ms_bf16* X, const ms_bf16* E_i, const int64_t
                   "vocab_ce_shard_fwd");
 }
 
+size_t vocab_ce_bwd_workspace_bytes(int64_t T, int64_t h, int64_t v_i) {
+  if (check_dims(T, {{"h", h}, {"v_i", v_i}}) != MS_OK) return 0;
+  return mshard::ce_bwd_workspace_layout(T, h, v_i).bytes;
+}
+
+ms_status vocab_ce_shard_bwd(const ms_bf16* X, const ms_bf16* E_i, const int64_t* target, const float* m,
+                             const float* s, int32_t t, const float* dloss, float grad_scale, int64_t T, int64_t h,
+                             int64_t v_i, int64_t vocab_start, float* dX_i, ms_bf16* dE_i, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  const DisarmOnReturn disarm{mshard::kTkCeBwdL, mshard::kTkCeBwdDE};
+  MS_TRY(check_dims(T, {{"h", h}, {"v_i", v_i}}));
+  if (t < 1) return fail(MS_ERR_SHAPE, "t must be >= 1 (got %d)", (int)t);
+  if (vocab_start < 0) return fail(MS_ERR_SHAPE, "vocab_start must be >= 0 (got %lld)", (long long)vocab_start);
+  std::vector<Buf> bufs = {{X, nbytes(T, h, 2), "X", false},          {E_i, nbytes(h, v_i, 2), "E_i", false},
+                           {target, nbytes(T, 1, 8), "target", false},  {m, nbytes(t, T, 4), "m", false},
+                           {s, nbytes(t, T, 4), "s", false},            {dX_i, nbytes(T, h, 4), "dX_i", true},
+                           {dE_i, nbytes(h, v_i, 2), "dE_i", true}};
+  if (dloss) bufs.push_back({dloss, nbytes(T, 1, 4), "dloss", false});
+  MS_TRY(check_workspace(workspace, workspace_bytes, mshard::ce_bwd_workspace_layout(T, h, v_i).bytes, bufs));
+  MS_TRY(check_bufs(bufs));
+  MS_TRY(check_device());
+  return launched(mshard::launch_vocab_ce_bwd(X, E_i, target, m, s, (int)t, dloss, grad_scale, T, h, v_i,
+                                              vocab_start, dX_i, dE_i, workspace, (hipStream_t)stream),
+                  "vocab_ce_shard_bwd");
+}
+
 size_t ce_combine_workspace_bytes(int32_t t, int64_t T) {
   (void)t;
   (void)T;

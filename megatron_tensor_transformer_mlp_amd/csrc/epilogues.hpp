@@ -466,4 +466,69 @@ struct EpiCE {
   }
 };
 
+// Cross-entropy backward epilogue of the recomputed logits L = X E_i: the
+// logit gradient of sum_t coef_t loss_t,
+//   dL[t, j] = coef_t (exp(L[t, j] - M_t) / S_t - [j is y_t's shard column])
+//            = exp2(L log2 e - M_t log2 e) (coef_t / S_t) - [j is the target] coef_t,
+// stored as bf16.  (M_t, S_t) are the token's statistics over the whole
+// vocabulary, so the softmax is the global one.  Each token has a 16-byte
+// record {M log2 e, coef / S, coef, target column in this shard or -1 (int
+// bits)}; the rows are walked like EpiDGelu's, with the next 8 rows' records
+// loaded while the current 8 are computed.
+struct EpiCEGrad {
+  const f32x4_t* stats;  // [M] records
+  uint16_t* dL;
+  int64_t ld;
+  int M, N;
+  __device__ void operator()(AccTile& acc, const EpiCtx& c) const {
+    const int64_t base = (int64_t)c.m0 * ld + c.n0;
+    const rsrc_t rd = make_rsrc(dL + base, ((int64_t)M * ld - base) * 2);
+    const rsrc_t rs = make_rsrc(stats + c.m0, (int64_t)(M - c.m0) * 16);
+    const int mrem = M - c.m0, nrem = N - c.n0;
+    char* region = epi_region(c);
+    const int q = c.lane & 31;
+    const int cl = c.wn * kWaveN + q * 4;
+    const int col = c.n0 + cl;  // shard column of this lane's first value
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      epi_stage_half(acc, region, h, c.lane);  // h must be a constant: acc is indexed by it
+      auto load_s = [&](int it0, u32x4_t (&ss)[8]) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int rl = c.wm * kWaveM + h * 64 + (it0 + u) * 2 + (c.lane >> 5);
+          ss[u] = buf_load16(rs, rl < mrem ? (uint32_t)rl * 16u : kOOB);
+        }
+      };
+      u32x4_t scur[8], snext[8];
+      load_s(0, scur);
+#pragma unroll 2
+      for (int it0 = 0; it0 < 32; it0 += 8) {
+        if (it0 + 8 < 32) load_s(it0 + 8, snext);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int lr = (it0 + u) * 2 + (c.lane >> 5);
+          const int rl = c.wm * kWaveM + h * 64 + lr;
+          const bool ok = rl < mrem && cl < nrem;
+          const f32x4_t v = epi_read(region, lr, q);
+          const float ml = __uint_as_float(scur[u][0]);
+          const float cs = __uint_as_float(scur[u][1]);
+          const float cf = __uint_as_float(scur[u][2]);
+          const int tcol = (int)scur[u][3];
+          float d[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(v[r], kLog2e, -ml));
+            d[r] = __builtin_fmaf(e, cs, col + r == tcol ? -cf : 0.0f);
+          }
+          buf_store8(u32x2_t{pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3])}, rd,
+                     ok ? (uint32_t)(((int64_t)rl * ld + cl) * 2) : kOOB);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) scur[u] = snext[u];
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+};
+
 }  // namespace mshard

@@ -118,6 +118,27 @@ __global__ void __launch_bounds__(256) ce_combine_tokens(const float* __restrict
   loss[i] = logf(S) + M - Z;
 }
 
+// Per token, the record the cross-entropy backward's epilogue reads: the
+// ranks' (m, s) merged in ascending rank order as in ce_combine_tokens, then
+// {M log2 e, coef / S, coef, target column in this shard or -1}, with
+// coef = scale * dloss[i] (dloss may be null: 1).
+__global__ void __launch_bounds__(256) ce_bwd_rowstats(const float* __restrict__ m, const float* __restrict__ s,
+                                                       int t, int64_t T, const float* __restrict__ dloss,
+                                                       float scale, const int64_t* __restrict__ target,
+                                                       int64_t vocab_start, int64_t v, f32x4_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= T) return;
+  float M = -INFINITY, S = 0.f;
+  for (int r = 0; r < t; ++r) {
+    const int64_t o = (int64_t)r * T + i;
+    lse_merge(M, S, m[o], s[o]);
+  }
+  const float coef = dloss ? scale * dloss[i] : scale;
+  const int64_t tc = target[i] - vocab_start;
+  const int col = (tc >= 0 && tc < v) ? (int)tc : -1;
+  out[i] = f32x4_t{M * kLog2e, coef / S, coef, __int_as_float(col)};
+}
+
 // Mean of loss[0..T): thread j sums j, j+1024, ... in order, then a fixed
 // binary tree over the 1024 thread sums.  One workgroup.
 __global__ void __launch_bounds__(1024) mean_fixed_tree(const float* __restrict__ x, int64_t T,
@@ -206,12 +227,14 @@ double reduce_us(int64_t M, int64_t N, int S) {
   return S == 1 ? 0.0 : (double)(4 * S + 2) * (double)M * (double)N / 4e6 + 3.0;
 }
 
-// Weight gradient [M x N] (contraction over T) with partner GEMM blocks `p`.
-void plan_pair(int64_t M, int64_t N, int64_t T, BlockList p, int& S_out, bool& paired, bool& partner_first) {
+// Weight gradient [M x N] (contraction over T) with partner GEMM blocks `p`;
+// K splits above max_splits are not considered.
+void plan_pair(int64_t M, int64_t N, int64_t T, BlockList p, int& S_out, bool& paired, bool& partner_first,
+               int max_splits = 8) {
   const int64_t nk = (T + kBK - 1) / kBK;
   const double alone = makespan_us({p});
   double best = 1e300;
-  for (int S = 1; S <= 8; S *= 2) {
+  for (int S = 1; S <= max_splits; S *= 2) {
     if (S > 1 && nk / S < 8) break;
     const BlockList w{tile_count(M, N) * S, block_cost(T, S, S == 1 ? kEpiBF16 : kEpiF32)};
     const double seq = makespan_us({w}) + alone + reduce_us(M, N, S);
@@ -276,6 +299,35 @@ CeWorkspace ce_workspace_layout(int64_t T, int64_t v) {
   w.off_s = one;
   w.off_z = 2 * one;
   w.bytes = 3 * one;
+  return w;
+}
+
+// Cross-entropy backward: per-token records, the bf16 logit gradient dL
+// [T x v], and the split-K slices of dE when the plan splits it.  dE = X^T dL
+// and dX = dL E^T are independent and planned like the MLP's (dA, dX); the
+// split is capped so that the whole workspace stays below 2^31 bytes.
+CeBwdWorkspace ce_bwd_workspace_layout(int64_t T, int64_t h, int64_t v) {
+  static std::mutex mu;
+  static std::map<std::array<int64_t, 3>, CeBwdWorkspace> cache;
+  const std::array<int64_t, 3> key{T, h, v};
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+  }
+  auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  CeBwdWorkspace w;
+  w.off_stats = 0;
+  w.off_dL = align((size_t)T * 16);
+  w.off_splitk = w.off_dL + align((size_t)T * v * 2);
+  const size_t slice = (size_t)h * v * 4;
+  int max_splits = 1;
+  while (max_splits < 8 && w.off_splitk + align(slice * 2 * max_splits) < ((size_t)1 << 31)) max_splits *= 2;
+  const BlockList dx{tile_count(T, h), block_cost(v, 1, kEpiF32)};
+  plan_pair(h, v, T, dx, w.splits_dE, w.paired, w.dx_first, max_splits);
+  w.bytes = w.off_splitk + (w.splits_dE > 1 ? align(slice * w.splits_dE) : 0);
+  std::lock_guard<std::mutex> lock(mu);
+  cache.emplace(key, w);
   return w;
 }
 
@@ -427,6 +479,42 @@ hipError_t launch_vocab_ce(const uint16_t* X, const uint16_t* E, const int64_t* 
   hipLaunchKernelGGL(ce_tile_combine, dim3((unsigned)((T + 63) / 64)), dim3(512), 0, st, pm, ps, pz, w.parts,
                      (int)T, m, s, z);
   return hipGetLastError();
+}
+
+hipError_t launch_vocab_ce_bwd(const uint16_t* X, const uint16_t* E, const int64_t* target, const float* m,
+                               const float* s, int t, const float* dloss, float scale, int64_t T, int64_t h,
+                               int64_t v, int64_t vocab_start, float* dX, uint16_t* dE, void* ws, hipStream_t st) {
+  const CeBwdWorkspace w = ce_bwd_workspace_layout(T, h, v);
+  f32x4_t* stats = (f32x4_t*)((char*)ws + w.off_stats);
+  uint16_t* dL = (uint16_t*)((char*)ws + w.off_dL);
+  float* splitk = (float*)((char*)ws + w.off_splitk);
+  hipLaunchKernelGGL(ce_bwd_rowstats, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, st, m, s, t, T, dloss,
+                     scale, target, vocab_start, v, stats);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  // dL from the recomputed logits X E:  NN, M = T, N = v, K = h
+  {
+    const GemmGeom g = make_geom(T, v, h, 1);
+    const Operand a{X, h, T * h}, b{E, v, h * v};
+    const EpiCEGrad e{stats, dL, v, (int)T, (int)v};
+    if ((err = launch_gemm<true, false>(kTkCeBwdL, g, a, b, e, st)) != hipSuccess) return err;
+  }
+  // dE = X^T dL:  [h x v], contraction over tokens;  dX = dL E^T:  NT, M = T, N = h, K = v;
+  // E stored [h x v] = [N x K]
+  const WeightGrad we = weight_grad_setup(X, h, dL, v, T, h, v, w.splits_dE, dE, splitk);
+  const GemmGeom gx = make_geom(T, h, v, 1);
+  const Operand ax{dL, v, T * v}, bx{E, v, h * v};
+  const EpiStoreF32 ex{dX, h, (int)T, (int)h, 0};
+  if (w.paired) {
+    err = launch_gemm_pair<false, false, true, true>(kTkCeBwdDE, we.g, we.a, we.b, we.e, kTkCeBwdDX, gx, ax, bx, ex,
+                                                     w.dx_first, st);
+  } else {
+    err = launch_gemm<true, true>(kTkCeBwdDX, gx, ax, bx, ex, st);
+    if (err == hipSuccess) err = launch_gemm<false, false>(kTkCeBwdDE, we.g, we.a, we.b, we.e, st);
+  }
+  if (err != hipSuccess) return err;
+  if (we.S > 1) err = launch_splitk_reduce(splitk, h, v, we.S, dE, st);
+  return err;
 }
 
 hipError_t launch_ce_combine(const float* m, const float* s, const float* z, int t, int64_t T, float* loss,

@@ -32,8 +32,21 @@ struct CeWorkspace {
   int parts;
 };
 
+struct CeBwdWorkspace {
+  size_t off_stats;   // [T] 16-byte per-token records
+  size_t off_dL;      // bf16 [T x v]: the logit gradient
+  size_t off_splitk;  // fp32 [S x h*v]: split-K slices of dE
+  size_t bytes;
+  int splits_dE;      // K split of dE (1 = none)
+  bool paired;        // dE and dX share one launch
+  bool dx_first;      // in the paired launch, dX's blocks lead
+};
+
 // Kernel ids for the measurement hook (same values as ms_kernel in mshard.h).
-enum TimedKernel { kTkCeGemm = 0, kTkFwdH, kTkFwdZ, kTkBwdDH, kTkBwdDB, kTkBwdDA, kTkBwdDX, kTkCount };
+enum TimedKernel {
+  kTkCeGemm = 0, kTkFwdH, kTkFwdZ, kTkBwdDH, kTkBwdDB, kTkBwdDA, kTkBwdDX, kTkCeBwdL, kTkCeBwdDX, kTkCeBwdDE,
+  kTkCount
+};
 
 // Records the armed event (if any) of kernel `id` on `st`; `after` picks which
 // of the pair.  Defined by the ABI layer, which owns the per-thread arming.
@@ -42,6 +55,7 @@ void record_armed_event(int id, bool after, hipStream_t st);
 BwdPlan plan_backward(int64_t T, int64_t h, int64_t f);
 MlpWorkspace mlp_workspace_layout(int64_t T, int64_t h, int64_t f);
 CeWorkspace ce_workspace_layout(int64_t T, int64_t v);
+CeBwdWorkspace ce_bwd_workspace_layout(int64_t T, int64_t h, int64_t v);
 
 hipError_t launch_mlp_fwd(const uint16_t* X, const uint16_t* A, const uint16_t* b1, const uint16_t* B,
                           int64_t T, int64_t h, int64_t f, int gelu, uint16_t* H, uint16_t* Y, float* Z,
@@ -52,6 +66,9 @@ hipError_t launch_mlp_bwd(const uint16_t* X, const uint16_t* A, const uint16_t* 
 hipError_t launch_vocab_ce(const uint16_t* X, const uint16_t* E, const int64_t* target, int64_t T, int64_t h,
                            int64_t v, int64_t vocab_start, float* m, float* s, float* z, void* ws,
                            hipStream_t st);
+hipError_t launch_vocab_ce_bwd(const uint16_t* X, const uint16_t* E, const int64_t* target, const float* m,
+                               const float* s, int t, const float* dloss, float scale, int64_t T, int64_t h,
+                               int64_t v, int64_t vocab_start, float* dX, uint16_t* dE, void* ws, hipStream_t st);
 hipError_t launch_ce_combine(const float* m, const float* s, const float* z, int t, int64_t T, float* loss,
                              float* loss_mean, hipStream_t st);
 

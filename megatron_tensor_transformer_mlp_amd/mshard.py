@@ -6,8 +6,8 @@ device pointers plus the current HIP stream.  If the library is not built the
 import fails loudly; there is no fallback.
 
 Entry points mirror the C ABI in include/mshard.h:
-  mlp_shard_fwd, mlp_shard_bwd, vocab_ce_shard_fwd, ce_combine, plus the
-  workspace-size queries.
+  mlp_shard_fwd, mlp_shard_bwd, vocab_ce_shard_fwd, ce_combine,
+  vocab_ce_shard_bwd, plus the workspace-size queries.
 """
 from __future__ import annotations
 
@@ -26,11 +26,13 @@ STATUS_NAMES = ["MS_OK", "MS_ERR_NULL", "MS_ERR_SHAPE", "MS_ERR_ALIGN", "MS_ERR_
 GELU = {"erf": 0, "tanh": 1}
 
 EXPORTED = ("mlp_shard_workspace_bytes", "mlp_shard_fwd", "mlp_shard_bwd", "vocab_ce_workspace_bytes",
-            "vocab_ce_shard_fwd", "ce_combine_workspace_bytes", "ce_combine", "ms_arm_kernel_events",
+            "vocab_ce_shard_fwd", "ce_combine_workspace_bytes", "ce_combine", "vocab_ce_bwd_workspace_bytes",
+            "vocab_ce_shard_bwd", "ms_arm_kernel_events",
             "ms_last_error", "ms_version")
 
 # ms_kernel ids: the single GEMM launches ms_arm_kernel_events can bracket
-KERNELS = {"ce_gemm": 0, "fwd_h": 1, "fwd_z": 2, "bwd_dh": 3, "bwd_db": 4, "bwd_da": 5, "bwd_dx": 6}
+KERNELS = {"ce_gemm": 0, "fwd_h": 1, "fwd_z": 2, "bwd_dh": 3, "bwd_db": 4, "bwd_da": 5, "bwd_dx": 6,
+           "ce_bwd_l": 7, "ce_bwd_dx": 8, "ce_bwd_de": 9}
 
 
 class MshardError(RuntimeError):
@@ -58,6 +60,9 @@ def _load() -> ctypes.CDLL:
         "vocab_ce_shard_fwd": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
         "ce_combine_workspace_bytes": (_sz, [_i32, _i64]),
         "ce_combine": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i64, _vp, _vp, _vp, _sz, _vp]),
+        "vocab_ce_bwd_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+        "vocab_ce_shard_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, ctypes.c_float, _i64, _i64, _i64,
+                                              _i64, _vp, _vp, _vp, _sz, _vp]),
         "ms_arm_kernel_events": (ctypes.c_int, [ctypes.c_int, _vp, _vp]),
         "ms_last_error": (ctypes.c_char_p, []),
         "ms_version": (ctypes.c_char_p, []),
@@ -120,6 +125,10 @@ def mlp_shard_workspace_bytes(T: int, h: int, f_i: int) -> int:
 
 def vocab_ce_workspace_bytes(T: int, h: int, v_i: int) -> int:
     return int(LIB.vocab_ce_workspace_bytes(T, h, v_i))
+
+
+def vocab_ce_bwd_workspace_bytes(T: int, h: int, v_i: int) -> int:
+    return int(LIB.vocab_ce_bwd_workspace_bytes(T, h, v_i))
 
 
 def ce_combine_workspace_bytes(t: int, T: int) -> int:
@@ -212,3 +221,32 @@ def ce_combine(m: torch.Tensor, s: torch.Tensor, z: torch.Tensor, want_mean: boo
     st = LIB.ce_combine(_ptr(m), _ptr(s), _ptr(z), t, T, _ptr(loss), _ptr(mean), None, 0, _stream(m.device))
     _check(st, "ce_combine")
     return loss, mean
+
+
+def vocab_ce_shard_bwd(X, E_i, target, m, s, vocab_start: int, dloss: Optional[torch.Tensor] = None,
+                       grad_scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None, out=None):
+    """(dX_i fp32 [T, h], dE_i bf16 [h, v_i]) = backward of this rank's fused logits GEMM + CE.
+
+    m, s: fp32 [t, T], every rank's forward partials in rank order.  The objective is
+    sum_t coef[t] * loss[t] with coef = grad_scale * dloss (grad_scale alone without
+    dloss); grad_scale defaults to 1/T, the gradient of the mean loss."""
+    T, h = X.shape
+    v_i = E_i.shape[1]
+    t = m.shape[0]
+    _dev(X, "X", torch.bfloat16, (T, h)); _dev(E_i, "E_i", torch.bfloat16, (h, v_i))
+    _dev(target, "target", torch.int64, (T,))
+    _dev(m, "m", torch.float32, (t, T)); _dev(s, "s", torch.float32, (t, T))
+    if dloss is not None:
+        _dev(dloss, "dloss", torch.float32, (T,))
+    scale = 1.0 / T if grad_scale is None else float(grad_scale)
+    if out is None:
+        dX = torch.empty((T, h), dtype=torch.float32, device=X.device)
+        dE = torch.empty((h, v_i), dtype=torch.bfloat16, device=X.device)
+    else:
+        dX, dE = out
+    nbytes = vocab_ce_bwd_workspace_bytes(T, h, v_i)
+    ws = _workspace(nbytes, X.device, workspace)
+    st = LIB.vocab_ce_shard_bwd(_ptr(X), _ptr(E_i), _ptr(target), _ptr(m), _ptr(s), t, _ptr(dloss), scale, T, h,
+                                v_i, int(vocab_start), _ptr(dX), _ptr(dE), _ptr(ws), nbytes, _stream(X.device))
+    _check(st, "vocab_ce_shard_bwd")
+    return dX, dE

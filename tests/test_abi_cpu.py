@@ -101,6 +101,47 @@ def test_ce_validation(ms):
     assert ce(z=p[4] + 16) == ms.MS_ERR_ALIAS
 
 
+def test_ce_bwd_workspace_sizes(ms):
+    T, h, v = 8192, 1600, 50304
+    need = ms.vocab_ce_bwd_workspace_bytes(T, h, v)
+    assert need >= T * v * 2 + T * 16          # the bf16 logit gradient and the per-token records
+    assert need < 1 << 31                      # the whole workspace stays addressable as one buffer
+    assert ms.vocab_ce_bwd_workspace_bytes(T, h, v - 4) == 0
+    assert ms.vocab_ce_bwd_workspace_bytes(0, h, v) == 0
+    # a logit gradient of 2^31 bytes or more cannot be held: the size is reported and the call refused
+    assert ms.vocab_ce_bwd_workspace_bytes(1 << 16, 64, 1 << 14) >= 1 << 31
+
+
+def test_ce_bwd_validation(ms):
+    T, h, v, t = 128, 64, 512, 2
+    need = ms.vocab_ce_bwd_workspace_bytes(T, h, v)
+    p = [FAKE + (i << 30) for i in range(10)]
+
+    def bwd(X=p[0], tgt=p[2], m=p[3], s=p[4], t_=t, dloss=None, T_=T, v_=v, start=0, dX=p[5], dE=p[6],
+            ws=p[7], nbytes=need):
+        return ms.LIB.vocab_ce_shard_bwd(X, p[1], tgt, m, s, t_, dloss, 1.0 / T, T_, h, v_, start, dX, dE, ws,
+                                         nbytes, None)
+
+    assert bwd(X=None) == ms.MS_ERR_NULL
+    assert bwd(tgt=None) == ms.MS_ERR_NULL
+    assert bwd(s=None) == ms.MS_ERR_NULL
+    assert bwd(t_=0) == ms.MS_ERR_SHAPE
+    assert bwd(v_=500) == ms.MS_ERR_SHAPE
+    assert bwd(T_=0) == ms.MS_ERR_SHAPE
+    assert bwd(start=-1) == ms.MS_ERR_SHAPE
+    assert bwd(ws=None) == ms.MS_ERR_WORKSPACE
+    assert bwd(nbytes=need - 1) == ms.MS_ERR_WORKSPACE
+    assert bwd(dX=p[0] + 64) == ms.MS_ERR_ALIAS          # dX_i on top of X
+    assert bwd(dE=p[5] + 16) == ms.MS_ERR_ALIAS          # the two outputs overlap
+    assert bwd(dloss=p[7] + 256) == ms.MS_ERR_ALIAS      # dloss inside the workspace
+    assert bwd(dloss=p[8] + 4) == ms.MS_ERR_ALIGN
+    assert bwd(m=p[3] + 8) == ms.MS_ERR_ALIGN
+    big_T, big_v = 1 << 16, 1 << 14                       # dL alone would be 2 GiB
+    assert ms.LIB.vocab_ce_shard_bwd(p[0], p[1], p[2], p[3], p[4], 1, None, 1.0, big_T, 8, big_v, 0, p[5], p[6],
+                                     p[7], 1 << 40, None) == ms.MS_ERR_SHAPE
+    assert "2^31" in ms.LIB.ms_last_error().decode()
+
+
 def test_combine_validation(ms):
     p = [FAKE + (i << 30) for i in range(5)]
     assert ms.LIB.ce_combine(p[0], p[1], p[2], 0, 16, p[3], p[4], None, 0, None) == ms.MS_ERR_SHAPE
@@ -130,11 +171,11 @@ def test_binding_has_no_fallback():
 
 def test_arm_kernel_events_validation(ms):
     fake_ev = FAKE  # never recorded: the arming is cleared again below without a launch
-    assert ms.LIB.ms_arm_kernel_events(7, None, None) == ms.MS_ERR_ENUM
+    assert ms.LIB.ms_arm_kernel_events(10, None, None) == ms.MS_ERR_ENUM
     assert ms.LIB.ms_arm_kernel_events(-1, None, None) == ms.MS_ERR_ENUM
     assert ms.LIB.ms_arm_kernel_events(0, fake_ev, None) == ms.MS_ERR_NULL
     assert "both events" in ms.LIB.ms_last_error().decode()
     assert ms.LIB.ms_arm_kernel_events(0, None, None) == ms.MS_OK
-    for k in range(7):
+    for k in range(10):
         assert ms.LIB.ms_arm_kernel_events(k, None, None) == ms.MS_OK
-    assert set(ms.KERNELS.values()) == set(range(7))
+    assert set(ms.KERNELS.values()) == set(range(10))
