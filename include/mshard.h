@@ -38,7 +38,7 @@
  *   - Validation runs first, on the host, without touching device memory.  On
  *     any error nothing is enqueued, the status is returned, and
  *     ms_last_error() gives a message.  Checks: required pointers non-NULL;
- *     T >= 1 and h, f_i, v_i >= 8 and multiples of 8; every buffer and the
+ *     T >= 1 and h, f_i, v_i >= 8, multiples of 8 and below 2^22; every buffer and the
  *     workspace 16-byte aligned; every buffer smaller than 2^31 bytes; no output
  *     overlapping an input, another output or the workspace; workspace at least
  *     the size the matching *_workspace_bytes function returns.

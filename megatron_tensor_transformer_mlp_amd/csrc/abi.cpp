@@ -60,13 +60,19 @@ size_t nbytes(int64_t a, int64_t b, int64_t esize) {
   return (size_t)(ab * esize);
 }
 
+// h, f_i and v_i are the leading dimensions of the GEMM operands; keeping them
+// below 2^22 elements keeps every per-lane load offset of a 256-row tile, and
+// every masked one, inside 32 bits (the kernels rely on it).
+constexpr int64_t kMaxLd = (int64_t)1 << 22;
+
 ms_status check_dims(int64_t T, std::initializer_list<std::pair<const char*, int64_t>> dims) {
   if (T < 1) return fail(MS_ERR_SHAPE, "T must be >= 1 (got %lld)", (long long)T);
   if (T > INT32_MAX) return fail(MS_ERR_SHAPE, "T too large (%lld)", (long long)T);
   for (auto& d : dims) {
     if (d.second < 8 || d.second % 8 != 0)
       return fail(MS_ERR_SHAPE, "%s must be a positive multiple of 8 (got %lld)", d.first, (long long)d.second);
-    if (d.second > INT32_MAX) return fail(MS_ERR_SHAPE, "%s too large (%lld)", d.first, (long long)d.second);
+    if (d.second >= kMaxLd)
+      return fail(MS_ERR_SHAPE, "%s must be < 2^22 (got %lld)", d.first, (long long)d.second);
   }
   return MS_OK;
 }

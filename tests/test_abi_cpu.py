@@ -68,6 +68,11 @@ def test_fwd_validation(ms):
     assert _fwd(ms, Z=FAKE + 16) == ms.MS_ERR_ALIAS                   # output overlaps input X
     assert _fwd(ms, T=1 << 20, h=1 << 12) == ms.MS_ERR_SHAPE          # X would be >= 2^31 bytes... 8 GiB
     assert "2^31" in ms.LIB.ms_last_error().decode()
+    # every buffer under 2^31 bytes, but a leading dimension of 2^25 elements: refused
+    assert _fwd(ms, T=1, h=8, f=1 << 25) == ms.MS_ERR_SHAPE
+    assert "2^22" in ms.LIB.ms_last_error().decode()
+    assert ms.mlp_shard_workspace_bytes(8, 8, (1 << 22) - 8) > 0
+    assert ms.mlp_shard_workspace_bytes(8, 8, 1 << 22) == 0
 
 
 def test_bwd_validation(ms):
