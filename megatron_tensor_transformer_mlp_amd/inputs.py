@@ -5,8 +5,10 @@ and the fp64 CPU oracle.  It draws random numbers, scales them and rounds them
 to bf16 bit patterns; it contains none of the method's arithmetic.
 
 Recipe (the same bytes feed both sides):
-  * ``np.random.SeedSequence(seed).spawn(7)`` gives one child per stream, in
-    the fixed order X, A, B, E, dZ, targets, b1.  Weight streams (A, B, E, b1)
+  * ``np.random.SeedSequence(seed).spawn(9)`` gives one child per stream, in
+    the fixed order X, A, B, E, dZ, targets, b1, Wqkv, Wo (children are
+    positional, so the first seven are those of the original seven-stream
+    recipe).  Weight streams (A, B, E, b1, Wqkv, Wo)
     spawn one grandchild per tensor-parallel rank, so rank r's shard is drawn
     directly (entries are iid, which has the same law as slicing a full draw).
   * Normals are drawn as float32 from PCG64, multiplied by a float32 sigma and
@@ -15,9 +17,10 @@ Recipe (the same bytes feed both sides):
     a single draw would.
   * Targets are int64 global vocabulary ids, uniform over [0, v_global).
 
-Shapes follow the Megatron-LM paper notes (MLP-block split and vocab-embedding
-parallelism sections): X[T x h], A_i[h x f_i], B_i[f_i x h], E_i[h x v_i],
-dZ[T x h], all row-major.
+Shapes follow the Megatron-LM paper notes (MLP-block split, self-attention
+block split and vocab-embedding parallelism sections): X[T x h], A_i[h x f_i],
+B_i[f_i x h], E_i[h x v_i], dZ[T x h], Wqkv_i[h x 3nd], Wo_i[nd x h], all
+row-major.
 """
 from __future__ import annotations
 
@@ -26,7 +29,7 @@ from typing import Dict, List, Optional
 
 import numpy as np
 
-STREAMS = ("X", "A", "B", "E", "dZ", "targets", "b1")
+STREAMS = ("X", "A", "B", "E", "dZ", "targets", "b1", "Wqkv", "Wo")
 _ELEMS_PER_BLOCK = 1 << 24
 
 
@@ -156,3 +159,68 @@ def sample_indices(n: int, count: int, seed: int, edges: List[int]) -> np.ndarra
     pick = g.choice(n, size=min(count, n), replace=False)
     extra = np.array([e for e in edges if 0 <= e < n], dtype=np.int64)
     return np.unique(np.concatenate([pick.astype(np.int64), extra]))
+
+
+@dataclasses.dataclass(frozen=True)
+class AttnConfig:
+    """One rank's self-attention shard: b sequences of s tokens, hidden h, n_heads
+    heads of size d in the whole layer, t ranks (n_heads / t heads each)."""
+    name: str
+    b: int
+    s: int
+    h: int
+    n_heads: int
+    d: int
+    t: int
+    causal: bool
+    sigma_w: float = 0.02
+
+    @property
+    def T(self) -> int:
+        return self.b * self.s
+
+    @property
+    def n(self) -> int:
+        """Heads on one rank."""
+        return self.n_heads // self.t
+
+
+# Attention shards of the same five layers.  The 8.3B-GPT-like shard's head size
+# of 96 is the one the paper notes give for their GPT scaling models; the other
+# head counts are those of the named models' published configurations.
+ATTN_CONFIGS: Dict[str, AttnConfig] = {
+    "tiny": AttnConfig("tiny", b=2, s=32, h=64, n_heads=4, d=16, t=1, causal=True),
+    "gpt2_1p5b": AttnConfig("gpt2_1p5b", b=8, s=1024, h=1600, n_heads=25, d=64, t=1, causal=True),
+    "gpt_8p3b_t8": AttnConfig("gpt_8p3b_t8", b=8, s=1024, h=3072, n_heads=32, d=96, t=8, causal=True),
+    "bert_3p9b_t4": AttnConfig("bert_3p9b_t4", b=16, s=512, h=2560, n_heads=40, d=64, t=4, causal=False),
+    "bloom_176b_t4": AttnConfig("bloom_176b_t4", b=1, s=2048, h=14336, n_heads=112, d=128, t=4, causal=True,
+                                sigma_w=0.006),
+}
+
+
+def make_attn_inputs(b: int, s: int, h: int, n: int, d: int, *, t: int = 1, rank: int = 0,
+                     sigma_w: float = 0.02, seed: int = 1234,
+                     want=("X", "Wqkv", "Wo", "dZ")) -> Dict[str, np.ndarray]:
+    """Rank ``rank``'s attention-shard inputs as bf16 bit patterns (uint16).
+
+    X[b*s, h] and dZ[b*s, h] are the same draws as the MLP shard's for the same
+    token count and hidden size; Wqkv[h, 3nd] and Wo[nd, h] come from their
+    own streams, one grandchild per rank (n = heads on this rank)."""
+    ch = _children(seed)
+    T = b * s
+    out: Dict[str, np.ndarray] = {}
+    if "X" in want:
+        out["X"] = _normal_bf16(ch["X"], (T, h), 1.0)
+    if "Wqkv" in want:
+        out["Wqkv"] = _normal_bf16(_rank_child(ch["Wqkv"], t, rank), (h, 3 * n * d), sigma_w)
+    if "Wo" in want:
+        out["Wo"] = _normal_bf16(_rank_child(ch["Wo"], t, rank), (n * d, h), sigma_w)
+    if "dZ" in want:
+        out["dZ"] = _normal_bf16(ch["dZ"], (T, h), 1.0)
+    return out
+
+
+def make_attn_config_inputs(cfg: AttnConfig, *, rank: int = 0, seed: int = 1234,
+                            want=("X", "Wqkv", "Wo", "dZ")) -> Dict[str, np.ndarray]:
+    return make_attn_inputs(cfg.b, cfg.s, cfg.h, cfg.n, cfg.d, t=cfg.t, rank=rank, sigma_w=cfg.sigma_w, seed=seed,
+                            want=want)

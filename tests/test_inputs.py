@@ -51,3 +51,21 @@ def test_config_table():
 def test_sample_indices_include_edges():
     s = inputs.sample_indices(1000, 50, 7, [0, 255, 256, 999, 5000])
     assert {0, 255, 256, 999} <= set(s.tolist()) and 5000 not in s and len(s) >= 50
+
+
+def test_attn_inputs_shapes_and_sharing():
+    c = inputs.ATTN_CONFIGS["tiny"]
+    a = inputs.make_attn_config_inputs(c)
+    n, d, h, T = c.n, c.d, c.h, c.T
+    assert a["X"].shape == (T, h) and a["dZ"].shape == (T, h)
+    assert a["Wqkv"].shape == (h, 3 * n * d) and a["Wo"].shape == (n * d, h)
+    m = inputs.make_inputs(T, h, 8, 8)
+    np.testing.assert_array_equal(a["X"], m["X"])     # the same token activations as the MLP shard
+    np.testing.assert_array_equal(a["dZ"], m["dZ"])
+    r1 = inputs.make_attn_inputs(2, 16, 64, 2, 16, t=2, rank=1)
+    r0 = inputs.make_attn_inputs(2, 16, 64, 2, 16, t=2, rank=0)
+    assert not np.array_equal(r0["Wqkv"], r1["Wqkv"]) and not np.array_equal(r0["Wo"], r1["Wo"])
+    for cfg in inputs.ATTN_CONFIGS.values():
+        assert cfg.n * cfg.t == cfg.n_heads and cfg.n_heads * cfg.d == cfg.h
+        assert cfg.T == inputs.CONFIGS[cfg.name].T and cfg.h == inputs.CONFIGS[cfg.name].h
+        assert cfg.t == inputs.CONFIGS[cfg.name].t
