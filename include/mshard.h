@@ -201,6 +201,28 @@ typedef enum {
  * unknown k, MS_ERR_NULL if exactly one event is NULL. */
 ms_status ms_arm_kernel_events(ms_kernel k, void* before, void* after);
 
+/* Number of 64-bit words ms_fingerprint writes for a buffer of `bytes` bytes
+ * in chunks of `chunk_bytes`: 1 + ceil(bytes / chunk_bytes), or 2 when bytes
+ * is 0.  Returns 0 when chunk_bytes is not a positive multiple of 8 (at most
+ * 2^40), bytes >= 2^48, or there would be 2^31 chunks or more. */
+size_t ms_fingerprint_words(size_t bytes, size_t chunk_bytes);
+
+/* Fingerprint of a device buffer, for finding the first call whose outputs
+ * differ between two runs (determinism news item, "debugging methodology":
+ * tensors fingerprinted on the GPU, chunk-wise where the order of the data
+ * matters).  The hash is XXH64 with seed 0 (xxHash's published
+ * specification).  The buffer is split into chunks of chunk_bytes (the last
+ * one shorter; one empty chunk when bytes is 0).
+ * Output : out[1 + k] = XXH64 of chunk k; out[0] = XXH64 of out[1 ..] as
+ *          little-endian 64-bit words, in chunk order.  out is a DEVICE array
+ *          of ms_fingerprint_words(bytes, chunk_bytes) uint64.
+ * Inputs : buf, a DEVICE pointer, 8-byte aligned; it may hold any bytes.
+ * Errors : MS_ERR_SHAPE for sizes ms_fingerprint_words rejects, MS_ERR_NULL,
+ *          MS_ERR_ALIGN (8 bytes for buf and out), MS_ERR_ALIAS if out
+ *          overlaps buf.  One thread hashes each chunk: a debugging aid, not
+ *          a fast path. */
+ms_status ms_fingerprint(const void* buf, size_t bytes, size_t chunk_bytes, uint64_t* out, void* stream);
+
 /* Text for the last non-OK status returned on the calling thread ("" if none).
  * The pointer stays valid until the next library call on this thread. */
 const char* ms_last_error(void);

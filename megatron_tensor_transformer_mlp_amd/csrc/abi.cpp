@@ -264,6 +264,29 @@ ms_status ce_combine(const float* m, const float* s, const float* z, int32_t t, 
   return launched(mshard::launch_ce_combine(m, s, z, t, T, loss, loss_mean, (hipStream_t)stream), "ce_combine");
 }
 
+size_t ms_fingerprint_words(size_t bytes, size_t chunk_bytes) {
+  if (chunk_bytes < 8 || chunk_bytes % 8 != 0 || chunk_bytes > ((size_t)1 << 40)) return 0;
+  if (bytes >= ((size_t)1 << 48)) return 0;
+  const uint64_t n = mshard::fingerprint_chunk_count(bytes, chunk_bytes);
+  if (n > (uint64_t)INT32_MAX) return 0;
+  return (size_t)(1 + n);
+}
+
+ms_status ms_fingerprint(const void* buf, size_t bytes, size_t chunk_bytes, uint64_t* out, void* stream) {
+  const size_t words = ms_fingerprint_words(bytes, chunk_bytes);
+  if (words == 0)
+    return fail(MS_ERR_SHAPE, "chunk_bytes must be a positive multiple of 8 (<= 2^40), bytes < 2^48 and at most "
+                "2^31 - 1 chunks (got bytes %zu, chunk_bytes %zu)", bytes, chunk_bytes);
+  if (!buf) return fail(MS_ERR_NULL, "buf is NULL");
+  if (!out) return fail(MS_ERR_NULL, "out is NULL");
+  if (((uintptr_t)buf & 7) != 0) return fail(MS_ERR_ALIGN, "buf is not 8-byte aligned");
+  if (((uintptr_t)out & 7) != 0) return fail(MS_ERR_ALIGN, "out is not 8-byte aligned");
+  const uintptr_t b0 = (uintptr_t)buf, b1 = b0 + bytes, o0 = (uintptr_t)out, o1 = o0 + words * 8;
+  if (b0 < o1 && o0 < b1) return fail(MS_ERR_ALIAS, "out overlaps buf");
+  MS_TRY(check_device());
+  return launched(mshard::launch_fingerprint(buf, bytes, chunk_bytes, out, (hipStream_t)stream), "ms_fingerprint");
+}
+
 ms_status ms_arm_kernel_events(ms_kernel k, void* before, void* after) {
   if ((int)k < 0 || (int)k >= mshard::kTkCount) return fail(MS_ERR_ENUM, "unknown kernel id %d", (int)k);
   if ((before == nullptr) != (after == nullptr))

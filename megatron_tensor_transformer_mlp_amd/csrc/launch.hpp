@@ -69,6 +69,8 @@ hipError_t launch_vocab_ce(const uint16_t* X, const uint16_t* E, const int64_t* 
 hipError_t launch_vocab_ce_bwd(const uint16_t* X, const uint16_t* E, const int64_t* target, const float* m,
                                const float* s, int t, const float* dloss, float scale, int64_t T, int64_t h,
                                int64_t v, int64_t vocab_start, float* dX, uint16_t* dE, void* ws, hipStream_t st);
+uint64_t fingerprint_chunk_count(uint64_t bytes, uint64_t chunk);
+hipError_t launch_fingerprint(const void* buf, uint64_t bytes, uint64_t chunk, uint64_t* out, hipStream_t st);
 hipError_t launch_ce_combine(const float* m, const float* s, const float* z, int t, int64_t T, float* loss,
                              float* loss_mean, hipStream_t st);
 

@@ -27,7 +27,7 @@ GELU = {"erf": 0, "tanh": 1}
 
 EXPORTED = ("mlp_shard_workspace_bytes", "mlp_shard_fwd", "mlp_shard_bwd", "vocab_ce_workspace_bytes",
             "vocab_ce_shard_fwd", "ce_combine_workspace_bytes", "ce_combine", "vocab_ce_bwd_workspace_bytes",
-            "vocab_ce_shard_bwd", "ms_arm_kernel_events",
+            "vocab_ce_shard_bwd", "ms_fingerprint_words", "ms_fingerprint", "ms_arm_kernel_events",
             "ms_last_error", "ms_version")
 
 # ms_kernel ids: the single GEMM launches ms_arm_kernel_events can bracket
@@ -63,6 +63,8 @@ def _load() -> ctypes.CDLL:
         "vocab_ce_bwd_workspace_bytes": (_sz, [_i64, _i64, _i64]),
         "vocab_ce_shard_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, ctypes.c_float, _i64, _i64, _i64,
                                               _i64, _vp, _vp, _vp, _sz, _vp]),
+        "ms_fingerprint_words": (_sz, [_sz, _sz]),
+        "ms_fingerprint": (ctypes.c_int, [_vp, _sz, _sz, _vp, _vp]),
         "ms_arm_kernel_events": (ctypes.c_int, [ctypes.c_int, _vp, _vp]),
         "ms_last_error": (ctypes.c_char_p, []),
         "ms_version": (ctypes.c_char_p, []),
@@ -250,3 +252,25 @@ def vocab_ce_shard_bwd(X, E_i, target, m, s, vocab_start: int, dloss: Optional[t
                                 v_i, int(vocab_start), _ptr(dX), _ptr(dE), _ptr(ws), nbytes, _stream(X.device))
     _check(st, "vocab_ce_shard_bwd")
     return dX, dE
+
+
+def fingerprint_words(nbytes: int, chunk_bytes: int) -> int:
+    return int(LIB.ms_fingerprint_words(nbytes, chunk_bytes))
+
+
+def fingerprint(t: torch.Tensor, chunk_bytes: int = 1 << 16) -> torch.Tensor:
+    """Device int64 tensor [1 + chunks]: XXH64 of the tensor's bytes as a whole
+    (element 0) and per chunk of ``chunk_bytes`` (elements 1 ..), computed by the
+    library on the current stream.  The tensor must be contiguous on a HIP device."""
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError("fingerprint needs a tensor on a HIP device")
+    if not t.is_contiguous():
+        raise ValueError("fingerprint needs a contiguous tensor")
+    nbytes = t.numel() * t.element_size()
+    words = fingerprint_words(nbytes, chunk_bytes)
+    if words == 0:
+        raise ValueError(f"chunk_bytes {chunk_bytes} must be a positive multiple of 8")
+    out = torch.empty(words, dtype=torch.int64, device=t.device)
+    ptr = t.data_ptr() if nbytes else out.data_ptr() + words * 8  # any aligned address: nothing is read
+    _check(LIB.ms_fingerprint(ptr, nbytes, chunk_bytes, out.data_ptr(), _stream(t.device)), "ms_fingerprint")
+    return out
