@@ -14,7 +14,7 @@
 // Work decomposition
 //   * One workgroup = 256 threads = 4 wave64s computes a 256 x 256 tile of C.
 //     The waves form a 2 x 2 grid, each owning a 128 x 128 sub-tile held as
-//     4 x 4 fp32 32x32 MFMA accumulators (256 accumulation registers per lane).
+//     8 x 8 fp32 16x16 MFMA accumulators (256 accumulation registers per lane).
 //   * K advances in steps of 32.  A ring of 4 LDS stages (32 KiB each: the A
 //     and B tiles of one step) holds step kt being consumed, kt+1 and kt+2
 //     resident or landing, and kt+3 being loaded; the loads of kt+3 are
@@ -23,14 +23,15 @@
 //     registers); the layouts (see below) make every fragment read
 //     conflict-free: K-major tiles are read with ds_read_b128, M/N-major tiles
 //     with the transposing ds_read_b64_tr_b16.
-//   * MFMA v_mfma_f32_32x32x16_bf16 (16 k per instruction; 2 k steps per LDS
-//     stage).  The fragments of k step s+1 are read from LDS while the 16
-//     MFMAs of step s run (two fragment register sets).
+//   * MFMA v_mfma_f32_16x16x32_bf16 (32 k per instruction: one per LDS
+//     stage and 16x16 block).  The fragments of k tile kt+1 are read from LDS
+//     while the 64 MFMAs of tile kt run (two fragment register sets).
 //   * The MFMA is issued with the B fragment as its first operand and the A
-//     fragment as its second, so each lane ends up holding, for every 32x32
-//     block, row l%32 and the four 4-column groups 8g + 4*(l/32) .. +3
-//     (g = 0..3): row-contiguous 16-byte (fp32) or 8-byte (bf16) output
-//     vectors, and per-row reductions need only lanes l and l^32.
+//     fragment as its second, so each lane ends up holding, for every 16x16
+//     block, row l%16 and the 4 columns 4*(l/16) .. +3: row-contiguous
+//     16-byte (fp32) or 8-byte (bf16) output vectors.  The four lanes
+//     l%16 + 16g share a row, so per-row reductions exchange over lanes l^16
+//     and l^32.
 //   * All global accesses use buffer instructions on per-tile resources:
 //     masked-off lanes get an offset beyond the resource, so edge tiles read
 //     zeros and drop their stores without branches.
