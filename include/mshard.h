@@ -142,6 +142,53 @@ ms_status ce_combine(const float* m, const float* s, const float* z, int32_t t, 
                      float* loss, float* loss_mean,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace attn_shard_bwd needs: dO, the per-row delta,
+ * dQKV and, when a token contraction is split, fp32 slices of the weight
+ * gradients.  attn_shard_fwd needs none.  Returns 0 for invalid sizes. */
+size_t attn_shard_workspace_bytes(int64_t b, int64_t s, int64_t h, int64_t n, int64_t d);
+
+/* Forward of one rank's self-attention shard (explainer, "attention"; paper
+ * notes, "self-attention block split": the Q, K, V projections are split by
+ * columns so each rank computes its own heads with no exchange, the output
+ * projection is split by rows so this rank's heads give a partial that g
+ * sums):
+ *     [Q | K | V] = X Wqkv_i,
+ *     O_i[:, head j] = softmax(Q_j K_j^T / sqrt(d) + mask) V_j   per sequence,
+ *     Z_i = O_i Wo_i.
+ * The per-head formula is the textbook scaled dot-product attention (the
+ * pages name heads only); mask: causal (a token sees itself and earlier
+ * tokens of its sequence) when `causal` is 1, none when 0.
+ * Sizes  : b sequences of s tokens (T = b*s rows, sequence-major), hidden h,
+ *          n heads of size d on this rank (d a multiple of 16, 16..128).
+ * Inputs : X[T x h]; Wqkv_i[h x 3nd] = [W_Q,i | W_K,i | W_V,i], head j at
+ *          columns j*d of each block; Wo_i[nd x h] (the matching rows of W_O);
+ *          all bf16.
+ * Outputs: QKV[T x 3nd] and O[T x nd] bf16, lse[n x T] fp32 (natural log of
+ *          each softmax row's normaliser), all saved for the backward;
+ *          Z_i[T x h] fp32 (this rank's partial). */
+ms_status attn_shard_fwd(const ms_bf16* X, const ms_bf16* Wqkv_i, const ms_bf16* Wo_i,
+                         int64_t b, int64_t s, int64_t h, int64_t n, int64_t d, int32_t causal,
+                         ms_bf16* QKV, ms_bf16* O, float* lse, float* Z_i,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward of attn_shard_fwd by the chain rule, dZ arriving unchanged through
+ * g's backward:
+ *     dO = dZ Wo_i^T,  dWo_i = O^T dZ;  per sequence and head, with P the
+ *     softmax and delta = rowsum(dO * O):  dV = P^T dO,
+ *     dS = P * (dO V^T - delta),  dQ = dS K / sqrt(d),  dK = dS^T Q / sqrt(d);
+ *     dWqkv_i = X^T [dQ | dK | dV],  dX_i = [dQ | dK | dV] Wqkv_i^T.
+ * The attention core recomputes P from QKV and lse; dO and dQKV are rounded
+ * to bf16 in the workspace.  Two kernels (one over key blocks for dK and dV,
+ * one over query blocks for dQ) keep every sum in a fixed order.
+ * Inputs : X, Wqkv_i, Wo_i, dZ[T x h] bf16; QKV, O, lse from the forward.
+ * Outputs: dX_i[T x h] fp32 (this rank's partial; f sums it); dWqkv_i[h x 3nd],
+ *          dWo_i[nd x h] bf16. */
+ms_status attn_shard_bwd(const ms_bf16* X, const ms_bf16* Wqkv_i, const ms_bf16* Wo_i,
+                         const ms_bf16* QKV, const ms_bf16* O, const float* lse, const ms_bf16* dZ,
+                         int64_t b, int64_t s, int64_t h, int64_t n, int64_t d, int32_t causal,
+                         float* dX_i, ms_bf16* dWqkv_i, ms_bf16* dWo_i,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace vocab_ce_shard_bwd needs: the per-token records,
  * the bf16 logit gradient [T x v_i] and, when the token contraction of dE_i
  * is split, its fp32 slices.  Returns 0 for invalid sizes. */
@@ -173,8 +220,9 @@ ms_status vocab_ce_shard_bwd(const ms_bf16* X, const ms_bf16* E_i, const int64_t
                              float* dX_i, ms_bf16* dE_i,
                              void* workspace, size_t workspace_bytes, void* stream);
 
-/* Kernels that ms_arm_kernel_events can bracket (one GEMM launch each; the
- * split-K reductions and CE tile-combine kernels are not included). */
+/* Kernels that ms_arm_kernel_events can bracket (one GEMM launch each, or the
+ * attention core's launches as one; the split-K reductions and CE
+ * tile-combine kernels are not included). */
 typedef enum {
   MS_K_CE_GEMM = 0, /* vocab_ce_shard_fwd: X E_i with the fused CE epilogue     */
   MS_K_FWD_H = 1,   /* mlp_shard_fwd:  X A_i (+ b1) with the GeLU epilogue      */
@@ -186,7 +234,15 @@ typedef enum {
   MS_K_CE_BWD_L = 7,  /* vocab_ce_shard_bwd: X E_i recomputed -> dL             */
   MS_K_CE_BWD_DX = 8, /* vocab_ce_shard_bwd: dL E_i^T -> dX_i                   */
   MS_K_CE_BWD_DE = 9, /* vocab_ce_shard_bwd: X^T dL -> dE_i                     */
-  MS_K_COUNT = 10
+  MS_K_ATTN_QKV = 10,       /* attn_shard_fwd: X Wqkv_i -> QKV                    */
+  MS_K_ATTN_CORE_FWD = 11,  /* attn_shard_fwd: the attention core                 */
+  MS_K_ATTN_OUT = 12,       /* attn_shard_fwd: O Wo_i -> Z_i                      */
+  MS_K_ATTN_BWD_DO = 13,    /* attn_shard_bwd: dZ Wo_i^T -> dO                    */
+  MS_K_ATTN_BWD_DWO = 14,   /* attn_shard_bwd: O^T dZ -> dWo_i                    */
+  MS_K_ATTN_CORE_BWD = 15,  /* attn_shard_bwd: delta and the core's dQ, dK, dV    */
+  MS_K_ATTN_BWD_DWQKV = 16, /* attn_shard_bwd: X^T dQKV -> dWqkv_i                */
+  MS_K_ATTN_BWD_DX = 17,    /* attn_shard_bwd: dQKV Wqkv_i^T -> dX_i              */
+  MS_K_COUNT = 18
 } ms_kernel;
 
 /* Measurement hook, no effect on results.  Arms two caller-created HIP events

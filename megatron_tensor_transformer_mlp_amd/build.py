@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libmshard.so")
-SOURCES = ["kernels.hip", "fingerprint.hip", "abi.cpp"]
+SOURCES = ["kernels.hip", "attention.hip", "fingerprint.hip", "abi.cpp"]
 HEADERS = ["gemm_core.hpp", "epilogues.hpp", "launch.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -136,6 +136,20 @@ ms_status launched(hipError_t e, const char* what) {
     if (_st != MS_OK) return _st;   \
   } while (0)
 
+// Attention shard sizes: b, s >= 1 (b*s tokens, grid limits on b and n), h as
+// the other entry points, n >= 1 heads of size d (a multiple of 16, 16..128).
+ms_status check_attn(int64_t b, int64_t s, int64_t h, int64_t n, int64_t d, int32_t causal) {
+  if (b < 1 || s < 1 || n < 1) return fail(MS_ERR_SHAPE, "b, s and n must be >= 1 (got %lld, %lld, %lld)",
+                                           (long long)b, (long long)s, (long long)n);
+  if (b > 65535 || n > 65535) return fail(MS_ERR_SHAPE, "b and n must be <= 65535");
+  if (s > INT32_MAX / b) return fail(MS_ERR_SHAPE, "b*s too large");
+  if (d < 16 || d > 128 || d % 16 != 0)
+    return fail(MS_ERR_SHAPE, "d must be a multiple of 16 in [16, 128] (got %lld)", (long long)d);
+  if (causal != 0 && causal != 1) return fail(MS_ERR_ENUM, "causal must be 0 or 1 (got %d)", (int)causal);
+  MS_TRY(check_dims(b * s, {{"h", h}, {"3nd", 3 * n * d}}));
+  return MS_OK;
+}
+
 }  // namespace
 
 namespace mshard {
@@ -214,6 +228,51 @@ ms_status vocab_ce_shard_fwd(const ms_bf16* X, const ms_bf16* E_i, const int64_t
   return launched(mshard::launch_vocab_ce(X, E_i, target, T, h, v_i, vocab_start, m_i, s_i, z_i, workspace,
                                           (hipStream_t)stream),
                   "vocab_ce_shard_fwd");
+}
+
+size_t attn_shard_workspace_bytes(int64_t b, int64_t s, int64_t h, int64_t n, int64_t d) {
+  if (check_attn(b, s, h, n, d, 0) != MS_OK) return 0;
+  return mshard::attn_workspace_layout(b, s, h, n, d).bytes;
+}
+
+ms_status attn_shard_fwd(const ms_bf16* X, const ms_bf16* Wqkv_i, const ms_bf16* Wo_i, int64_t b, int64_t s,
+                         int64_t h, int64_t n, int64_t d, int32_t causal, ms_bf16* QKV, ms_bf16* O, float* lse,
+                         float* Z_i, void* workspace, size_t workspace_bytes, void* stream) {
+  const DisarmOnReturn disarm{mshard::kTkAttnQkv, mshard::kTkAttnOut};
+  (void)workspace;
+  (void)workspace_bytes;  // the forward needs no workspace
+  MS_TRY(check_attn(b, s, h, n, d, causal));
+  const int64_t T = b * s, nd = n * d;
+  std::vector<Buf> bufs = {{X, nbytes(T, h, 2), "X", false},          {Wqkv_i, nbytes(h, 3 * nd, 2), "Wqkv_i", false},
+                           {Wo_i, nbytes(nd, h, 2), "Wo_i", false},   {QKV, nbytes(T, 3 * nd, 2), "QKV", true},
+                           {O, nbytes(T, nd, 2), "O", true},          {lse, nbytes(n, T, 4), "lse", true},
+                           {Z_i, nbytes(T, h, 4), "Z_i", true}};
+  MS_TRY(check_bufs(bufs));
+  MS_TRY(check_device());
+  return launched(mshard::launch_attn_fwd(X, Wqkv_i, Wo_i, b, s, h, n, d, causal == 1, QKV, O, lse, Z_i,
+                                          (hipStream_t)stream),
+                  "attn_shard_fwd");
+}
+
+ms_status attn_shard_bwd(const ms_bf16* X, const ms_bf16* Wqkv_i, const ms_bf16* Wo_i, const ms_bf16* QKV,
+                         const ms_bf16* O, const float* lse, const ms_bf16* dZ, int64_t b, int64_t s, int64_t h,
+                         int64_t n, int64_t d, int32_t causal, float* dX_i, ms_bf16* dWqkv_i, ms_bf16* dWo_i,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  const DisarmOnReturn disarm{mshard::kTkAttnBwdDO, mshard::kTkAttnBwdDX};
+  MS_TRY(check_attn(b, s, h, n, d, causal));
+  const int64_t T = b * s, nd = n * d;
+  std::vector<Buf> bufs = {{X, nbytes(T, h, 2), "X", false},          {Wqkv_i, nbytes(h, 3 * nd, 2), "Wqkv_i", false},
+                           {Wo_i, nbytes(nd, h, 2), "Wo_i", false},   {QKV, nbytes(T, 3 * nd, 2), "QKV", false},
+                           {O, nbytes(T, nd, 2), "O", false},         {lse, nbytes(n, T, 4), "lse", false},
+                           {dZ, nbytes(T, h, 2), "dZ", false},        {dX_i, nbytes(T, h, 4), "dX_i", true},
+                           {dWqkv_i, nbytes(h, 3 * nd, 2), "dWqkv_i", true},
+                           {dWo_i, nbytes(nd, h, 2), "dWo_i", true}};
+  MS_TRY(check_workspace(workspace, workspace_bytes, mshard::attn_workspace_layout(b, s, h, n, d).bytes, bufs));
+  MS_TRY(check_bufs(bufs));
+  MS_TRY(check_device());
+  return launched(mshard::launch_attn_bwd(X, Wqkv_i, Wo_i, QKV, O, lse, dZ, b, s, h, n, d, causal == 1, dX_i,
+                                          dWqkv_i, dWo_i, workspace, (hipStream_t)stream),
+                  "attn_shard_bwd");
 }
 
 size_t vocab_ce_bwd_workspace_bytes(int64_t T, int64_t h, int64_t v_i) {

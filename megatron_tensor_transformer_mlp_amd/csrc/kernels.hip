@@ -8,6 +8,7 @@
 #include "launch.hpp"
 
 #include <array>
+#include <cmath>
 #include <functional>
 #include <map>
 #include <mutex>
@@ -331,6 +332,36 @@ CeBwdWorkspace ce_bwd_workspace_layout(int64_t T, int64_t h, int64_t v) {
   return w;
 }
 
+AttnWorkspace attn_workspace_layout(int64_t b, int64_t s, int64_t h, int64_t n, int64_t d) {
+  static std::mutex mu;
+  static std::map<std::array<int64_t, 5>, AttnWorkspace> cache;
+  const std::array<int64_t, 5> key{b, s, h, n, d};
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+  }
+  auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const int64_t T = b * s, nd = n * d;
+  AttnWorkspace w;
+  w.off_dO = 0;
+  w.off_delta = align((size_t)T * nd * 2);
+  w.off_dqkv = w.off_delta + align((size_t)n * T * 4);
+  w.off_splitk = w.off_dqkv + align((size_t)T * 3 * nd * 2);
+  const size_t slice = (size_t)h * 3 * nd * 4;  // the larger of the two weight gradients
+  int max_splits = 1;
+  while (max_splits < 8 && w.off_splitk + align(slice * 2 * max_splits) < ((size_t)1 << 31)) max_splits *= 2;
+  const BlockList dO{tile_count(T, nd), block_cost(h, 1, kEpiBF16)};
+  const BlockList dx{tile_count(T, h), block_cost(3 * nd, 1, kEpiF32)};
+  plan_pair(nd, h, T, dO, w.splits_wo, w.pair_o, w.o_first, max_splits);
+  plan_pair(h, 3 * nd, T, dx, w.splits_wqkv, w.pair_x, w.x_first, max_splits);
+  const int S = w.splits_wo > w.splits_wqkv ? w.splits_wo : w.splits_wqkv;
+  w.bytes = w.off_splitk + (S > 1 ? align(slice * S) : 0);
+  std::lock_guard<std::mutex> lock(mu);
+  cache.emplace(key, w);
+  return w;
+}
+
 // ---------------------------------------------------------------------------
 // Entry-point launch sequences (arguments already validated by the ABI layer)
 
@@ -514,6 +545,90 @@ hipError_t launch_vocab_ce_bwd(const uint16_t* X, const uint16_t* E, const int64
   }
   if (err != hipSuccess) return err;
   if (we.S > 1) err = launch_splitk_reduce(splitk, h, v, we.S, dE, st);
+  return err;
+}
+
+// Self-attention shard ([EXPL] "attention"; [NOTES] "self-attention block
+// split"): QKV = X Wqkv_i (column shard, this rank's heads), the attention
+// core per head, Z_i = O_i W_O,i (row shard: this rank's fp32 partial).
+static AttnGeom attn_geom(int64_t b, int64_t s, int64_t n, int64_t d) {
+  AttnGeom g;
+  g.b = (int)b;
+  g.s = (int)s;
+  g.n = (int)n;
+  g.d = (int)d;
+  g.ld_qkv = (int)(3 * n * d);
+  g.ld_o = (int)(n * d);
+  g.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
+  return g;
+}
+
+hipError_t launch_attn_fwd(const uint16_t* X, const uint16_t* Wqkv, const uint16_t* Wo, int64_t b, int64_t s,
+                           int64_t h, int64_t n, int64_t d, bool causal, uint16_t* QKV, uint16_t* O, float* lse,
+                           float* Z, hipStream_t st) {
+  const int64_t T = b * s, nd = n * d;
+  hipError_t err;
+  {  // QKV = X Wqkv:  NN, M = T, N = 3nd, K = h
+    const GemmGeom g = make_geom(T, 3 * nd, h, 1);
+    const Operand a{X, h, T * h}, bo{Wqkv, 3 * nd, h * 3 * nd};
+    const EpiStoreBF16 e{QKV, 3 * nd, (int)T, (int)(3 * nd)};
+    if ((err = launch_gemm<true, false>(kTkAttnQkv, g, a, bo, e, st)) != hipSuccess) return err;
+  }
+  record_armed_event(kTkAttnCoreFwd, false, st);
+  err = launch_attn_core_fwd(attn_geom(b, s, n, d), causal, QKV, O, lse, st);
+  record_armed_event(kTkAttnCoreFwd, true, st);
+  if (err != hipSuccess) return err;
+  // Z = O Wo:  NN, M = T, N = h, K = nd
+  const GemmGeom g = make_geom(T, h, nd, 1);
+  const Operand a{O, nd, T * nd}, bo{Wo, h, nd * h};
+  const EpiStoreF32 e{Z, h, (int)T, (int)h, 0};
+  return launch_gemm<true, false>(kTkAttnOut, g, a, bo, e, st);
+}
+
+hipError_t launch_attn_bwd(const uint16_t* X, const uint16_t* Wqkv, const uint16_t* Wo, const uint16_t* QKV,
+                           const uint16_t* O, const float* lse, const uint16_t* dZ, int64_t b, int64_t s, int64_t h,
+                           int64_t n, int64_t d, bool causal, float* dX, uint16_t* dWqkv, uint16_t* dWo, void* ws,
+                           hipStream_t st) {
+  const int64_t T = b * s, nd = n * d;
+  const AttnWorkspace w = attn_workspace_layout(b, s, h, n, d);
+  uint16_t* dO = (uint16_t*)((char*)ws + w.off_dO);
+  float* delta = (float*)((char*)ws + w.off_delta);
+  uint16_t* dqkv = (uint16_t*)((char*)ws + w.off_dqkv);
+  float* splitk = (float*)((char*)ws + w.off_splitk);
+  hipError_t err;
+  // dO = dZ Wo^T:  NT, M = T, N = nd, K = h; Wo stored [nd x h] = [N x K]
+  const GemmGeom go = make_geom(T, nd, h, 1);
+  const Operand ao{dZ, h, T * h}, bo{Wo, h, nd * h};
+  const EpiStoreBF16 eo{dO, nd, (int)T, (int)nd};
+  // dW_O = O^T dZ:  [nd x h], contraction over tokens (independent of dO)
+  const WeightGrad wo = weight_grad_setup(O, nd, dZ, h, T, nd, h, w.splits_wo, dWo, splitk);
+  if (w.pair_o) {
+    err = launch_gemm_pair<false, false, true, true>(kTkAttnBwdDWo, wo.g, wo.a, wo.b, wo.e, kTkAttnBwdDO, go, ao, bo,
+                                                     eo, w.o_first, st);
+  } else {
+    err = launch_gemm<true, true>(kTkAttnBwdDO, go, ao, bo, eo, st);
+    if (err == hipSuccess) err = launch_gemm<false, false>(kTkAttnBwdDWo, wo.g, wo.a, wo.b, wo.e, st);
+  }
+  if (err != hipSuccess) return err;
+  if (wo.S > 1 && (err = launch_splitk_reduce(splitk, nd, h, wo.S, dWo, st)) != hipSuccess) return err;
+  record_armed_event(kTkAttnCoreBwd, false, st);
+  err = launch_attn_core_bwd(attn_geom(b, s, n, d), causal, QKV, O, dO, lse, delta, dqkv, st);
+  record_armed_event(kTkAttnCoreBwd, true, st);
+  if (err != hipSuccess) return err;
+  // dWqkv = X^T dQKV:  [h x 3nd];  dX = dQKV Wqkv^T:  NT, M = T, N = h, K = 3nd; Wqkv stored [h x 3nd] = [N x K]
+  const WeightGrad wq = weight_grad_setup(X, h, dqkv, 3 * nd, T, h, 3 * nd, w.splits_wqkv, dWqkv, splitk);
+  const GemmGeom gx = make_geom(T, h, 3 * nd, 1);
+  const Operand ax{dqkv, 3 * nd, T * 3 * nd}, bx{Wqkv, 3 * nd, h * 3 * nd};
+  const EpiStoreF32 ex{dX, h, (int)T, (int)h, 0};
+  if (w.pair_x) {
+    err = launch_gemm_pair<false, false, true, true>(kTkAttnBwdDWqkv, wq.g, wq.a, wq.b, wq.e, kTkAttnBwdDX, gx, ax, bx,
+                                                     ex, w.x_first, st);
+  } else {
+    err = launch_gemm<true, true>(kTkAttnBwdDX, gx, ax, bx, ex, st);
+    if (err == hipSuccess) err = launch_gemm<false, false>(kTkAttnBwdDWqkv, wq.g, wq.a, wq.b, wq.e, st);
+  }
+  if (err != hipSuccess) return err;
+  if (wq.S > 1) err = launch_splitk_reduce(splitk, h, 3 * nd, wq.S, dWqkv, st);
   return err;
 }
 

@@ -42,10 +42,33 @@ struct CeBwdWorkspace {
   bool dx_first;      // in the paired launch, dX's blocks lead
 };
 
+// One rank's attention core: b sequences of s tokens, n heads of size d.
+struct AttnGeom {
+  int b, s, n, d;
+  int ld_qkv;        // 3 n d: row stride of QKV
+  int ld_o;          // n d: row stride of O (and dO)
+  float scale_log2;  // log2(e) / sqrt(d)
+};
+
+// Attention shard backward workspace: dO, delta, dQKV and the split-K slices
+// of the two weight gradients; each weight gradient is planned with its
+// independent partner GEMM (dW_O with dO, dWqkv with dX).
+struct AttnWorkspace {
+  size_t off_dO;      // bf16 [T x nd]
+  size_t off_delta;   // fp32 [n x T]
+  size_t off_dqkv;    // bf16 [T x 3nd]
+  size_t off_splitk;  // fp32 slices
+  size_t bytes;
+  int splits_wo, splits_wqkv;
+  bool pair_o, o_first;   // dW_O with dO in one launch; dO's blocks lead
+  bool pair_x, x_first;   // dWqkv with dX in one launch; dX's blocks lead
+};
+
 // Kernel ids for the measurement hook (same values as ms_kernel in mshard.h).
 enum TimedKernel {
   kTkCeGemm = 0, kTkFwdH, kTkFwdZ, kTkBwdDH, kTkBwdDB, kTkBwdDA, kTkBwdDX, kTkCeBwdL, kTkCeBwdDX, kTkCeBwdDE,
-  kTkCount
+  kTkAttnQkv, kTkAttnCoreFwd, kTkAttnOut, kTkAttnBwdDO, kTkAttnBwdDWo, kTkAttnCoreBwd, kTkAttnBwdDWqkv,
+  kTkAttnBwdDX, kTkCount
 };
 
 // Records the armed event (if any) of kernel `id` on `st`; `after` picks which
@@ -56,6 +79,7 @@ BwdPlan plan_backward(int64_t T, int64_t h, int64_t f);
 MlpWorkspace mlp_workspace_layout(int64_t T, int64_t h, int64_t f);
 CeWorkspace ce_workspace_layout(int64_t T, int64_t v);
 CeBwdWorkspace ce_bwd_workspace_layout(int64_t T, int64_t h, int64_t v);
+AttnWorkspace attn_workspace_layout(int64_t b, int64_t s, int64_t h, int64_t n, int64_t d);
 
 hipError_t launch_mlp_fwd(const uint16_t* X, const uint16_t* A, const uint16_t* b1, const uint16_t* B,
                           int64_t T, int64_t h, int64_t f, int gelu, uint16_t* H, uint16_t* Y, float* Z,
@@ -69,6 +93,19 @@ hipError_t launch_vocab_ce(const uint16_t* X, const uint16_t* E, const int64_t* 
 hipError_t launch_vocab_ce_bwd(const uint16_t* X, const uint16_t* E, const int64_t* target, const float* m,
                                const float* s, int t, const float* dloss, float scale, int64_t T, int64_t h,
                                int64_t v, int64_t vocab_start, float* dX, uint16_t* dE, void* ws, hipStream_t st);
+int attn_padded_dim(int d);
+hipError_t launch_attn_core_fwd(const AttnGeom& g, bool causal, const uint16_t* qkv, uint16_t* out, float* lse,
+                                hipStream_t st);
+hipError_t launch_attn_core_bwd(const AttnGeom& g, bool causal, const uint16_t* qkv, const uint16_t* out,
+                                const uint16_t* dout, const float* lse, float* delta, uint16_t* dqkv,
+                                hipStream_t st);
+hipError_t launch_attn_fwd(const uint16_t* X, const uint16_t* Wqkv, const uint16_t* Wo, int64_t b, int64_t s,
+                           int64_t h, int64_t n, int64_t d, bool causal, uint16_t* QKV, uint16_t* O, float* lse,
+                           float* Z, hipStream_t st);
+hipError_t launch_attn_bwd(const uint16_t* X, const uint16_t* Wqkv, const uint16_t* Wo, const uint16_t* QKV,
+                           const uint16_t* O, const float* lse, const uint16_t* dZ, int64_t b, int64_t s, int64_t h,
+                           int64_t n, int64_t d, bool causal, float* dX, uint16_t* dWqkv, uint16_t* dWo, void* ws,
+                           hipStream_t st);
 uint64_t fingerprint_chunk_count(uint64_t bytes, uint64_t chunk);
 hipError_t launch_fingerprint(const void* buf, uint64_t bytes, uint64_t chunk, uint64_t* out, hipStream_t st);
 hipError_t launch_ce_combine(const float* m, const float* s, const float* z, int t, int64_t T, float* loss,

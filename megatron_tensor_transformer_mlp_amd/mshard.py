@@ -7,7 +7,8 @@ import fails loudly; there is no fallback.
 
 Entry points mirror the C ABI in include/mshard.h:
   mlp_shard_fwd, mlp_shard_bwd, vocab_ce_shard_fwd, ce_combine,
-  vocab_ce_shard_bwd, plus the workspace-size queries.
+  vocab_ce_shard_bwd, attn_shard_fwd, attn_shard_bwd, fingerprint, plus the
+  workspace-size queries.
 """
 from __future__ import annotations
 
@@ -27,12 +28,14 @@ GELU = {"erf": 0, "tanh": 1}
 
 EXPORTED = ("mlp_shard_workspace_bytes", "mlp_shard_fwd", "mlp_shard_bwd", "vocab_ce_workspace_bytes",
             "vocab_ce_shard_fwd", "ce_combine_workspace_bytes", "ce_combine", "vocab_ce_bwd_workspace_bytes",
-            "vocab_ce_shard_bwd", "ms_fingerprint_words", "ms_fingerprint", "ms_arm_kernel_events",
+            "vocab_ce_shard_bwd", "attn_shard_workspace_bytes", "attn_shard_fwd", "attn_shard_bwd",
+            "ms_fingerprint_words", "ms_fingerprint", "ms_arm_kernel_events",
             "ms_last_error", "ms_version")
 
 # ms_kernel ids: the single GEMM launches ms_arm_kernel_events can bracket
 KERNELS = {"ce_gemm": 0, "fwd_h": 1, "fwd_z": 2, "bwd_dh": 3, "bwd_db": 4, "bwd_da": 5, "bwd_dx": 6,
-           "ce_bwd_l": 7, "ce_bwd_dx": 8, "ce_bwd_de": 9}
+           "ce_bwd_l": 7, "ce_bwd_dx": 8, "ce_bwd_de": 9, "attn_qkv": 10, "attn_core_fwd": 11, "attn_out": 12,
+           "attn_bwd_do": 13, "attn_bwd_dwo": 14, "attn_core_bwd": 15, "attn_bwd_dwqkv": 16, "attn_bwd_dx": 17}
 
 
 class MshardError(RuntimeError):
@@ -63,6 +66,11 @@ def _load() -> ctypes.CDLL:
         "vocab_ce_bwd_workspace_bytes": (_sz, [_i64, _i64, _i64]),
         "vocab_ce_shard_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, ctypes.c_float, _i64, _i64, _i64,
                                               _i64, _vp, _vp, _vp, _sz, _vp]),
+        "attn_shard_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64]),
+        "attn_shard_fwd": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp,
+                                          _sz, _vp]),
+        "attn_shard_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i32, _vp,
+                                          _vp, _vp, _vp, _sz, _vp]),
         "ms_fingerprint_words": (_sz, [_sz, _sz]),
         "ms_fingerprint": (ctypes.c_int, [_vp, _sz, _sz, _vp, _vp]),
         "ms_arm_kernel_events": (ctypes.c_int, [ctypes.c_int, _vp, _vp]),
@@ -274,3 +282,54 @@ def fingerprint(t: torch.Tensor, chunk_bytes: int = 1 << 16) -> torch.Tensor:
     ptr = t.data_ptr() if nbytes else out.data_ptr() + words * 8  # any aligned address: nothing is read
     _check(LIB.ms_fingerprint(ptr, nbytes, chunk_bytes, out.data_ptr(), _stream(t.device)), "ms_fingerprint")
     return out
+
+
+def attn_shard_workspace_bytes(b: int, s: int, h: int, n: int, d: int) -> int:
+    return int(LIB.attn_shard_workspace_bytes(b, s, h, n, d))
+
+
+def attn_shard_fwd(X, Wqkv_i, Wo_i, b: int, s: int, n: int, d: int, causal: bool = True, out=None):
+    """(QKV bf16 [T, 3nd], O bf16 [T, nd], lse fp32 [n, T], Z_i fp32 [T, h]) = forward of one
+    rank's self-attention shard over b sequences of s tokens (T = b*s), n heads of size d."""
+    T, h = X.shape
+    nd = n * d
+    if T != b * s:
+        raise ValueError(f"X has {T} rows, expected b*s = {b * s}")
+    bf = torch.bfloat16
+    _dev(X, "X", bf, (T, h)); _dev(Wqkv_i, "Wqkv_i", bf, (h, 3 * nd)); _dev(Wo_i, "Wo_i", bf, (nd, h))
+    if out is None:
+        QKV = torch.empty((T, 3 * nd), dtype=bf, device=X.device)
+        O = torch.empty((T, nd), dtype=bf, device=X.device)
+        lse = torch.empty((n, T), dtype=torch.float32, device=X.device)
+        Z = torch.empty((T, h), dtype=torch.float32, device=X.device)
+    else:
+        QKV, O, lse, Z = out
+    st = LIB.attn_shard_fwd(_ptr(X), _ptr(Wqkv_i), _ptr(Wo_i), b, s, h, n, d, int(bool(causal)), _ptr(QKV), _ptr(O),
+                            _ptr(lse), _ptr(Z), None, 0, _stream(X.device))
+    _check(st, "attn_shard_fwd")
+    return QKV, O, lse, Z
+
+
+def attn_shard_bwd(X, Wqkv_i, Wo_i, QKV, O, lse, dZ, b: int, s: int, n: int, d: int, causal: bool = True,
+                   workspace: Optional[torch.Tensor] = None, out=None):
+    """(dX_i fp32 [T, h], dWqkv_i bf16 [h, 3nd], dWo_i bf16 [nd, h]) = backward of attn_shard_fwd."""
+    T, h = X.shape
+    nd = n * d
+    bf = torch.bfloat16
+    for t, nm, shp, dt in ((X, "X", (T, h), bf), (Wqkv_i, "Wqkv_i", (h, 3 * nd), bf), (Wo_i, "Wo_i", (nd, h), bf),
+                           (QKV, "QKV", (T, 3 * nd), bf), (O, "O", (T, nd), bf), (lse, "lse", (n, T), torch.float32),
+                           (dZ, "dZ", (T, h), bf)):
+        _dev(t, nm, dt, shp)
+    if out is None:
+        dX = torch.empty((T, h), dtype=torch.float32, device=X.device)
+        dWqkv = torch.empty((h, 3 * nd), dtype=bf, device=X.device)
+        dWo = torch.empty((nd, h), dtype=bf, device=X.device)
+    else:
+        dX, dWqkv, dWo = out
+    nbytes = attn_shard_workspace_bytes(b, s, h, n, d)
+    ws = _workspace(nbytes, X.device, workspace)
+    st = LIB.attn_shard_bwd(_ptr(X), _ptr(Wqkv_i), _ptr(Wo_i), _ptr(QKV), _ptr(O), _ptr(lse), _ptr(dZ), b, s, h, n,
+                            d, int(bool(causal)), _ptr(dX), _ptr(dWqkv), _ptr(dWo), _ptr(ws), nbytes,
+                            _stream(X.device))
+    _check(st, "attn_shard_bwd")
+    return dX, dWqkv, dWo

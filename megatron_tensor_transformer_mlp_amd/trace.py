@@ -24,7 +24,8 @@ import torch
 
 from . import mshard as _mshard
 
-TRACED = ("mlp_shard_fwd", "mlp_shard_bwd", "vocab_ce_shard_fwd", "vocab_ce_shard_bwd", "ce_combine")
+TRACED = ("mlp_shard_fwd", "mlp_shard_bwd", "vocab_ce_shard_fwd", "vocab_ce_shard_bwd", "ce_combine",
+          "attn_shard_fwd", "attn_shard_bwd")
 
 
 def _outputs(result) -> List[Optional[torch.Tensor]]:

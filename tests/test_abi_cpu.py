@@ -147,6 +147,46 @@ def test_ce_bwd_validation(ms):
     assert "2^31" in ms.LIB.ms_last_error().decode()
 
 
+def test_attn_workspace_sizes(ms):
+    b, s, h, n, d = 8, 1024, 1600, 25, 64
+    T, nd = b * s, n * d
+    need = ms.attn_shard_workspace_bytes(b, s, h, n, d)
+    assert need >= T * nd * 2 + n * T * 4 + T * 3 * nd * 2      # dO, delta, dQKV
+    assert need < 1 << 31
+    assert ms.attn_shard_workspace_bytes(b, s, h, n, 24) == 0     # d not a multiple of 16
+    assert ms.attn_shard_workspace_bytes(b, s, h, n, 144) == 0    # d above 128
+    assert ms.attn_shard_workspace_bytes(0, s, h, n, d) == 0
+    assert ms.attn_shard_workspace_bytes(b, s, 1604, n, d) == 0   # h not a multiple of 8
+    assert ms.attn_shard_workspace_bytes(1, 2048, 14336, 28, 128) < 1 << 31
+
+
+def test_attn_validation(ms):
+    b, s, h, n, d = 2, 32, 64, 4, 16
+    T, nd = b * s, n * d
+    p = [FAKE + (i << 30) for i in range(12)]
+
+    def fwd(X=p[0], b_=b, s_=s, n_=n, d_=d, causal=1, O=p[4], lse=p[5]):
+        return ms.LIB.attn_shard_fwd(X, p[1], p[2], b_, s_, h, n_, d_, causal, p[3], O, lse, p[6], None, 0, None)
+
+    assert fwd(X=None) == ms.MS_ERR_NULL
+    assert fwd(d_=24) == ms.MS_ERR_SHAPE
+    assert fwd(d_=0) == ms.MS_ERR_SHAPE
+    assert fwd(n_=0) == ms.MS_ERR_SHAPE
+    assert fwd(b_=70000) == ms.MS_ERR_SHAPE
+    assert fwd(causal=2) == ms.MS_ERR_ENUM
+    assert fwd(O=p[3] + 64) == ms.MS_ERR_ALIAS        # O on top of QKV
+    assert fwd(lse=p[5] + 4) == ms.MS_ERR_ALIGN
+    need = ms.attn_shard_workspace_bytes(b, s, h, n, d)
+
+    def bwd(ws=p[10], nbytes=need, dX=p[7]):
+        return ms.LIB.attn_shard_bwd(p[0], p[1], p[2], p[3], p[4], p[5], p[6], b, s, h, n, d, 1, dX, p[8], p[9],
+                                     ws, nbytes, None)
+
+    assert bwd(ws=None) == ms.MS_ERR_WORKSPACE
+    assert bwd(nbytes=need - 1) == ms.MS_ERR_WORKSPACE
+    assert bwd(dX=p[6] + 16) == ms.MS_ERR_ALIAS       # dX_i on top of dZ
+
+
 def test_combine_validation(ms):
     p = [FAKE + (i << 30) for i in range(5)]
     assert ms.LIB.ce_combine(p[0], p[1], p[2], 0, 16, p[3], p[4], None, 0, None) == ms.MS_ERR_SHAPE
@@ -176,11 +216,11 @@ def test_binding_has_no_fallback():
 
 def test_arm_kernel_events_validation(ms):
     fake_ev = FAKE  # never recorded: the arming is cleared again below without a launch
-    assert ms.LIB.ms_arm_kernel_events(10, None, None) == ms.MS_ERR_ENUM
+    assert ms.LIB.ms_arm_kernel_events(18, None, None) == ms.MS_ERR_ENUM
     assert ms.LIB.ms_arm_kernel_events(-1, None, None) == ms.MS_ERR_ENUM
     assert ms.LIB.ms_arm_kernel_events(0, fake_ev, None) == ms.MS_ERR_NULL
     assert "both events" in ms.LIB.ms_last_error().decode()
     assert ms.LIB.ms_arm_kernel_events(0, None, None) == ms.MS_OK
-    for k in range(10):
+    for k in range(18):
         assert ms.LIB.ms_arm_kernel_events(k, None, None) == ms.MS_OK
-    assert set(ms.KERNELS.values()) == set(range(10))
+    assert set(ms.KERNELS.values()) == set(range(18))
