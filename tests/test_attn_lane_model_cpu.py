@@ -1,0 +1,328 @@
+"""Lane-exact model of the attention kernels' index arithmetic (CPU only).
+
+The attention core kernels (attention.hip) rest on three facts about gfx950:
+  * v_mfma_f32_16x16x32_bf16: lane l supplies row l%16, k = 8(l/16) .. +7 of
+    its first operand and column l%16 of its second, and receives
+    D[4(l/16) + r][l%16], r = 0..3;
+  * ds_read_b64_tr_b16: within each group of 16 lanes, result lane i takes
+    element i%4 of the 8 bytes that source lane i/4 + 4e addressed (the
+    mapping measured with a probe on the GPU);
+  * bf16 operands, fp32 accumulation.
+This test re-enacts, lane by lane, the forward kernel and the two backward
+kernels (dK/dV over key blocks, dQ over query blocks) with those semantics:
+the same fragment addresses, padded LDS pitch, key permutation of P and dS,
+masks and online softmax.  With exact arithmetic the model must reproduce
+the oracle's attention and torch's attention gradients to rounding, for
+every head size the kernels are built for, causal and not, with ragged
+sequence lengths.  It checks the design of the kernels' indexing; it does
+not run the HIP code.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from megatron_tensor_transformer_mlp_amd import inputs
+from oracle import attn
+
+BM, BN = 128, 64
+
+
+def mfma(src0, src1, acc):
+    """src0, src1: [64][8]; acc [64][4].  D = A0 @ B1 with lane l holding A0[l%16][8g+e], B1[8g+e][l%16];
+    lane l gets D[4g + r][l%16]."""
+    A0 = np.zeros((16, 32)); B1 = np.zeros((32, 16))
+    for l in range(64):
+        g, i = l // 16, l % 16
+        A0[i, 8 * g:8 * g + 8] = src0[l]
+        B1[8 * g:8 * g + 8, i] = src1[l]
+    D = A0 @ B1
+    out = acc.copy()
+    for l in range(64):
+        g = l // 16
+        for r in range(4):
+            out[l, r] += D[4 * g + r, l % 16]
+    return out
+
+
+class Lds:
+    def __init__(self, nbytes):
+        self.b = np.zeros(nbytes // 2)  # bf16 elements as float
+    def write16(self, addr, vals8):
+        assert addr % 16 == 0
+        self.b[addr // 2:addr // 2 + 8] = vals8
+    def read_b128(self, addr):
+        assert addr % 16 == 0
+        return self.b[addr // 2:addr // 2 + 8].copy()
+    def read_tr(self, addrs):
+        """ds_read_b64_tr_b16: result lane i (group G) elem e = src[16G + i//4 + 4e][i%4]."""
+        src = [self.b[a // 2:a // 2 + 4] for a in addrs]
+        for a in addrs:
+            assert a % 8 == 0
+        out = np.zeros((64, 4))
+        for l in range(64):
+            G, i = l // 16, l % 16
+            for e in range(4):
+                out[l, e] = src[16 * G + i // 4 + 4 * e][i % 4]
+        return out
+
+
+def bf16r(x):
+    return inputs.bf16_bits_to_f32(inputs.round_to_bf16_bits(np.asarray(x, np.float32))).astype(np.float64)
+
+
+def model_fwd(QKV, b, s, n, d, causal, round_p=True):
+    D = ((d + 31) // 32) * 32
+    KD, ND = D // 32, D // 16
+    pitch = 2 * D + 16
+    ld = 3 * n * d
+    T = b * s
+    O = np.full((T, n * d), np.nan)
+    lse = np.full((n, T), np.nan)
+    scale_log2 = math.log2(math.e) / math.sqrt(d)
+
+    def tile_load(lds, base_col, bi, row0):
+        for tid in range(256):
+            for u in range(D // 32):
+                i = tid + 256 * u
+                row, c = i // (D // 8), i % (D // 8)
+                ok = row0 + row < s and c * 8 < d
+                vals = QKV[bi * s + row0 + row, base_col + c * 8: base_col + c * 8 + 8] if ok else np.zeros(8)
+                lds.write16(row * pitch + c * 16, vals)
+
+    for bi in range(b):
+        for j in range(n):
+            for qb in range((s + BM - 1) // BM):
+                q0 = qb * BM
+                kv_end = min(s, q0 + BM) if causal else s
+                nkb = (kv_end + BN - 1) // BN
+                for w in range(4):
+                    qf = np.zeros((2, KD, 64, 8))
+                    for rb in range(2):
+                        for l in range(64):
+                            row = q0 + 32 * w + 16 * rb + l % 16
+                            for kk in range(KD):
+                                c = kk * 4 + l // 16
+                                if row < s and c * 8 < d:
+                                    qf[rb, kk, l] = QKV[bi * s + row, j * d + c * 8: j * d + c * 8 + 8]
+                    o = np.zeros((2, ND, 64, 4)); m = np.full((2, 64), -np.inf); lsum = np.zeros((2, 64))
+                    for kb in range(nkb):
+                        kt, vt = Lds(BN * pitch), Lds(BN * pitch)
+                        tile_load(kt, n * d + j * d, bi, kb * BN)
+                        tile_load(vt, 2 * n * d + j * d, bi, kb * BN)
+                        for rb in range(2):
+                            sacc = np.zeros((4, 64, 4))
+                            for kb16 in range(4):
+                                for kk in range(KD):
+                                    kfrag = np.array([kt.read_b128((kb16 * 16 + l % 16) * pitch + (kk * 4 + l // 16) * 16)
+                                                      for l in range(64)])
+                                    sacc[kb16] = mfma(kfrag, qf[rb, kk], sacc[kb16])
+                            t = np.zeros((4, 64, 4))
+                            for l in range(64):
+                                q = q0 + 32 * w + 16 * rb + l % 16
+                                for kb16 in range(4):
+                                    for r in range(4):
+                                        key = kb * BN + kb16 * 16 + 4 * (l // 16) + r
+                                        valid = key < s and (not causal or key <= q)
+                                        t[kb16, l, r] = sacc[kb16, l, r] * scale_log2 if valid else -np.inf
+                            mx = t.max(axis=(0, 2))  # per lane
+                            # merge over the 4 lanes of a row: l, l^16, l^32, l^48
+                            mxr = np.array([max(mx[l], mx[l ^ 16], mx[l ^ 32], mx[l ^ 48]) for l in range(64)])
+                            mnew = np.maximum(m[rb], mxr)
+                            msub = np.where(mnew == -np.inf, 0.0, mnew)
+                            corr = np.exp2(m[rb] - msub)
+                            p = np.exp2(t - msub[None, :, None])
+                            ps = p.sum(axis=(0, 2))
+                            psr = np.array([ps[l] + ps[l ^ 16] + ps[l ^ 32] + ps[l ^ 48] for l in range(64)])
+                            lsum[rb] = lsum[rb] * corr + psr
+                            m[rb] = mnew
+                            o[rb] *= corr[None, :, None]
+                            pr = bf16r(p) if round_p else p
+                            pf = np.zeros((2, 64, 8))
+                            for c in range(2):
+                                pf[c, :, 0:4] = pr[2 * c]
+                                pf[c, :, 4:8] = pr[2 * c + 1]
+                            for nb in range(ND):
+                                for c in range(2):
+                                    lo = vt.read_tr([(32 * c + 0 + 4 * (l // 16) + ((l % 16) >> 2)) * pitch
+                                                     + (16 * nb + 4 * ((l % 16) & 3)) * 2 for l in range(64)])
+                                    hi = vt.read_tr([(32 * c + 16 + 4 * (l // 16) + ((l % 16) >> 2)) * pitch
+                                                     + (16 * nb + 4 * ((l % 16) & 3)) * 2 for l in range(64)])
+                                    vf = np.concatenate([lo, hi], axis=1)
+                                    o[rb, nb] = mfma(vf, pf[c], o[rb, nb])
+                    for rb in range(2):
+                        for l in range(64):
+                            q = q0 + 32 * w + 16 * rb + l % 16
+                            if q >= s:
+                                continue
+                            inv = 1.0 / lsum[rb, l]
+                            for nb in range(ND):
+                                col = 16 * nb + 4 * (l // 16)
+                                if col < d:
+                                    O[bi * s + q, j * d + col:j * d + col + 4] = o[rb, nb, l] * inv
+                            if l // 16 == 0:
+                                lse[j, bi * s + q] = (m[rb, l] + math.log2(lsum[rb, l])) * math.log(2)
+    return O, lse
+
+
+
+def tile_load(lds, src, s, d, D, pitch, row0):
+    """src: [s, d] rows of one sequence/head block."""
+    for tid in range(256):
+        for u in range(D // 32):
+            i = tid + 256 * u
+            row, c = i // (D // 8), i % (D // 8)
+            ok = row0 + row < s and c * 8 < d
+            vals = src[row0 + row, c * 8:c * 8 + 8] if ok else np.zeros(8)
+            lds.write16(row * pitch + c * 16, vals)
+
+
+def kfrag_rows(src, rows_fn, kk, s, d):
+    """Register fragments: lane l holds src[row(l)][32kk + 8g .. +7] (zeros out of range)."""
+    out = np.zeros((64, 8))
+    for l in range(64):
+        row, c = rows_fn(l), kk * 4 + l // 16
+        if row < s and c * 8 < d:
+            out[l] = src[row, c * 8:c * 8 + 8]
+    return out
+
+
+def dkdv(Qs, Ks, Vs, dOs, lse, delta, s, d, causal, rnd):
+    """One (sequence, head): returns dK, dV [s, d]."""
+    D = ((d + 31) // 32) * 32; KD, ND = D // 32, D // 16; pitch = 2 * D + 16
+    scale_log2 = math.log2(math.e) / math.sqrt(d)
+    dK = np.full((s, d), np.nan); dV = np.full((s, d), np.nan)
+    for kb in range((s + BN - 1) // BN):
+        k0 = kb * BN
+        for w in range(4):
+            key_of = lambda l: k0 + 16 * w + l % 16
+            kf = [kfrag_rows(Ks, key_of, kk, s, d) for kk in range(KD)]
+            vf = [kfrag_rows(Vs, key_of, kk, s, d) for kk in range(KD)]
+            dk = np.zeros((ND, 64, 4)); dv = np.zeros((ND, 64, 4))
+            qstart = k0 if causal else 0
+            nqb = (s - qstart + BN - 1) // BN if qstart < s else 0
+            for qb in range(nqb):
+                qbase = qstart + qb * BN
+                Qt, Dt = Lds(BN * pitch), Lds(BN * pitch)
+                tile_load(Qt, Qs, s, d, D, pitch, qbase); tile_load(Dt, dOs, s, d, D, pitch, qbase)
+                sl = np.array([lse[qbase + i] * math.log2(math.e) if qbase + i < s else 0 for i in range(BN)])
+                sd = np.array([delta[qbase + i] if qbase + i < s else 0 for i in range(BN)])
+                p = np.zeros((4, 64, 4)); ds = np.zeros((4, 64, 4))
+                for qb16 in range(4):
+                    sacc = np.zeros((64, 4)); dpacc = np.zeros((64, 4))
+                    for kk in range(KD):
+                        offs = [(qb16 * 16 + l % 16) * pitch + (kk * 4 + l // 16) * 16 for l in range(64)]
+                        sacc = mfma(np.array([Qt.read_b128(o) for o in offs]), kf[kk], sacc)
+                        dpacc = mfma(np.array([Dt.read_b128(o) for o in offs]), vf[kk], dpacc)
+                    for l in range(64):
+                        key = key_of(l)
+                        for r in range(4):
+                            ql = qb16 * 16 + 4 * (l // 16) + r
+                            q = qbase + ql
+                            valid = q < s and key < s and (not causal or key <= q)
+                            p[qb16, l, r] = 2.0 ** (sacc[l, r] * scale_log2 - sl[ql]) if valid else 0.0
+                            ds[qb16, l, r] = p[qb16, l, r] * (dpacc[l, r] - sd[ql])
+                pr, dsr = (bf16r(p), bf16r(ds)) if rnd else (p, ds)
+                pf = np.zeros((2, 64, 8)); dsf = np.zeros((2, 64, 8))
+                for c in range(2):
+                    pf[c, :, :4], pf[c, :, 4:] = pr[2 * c], pr[2 * c + 1]
+                    dsf[c, :, :4], dsf[c, :, 4:] = dsr[2 * c], dsr[2 * c + 1]
+                for nb in range(ND):
+                    for c in range(2):
+                        a0 = [(32 * c + 4 * (l // 16) + ((l % 16) >> 2)) * pitch + (16 * nb + 4 * ((l % 16) & 3)) * 2 for l in range(64)]
+                        a1 = [(32 * c + 16 + 4 * (l // 16) + ((l % 16) >> 2)) * pitch + (16 * nb + 4 * ((l % 16) & 3)) * 2 for l in range(64)]
+                        dv[nb] = mfma(np.concatenate([Dt.read_tr(a0), Dt.read_tr(a1)], axis=1), pf[c], dv[nb])
+                        dk[nb] = mfma(np.concatenate([Qt.read_tr(a0), Qt.read_tr(a1)], axis=1), dsf[c], dk[nb])
+            for l in range(64):
+                key = key_of(l)
+                if key >= s:
+                    continue
+                for nb in range(ND):
+                    col = 16 * nb + 4 * (l // 16)
+                    if col < d:
+                        dK[key, col:col + 4] = dk[nb, l] / math.sqrt(d)
+                        dV[key, col:col + 4] = dv[nb, l]
+    return dK, dV
+
+
+def dq(Qs, Ks, Vs, dOs, lse, delta, s, d, causal, rnd):
+    D = ((d + 31) // 32) * 32; KD, ND = D // 32, D // 16; pitch = 2 * D + 16
+    scale_log2 = math.log2(math.e) / math.sqrt(d)
+    dQ = np.full((s, d), np.nan)
+    for qbk in range((s + BM - 1) // BM):
+        q0 = qbk * BM
+        kv_end = min(s, q0 + BM) if causal else s
+        nkb = (kv_end + BN - 1) // BN
+        for w in range(4):
+            accs = np.zeros((2, ND, 64, 4))
+            for rb in range(2):
+                row_of = lambda l: q0 + 32 * w + 16 * rb + l % 16
+                qf = [kfrag_rows(Qs, row_of, kk, s, d) for kk in range(KD)]
+                df = [kfrag_rows(dOs, row_of, kk, s, d) for kk in range(KD)]
+                lq = np.array([lse[row_of(l)] * math.log2(math.e) if row_of(l) < s else 0 for l in range(64)])
+                dl = np.array([delta[row_of(l)] if row_of(l) < s else 0 for l in range(64)])
+                for kb in range(nkb):
+                    Kt, Vt = Lds(BN * pitch), Lds(BN * pitch)
+                    tile_load(Kt, Ks, s, d, D, pitch, kb * BN); tile_load(Vt, Vs, s, d, D, pitch, kb * BN)
+                    ds = np.zeros((4, 64, 4))
+                    for kb16 in range(4):
+                        sacc = np.zeros((64, 4)); dpacc = np.zeros((64, 4))
+                        for kk in range(KD):
+                            offs = [(kb16 * 16 + l % 16) * pitch + (kk * 4 + l // 16) * 16 for l in range(64)]
+                            sacc = mfma(np.array([Kt.read_b128(o) for o in offs]), qf[kk], sacc)
+                            dpacc = mfma(np.array([Vt.read_b128(o) for o in offs]), df[kk], dpacc)
+                        for l in range(64):
+                            q = row_of(l)
+                            for r in range(4):
+                                key = kb * BN + kb16 * 16 + 4 * (l // 16) + r
+                                valid = q < s and key < s and (not causal or key <= q)
+                                pv = 2.0 ** (sacc[l, r] * scale_log2 - lq[l]) if valid else 0.0
+                                ds[kb16, l, r] = pv * (dpacc[l, r] - dl[l])
+                    dsr = bf16r(ds) if rnd else ds
+                    dsf = np.zeros((2, 64, 8))
+                    for c in range(2):
+                        dsf[c, :, :4], dsf[c, :, 4:] = dsr[2 * c], dsr[2 * c + 1]
+                    for nb in range(ND):
+                        for c in range(2):
+                            a0 = [(32 * c + 4 * (l // 16) + ((l % 16) >> 2)) * pitch + (16 * nb + 4 * ((l % 16) & 3)) * 2 for l in range(64)]
+                            a1 = [(32 * c + 16 + 4 * (l // 16) + ((l % 16) >> 2)) * pitch + (16 * nb + 4 * ((l % 16) & 3)) * 2 for l in range(64)]
+                            accs[rb, nb] = mfma(np.concatenate([Kt.read_tr(a0), Kt.read_tr(a1)], axis=1), dsf[c], accs[rb, nb])
+                for l in range(64):
+                    q = row_of(l)
+                    if q >= s:
+                        continue
+                    for nb in range(ND):
+                        col = 16 * nb + 4 * (l // 16)
+                        if col < d:
+                            dQ[q, col:col + 4] = accs[rb, nb, l] / math.sqrt(d)
+    return dQ
+
+
+
+
+@pytest.mark.parametrize("b,s,n,d,causal", [(2, 70, 2, 32, True), (1, 130, 1, 64, False), (1, 64, 1, 16, True),
+                                            (1, 96, 1, 96, True), (1, 64, 1, 128, False)])
+def test_forward_model_is_exact(b, s, n, d, causal):
+    rng = np.random.default_rng(s * d)
+    QKV = bf16r(rng.standard_normal((b * s, 3 * n * d)))
+    O, lse = model_fwd(QKV, b, s, n, d, causal, round_p=False)
+    want = attn.attention_core(QKV[:, :n * d], QKV[:, n * d:2 * n * d], QKV[:, 2 * n * d:], n, d, b, s, causal)
+    np.testing.assert_allclose(O, want["O"], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, want["lse"], rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("s,d,causal", [(70, 16, True), (130, 64, False), (96, 96, True), (64, 128, False)])
+def test_backward_model_is_exact(s, d, causal):
+    rng = np.random.default_rng(s + d)
+    Q, K, V, dO = (bf16r(rng.standard_normal((s, d))) for _ in range(4))
+    Qt, Kt, Vt = (torch.tensor(x, requires_grad=True) for x in (Q, K, V))
+    Ot = torch.nn.functional.scaled_dot_product_attention(Qt[None, None], Kt[None, None], Vt[None, None],
+                                                          is_causal=causal)[0, 0]
+    (Ot * torch.tensor(dO)).sum().backward()
+    w = attn.attention_core(Q, K, V, 1, d, 1, s, causal)
+    delta = (dO * w["O"]).sum(axis=1)
+    dK, dV = dkdv(Q, K, V, dO, w["lse"][0], delta, s, d, causal, False)
+    dQ = dq(Q, K, V, dO, w["lse"][0], delta, s, d, causal, False)
+    for got, want in ((dQ, Qt.grad), (dK, Kt.grad), (dV, Vt.grad)):
+        np.testing.assert_allclose(got, want.numpy(), rtol=1e-11, atol=1e-12)
