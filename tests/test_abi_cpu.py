@@ -224,3 +224,12 @@ def test_arm_kernel_events_validation(ms):
     for k in range(18):
         assert ms.LIB.ms_arm_kernel_events(k, None, None) == ms.MS_OK
     assert set(ms.KERNELS.values()) == set(range(18))
+
+
+def test_bench_breakdown_arms_only_step_kernels(ms):
+    """The benchmark's per-GEMM breakdown arms exactly the seven GEMM launches of its
+    step; ids of entry points the step never calls would leave unrecorded events."""
+    import bench
+    assert len(bench.STEP_KERNELS) == len(set(bench.STEP_KERNELS)) == 7
+    assert set(bench.STEP_KERNELS) <= set(ms.KERNELS)
+    assert not any(k.startswith(("ce_bwd", "attn")) for k in bench.STEP_KERNELS)
