@@ -1,6 +1,10 @@
-// kernels.hip - launchers for the MLP shard and CE shard, plus the small
-// fixed-order reduction kernels (split-K slices, bias-gradient partials, CE
-// tile partials, CE shard combine).  Every reduction adds its terms in an order
+// kernels.hip - the GEMM instantiations and launch sequences of every entry
+// point (MLP shard forward and backward, CE shard forward and backward,
+// attention shard forward and backward: its core kernels are in
+// attention.hip), the backward launch planner, the workspace layouts, and the
+// small fixed-order reduction kernels (split-K slices, bias-gradient partials,
+// CE tile partials, CE shard combine, CE backward row statistics).  Every
+// reduction adds its terms in an order
 // fixed by the shapes alone, with one private slot per writer and no atomics,
 // which is what makes repeated calls bitwise identical (Megatron Core
 // bitwise-determinism news item, news.hamidun.com: fixed reduction order and
