@@ -1,4 +1,5 @@
-"""The attention and fingerprint kernels' own sources, run on the CPU (host emulation).
+"""The attention, fingerprint and cross-entropy-gradient kernels' own sources, run
+on the CPU (host emulation).
 
 attention.hip and fingerprint.hip are compiled unmodified for the host with
 tests/cpu_emu: one OS thread per lane, one workgroup at a time, std::barrier
@@ -17,7 +18,16 @@ library (fingerprints).  Arithmetic is fp32 with bf16 operands and outputs, so
 the bar is the GPU bar: relative Frobenius error <= 1e-2; lse and fingerprints
 much tighter.  This checks the kernel sources' indexing and control flow; it
 does not replace running them on the GPU.
+
+The cross-entropy backward's epilogue (EpiCEGrad in epilogues.hpp) is run the
+same way over every tile of a ragged logit matrix, with tests/cpu_emu's
+stand-in for the GEMM core (its accumulator lane layout, buffer resources that
+read zero past their end and drop stores there).  epilogues.hpp is used as is,
+except that its three inline-assembly statements are removed mechanically: an
+LDS wait (every access is synchronous here) and two register reads of another
+epilogue that is not compiled in.
 """
+import re
 import os
 import shutil
 import subprocess
@@ -47,11 +57,21 @@ def drivers(tmp_path_factory):
     for f in ("epilogues.hpp", "attn_driver.cpp", "fp_driver.cpp"):
         shutil.copy(os.path.join(EMU, f), d)
     shutil.copytree(os.path.join(EMU, "hip"), os.path.join(d, "hip"))
+    # the epilogue under its own name, beside the stand-in core, for the CE-gradient driver
+    e = os.path.join(d, "ce")
+    os.makedirs(e)
+    src = open(os.path.join(CSRC, "epilogues.hpp")).read()
+    src, n = re.subn(r"\basm\b(\s+volatile)?\s*\((?:[^()]|\([^()]*\))*\)\s*;", ";", src)
+    assert n == 3 and "asm" not in re.sub(r"//[^\n]*", "", src)
+    open(os.path.join(e, "epilogues.hpp"), "w").write(src)
+    for f in ("gemm_core.hpp", "ce_grad_driver.cpp"):
+        shutil.copy(os.path.join(EMU, f), e)
+    shutil.copytree(os.path.join(EMU, "hip"), os.path.join(e, "hip"))
     out = {}
-    for name in ("attn_driver", "fp_driver"):
-        exe = os.path.join(d, name)
-        subprocess.run([CLANG, "-std=c++20", "-O1", "-x", "c++", f"-I{d}", os.path.join(d, name + ".cpp"), "-o", exe,
-                        "-lpthread"], check=True, capture_output=True)
+    for name, where in (("attn_driver", d), ("fp_driver", d), ("ce_grad_driver", e)):
+        exe = os.path.join(where, name)
+        subprocess.run([CLANG, "-std=c++20", "-O1", "-x", "c++", f"-I{where}", os.path.join(where, name + ".cpp"),
+                        "-o", exe, "-lpthread"], check=True, capture_output=True)
         out[name] = exe
     return out, d
 
@@ -107,3 +127,40 @@ def test_fingerprint_kernel_emulated(drivers, nbytes, chunk):
     parts = [data[k:k + chunk] for k in range(0, nbytes, chunk)] or [b""]
     assert words[1:] == [xxhash.xxh64(p).intdigest() for p in parts]
     assert words[0] == xxhash.xxh64(b"".join(w.to_bytes(8, "little") for w in words[1:])).intdigest()
+
+
+def test_ce_gradient_epilogue_emulated(drivers):
+    """dL = coef (exp(L - M) / S - one-hot) over a 300 x 520 logit block (2 x 3 tiles with
+    ragged edges), targets on tile and shard edges and outside the shard, masked tokens."""
+    exes, tmp = drivers
+    M, N = 300, 520
+    rng = np.random.default_rng(7)
+    L = (rng.standard_normal((M, N)) * 3).astype(np.float32)
+    tcol = rng.integers(0, N, size=M)
+    tcol[:8] = [0, N - 1, 255, 256, 511, 512, -1, -1]          # tile and shard edges; not in this shard
+    coef = rng.uniform(0.5, 1.5, size=M) / M
+    coef[10:14] = 0.0                                          # masked tokens
+    Ld = L.astype(np.float64)
+    Mx = Ld.max(axis=1) + rng.uniform(0, 1, size=M)          # combined max over a larger vocabulary
+    S = np.exp(Ld - Mx[:, None]).sum(axis=1) + rng.uniform(0, 5, size=M)
+    rec = np.zeros((M, 4), dtype=np.float32)
+    rec[:, 0] = (Mx * np.log2(np.e)).astype(np.float32)
+    rec[:, 1] = (coef / S).astype(np.float32)
+    rec[:, 2] = coef.astype(np.float32)
+    rec = rec.view(np.uint32)
+    rec[:, 3] = tcol.astype(np.int32).view(np.uint32)
+    case = os.path.join(tmp, "ce_grad")
+    os.makedirs(case, exist_ok=True)
+    L.tofile(os.path.join(case, "logits.bin"))
+    rec.tofile(os.path.join(case, "stats.bin"))
+    subprocess.run([exes["ce_grad_driver"], str(M), str(N), case], check=True, timeout=300)
+    dl_bits = np.fromfile(os.path.join(case, "dl.bin"), dtype=np.uint16).reshape(M, N)
+    assert not (dl_bits == 0xFFFF).any()                       # every element written
+    got = _f64(dl_bits)
+    onehot = np.arange(N)[None, :] == tcol[:, None]
+    want = coef[:, None] * (np.exp(Ld - Mx[:, None]) / S[:, None] - onehot)
+    assert rel_fro(got, want) <= 1e-2
+    np.testing.assert_allclose(got, want, rtol=2 ** -7, atol=1e-12)
+    sel = (tcol >= 0) & (coef > 0)                             # the target column is a row's only negative entry
+    assert (got[sel, tcol[sel]] < 0).all() and ((got < 0).sum(axis=1) == sel).all()
+    assert not got[10:14].any()                                # masked tokens: exactly zero
