@@ -279,7 +279,7 @@ def fingerprint(t: torch.Tensor, chunk_bytes: int = 1 << 16) -> torch.Tensor:
     if words == 0:
         raise ValueError(f"chunk_bytes {chunk_bytes} must be a positive multiple of 8")
     out = torch.empty(words, dtype=torch.int64, device=t.device)
-    ptr = t.data_ptr() if nbytes else out.data_ptr() + words * 8  # any aligned address: nothing is read
+    ptr = t.data_ptr() if nbytes else out.data_ptr()  # zero bytes: the address is never read
     _check(LIB.ms_fingerprint(ptr, nbytes, chunk_bytes, out.data_ptr(), _stream(t.device)), "ms_fingerprint")
     return out
 
