@@ -8,25 +8,6 @@
 
 #include <type_traits>
 
-inline uint32_t __float_as_uint(float f) { uint32_t u; std::memcpy(&u, &f, 4); return u; }
-inline float __shfl_xor(float x, int, int) { return x; }  // used only by an epilogue variant not exercised here
-inline bool __any(bool x) { return x; }                     // idem
-
-// Both lanes of each pair (l, l^16) / (l, l^32) receive (lower lane's value, upper lane's value).
-struct emu_pair { uint32_t v[2]; uint32_t operator[](int i) const { return v[i]; } };
-inline emu_pair emu_permlane_swap(uint32_t x, int m) {
-  emu::deposit(x);
-  emu::wave_sync();
-  const int l = threadIdx.x % 64, o = l ^ m;
-  emu_pair r{{emu::fetch<uint32_t>(l < o ? l : o), emu::fetch<uint32_t>(l < o ? o : l)}};
-  emu::wave_sync();
-  return r;
-}
-#define __builtin_amdgcn_permlane16_swap(A, B, C, D) emu_permlane_swap(A, 16)
-#define __builtin_amdgcn_permlane32_swap(A, B, C, D) emu_permlane_swap(A, 32)
-#define __builtin_amdgcn_rcpf(x) (1.0f / (x))
-#define __builtin_amdgcn_wave_barrier() emu::wave_sync()
-
 namespace mshard {
 
 typedef unsigned short bf16x8_t __attribute__((ext_vector_type(8)));

@@ -17,6 +17,8 @@
 #define __host__
 #define __forceinline__ inline
 #define __launch_bounds__(...)
+#define amdgpu_flat_work_group_size(...) unused
+#define amdgpu_waves_per_eu(...) unused
 #define __shared__ static
 
 typedef int hipError_t;
@@ -85,6 +87,142 @@ inline void launch(dim3 grid, dim3 block, F kernel, A... args) {
 
 #define hipLaunchKernelGGL(K, GRID, BLOCK, SHMEM, STREAM, ...) emu::launch(GRID, BLOCK, K, __VA_ARGS__)
 inline void __syncthreads() { emu::g_block->all.arrive_and_wait(); }
+
+// ---- builtins of the GEMM core and the epilogues
+namespace emu {
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+struct Rsrc {
+  char* base;
+  int64_t bytes;
+};
+inline Rsrc make_rsrc(const void* base, int n) { return Rsrc{(char*)base, n}; }
+template <class V>
+inline V rload(Rsrc r, int off) {
+  V v{};
+  if (off >= 0 && (int64_t)off + (int64_t)sizeof(V) <= r.bytes) std::memcpy(&v, r.base + off, sizeof(V));
+  return v;
+}
+template <class V>
+inline void rstore(V v, Rsrc r, int off) {
+  if (off >= 0 && (int64_t)off + (int64_t)sizeof(V) <= r.bytes) std::memcpy(r.base + off, &v, sizeof(V));
+}
+// Both lanes of each pair (l, l^m) receive (lower lane's value, upper lane's value).
+struct Pair {
+  uint32_t v[2];
+  uint32_t operator[](int i) const { return v[i]; }
+};
+inline Pair permlane_swap(uint32_t x, int m) {
+  deposit(x);
+  wave_sync();
+  const int l = threadIdx.x % 64, o = l ^ m;
+  Pair r{{fetch<uint32_t>(l < o ? l : o), fetch<uint32_t>(l < o ? o : l)}};
+  wave_sync();
+  return r;
+}
+inline float shfl_xor(float x, int m) {
+  deposit(x);
+  wave_sync();
+  const float v = fetch<float>((threadIdx.x % 64) ^ m);
+  wave_sync();
+  return v;
+}
+inline bool any(bool x) {
+  deposit((int)x);
+  wave_sync();
+  int r = 0;
+  for (int l = 0; l < 64; ++l) r |= fetch<int>(l);
+  wave_sync();
+  return r != 0;
+}
+// buffer_load_dwordx4 ... lds: lane l's 16 bytes from the buffer the descriptor
+// {base low, base high (16 bits), bytes, flags} describes, at byte offset off,
+// land at LDS byte 16*l of the 1 KiB at lds_addr; past the buffer they are zero.
+// (The hardware writes LDS later, at the wave's vmcnt wait; here the bytes land
+// at once, which the kernels' waits and barriers make indistinguishable.)
+inline void dma16(u32x4 desc, uint32_t off, uint32_t lds_addr) {
+  const char* base = (const char*)(uintptr_t)((uint64_t)desc[0] | ((uint64_t)(desc[1] & 0xffffu) << 32));
+  char* dst = (char*)(uintptr_t)lds_addr + 16 * (threadIdx.x % 64);
+  if ((uint64_t)off + 16 <= (uint64_t)desc[2]) std::memcpy(dst, base + off, 16);
+  else std::memset(dst, 0, 16);
+}
+
+inline float bf16f(unsigned short u) {
+  uint32_t x = (uint32_t)u << 16;
+  float v;
+  std::memcpy(&v, &x, 4);
+  return v;
+}
+// fp32 -> bf16 bits, round to nearest even, NaN kept quiet.
+inline uint32_t bf16_rne(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+inline uint32_t pack_bf16x2_rne(float lo, float hi) { return bf16_rne(lo) | (bf16_rne(hi) << 16); }
+
+// v_mfma_f32_16x16x32_bf16 on any 16-byte operand type holding bf16 bit
+// patterns: lane l supplies row l%16, k = 8(l/16) .. +7 of the first operand and
+// column l%16 of the second; it receives D[4(l/16) + r][l%16].
+template <class V, class A>
+inline A mfma16x16x32(const V& a, const V& b, const A& c) {
+  typedef unsigned short us8 __attribute__((ext_vector_type(8)));
+  struct Ops { us8 a, b; };
+  deposit(Ops{__builtin_bit_cast(us8, a), __builtin_bit_cast(us8, b)});
+  wave_sync();
+  Ops all[64];
+  for (int l = 0; l < 64; ++l) all[l] = fetch<Ops>(l);
+  wave_sync();
+  const int l = threadIdx.x % 64, g = l / 16, col = l % 16;
+  A out = c;
+  for (int r = 0; r < 4; ++r) {
+    const int i = 4 * g + r;
+    float acc = 0.f;
+    for (int k = 0; k < 32; ++k) acc += bf16f(all[i + 16 * (k / 8)].a[k % 8]) * bf16f(all[col + 16 * (k / 8)].b[k % 8]);
+    out[r] += acc;
+  }
+  return out;
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, result lane i, element e is
+// element i%4 of the 8 bytes source lane i/4 + 4e addressed.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+inline s16x4 ds_read_tr16(const char* p) {
+  deposit(p);
+  wave_sync();
+  const int l = threadIdx.x % 64, G = l / 16, i = l % 16;
+  s16x4 out;
+  for (int e = 0; e < 4; ++e) {
+    const char* src = fetch<const char*>(16 * G + i / 4 + 4 * e);
+    short v;
+    std::memcpy(&v, src + 2 * (i % 4), 2);
+    out[e] = v;
+  }
+  wave_sync();
+  return out;
+}
+}  // namespace emu
+
+typedef emu::Rsrc __amdgpu_buffer_rsrc_t;
+#define __builtin_amdgcn_make_buffer_rsrc(P, S, N, F) emu::make_rsrc(P, N)
+#define __builtin_amdgcn_raw_buffer_load_b128(R, O, S, A) emu::rload<emu::u32x4>(R, O)
+#define __builtin_amdgcn_raw_buffer_load_b64(R, O, S, A) emu::rload<emu::u32x2>(R, O)
+#define __builtin_amdgcn_raw_buffer_store_b128(V, R, O, S, A) emu::rstore<emu::u32x4>(V, R, O)
+#define __builtin_amdgcn_raw_buffer_store_b64(V, R, O, S, A) emu::rstore<emu::u32x2>(V, R, O)
+#define __builtin_amdgcn_raw_buffer_store_b32(V, R, O, S, A) emu::rstore<uint32_t>(V, R, O)
+#define __builtin_amdgcn_s_waitcnt(x) ((void)0)
+#define __builtin_amdgcn_sched_barrier(x) ((void)0)
+#define __builtin_amdgcn_s_barrier() __syncthreads()
+#define __builtin_amdgcn_readfirstlane(x) (x)
+#define __builtin_amdgcn_wave_barrier() emu::wave_sync()
+#define __builtin_amdgcn_rcpf(x) (1.0f / (x))
+#define __builtin_amdgcn_permlane16_swap(A, B, C, D) emu::permlane_swap(A, 16)
+#define __builtin_amdgcn_permlane32_swap(A, B, C, D) emu::permlane_swap(A, 32)
+inline uint32_t __float_as_uint(float f) { uint32_t u; std::memcpy(&u, &f, 4); return u; }
+inline float __shfl_xor(float x, int m, int) { return emu::shfl_xor(x, m); }
+inline bool __any(bool x) { return emu::any(x); }
 
 #define __builtin_amdgcn_exp2f(x) exp2f(x)
 #define __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, C, X, Y, Z) emu::mfma16x16x32(A, B, C)

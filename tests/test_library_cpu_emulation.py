@@ -1,0 +1,208 @@
+"""The whole library's launch sequences run on the CPU, against the fp64 oracle.
+
+tests/cpu_emu/prep.py copies every kernel source of the library (the GEMM core
+and its epilogues included), replacing each inline-assembly statement by its
+emulated meaning; tests/cpu_emu/hip/hip_runtime.h runs each workgroup as one OS
+thread per lane with emulated MFMA, direct-to-LDS loads, transposing LDS reads,
+buffer resources (out-of-range loads read zero, stores are dropped) and lane
+exchanges.  tests/cpu_emu/lib_driver.cpp calls the library's own launch
+functions (kernels.hip, attention.hip): the same launch plans, workspace
+layouts, paired and split-K launches, grids and kernel arguments as on the GPU.
+
+What this shows: indexing, tiling, masking of ragged edges, the K tail, split-K
+slices and their fixed-order reduction, paired launches, workspace offsets and
+every epilogue compute the definitions the oracle writes out.  What it does not
+show: anything about timing on the GPU (the direct-to-LDS loads land at once
+here, where the hardware needs the kernels' own waits and barriers), nor the
+hardware's exp2 and reciprocal rounding.  Outputs and workspaces start as NaN,
+so an element left unwritten fails.  Tolerances are those of the GPU parity
+tests: relative Frobenius 1e-2 for bf16-input GEMM outputs and gradients, 1e-4
+for the CE partials, the per-token loss and its mean.
+"""
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+
+import oracle
+from megatron_tensor_transformer_mlp_amd import inputs
+from oracle import attn
+from tests.conftest import rel_fro
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "megatron_tensor_transformer_mlp_amd", "csrc")
+EMU = os.path.join(ROOT, "tests", "cpu_emu")
+CLANG = "/opt/rocm/llvm/bin/clang++"
+TOL = 1e-2
+CE_TOL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def lib(tmp_path_factory):
+    if not os.path.exists(CLANG):
+        pytest.skip("clang++ not found")
+    sys.path.insert(0, EMU)
+    try:
+        import prep
+    finally:
+        sys.path.remove(EMU)
+    d = str(tmp_path_factory.mktemp("libemu"))
+    prep.prepare(CSRC, EMU, d)
+    srcs = ["kernels.hip", "attention.hip", "fingerprint.hip", "lib_driver.cpp"]
+
+    def compile_one(src):
+        obj = os.path.join(d, src.split(".")[0] + ".o")
+        subprocess.run([CLANG, "-std=c++20", "-O1", "-fno-pic", "-w", "-x", "c++", f"-I{d}", "-c",
+                        os.path.join(d, src), "-o", obj], check=True, capture_output=True)
+        return obj
+
+    with ThreadPoolExecutor(4) as ex:
+        objs = list(ex.map(compile_one, srcs))
+    exe = os.path.join(d, "lib_driver")
+    # -no-pie: the static LDS arrays sit below 4 GiB, where the kernels' 32-bit LDS addresses reach them
+    subprocess.run([CLANG, "-no-pie", *objs, "-o", exe, "-lpthread"], check=True, capture_output=True)
+    return exe, d
+
+
+def run(exe, case, *args):
+    subprocess.run([exe, *[str(a) for a in args], case], check=True, timeout=600)
+
+
+def f64(u):
+    return inputs.bf16_bits_to_f32(u).astype(np.float64)
+
+
+def put(case, **arrays):
+    os.makedirs(case, exist_ok=True)
+    for k, a in arrays.items():
+        np.ascontiguousarray(a).tofile(os.path.join(case, k + ".bin"))
+
+
+def get(case, name, dtype, shape):
+    a = np.fromfile(os.path.join(case, name + ".bin"), dtype=dtype).reshape(shape)
+    return f64(a) if dtype == np.uint16 else a.astype(np.float64)
+
+
+def plan(exe, d, *shape):
+    out = subprocess.run([exe, "plan", *[str(a) for a in shape], d], check=True, capture_output=True,
+                         text=True).stdout
+    return {line.split()[0]: dict(kv.split("=") for kv in line.split()[1:]) for line in out.splitlines()}
+
+
+# T, h, f, gelu (0 erf, 1 tanh), bias: ragged tokens and FFN columns, a K tail of 8
+# (h = 200), and a token count whose weight gradients are split over K
+@pytest.mark.parametrize("T,h,f,gelu,bias", [(300, 128, 264, 0, 1), (600, 200, 264, 1, 0), (1100, 256, 256, 0, 1)])
+def test_mlp_shard_emulated(lib, T, h, f, gelu, bias):
+    exe, d = lib
+    x = inputs.make_inputs(T, h, f, 64, bias=True)
+    case = os.path.join(d, f"mlp_{T}_{h}_{f}_{gelu}_{bias}")
+    put(case, X=x["X"], A=x["A"], B=x["B"], dZ=x["dZ"], b1=x["b1"])
+    run(exe, case, "mlp_fwd", T, h, f, gelu, bias)
+    run(exe, case, "mlp_bwd", T, h, f, gelu, bias)
+    form, b1 = ("tanh" if gelu else "erf"), (x["b1"] if bias else None)
+    of = oracle.mlp_shard_fwd(x["X"], x["A"], x["B"], b1, form)
+    ob = oracle.mlp_shard_bwd(x["X"], x["A"], x["B"], x["dZ"], b1, form)
+    got = {"H": get(case, "H", np.uint16, (T, f)), "Y": get(case, "Y", np.uint16, (T, f)),
+           "Z": get(case, "Z", np.float32, (T, h)), "dX": get(case, "dX", np.float32, (T, h)),
+           "dA": get(case, "dA", np.uint16, (h, f)), "dB": get(case, "dB", np.uint16, (f, h))}
+    if bias:
+        got["db1"] = get(case, "db1", np.uint16, (f,))
+    want = {**of, **ob}
+    errs = {k: rel_fro(v, want[k]) for k, v in got.items()}
+    print(case, {k: f"{e:.1e}" for k, e in errs.items()})
+    assert all(e <= TOL for e in errs.values()), errs
+
+
+def test_vocab_ce_two_shards_emulated(lib):
+    """Both ranks' forward partials, the fixed-order combine, and rank 0's backward
+    with a per-token upstream gradient (every seventh token weighted 0)."""
+    exe, d = lib
+    T, h, v, t = 300, 128, 520, 2
+    case = os.path.join(d, "ce2")
+    ms_, ss_, zs_ = [], [], []
+    for r in range(t):
+        x = inputs.make_inputs(T, h, 64, v, t=t, rank=r)
+        put(case, X=x["X"], E=x["E"], target=x["targets"])
+        run(exe, case, "ce_fwd", T, h, v, int(x["vocab_start"]))
+        o = oracle.vocab_ce_shard(x["X"], x["E"], x["targets"], int(x["vocab_start"]))
+        m, s, z = (get(case, k, np.float32, (T,)) for k in ("m", "s", "z"))
+        assert np.abs(m - o["m"]).max() <= CE_TOL * np.abs(o["m"]).max()
+        assert np.abs(s / o["s"] - 1).max() <= CE_TOL
+        assert np.abs(z - o["z"]).max() <= CE_TOL * np.abs(o["z"]).max()
+        assert (z[(x["targets"] < r * v) | (x["targets"] >= (r + 1) * v)] == 0).all()
+        ms_.append(m), ss_.append(s), zs_.append(z)
+    M, S, Zp = (np.stack(a).astype(np.float32) for a in (ms_, ss_, zs_))
+    put(case, m=M, s=S, z=Zp)
+    run(exe, case, "combine", t, T)
+    oc = oracle.ce_combine(M, S, Zp)
+    assert np.abs(get(case, "loss", np.float32, (T,)) / oc["loss"] - 1).max() <= CE_TOL
+    assert abs(get(case, "mean", np.float32, (1,))[0] / oc["mean"] - 1) <= CE_TOL
+    x = inputs.make_inputs(T, h, 64, v, t=t, rank=0)
+    dl = np.random.default_rng(5).uniform(0.5, 1.5, T).astype(np.float32)
+    dl[::7] = 0
+    put(case, X=x["X"], E=x["E"], target=x["targets"], dloss=dl)
+    scale = np.float32(1.0 / T)
+    run(exe, case, "ce_bwd", T, h, v, 0, t, repr(float(scale)), 1)
+    ob = oracle.vocab_ce_shard_bwd(x["X"], x["E"], x["targets"], 0, M, S, float(scale) * dl.astype(np.float64))
+    assert rel_fro(get(case, "dX", np.float32, (T, h)), ob["dX"]) <= TOL
+    assert rel_fro(get(case, "dE", np.uint16, (h, v)), ob["dE"]) <= TOL
+
+
+def test_vocab_ce_bwd_split_k_emulated(lib):
+    """One shard owning the whole vocabulary, the mean-loss gradient (no dloss), at a
+    token count whose dE GEMM is split over K."""
+    exe, d = lib
+    T, h, v = 1100, 256, 256
+    assert int(plan(exe, d, T, h, 256, v, 1, 64, 1, 64)["ce_bwd"]["splits_dE"]) > 1
+    x = inputs.make_inputs(T, h, 64, v)
+    case = os.path.join(d, "ce1")
+    put(case, X=x["X"], E=x["E"], target=x["targets"])
+    run(exe, case, "ce_fwd", T, h, v, 0)
+    M, S = (get(case, k, np.float32, (T,)).astype(np.float32)[None] for k in ("m", "s"))
+    put(case, m=M, s=S)
+    scale = np.float32(1.0 / T)
+    run(exe, case, "ce_bwd", T, h, v, 0, 1, repr(float(scale)), 0)
+    ob = oracle.vocab_ce_shard_bwd(x["X"], x["E"], x["targets"], 0, M, S, float(scale))
+    assert rel_fro(get(case, "dX", np.float32, (T, h)), ob["dX"]) <= TOL
+    assert rel_fro(get(case, "dE", np.uint16, (h, v)), ob["dE"]) <= TOL
+
+
+# b, s, h, n, d, causal: the tiny layer, ragged sequences, every head size, and
+# a token count whose weight gradients are split over K
+@pytest.mark.parametrize("b,s,h,n,hd,causal", [
+    (2, 32, 64, 4, 16, True), (2, 70, 96, 3, 32, True), (1, 130, 128, 2, 64, False), (1, 96, 192, 2, 96, True),
+    (1, 64, 256, 2, 128, False), (3, 1, 64, 2, 32, True), (2, 550, 128, 1, 64, True)])
+def test_attn_shard_emulated(lib, b, s, h, n, hd, causal):
+    exe, d = lib
+    a = inputs.make_attn_inputs(b, s, h, n, hd)
+    case = os.path.join(d, f"attn_{b}_{s}_{h}_{n}_{hd}_{int(causal)}")
+    put(case, X=a["X"], Wqkv=a["Wqkv"], Wo=a["Wo"], dZ=a["dZ"])
+    run(exe, case, "attn_fwd", b, s, h, n, hd, int(causal))
+    run(exe, case, "attn_bwd", b, s, h, n, hd, int(causal))
+    T, nd = b * s, n * hd
+    got = {"QKV": get(case, "QKV", np.uint16, (T, 3 * nd)), "O": get(case, "O", np.uint16, (T, nd)),
+           "lse": get(case, "lse", np.float32, (n, T)), "Z": get(case, "Z", np.float32, (T, h)),
+           "dX": get(case, "dX", np.float32, (T, h)), "dWqkv": get(case, "dWqkv", np.uint16, (h, 3 * nd)),
+           "dWo": get(case, "dWo", np.uint16, (nd, h))}
+    want = {**attn.attn_shard_fwd(a["X"], a["Wqkv"], a["Wo"], n, hd, b, s, causal),
+            **attn.attn_shard_bwd(a["X"], a["Wqkv"], a["Wo"], a["dZ"], n, hd, b, s, causal)}
+    errs = {k: rel_fro(v, want[k]) for k, v in got.items()}
+    print(case, {k: f"{e:.1e}" for k, e in errs.items()})
+    assert all(e <= TOL for e in errs.values()), errs
+
+
+def test_emulated_cases_cover_the_plans(lib):
+    """The shapes above run both unsplit and split-K weight gradients in every
+    backward, and paired launches with either GEMM leading."""
+    exe, d = lib
+    p_small = plan(exe, d, 300, 128, 264, 520, 2, 70, 3, 32)
+    p_split = plan(exe, d, 1100, 256, 256, 256, 2, 550, 1, 64)
+    assert p_small["mlp"]["splits_dA"] == "1" and int(p_split["mlp"]["splits_dA"]) > 1
+    assert int(p_split["mlp"]["splits_dB"]) > 1
+    assert p_small["ce_bwd"]["splits_dE"] == "1"
+    assert p_split["attn"]["splits_wqkv"] != "1" or p_split["attn"]["splits_wo"] != "1"
+    assert {p_small["mlp"]["dx_first"], p_split["mlp"]["dx_first"]} == {"0", "1"}
+    assert p_small["mlp"]["pair_ax"] == "1" and p_small["ce_bwd"]["paired"] == "1"
