@@ -10,6 +10,7 @@
 //   lib_driver combine  t T dir             : m s z                   -> loss mean
 //   lib_driver attn_fwd b s h n d causal dir: X Wqkv Wo               -> QKV O lse Z
 //   lib_driver attn_bwd b s h n d causal dir: X Wqkv Wo QKV O lse dZ  -> dX dWqkv dWo
+//   lib_driver fingerprint bytes chunk dir  : buf                     -> fp (1 + chunks words)
 //   lib_driver plan     T h f v b s n d dir : prints the backward launch plans of these shapes
 #include <cstdio>
 #include <cstdlib>
@@ -130,6 +131,12 @@ int main(int argc, char** argv) {
          "launch_attn_bwd");
       wr("dX", dX, T * h * 4), wr("dWqkv", dWqkv, h * 3 * nd * 2), wr("dWo", dWo, nd * h * 2);
     }
+  } else if (op == "fingerprint") {
+    const int64_t bytes = I(0), chunk = I(1);
+    const uint64_t words = 1 + mshard::fingerprint_chunk_count(bytes, chunk);
+    auto buf = rd("buf", bytes), fp = out(words * 8);
+    ok(mshard::launch_fingerprint(buf.data(), bytes, chunk, P<uint64_t>(fp), nullptr), "launch_fingerprint");
+    wr("fp", fp, words * 8);
   } else if (op == "plan") {
     const int64_t T = I(0), h = I(1), f = I(2), v = I(3), b = I(4), s = I(5), n = I(6), d = I(7);
     const mshard::MlpWorkspace mw = mshard::mlp_workspace_layout(T, h, f);

@@ -40,22 +40,19 @@ TOL = 1e-2
 CE_TOL = 1e-4
 
 
-@pytest.fixture(scope="module")
-def lib(tmp_path_factory):
-    if not os.path.exists(CLANG):
-        pytest.skip("clang++ not found")
+def build(d, sanitize=False):
     sys.path.insert(0, EMU)
     try:
         import prep
     finally:
         sys.path.remove(EMU)
-    d = str(tmp_path_factory.mktemp("libemu"))
     prep.prepare(CSRC, EMU, d)
     srcs = ["kernels.hip", "attention.hip", "fingerprint.hip", "lib_driver.cpp"]
+    flags = ["-g", "-fsanitize=address", "-fno-omit-frame-pointer"] if sanitize else []
 
     def compile_one(src):
         obj = os.path.join(d, src.split(".")[0] + ".o")
-        subprocess.run([CLANG, "-std=c++20", "-O1", "-fno-pic", "-w", "-x", "c++", f"-I{d}", "-c",
+        subprocess.run([CLANG, "-std=c++20", "-O1", "-fno-pic", "-w", *flags, "-x", "c++", f"-I{d}", "-c",
                         os.path.join(d, src), "-o", obj], check=True, capture_output=True)
         return obj
 
@@ -63,12 +60,21 @@ def lib(tmp_path_factory):
         objs = list(ex.map(compile_one, srcs))
     exe = os.path.join(d, "lib_driver")
     # -no-pie: the static LDS arrays sit below 4 GiB, where the kernels' 32-bit LDS addresses reach them
-    subprocess.run([CLANG, "-no-pie", *objs, "-o", exe, "-lpthread"], check=True, capture_output=True)
-    return exe, d
+    subprocess.run([CLANG, "-no-pie", *flags[1:2], *objs, "-o", exe, "-lpthread"], check=True, capture_output=True)
+    return exe
+
+
+@pytest.fixture(scope="module")
+def lib(tmp_path_factory):
+    if not os.path.exists(CLANG):
+        pytest.skip("clang++ not found")
+    d = str(tmp_path_factory.mktemp("libemu"))
+    return build(d), d
 
 
 def run(exe, case, *args):
-    subprocess.run([exe, *[str(a) for a in args], case], check=True, timeout=600)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:halt_on_error=1:exitcode=23")
+    subprocess.run([exe, *[str(a) for a in args], case], check=True, timeout=900, env=env)
 
 
 def f64(u):
@@ -96,7 +102,10 @@ def plan(exe, d, *shape):
 # (h = 200), and a token count whose weight gradients are split over K
 @pytest.mark.parametrize("T,h,f,gelu,bias", [(300, 128, 264, 0, 1), (600, 200, 264, 1, 0), (1100, 256, 256, 0, 1)])
 def test_mlp_shard_emulated(lib, T, h, f, gelu, bias):
-    exe, d = lib
+    mlp_case(*lib, T, h, f, gelu, bias)
+
+
+def mlp_case(exe, d, T, h, f, gelu, bias):
     x = inputs.make_inputs(T, h, f, 64, bias=True)
     case = os.path.join(d, f"mlp_{T}_{h}_{f}_{gelu}_{bias}")
     put(case, X=x["X"], A=x["A"], B=x["B"], dZ=x["dZ"], b1=x["b1"])
@@ -119,7 +128,10 @@ def test_mlp_shard_emulated(lib, T, h, f, gelu, bias):
 def test_vocab_ce_two_shards_emulated(lib):
     """Both ranks' forward partials, the fixed-order combine, and rank 0's backward
     with a per-token upstream gradient (every seventh token weighted 0)."""
-    exe, d = lib
+    ce_two_shards(*lib)
+
+
+def ce_two_shards(exe, d):
     T, h, v, t = 300, 128, 520, 2
     case = os.path.join(d, "ce2")
     ms_, ss_, zs_ = [], [], []
@@ -176,7 +188,10 @@ def test_vocab_ce_bwd_split_k_emulated(lib):
     (2, 32, 64, 4, 16, True), (2, 70, 96, 3, 32, True), (1, 130, 128, 2, 64, False), (1, 96, 192, 2, 96, True),
     (1, 64, 256, 2, 128, False), (3, 1, 64, 2, 32, True), (2, 550, 128, 1, 64, True)])
 def test_attn_shard_emulated(lib, b, s, h, n, hd, causal):
-    exe, d = lib
+    attn_case(*lib, b, s, h, n, hd, causal)
+
+
+def attn_case(exe, d, b, s, h, n, hd, causal):
     a = inputs.make_attn_inputs(b, s, h, n, hd)
     case = os.path.join(d, f"attn_{b}_{s}_{h}_{n}_{hd}_{int(causal)}")
     put(case, X=a["X"], Wqkv=a["Wqkv"], Wo=a["Wo"], dZ=a["dZ"])
@@ -206,3 +221,37 @@ def test_emulated_cases_cover_the_plans(lib):
     assert p_split["attn"]["splits_wqkv"] != "1" or p_split["attn"]["splits_wo"] != "1"
     assert {p_small["mlp"]["dx_first"], p_split["mlp"]["dx_first"]} == {"0", "1"}
     assert p_small["mlp"]["pair_ax"] == "1" and p_small["ce_bwd"]["paired"] == "1"
+
+
+@pytest.mark.parametrize("nbytes,chunk", [(0, 64), (100, 32), (70000, 4096), (3 * 65536 + 5, 65536)])
+def test_fingerprint_emulated(lib, nbytes, chunk):
+    fingerprint_case(*lib, nbytes, chunk)
+
+
+def fingerprint_case(exe, d, nbytes, chunk):
+    from oracle import fingerprint as ofp
+    data = np.random.default_rng(nbytes).integers(0, 256, nbytes, dtype=np.uint8)
+    case = os.path.join(d, f"fp_{nbytes}_{chunk}")
+    put(case, buf=data)
+    run(exe, case, "fingerprint", nbytes, chunk)
+    got = np.fromfile(os.path.join(case, "fp.bin"), dtype=np.uint64)
+    want = ofp.fingerprint(data.tobytes(), chunk)
+    assert [int(w) for w in got] == [want["hash"], *want["chunks"]]
+
+
+def test_library_emulated_under_address_sanitizer(tmp_path):
+    """The same launch sequences built with AddressSanitizer: every global and LDS
+    access of every kernel stays inside its allocation (inputs, outputs and
+    workspaces are allocated at their exact sizes, so any read or write past an
+    end stops the run).  Buffer-resource accesses are checked against the
+    resource's extent, which must lie inside the allocation too."""
+    if not os.path.exists(CLANG):
+        pytest.skip("clang++ not found")
+    d = str(tmp_path)
+    exe = build(d, sanitize=True)
+    mlp_case(exe, d, 600, 200, 264, 1, 0)
+    ce_two_shards(exe, d)
+    attn_case(exe, d, 2, 70, 96, 3, 32, True)
+    attn_case(exe, d, 3, 1, 64, 2, 32, True)
+    fingerprint_case(exe, d, 100, 32)
+    fingerprint_case(exe, d, 0, 64)
