@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <deque>
 #include <functional>
 #include <thread>
 #include <vector>
@@ -137,14 +138,29 @@ inline bool any(bool x) {
 }
 // buffer_load_dwordx4 ... lds: lane l's 16 bytes from the buffer the descriptor
 // {base low, base high (16 bits), bytes, flags} describes, at byte offset off,
-// land at LDS byte 16*l of the 1 KiB at lds_addr; past the buffer they are zero.
-// (The hardware writes LDS later, at the wave's vmcnt wait; here the bytes land
-// at once, which the kernels' waits and barriers make indistinguishable.)
+// go to LDS byte 16*l of the 1 KiB at lds_addr; past the buffer they are zero.
+// The LDS write is held back until an s_waitcnt whose vector-memory count
+// leaves fewer of this lane's loads outstanding, the latest the hardware may
+// land it (other vector-memory operations would only make a wait stricter), so
+// a missing or too-loose wait leaves stale LDS bytes for the readers to see.
+struct PendingDma {
+  char* dst;
+  unsigned char data[16];
+};
+inline thread_local std::deque<PendingDma> t_dma;  // this lane's loads not yet landed, oldest first
 inline void dma16(u32x4 desc, uint32_t off, uint32_t lds_addr) {
   const char* base = (const char*)(uintptr_t)((uint64_t)desc[0] | ((uint64_t)(desc[1] & 0xffffu) << 32));
-  char* dst = (char*)(uintptr_t)lds_addr + 16 * (threadIdx.x % 64);
-  if ((uint64_t)off + 16 <= (uint64_t)desc[2]) std::memcpy(dst, base + off, 16);
-  else std::memset(dst, 0, 16);
+  PendingDma p;
+  p.dst = (char*)(uintptr_t)lds_addr + 16 * (threadIdx.x % 64);
+  if ((uint64_t)off + 16 <= (uint64_t)desc[2]) std::memcpy(p.data, base + off, 16);
+  else std::memset(p.data, 0, 16);
+  t_dma.push_back(p);
+}
+inline void wait_vmcnt(unsigned n) {
+  while (t_dma.size() > n) {
+    std::memcpy(t_dma.front().dst, t_dma.front().data, 16);
+    t_dma.pop_front();
+  }
 }
 
 inline float bf16f(unsigned short u) {
@@ -172,15 +188,21 @@ inline A mfma16x16x32(const V& a, const V& b, const A& c) {
   struct Ops { us8 a, b; };
   deposit(Ops{__builtin_bit_cast(us8, a), __builtin_bit_cast(us8, b)});
   wave_sync();
-  Ops all[64];
-  for (int l = 0; l < 64; ++l) all[l] = fetch<Ops>(l);
-  wave_sync();
   const int l = threadIdx.x % 64, g = l / 16, col = l % 16;
+  float av[4][32], bv[32];
+  for (int q = 0; q < 4; ++q) {
+    const us8 bq = fetch<Ops>(col + 16 * q).b;
+    for (int e = 0; e < 8; ++e) bv[8 * q + e] = bf16f(bq[e]);
+    for (int r = 0; r < 4; ++r) {
+      const us8 aq = fetch<Ops>(4 * g + r + 16 * q).a;
+      for (int e = 0; e < 8; ++e) av[r][8 * q + e] = bf16f(aq[e]);
+    }
+  }
+  wave_sync();
   A out = c;
   for (int r = 0; r < 4; ++r) {
-    const int i = 4 * g + r;
     float acc = 0.f;
-    for (int k = 0; k < 32; ++k) acc += bf16f(all[i + 16 * (k / 8)].a[k % 8]) * bf16f(all[col + 16 * (k / 8)].b[k % 8]);
+    for (int k = 0; k < 32; ++k) acc += av[r][k] * bv[k];
     out[r] += acc;
   }
   return out;
@@ -212,7 +234,7 @@ typedef emu::Rsrc __amdgpu_buffer_rsrc_t;
 #define __builtin_amdgcn_raw_buffer_store_b128(V, R, O, S, A) emu::rstore<emu::u32x4>(V, R, O)
 #define __builtin_amdgcn_raw_buffer_store_b64(V, R, O, S, A) emu::rstore<emu::u32x2>(V, R, O)
 #define __builtin_amdgcn_raw_buffer_store_b32(V, R, O, S, A) emu::rstore<uint32_t>(V, R, O)
-#define __builtin_amdgcn_s_waitcnt(x) ((void)0)
+#define __builtin_amdgcn_s_waitcnt(x) emu::wait_vmcnt(((x) & 15) | ((((x) >> 14) & 3) << 4))
 #define __builtin_amdgcn_sched_barrier(x) ((void)0)
 #define __builtin_amdgcn_s_barrier() __syncthreads()
 #define __builtin_amdgcn_readfirstlane(x) (x)
