@@ -1,16 +1,22 @@
-// Host emulation of the HIP subset that the attention and fingerprint kernels
-// use, for running their unmodified sources on the CPU in tests: a workgroup
-// runs as one OS thread per lane, workgroups run one after another, barriers
-// are std::barrier, and cross-lane operations exchange values through per-wave
-// slots (see epilogues.hpp here for their lane semantics).
+// Host emulation of the HIP subset that the library's kernels use, for running
+// their sources on the CPU in tests.  A workgroup's lanes run as cooperative
+// fibers on one OS thread, workgroups one after another.  A lane runs until it
+// reaches a barrier: the wave-wide one that every emulated cross-lane
+// operation passes through (values are exchanged in per-wave slots), or the
+// workgroup's.  A barrier opens once every lane it covers has arrived or has
+// finished (as on the hardware, finished lanes no longer hold a barrier); no
+// lane can pass one early, and a schedule in which no lane can move is
+// reported and aborts.  Under ThreadSanitizer or AddressSanitizer the fibers
+// are announced to the sanitizer, and a barrier is the only ordering between
+// lanes that ThreadSanitizer sees.
 #pragma once
-#include <barrier>
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <deque>
 #include <functional>
-#include <thread>
 #include <vector>
 
 #define __global__
@@ -22,6 +28,31 @@
 #define amdgpu_waves_per_eu(...) unused
 #define __shared__ static
 
+#if defined(__has_feature)
+#if __has_feature(thread_sanitizer)
+#define EMU_TSAN 1
+#endif
+#if __has_feature(address_sanitizer)
+#define EMU_ASAN 1
+#endif
+#endif
+#ifdef EMU_TSAN
+extern "C" void* __tsan_get_current_fiber(void);
+extern "C" void* __tsan_create_fiber(unsigned flags);
+extern "C" void __tsan_destroy_fiber(void* fiber);
+extern "C" void __tsan_switch_to_fiber(void* fiber, unsigned flags);
+extern "C" void __tsan_acquire(void* addr);
+extern "C" void __tsan_release(void* addr);
+extern "C" void AnnotateIgnoreReadsBegin(const char* file, int line);
+extern "C" void AnnotateIgnoreReadsEnd(const char* file, int line);
+extern "C" void AnnotateIgnoreWritesBegin(const char* file, int line);
+extern "C" void AnnotateIgnoreWritesEnd(const char* file, int line);
+#endif
+#ifdef EMU_ASAN
+extern "C" void __sanitizer_start_switch_fiber(void** fake_stack_save, const void* bottom, size_t size);
+extern "C" void __sanitizer_finish_switch_fiber(void* fake_stack_save, const void** bottom_old, size_t* size_old);
+#endif
+
 typedef int hipError_t;
 enum { hipSuccess = 0, hipErrorInvalidValue = 1 };
 typedef void* hipStream_t;
@@ -32,7 +63,6 @@ struct dim3 {
   dim3(unsigned a = 1, unsigned b = 1, unsigned c = 1) : x(a), y(b), z(c) {}
 };
 struct emu_idx { unsigned x, y, z; };
-inline thread_local emu_idx threadIdx, blockIdx;
 inline dim3 gridDim, blockDim;
 
 inline int min(int a, int b) { return a < b ? a : b; }
@@ -40,54 +70,264 @@ inline int max(int a, int b) { return a > b ? a : b; }
 inline float __int_as_float(int x) { float f; std::memcpy(&f, &x, 4); return f; }
 inline float __uint_as_float(unsigned x) { float f; std::memcpy(&f, &x, 4); return f; }
 
+// Saves the callee-saved registers on the current stack, stores its pointer at
+// *save and continues on the stack at next (System V x86-64).
+extern "C" void emu_swap_context(void** save, void* next);
+asm(R"(
+  .text
+  .weak emu_swap_context
+  .type emu_swap_context, @function
+emu_swap_context:
+  pushq %rbp
+  pushq %rbx
+  pushq %r12
+  pushq %r13
+  pushq %r14
+  pushq %r15
+  movq %rsp, (%rdi)
+  movq %rsi, %rsp
+  popq %r15
+  popq %r14
+  popq %r13
+  popq %r12
+  popq %rbx
+  popq %rbp
+  ret
+  .size emu_swap_context, .-emu_swap_context
+)");
+
 namespace emu {
+struct PendingDma {
+  char* dst;
+  unsigned char data[16];
+};
+struct Fiber {
+  void* sp = nullptr;
+  void* first_sp = nullptr;  // sp until the lane first runs
+  char* stack = nullptr;
+  emu_idx tid{0, 0, 0};
+  int state = 0;  // 0 runnable, 1 waiting at a barrier, 2 finished
+  int bar = -1;   // barrier waited at
+  unsigned gen = 0;
+  std::deque<PendingDma> dma;  // this lane's direct-to-LDS loads not yet landed, oldest first
+  void* tsan = nullptr;
+  void* asan_fake = nullptr;
+};
+struct Bar {
+  int participants = 0, arrived = 0;
+  unsigned gen = 0;
+};
+constexpr size_t kStack = 256 << 10;
 struct Block {
-  explicit Block(int threads) : all(threads) {}
-  std::barrier<> all;
-  std::barrier<> wave[4] = {std::barrier<>{64}, std::barrier<>{64}, std::barrier<>{64}, std::barrier<>{64}};
-  alignas(64) unsigned char slot[4][64][64];  // per wave, per lane: up to 64 bytes of exchange data
+  int n = 0, waves = 0;
+  std::vector<Bar> bars;  // one per wave, then the workgroup's
+  std::vector<unsigned char> slots;  // per wave, per lane: up to 64 bytes of exchange data
+  std::function<void()> body;
 };
 inline Block* g_block = nullptr;
+inline Fiber* g_cur = nullptr;
+inline std::vector<Fiber> g_fibers;
+inline std::vector<char*> g_stacks;
+inline void* g_sched_sp = nullptr;
+inline void* g_sched_tsan = nullptr;
+inline void* g_sched_fake = nullptr;
+inline const void* g_sched_bottom = nullptr;
+inline size_t g_sched_size = 0;
+}  // namespace emu
+
+namespace emu {
+inline Fiber* cur() { return __atomic_load_n(&g_cur, __ATOMIC_RELAXED); }
+inline char g_join;  // ThreadSanitizer: a finished workgroup's lanes release here, the scheduler acquires
+// ThreadSanitizer: the scheduler's bookkeeping is not kernel data; no race is reported on it
+inline void ignore_begin() {
+#ifdef EMU_TSAN
+  AnnotateIgnoreReadsBegin(__FILE__, __LINE__);
+  AnnotateIgnoreWritesBegin(__FILE__, __LINE__);
+#endif
+}
+inline void ignore_end() {
+#ifdef EMU_TSAN
+  AnnotateIgnoreWritesEnd(__FILE__, __LINE__);
+  AnnotateIgnoreReadsEnd(__FILE__, __LINE__);
+#endif
+}
+inline void tsan_release(void* p) {
+#ifdef EMU_TSAN
+  __tsan_release(p);
+#endif
+  (void)p;
+}
+inline void tsan_acquire(void* p) {
+#ifdef EMU_TSAN
+  __tsan_acquire(p);
+#endif
+  (void)p;
+}
+}  // namespace emu
+
+// threadIdx and blockIdx of the running lane
+#define threadIdx (emu::cur()->tid)
+inline emu_idx blockIdx;
+
+namespace emu {
+// scheduler -> fiber f, and back when it blocks or finishes; the first entry
+// into a lane orders the workgroup's set-up before it
+inline void enter(Fiber& f, bool first) {
+  __atomic_store_n(&g_cur, &f, __ATOMIC_RELAXED);
+#ifdef EMU_TSAN
+  __tsan_switch_to_fiber(f.tsan, first ? 0 : 1);
+#endif
+  (void)first;
+#ifdef EMU_ASAN
+  __sanitizer_start_switch_fiber(&g_sched_fake, f.stack, kStack);
+#endif
+  emu_swap_context(&g_sched_sp, f.sp);
+#ifdef EMU_ASAN
+  __sanitizer_finish_switch_fiber(g_sched_fake, nullptr, nullptr);
+#endif
+}
+inline void leave(bool finished) {
+  Fiber& f = *cur();
+#ifdef EMU_TSAN
+  __tsan_switch_to_fiber(__atomic_load_n(&g_sched_tsan, __ATOMIC_RELAXED), 1);
+#endif
+#ifdef EMU_ASAN
+  __sanitizer_start_switch_fiber(finished ? nullptr : &f.asan_fake, g_sched_bottom, g_sched_size);
+#endif
+  emu_swap_context(&f.sp, g_sched_sp);
+#ifdef EMU_ASAN
+  __sanitizer_finish_switch_fiber(f.asan_fake, nullptr, nullptr);
+#endif
+}
+inline void open_if_complete(Bar& b) {
+  if (b.arrived > 0 && b.arrived == b.participants) {
+    b.arrived = 0;
+    ++b.gen;
+  }
+}
+inline void arrive(int i) {
+  Bar& b = g_block->bars[i];
+  tsan_release(&b);
+  ignore_begin();
+  const bool last = ++b.arrived == b.participants;
+  if (last) {
+    open_if_complete(b);
+  } else {
+    Fiber& f = *cur();
+    f.state = 1;
+    f.bar = i;
+    f.gen = b.gen;
+  }
+  ignore_end();
+  if (!last) leave(false);
+  tsan_acquire(&b);
+}
+[[noreturn]] inline void fiber_main() {
+#ifdef EMU_ASAN
+  __sanitizer_finish_switch_fiber(nullptr, &g_sched_bottom, &g_sched_size);
+#endif
+  g_block->body();
+  Fiber& f = *cur();
+  for (int i : {(int)(f.tid.x / 64), g_block->waves}) tsan_release(&g_block->bars[i]);
+  tsan_release(&g_join);
+  ignore_begin();
+  f.state = 2;
+  f.dma.clear();  // loads never waited for: nothing reads them
+  for (int i : {(int)(f.tid.x / 64), g_block->waves}) {
+    Bar& b = g_block->bars[i];
+    --b.participants;
+    open_if_complete(b);
+  }
+  ignore_end();
+  leave(true);
+  std::abort();
+}
 
 template <class T>
 inline void deposit(const T& v) {
   static_assert(sizeof(T) <= 64, "slot size");
-  const int w = threadIdx.x / 64, l = threadIdx.x % 64;
-  std::memcpy(g_block->slot[w][l], &v, sizeof(T));
+  std::memcpy(&g_block->slots[(size_t)threadIdx.x * 64], &v, sizeof(T));
 }
 template <class T>
 inline T fetch(int lane) {
   T v;
-  std::memcpy(&v, g_block->slot[threadIdx.x / 64][lane], sizeof(T));
+  std::memcpy(&v, &g_block->slots[(size_t)((threadIdx.x / 64) * 64 + lane) * 64], sizeof(T));
   return v;
 }
-inline void wave_sync() { g_block->wave[threadIdx.x / 64].arrive_and_wait(); }
+inline void wave_sync() { arrive((int)(threadIdx.x / 64)); }
 
 template <class F, class... A>
 inline void launch(dim3 grid, dim3 block, F kernel, A... args) {
   gridDim = grid;
   blockDim = block;
+  const int n = (int)block.x;
+  while ((int)g_stacks.size() < n) g_stacks.push_back((char*)std::aligned_alloc(64, kStack));
+#ifdef EMU_TSAN
+  __atomic_store_n(&g_sched_tsan, __tsan_get_current_fiber(), __ATOMIC_RELAXED);
+#endif
+  ignore_begin();
+  g_fibers.resize(n);
   for (unsigned bz = 0; bz < grid.z; ++bz)
     for (unsigned by = 0; by < grid.y; ++by)
       for (unsigned bx = 0; bx < grid.x; ++bx) {
-        Block blk((int)block.x);
+        Block blk;
+        blk.n = n;
+        blk.waves = (n + 63) / 64;
+        blk.bars.resize(blk.waves + 1);
+        for (int w = 0; w < blk.waves; ++w) blk.bars[w].participants = min(64, n - 64 * w);
+        blk.bars[blk.waves].participants = n;
+        blk.slots.assign((size_t)blk.waves * 64 * 64, 0);
+        blk.body = [&] { kernel(args...); };
         g_block = &blk;
-        std::vector<std::thread> th;
-        th.reserve(block.x);
-        for (unsigned t = 0; t < block.x; ++t)
-          th.emplace_back([=] {
-            threadIdx = emu_idx{t, 0, 0};
-            blockIdx = emu_idx{bx, by, bz};
-            kernel(args...);
-          });
-        for (auto& x : th) x.join();
+        blockIdx = emu_idx{bx, by, bz};
+        for (int t = 0; t < n; ++t) {
+          Fiber& f = g_fibers[t];
+          f = Fiber{};
+          f.stack = g_stacks[t];
+          f.tid = emu_idx{(unsigned)t, 0, 0};
+          // initial frame: six zero registers, then fiber_main as the return address,
+          // then a zero return slot so that fiber_main starts with the ABI's alignment
+          uintptr_t top = ((uintptr_t)f.stack + kStack) & ~(uintptr_t)15;
+          void** sp = (void**)top;
+          *--sp = nullptr;
+          *--sp = (void*)&fiber_main;
+          for (int r = 0; r < 6; ++r) *--sp = nullptr;
+          f.sp = f.first_sp = sp;
+#ifdef EMU_TSAN
+          f.tsan = __tsan_create_fiber(0);
+#endif
+        }
+        int done = 0;
+        while (done < n) {
+          bool moved = false;
+          done = 0;
+          for (int t = 0; t < n; ++t) {
+            Fiber& f = g_fibers[t];
+            if (f.state == 1 && blk.bars[f.bar].gen != f.gen) f.state = 0;
+            if (f.state == 0) {
+              enter(f, f.sp == f.first_sp);
+              moved = true;
+            }
+            done += f.state == 2;
+          }
+          if (!moved && done < n) {
+            std::fprintf(stderr, "emulation: no lane can move (block %u,%u,%u)\n", bx, by, bz);
+            std::abort();
+          }
+        }
+        tsan_acquire(&g_join);
+#ifdef EMU_TSAN
+        for (int t = 0; t < n; ++t) __tsan_destroy_fiber(g_fibers[t].tsan);
+#endif
         g_block = nullptr;
+        __atomic_store_n(&g_cur, (Fiber*)nullptr, __ATOMIC_RELAXED);
       }
+  ignore_end();
 }
 }  // namespace emu
 
 #define hipLaunchKernelGGL(K, GRID, BLOCK, SHMEM, STREAM, ...) emu::launch(GRID, BLOCK, K, __VA_ARGS__)
-inline void __syncthreads() { emu::g_block->all.arrive_and_wait(); }
+inline void __syncthreads() { emu::arrive(emu::g_block->waves); }
 
 // ---- builtins of the GEMM core and the epilogues
 namespace emu {
@@ -143,23 +383,19 @@ inline bool any(bool x) {
 // leaves fewer of this lane's loads outstanding, the latest the hardware may
 // land it (other vector-memory operations would only make a wait stricter), so
 // a missing or too-loose wait leaves stale LDS bytes for the readers to see.
-struct PendingDma {
-  char* dst;
-  unsigned char data[16];
-};
-inline thread_local std::deque<PendingDma> t_dma;  // this lane's loads not yet landed, oldest first
 inline void dma16(u32x4 desc, uint32_t off, uint32_t lds_addr) {
   const char* base = (const char*)(uintptr_t)((uint64_t)desc[0] | ((uint64_t)(desc[1] & 0xffffu) << 32));
   PendingDma p;
   p.dst = (char*)(uintptr_t)lds_addr + 16 * (threadIdx.x % 64);
   if ((uint64_t)off + 16 <= (uint64_t)desc[2]) std::memcpy(p.data, base + off, 16);
   else std::memset(p.data, 0, 16);
-  t_dma.push_back(p);
+  cur()->dma.push_back(p);
 }
 inline void wait_vmcnt(unsigned n) {
-  while (t_dma.size() > n) {
-    std::memcpy(t_dma.front().dst, t_dma.front().data, 16);
-    t_dma.pop_front();
+  auto& q = cur()->dma;
+  while (q.size() > n) {
+    std::memcpy(q.front().dst, q.front().data, 16);
+    q.pop_front();
   }
 }
 

@@ -2,8 +2,8 @@
 on the CPU (host emulation).
 
 attention.hip and fingerprint.hip are compiled unmodified for the host with
-tests/cpu_emu: one OS thread per lane, one workgroup at a time, std::barrier
-for the workgroup barrier, and the three cross-lane operations the attention
+tests/cpu_emu: each lane a fiber, one workgroup at a time, lanes meeting at
+the workgroup barrier, and the three cross-lane operations the attention
 kernels use emulated with their lane semantics:
   * v_mfma_f32_16x16x32_bf16 - lane l supplies row l%16, k = 8(l/16) .. +7 of
     the first operand and column l%16 of the second, and receives

@@ -2,10 +2,10 @@
 
 tests/cpu_emu/prep.py copies every kernel source of the library (the GEMM core
 and its epilogues included), replacing each inline-assembly statement by its
-emulated meaning; tests/cpu_emu/hip/hip_runtime.h runs each workgroup as one OS
-thread per lane with emulated MFMA, direct-to-LDS loads, transposing LDS reads,
-buffer resources (out-of-range loads read zero, stores are dropped) and lane
-exchanges.  tests/cpu_emu/lib_driver.cpp calls the library's own launch
+emulated meaning; tests/cpu_emu/hip/hip_runtime.h runs each workgroup's lanes
+as fibers that meet at barriers, with emulated MFMA, direct-to-LDS loads,
+transposing LDS reads, buffer resources (out-of-range loads read zero, stores
+are dropped) and lane exchanges.  tests/cpu_emu/lib_driver.cpp calls the library's own launch
 functions (kernels.hip, attention.hip): the same launch plans, workspace
 layouts, paired and split-K launches, grids and kernel arguments as on the GPU.
 
@@ -250,8 +250,8 @@ def test_library_emulated_under_sanitizer(tmp_path, sanitizer):
     are checked against the resource's extent, which must lie inside the
     allocation too).
     thread: every exchange between waves through LDS or memory is ordered by a
-    workgroup barrier (lanes run as threads, and a wave's lanes meet at each
-    emulated wave-wide operation), and the main loop's vector-memory waits
+    workgroup barrier (each lane is a fiber that the sanitizer tracks like a
+    thread, and a wave's lanes meet at each emulated wave-wide operation), and the main loop's vector-memory waits
     land each direct-to-LDS load before its readers' barrier: a wave's loads
     are held back until its own wait requires them, so a missing barrier or a
     too-loose wait shows up as a race on LDS."""
