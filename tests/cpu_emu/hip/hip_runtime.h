@@ -122,6 +122,7 @@ struct Block {
   int n = 0, waves = 0;
   std::vector<Bar> bars;  // one per wave, then the workgroup's
   std::vector<unsigned char> slots;  // per wave, per lane: up to 64 bytes of exchange data
+  std::vector<float> results;        // per wave: one 16 x 16 MFMA result block
   std::function<void()> body;
 };
 inline Block* g_block = nullptr;
@@ -255,6 +256,7 @@ inline T fetch(int lane) {
   return v;
 }
 inline void wave_sync() { arrive((int)(threadIdx.x / 64)); }
+inline float* wave_result() { return &g_block->results[(size_t)(threadIdx.x / 64) * 256]; }
 
 template <class F, class... A>
 inline void launch(dim3 grid, dim3 block, F kernel, A... args) {
@@ -267,9 +269,27 @@ inline void launch(dim3 grid, dim3 block, F kernel, A... args) {
 #endif
   ignore_begin();
   g_fibers.resize(n);
+  // EMU_SAMPLE=k: a GEMM launch (a kernel taking a GemmGeom) or a launch over a
+  // 2-D or 3-D grid (the attention cores) of more than 16k workgroups runs only
+  // k at each end of its linear workgroup order and k spread evenly between:
+  // full-size shapes checked on a sample, the outputs of the others left as
+  // they were.  Every other launch (the small per-token and reduction
+  // kernels) runs in full.
+  const uint64_t G = (uint64_t)grid.x * grid.y * grid.z;
+  const char* env = std::getenv("EMU_SAMPLE");
+  const bool may_sample = grid.y * grid.z > 1 || std::strstr(__PRETTY_FUNCTION__, "GemmGeom");
+  const uint64_t k = env && may_sample ? std::strtoull(env, nullptr, 10) : 0;
+  auto sampled = [&](uint64_t lin) {
+    if (k == 0 || G <= 16 * k) return true;
+    if (lin < k || lin >= G - k) return true;
+    for (uint64_t i = 1; i <= k; ++i)
+      if (lin == i * G / (k + 1)) return true;
+    return false;
+  };
   for (unsigned bz = 0; bz < grid.z; ++bz)
     for (unsigned by = 0; by < grid.y; ++by)
       for (unsigned bx = 0; bx < grid.x; ++bx) {
+        if (!sampled(bx + (uint64_t)grid.x * (by + (uint64_t)grid.y * bz))) continue;
         Block blk;
         blk.n = n;
         blk.waves = (n + 63) / 64;
@@ -277,6 +297,7 @@ inline void launch(dim3 grid, dim3 block, F kernel, A... args) {
         for (int w = 0; w < blk.waves; ++w) blk.bars[w].participants = min(64, n - 64 * w);
         blk.bars[blk.waves].participants = n;
         blk.slots.assign((size_t)blk.waves * 64 * 64, 0);
+        blk.results.assign((size_t)blk.waves * 256, 0.f);
         blk.body = [&] { kernel(args...); };
         g_block = &blk;
         blockIdx = emu_idx{bx, by, bz};
@@ -417,30 +438,41 @@ inline uint32_t pack_bf16x2_rne(float lo, float hi) { return bf16_rne(lo) | (bf1
 
 // v_mfma_f32_16x16x32_bf16 on any 16-byte operand type holding bf16 bit
 // patterns: lane l supplies row l%16, k = 8(l/16) .. +7 of the first operand and
-// column l%16 of the second; it receives D[4(l/16) + r][l%16].
+// column l%16 of the second; it receives C[r] + D[4(l/16) + r][l%16], with D's
+// sum over k formed in k order.  The wave's lane 0 forms its 16 x 16 block D once.
+// (ThreadSanitizer leaves this function's accesses, which are the emulation's
+// own exchange data, unchecked: the operands come from registers.)
 template <class V, class A>
-inline A mfma16x16x32(const V& a, const V& b, const A& c) {
+__attribute__((no_sanitize("thread"))) inline A mfma16x16x32(const V& a, const V& b, const A& c) {
   typedef unsigned short us8 __attribute__((ext_vector_type(8)));
   struct Ops { us8 a, b; };
   deposit(Ops{__builtin_bit_cast(us8, a), __builtin_bit_cast(us8, b)});
   wave_sync();
-  const int l = threadIdx.x % 64, g = l / 16, col = l % 16;
-  float av[4][32], bv[32];
-  for (int q = 0; q < 4; ++q) {
-    const us8 bq = fetch<Ops>(col + 16 * q).b;
-    for (int e = 0; e < 8; ++e) bv[8 * q + e] = bf16f(bq[e]);
-    for (int r = 0; r < 4; ++r) {
-      const us8 aq = fetch<Ops>(4 * g + r + 16 * q).a;
-      for (int e = 0; e < 8; ++e) av[r][8 * q + e] = bf16f(aq[e]);
+  const int l = threadIdx.x % 64;
+  if (l == 0) {
+    // bf16 products are exact in fp32, so only the order of the additions matters:
+    // each of the 16 columns j (one vector lane each) adds its 32 products in k order
+    typedef float f32x16 __attribute__((ext_vector_type(16)));
+    float av[16][32];
+    f32x16 bk[32];
+    for (int src = 0; src < 64; ++src) {
+      const Ops o = fetch<Ops>(src);
+      for (int e = 0; e < 8; ++e) {
+        av[src % 16][8 * (src / 16) + e] = bf16f(o.a[e]);
+        bk[8 * (src / 16) + e][src % 16] = bf16f(o.b[e]);
+      }
+    }
+    float* d = wave_result();
+    for (int i = 0; i < 16; ++i) {
+      f32x16 acc = 0.f;
+      for (int k = 0; k < 32; ++k) acc += av[i][k] * bk[k];
+      std::memcpy(d + 16 * i, &acc, sizeof(acc));
     }
   }
   wave_sync();
+  const float* d = wave_result();
   A out = c;
-  for (int r = 0; r < 4; ++r) {
-    float acc = 0.f;
-    for (int k = 0; k < 32; ++k) acc += av[r][k] * bv[k];
-    out[r] += acc;
-  }
+  for (int r = 0; r < 4; ++r) out[r] += d[16 * (4 * (l / 16) + r) + l % 16];
   return out;
 }
 

@@ -2,7 +2,8 @@
 // with the kernel sources prepared by prep.py and the HIP subset of
 // hip/hip_runtime.h.  Every buffer is a file of raw little-endian values in the
 // case directory; outputs and the workspace start filled with 0xff bytes (NaN
-// in bf16 and fp32), so an element a kernel fails to write shows up.
+// in bf16 and fp32), so an element a kernel fails to write shows up.  With
+// EMU_WRITE_DL set, ce_bwd also writes the logit gradient from its workspace.
 //   lib_driver mlp_fwd  T h f gelu bias dir : X A [b1] B              -> H Y Z
 //   lib_driver mlp_bwd  T h f gelu bias dir : X A B H Y dZ            -> dX dA dB [db1]
 //   lib_driver ce_fwd   T h v vstart dir    : X E target              -> m s z
@@ -10,8 +11,10 @@
 //   lib_driver combine  t T dir             : m s z                   -> loss mean
 //   lib_driver attn_fwd b s h n d causal dir: X Wqkv Wo               -> QKV O lse Z
 //   lib_driver attn_bwd b s h n d causal dir: X Wqkv Wo QKV O lse dZ  -> dX dWqkv dWo
+//   lib_driver attn_core b s n d causal dir : qkv dout                -> o lse dqkv (the core alone)
 //   lib_driver fingerprint bytes chunk dir  : buf                     -> fp (1 + chunks words)
 //   lib_driver plan     T h f v b s n d dir : prints the backward launch plans of these shapes
+#include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <string>
@@ -102,6 +105,11 @@ int main(int argc, char** argv) {
                                    P<uint16_t>(dE), ws.data(), nullptr),
        "launch_vocab_ce_bwd");
     wr("dX", dX, T * h * 4), wr("dE", dE, h * v * 2);
+    if (std::getenv("EMU_WRITE_DL")) {  // the logit gradient, from the workspace
+      std::vector<char> dL(ws.begin() + mshard::ce_bwd_workspace_layout(T, h, v).off_dL,
+                           ws.begin() + mshard::ce_bwd_workspace_layout(T, h, v).off_dL + T * v * 2);
+      wr("dL", dL, T * v * 2);
+    }
   } else if (op == "combine") {
     const int64_t t = I(0), T = I(1);
     auto m = rd("m", t * T * 4), s = rd("s", t * T * 4), z = rd("z", t * T * 4);
@@ -131,6 +139,19 @@ int main(int argc, char** argv) {
          "launch_attn_bwd");
       wr("dX", dX, T * h * 4), wr("dWqkv", dWqkv, h * 3 * nd * 2), wr("dWo", dWo, nd * h * 2);
     }
+  } else if (op == "attn_core") {
+    const int64_t b = I(0), s = I(1), n = I(2), d = I(3), causal = I(4);
+    const int64_t T = b * s, nd = n * d;
+    auto qkv = rd("qkv", T * 3 * nd * 2), dout = rd("dout", T * nd * 2);
+    auto o = out(T * nd * 2), lse = out(n * T * 4), delta = out(n * T * 4), dqkv = out(T * 3 * nd * 2);
+    mshard::AttnGeom g{(int)b, (int)s, (int)n, (int)d, (int)(3 * nd), (int)nd,
+                       (float)(1.4426950408889634 / std::sqrt((double)d))};
+    ok(mshard::launch_attn_core_fwd(g, causal != 0, C<uint16_t>(qkv), P<uint16_t>(o), P<float>(lse), nullptr),
+       "launch_attn_core_fwd");
+    ok(mshard::launch_attn_core_bwd(g, causal != 0, C<uint16_t>(qkv), C<uint16_t>(o), C<uint16_t>(dout), C<float>(lse),
+                                    P<float>(delta), P<uint16_t>(dqkv), nullptr),
+       "launch_attn_core_bwd");
+    wr("o", o, T * nd * 2), wr("lse", lse, n * T * 4), wr("dqkv", dqkv, T * 3 * nd * 2);
   } else if (op == "fingerprint") {
     const int64_t bytes = I(0), chunk = I(1);
     const uint64_t words = 1 + mshard::fingerprint_chunk_count(bytes, chunk);

@@ -268,3 +268,100 @@ def test_library_emulated_under_sanitizer(tmp_path, sanitizer):
         fingerprint_case(exe, d, 0, 64)
     else:
         attn_case(exe, d, 1, 130, 128, 2, 64, False)
+
+
+FULL = os.environ.get("MSHARD_FULL_SIZE_EMULATION") == "1"
+
+
+@pytest.fixture(scope="module")
+def lib_asan(tmp_path_factory):
+    if not os.path.exists(CLANG):
+        pytest.skip("clang++ not found")
+    d = str(tmp_path_factory.mktemp("libemu_asan"))
+    return build(d, sanitize="address"), d
+
+
+def sampled_rel_fro(got, want_fn):
+    """Relative Frobenius error over the entries the sampled workgroups wrote
+    (the others stay NaN); want_fn(rows, cols) gives the oracle on that grid."""
+    ok = ~np.isnan(got)
+    rows, cols = np.nonzero(ok.any(axis=1))[0], np.nonzero(ok.any(axis=0))[0]
+    assert len(rows) and len(cols)
+    want = want_fn(rows, cols)
+    sub, msk = got[np.ix_(rows, cols)], ok[np.ix_(rows, cols)]
+    return np.linalg.norm((sub - want)[msk]) / np.linalg.norm(want[msk]), want, sub, msk
+
+
+@pytest.mark.skipif(not FULL, reason="minutes of CPU and up to 8 GB of memory: set MSHARD_FULL_SIZE_EMULATION=1")
+@pytest.mark.parametrize("name", ["gpt2_1p5b", "gpt_8p3b_t8", "bert_3p9b_t4", "bloom_176b_t4"])
+def test_full_size_sampled_under_address_sanitizer(lib_asan, name):
+    """The CE backward and the attention shard at each workload's real shard shape,
+    under AddressSanitizer, with every GEMM and attention-core launch cut down to
+    six of its workgroups (two at each end of its workgroup order, two between;
+    the small per-token kernels run in full).  Every launch of both sequences
+    runs with the real grids, strides and workspace layout, and no access leaves
+    its allocation.  The values of the first stage of each sequence are checked
+    where the sampled workgroups wrote them: the logit gradient dL (with given
+    row statistics, so that its softmax term is not negligible), the QKV
+    projection, and the attention core's output on random full-size QKV."""
+    exe, d = lib_asan
+    env = dict(os.environ, EMU_SAMPLE="2", EMU_WRITE_DL="1")
+
+    def go(case, *args):
+        subprocess.run([exe, *[str(a) for a in args], case], check=True, timeout=3000,
+                       env=dict(env, ASAN_OPTIONS="detect_leaks=0:halt_on_error=1:exitcode=23"))
+
+    # vocab-parallel CE backward of rank 0
+    c = inputs.CONFIGS[name]
+    x = inputs.make_config_inputs(c, want=("X", "E", "targets"))
+    T, h, v, t = c.T, c.h, c.v_i, c.t
+    g = np.random.default_rng(7)
+    m = (0.1 * g.standard_normal((t, T))).astype(np.float32)
+    s = (20 * (1 + 0.1 * g.random((t, T)))).astype(np.float32)
+    case = os.path.join(d, f"full_ce_{name}")
+    put(case, X=x["X"], E=x["E"], target=x["targets"], m=m, s=s)
+    scale = float(np.float32(1.0 / T))
+    go(case, "ce_bwd", T, h, v, 0, t, repr(scale), 0)
+    st = oracle.ce_row_stats(m, s)
+    err, want, sub, msk = sampled_rel_fro(
+        get(case, "dL", np.uint16, (T, v)),
+        lambda r, cl: oracle.ref._ce_grad_block(f64(x["X"][r]) @ f64(x["E"][:, cl]), st["M"][r], st["S"][r],
+                                                np.full(len(r), scale), x["targets"][r], 0, cl))
+    soft = msk & (want > 0)
+    assert err <= TOL
+    assert np.linalg.norm((sub - want)[soft]) / np.linalg.norm(want[soft]) <= TOL
+    del x
+    subprocess.run(["rm", "-rf", case], check=True)
+
+    # attention shard, and its core alone on random full-size QKV
+    a_cfg = inputs.ATTN_CONFIGS[name]
+    b, sq, hh, n, hd, causal = a_cfg.b, a_cfg.s, a_cfg.h, a_cfg.n, a_cfg.d, a_cfg.causal
+    a = inputs.make_attn_config_inputs(a_cfg)
+    case = os.path.join(d, f"full_attn_{name}")
+    put(case, X=a["X"], Wqkv=a["Wqkv"], Wo=a["Wo"], dZ=a["dZ"])
+    go(case, "attn_fwd", b, sq, hh, n, hd, int(causal))
+    go(case, "attn_bwd", b, sq, hh, n, hd, int(causal))
+    T, nd = b * sq, n * hd
+    err = sampled_rel_fro(get(case, "QKV", np.uint16, (T, 3 * nd)),
+                          lambda r, cl: f64(a["X"][r]) @ f64(a["Wqkv"][:, cl]))[0]
+    assert err <= TOL
+    subprocess.run(["rm", "-rf", case], check=True)
+    g = np.random.default_rng(3)
+    q = inputs.round_to_bf16_bits(g.standard_normal((T, 3 * nd)).astype(np.float32))
+    do = inputs.round_to_bf16_bits(g.standard_normal((T, nd)).astype(np.float32))
+    case = os.path.join(d, f"full_core_{name}")
+    put(case, qkv=q, dout=do)
+    go(case, "attn_core", b, sq, n, hd, int(causal))
+    O = get(case, "o", np.uint16, (T, nd))
+    Q, K, V = f64(q[:, :nd]), f64(q[:, nd:2 * nd]), f64(q[:, 2 * nd:])
+    pairs = 0
+    for bi in range(b):
+        for j in range(n):
+            rs, cs = slice(bi * sq, (bi + 1) * sq), slice(j * hd, (j + 1) * hd)
+            okr = ~np.isnan(O[rs, cs]).any(axis=1)
+            if okr.any():
+                w = attn.attention_core(Q[rs, cs], K[rs, cs], V[rs, cs], 1, hd, 1, sq, causal)["O"]
+                assert rel_fro(O[rs, cs][okr], w[okr]) <= TOL
+                pairs += 1
+    assert pairs > 0
+    subprocess.run(["rm", "-rf", case], check=True)
