@@ -55,6 +55,7 @@ def _args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle CPU time")
     p.add_argument("--no-breakdown", action="store_true", help="skip the per-GEMM breakdown pass")
+    p.add_argument("--rows", default="", help="comma list of further rows timed after the step: ce_bwd, attn")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain device copy of 1 GiB (5 launches) and exit")
     return p.parse_args()
@@ -238,6 +239,63 @@ def main():
         kernels_us = {n: round(1e3 * float(np.mean([kev[r][i][0].elapsed_time(kev[r][i][1]) for r in range(reps)])), 1)
                       for i, n in enumerate(names)}
 
+    rows = [r for r in a.rows.split(",") if r]
+    unknown = sorted(set(rows) - {"ce_bwd", "attn"})
+    if unknown:
+        sys.exit(f"bench.py: unknown --rows entries {unknown} (known: ce_bwd, attn)")
+    extra = {}
+
+    def timed(fn, reps):
+        for _ in range(a.warmup):
+            fn()
+        evs = [(ev(), ev()) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for e0, e1 in evs:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+
+    if "ce_bwd" in rows:
+        ce_bwd_ws = torch.empty(max(mshard.vocab_ce_bwd_workspace_bytes(T, h, v), 1), dtype=torch.uint8, device=dev)
+        dXc = torch.empty((T, h), dtype=torch.float32, device=dev)
+        dEc = torch.empty((h, v), dtype=bf, device=dev)
+        ms_ce = timed(lambda: mshard.vocab_ce_shard_bwd(X, E, tg, m, s, vstart, workspace=ce_bwd_ws, out=(dXc, dEc)),
+                      a.steps)
+        flop = 3 * 2 * T * h * v  # logits recompute, dX = dL E^T, dE = X^T dL
+        extra["ce_bwd"] = {"ms": round(ms_ce, 4), "tflops": round(flop / (ms_ce * 1e-3) / 1e12, 2),
+                           "pct_of_peak": round(100 * flop / (ms_ce * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                           "algorithmic_flop": flop}
+    if "attn" in rows:
+        ac = inputs.ATTN_CONFIGS[cfg.name]
+        ad = inputs.make_attn_config_inputs(ac)
+        Xa, Wqkv, Wo, dZa = up(ad["X"]), up(ad["Wqkv"]), up(ad["Wo"]), up(ad["dZ"])
+        nd = ac.n * ac.d
+        QKV = torch.empty((T, 3 * nd), dtype=bf, device=dev)
+        Oa = torch.empty((T, nd), dtype=bf, device=dev)
+        lse = torch.empty((ac.n, T), dtype=torch.float32, device=dev)
+        Za = torch.empty((T, h), dtype=torch.float32, device=dev)
+        dXa = torch.empty((T, h), dtype=torch.float32, device=dev)
+        dWqkv = torch.empty((h, 3 * nd), dtype=bf, device=dev)
+        dWo = torch.empty((nd, h), dtype=bf, device=dev)
+        attn_ws = torch.empty(max(mshard.attn_shard_workspace_bytes(ac.b, ac.s, h, ac.n, ac.d), 1), dtype=torch.uint8,
+                              device=dev)
+        fwd = lambda: mshard.attn_shard_fwd(Xa, Wqkv, Wo, ac.b, ac.s, ac.n, ac.d, ac.causal, out=(QKV, Oa, lse, Za))
+        bwd = lambda: mshard.attn_shard_bwd(Xa, Wqkv, Wo, QKV, Oa, lse, dZa, ac.b, ac.s, ac.n, ac.d, ac.causal,
+                                            workspace=attn_ws, out=(dXa, dWqkv, dWo))
+        ms_f = timed(fwd, a.steps)
+        ms_b = timed(bwd, a.steps)
+        pairs = ac.b * ac.n * (ac.s * (ac.s + 1) // 2 if ac.causal else ac.s * ac.s)  # visible (query, key) pairs
+        proj = 2 * T * h * 3 * nd + 2 * T * nd * h
+        f_flop = proj + 4 * pairs * ac.d            # projections; S and P V
+        b_flop = 2 * proj + 8 * pairs * ac.d        # their gradients; dV, dP, dQ, dK (recompute not counted)
+        extra["attn"] = {"config": f"b={ac.b} s={ac.s} h={h} n={ac.n} d={ac.d} causal={ac.causal}",
+                         "fwd_ms": round(ms_f, 4), "bwd_ms": round(ms_b, 4),
+                         "fwd_tflops": round(f_flop / (ms_f * 1e-3) / 1e12, 2),
+                         "bwd_tflops": round(b_flop / (ms_b * 1e-3) / 1e12, 2),
+                         "algorithmic_flop": {"fwd": f_flop, "bwd": b_flop}}
+
     traffic, traffic_src = committed_traffic(cfg.name)
     out = {
         "metric": "MLP-shard fwd+bwd TFLOP/s + fused vocab-CE tokens/s, % of bf16 MFMA peak",
@@ -270,6 +328,7 @@ def main():
                      "algorithmic_flop_per_launch": ce_flop},
         "kernels_us": kernels_us,
     }
+    out.update(extra)
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, d, a.cpu_seconds)
     print(json.dumps(out), flush=True)
