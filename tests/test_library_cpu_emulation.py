@@ -183,11 +183,13 @@ def test_vocab_ce_bwd_split_k_emulated(lib):
     assert rel_fro(get(case, "dE", np.uint16, (h, v)), ob["dE"]) <= TOL
 
 
-# b, s, h, n, d, causal: the tiny layer, ragged sequences, every head size, and
-# a token count whose weight gradients are split over K
+# b, s, h, n, d, causal: the tiny layer, ragged sequences, every head size the
+# kernels are built for (32, 64, 96, 128) and the ones padded up to them (16, 48,
+# 80, 112), and a token count whose weight gradients are split over K
 @pytest.mark.parametrize("b,s,h,n,hd,causal", [
     (2, 32, 64, 4, 16, True), (2, 70, 96, 3, 32, True), (1, 130, 128, 2, 64, False), (1, 96, 192, 2, 96, True),
-    (1, 64, 256, 2, 128, False), (3, 1, 64, 2, 32, True), (2, 550, 128, 1, 64, True)])
+    (1, 64, 256, 2, 128, False), (3, 1, 64, 2, 32, True), (2, 550, 128, 1, 64, True),
+    (1, 150, 96, 2, 48, True), (2, 70, 160, 2, 80, False), (1, 140, 224, 2, 112, True)])
 def test_attn_shard_emulated(lib, b, s, h, n, hd, causal):
     attn_case(*lib, b, s, h, n, hd, causal)
 

@@ -68,6 +68,9 @@ def run_and_check(ms, d, b, s, n, hd, causal):
     (1, 64, 256, 2, 128, False),   # head size 128
     (3, 1, 64, 2, 32, True),       # one token per sequence
     (1, 300, 64, 1, 64, True),     # three query blocks, causal skipping
+    (1, 150, 96, 2, 48, True),     # head sizes padded up to the built ones: 48 -> 64
+    (2, 70, 160, 2, 80, False),    # 80 -> 96
+    (1, 140, 224, 2, 112, True),   # 112 -> 128
 ])
 def test_attn_full(ms, b, s, h, n, hd, causal):
     print(f"case attn b={b} s={s} h={h} n={n} d={hd} causal={causal}", flush=True)
