@@ -12,6 +12,7 @@ Entry points mirror the C ABI in include/mshard.h:
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional, Tuple
@@ -112,10 +113,14 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+# Device type every tensor must have (HIP devices are "cuda" in PyTorch-ROCm).
+_DEVICE_TYPE = "cuda"
+
+
 def _dev(t: torch.Tensor, name: str, dtype, shape) -> None:
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
+    if t.device.type != _DEVICE_TYPE:
         raise ValueError(f"{name} must be on a HIP device (got {t.device})")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
@@ -123,6 +128,41 @@ def _dev(t: torch.Tensor, name: str, dtype, shape) -> None:
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _outs(out, specs, device):
+    """Caller-supplied outputs: the library writes every byte of each one, so each
+    must have exactly the shape and dtype it would have been allocated with, be
+    contiguous and sit on the inputs' device.  ``specs`` holds (name, dtype, shape,
+    optional); an optional output may be None."""
+    if len(out) != len(specs):
+        raise ValueError(f"out must hold {len(specs)} tensors ({', '.join(n for n, *_ in specs)})")
+    for t, (name, dtype, shape, optional) in zip(out, specs):
+        if t is None:
+            if not optional:
+                raise ValueError(f"out: {name} is required")
+            continue
+        _dev(t, name, dtype, shape)
+        if t.device != device:
+            raise ValueError(f"out: {name} is on {t.device}, the inputs on {device}")
+    return out
+
+
+def _same_device(device, **tensors) -> None:
+    for name, t in tensors.items():
+        if t is not None and t.device != device:
+            raise ValueError(f"{name} is on {t.device}, X on {device}: every tensor must be on one device")
+
+
+def _on(device):
+    """The library launches on the current device: make it the tensors' one."""
+    return torch.cuda.device(device) if device.type == "cuda" else contextlib.nullcontext()
+
+
+def _gelu(gelu: str) -> int:
+    if gelu not in GELU:
+        raise ValueError(f"gelu must be one of {sorted(GELU)} (got {gelu!r})")
+    return GELU[gelu]
 
 
 def _stream(device) -> int:
@@ -149,8 +189,9 @@ def _workspace(nbytes: int, device, given: Optional[torch.Tensor]) -> Optional[t
     if nbytes == 0:
         return given
     if given is not None:
-        if given.device != device or given.numel() * given.element_size() < nbytes:
-            raise ValueError(f"workspace must be >= {nbytes} bytes on {device}")
+        if (not isinstance(given, torch.Tensor) or given.device != device or not given.is_contiguous()
+                or given.numel() * given.element_size() < nbytes):
+            raise ValueError(f"workspace must be a contiguous tensor of >= {nbytes} bytes on {device}")
         return given
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
@@ -164,14 +205,17 @@ def mlp_shard_fwd(X: torch.Tensor, A_i: torch.Tensor, B_i: torch.Tensor, b1_i: O
     _dev(X, "X", bf, (T, h)); _dev(A_i, "A_i", bf, (h, f_i)); _dev(B_i, "B_i", bf, (f_i, h))
     if b1_i is not None:
         _dev(b1_i, "b1_i", bf, (f_i,))
+    _same_device(X.device, A_i=A_i, B_i=B_i, b1_i=b1_i)
     if out is None:
         H = torch.empty((T, f_i), dtype=bf, device=X.device)
         Y = torch.empty((T, f_i), dtype=bf, device=X.device)
         Z = torch.empty((T, h), dtype=torch.float32, device=X.device)
     else:
-        H, Y, Z = out
-    st = LIB.mlp_shard_fwd(_ptr(X), _ptr(A_i), _ptr(b1_i), _ptr(B_i), T, h, f_i, GELU[gelu],
-                           _ptr(H), _ptr(Y), _ptr(Z), None, 0, _stream(X.device))
+        H, Y, Z = _outs(out, (("H", bf, (T, f_i), False), ("Y", bf, (T, f_i), False),
+                              ("Z", torch.float32, (T, h), False)), X.device)
+    with _on(X.device):
+        st = LIB.mlp_shard_fwd(_ptr(X), _ptr(A_i), _ptr(b1_i), _ptr(B_i), T, h, f_i, _gelu(gelu),
+                               _ptr(H), _ptr(Y), _ptr(Z), None, 0, _stream(X.device))
     _check(st, "mlp_shard_fwd")
     return H, Y, Z
 
@@ -185,17 +229,20 @@ def mlp_shard_bwd(X, A_i, B_i, H_i, Y_i, dZ, gelu: str = "erf", want_db1: bool =
     for t, n, s in ((X, "X", (T, h)), (A_i, "A_i", (h, f_i)), (B_i, "B_i", (f_i, h)), (H_i, "H_i", (T, f_i)),
                     (Y_i, "Y_i", (T, f_i)), (dZ, "dZ", (T, h))):
         _dev(t, n, bf, s)
+    _same_device(X.device, A_i=A_i, B_i=B_i, H_i=H_i, Y_i=Y_i, dZ=dZ)
     if out is None:
         dX = torch.empty((T, h), dtype=torch.float32, device=X.device)
         dA = torch.empty((h, f_i), dtype=bf, device=X.device)
         dB = torch.empty((f_i, h), dtype=bf, device=X.device)
         db1 = torch.empty((f_i,), dtype=bf, device=X.device) if want_db1 else None
     else:
-        dX, dA, dB, db1 = out
+        dX, dA, dB, db1 = _outs(out, (("dX", torch.float32, (T, h), False), ("dA", bf, (h, f_i), False),
+                                      ("dB", bf, (f_i, h), False), ("db1", bf, (f_i,), True)), X.device)
     nbytes = mlp_shard_workspace_bytes(T, h, f_i)
     ws = _workspace(nbytes, X.device, workspace)
-    st = LIB.mlp_shard_bwd(_ptr(X), _ptr(A_i), _ptr(B_i), _ptr(H_i), _ptr(Y_i), _ptr(dZ), T, h, f_i, GELU[gelu],
-                           _ptr(dX), _ptr(dA), _ptr(dB), _ptr(db1), _ptr(ws), nbytes, _stream(X.device))
+    with _on(X.device):
+        st = LIB.mlp_shard_bwd(_ptr(X), _ptr(A_i), _ptr(B_i), _ptr(H_i), _ptr(Y_i), _ptr(dZ), T, h, f_i, _gelu(gelu),
+                               _ptr(dX), _ptr(dA), _ptr(dB), _ptr(db1), _ptr(ws), nbytes, _stream(X.device))
     _check(st, "mlp_shard_bwd")
     return dX, dA, dB, db1
 
@@ -206,14 +253,16 @@ def vocab_ce_shard_fwd(X, E_i, target, vocab_start: int, workspace: Optional[tor
     v_i = E_i.shape[1]
     _dev(X, "X", torch.bfloat16, (T, h)); _dev(E_i, "E_i", torch.bfloat16, (h, v_i))
     _dev(target, "target", torch.int64, (T,))
+    _same_device(X.device, E_i=E_i, target=target)
     if out is None:
         m, s, z = (torch.empty((T,), dtype=torch.float32, device=X.device) for _ in range(3))
     else:
-        m, s, z = out
+        m, s, z = _outs(out, tuple((n, torch.float32, (T,), False) for n in ("m", "s", "z")), X.device)
     nbytes = vocab_ce_workspace_bytes(T, h, v_i)
     ws = _workspace(nbytes, X.device, workspace)
-    st = LIB.vocab_ce_shard_fwd(_ptr(X), _ptr(E_i), _ptr(target), T, h, v_i, int(vocab_start), _ptr(m), _ptr(s),
-                                _ptr(z), _ptr(ws), nbytes, _stream(X.device))
+    with _on(X.device):
+        st = LIB.vocab_ce_shard_fwd(_ptr(X), _ptr(E_i), _ptr(target), T, h, v_i, int(vocab_start), _ptr(m), _ptr(s),
+                                    _ptr(z), _ptr(ws), nbytes, _stream(X.device))
     _check(st, "vocab_ce_shard_fwd")
     return m, s, z
 
@@ -223,12 +272,15 @@ def ce_combine(m: torch.Tensor, s: torch.Tensor, z: torch.Tensor, want_mean: boo
     t, T = m.shape
     for x, n in ((m, "m"), (s, "s"), (z, "z")):
         _dev(x, n, torch.float32, (t, T))
+    _same_device(m.device, s=s, z=z)
     if out is None:
         loss = torch.empty((T,), dtype=torch.float32, device=m.device)
         mean = torch.empty((1,), dtype=torch.float32, device=m.device) if want_mean else None
     else:
-        loss, mean = out
-    st = LIB.ce_combine(_ptr(m), _ptr(s), _ptr(z), t, T, _ptr(loss), _ptr(mean), None, 0, _stream(m.device))
+        loss, mean = _outs(out, (("loss", torch.float32, (T,), False), ("mean", torch.float32, (1,), True)),
+                           m.device)
+    with _on(m.device):
+        st = LIB.ce_combine(_ptr(m), _ptr(s), _ptr(z), t, T, _ptr(loss), _ptr(mean), None, 0, _stream(m.device))
     _check(st, "ce_combine")
     return loss, mean
 
@@ -248,16 +300,19 @@ def vocab_ce_shard_bwd(X, E_i, target, m, s, vocab_start: int, dloss: Optional[t
     _dev(m, "m", torch.float32, (t, T)); _dev(s, "s", torch.float32, (t, T))
     if dloss is not None:
         _dev(dloss, "dloss", torch.float32, (T,))
+    _same_device(X.device, E_i=E_i, target=target, m=m, s=s, dloss=dloss)
     scale = 1.0 / T if grad_scale is None else float(grad_scale)
     if out is None:
         dX = torch.empty((T, h), dtype=torch.float32, device=X.device)
         dE = torch.empty((h, v_i), dtype=torch.bfloat16, device=X.device)
     else:
-        dX, dE = out
+        dX, dE = _outs(out, (("dX", torch.float32, (T, h), False), ("dE", torch.bfloat16, (h, v_i), False)),
+                       X.device)
     nbytes = vocab_ce_bwd_workspace_bytes(T, h, v_i)
     ws = _workspace(nbytes, X.device, workspace)
-    st = LIB.vocab_ce_shard_bwd(_ptr(X), _ptr(E_i), _ptr(target), _ptr(m), _ptr(s), t, _ptr(dloss), scale, T, h,
-                                v_i, int(vocab_start), _ptr(dX), _ptr(dE), _ptr(ws), nbytes, _stream(X.device))
+    with _on(X.device):
+        st = LIB.vocab_ce_shard_bwd(_ptr(X), _ptr(E_i), _ptr(target), _ptr(m), _ptr(s), t, _ptr(dloss), scale, T, h,
+                                    v_i, int(vocab_start), _ptr(dX), _ptr(dE), _ptr(ws), nbytes, _stream(X.device))
     _check(st, "vocab_ce_shard_bwd")
     return dX, dE
 
@@ -270,7 +325,7 @@ def fingerprint(t: torch.Tensor, chunk_bytes: int = 1 << 16) -> torch.Tensor:
     """Device int64 tensor [1 + chunks]: XXH64 of the tensor's bytes as a whole
     (element 0) and per chunk of ``chunk_bytes`` (elements 1 ..), computed by the
     library on the current stream.  The tensor must be contiguous on a HIP device."""
-    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+    if not isinstance(t, torch.Tensor) or t.device.type != _DEVICE_TYPE:
         raise ValueError("fingerprint needs a tensor on a HIP device")
     if not t.is_contiguous():
         raise ValueError("fingerprint needs a contiguous tensor")
@@ -280,7 +335,8 @@ def fingerprint(t: torch.Tensor, chunk_bytes: int = 1 << 16) -> torch.Tensor:
         raise ValueError(f"chunk_bytes {chunk_bytes} must be a positive multiple of 8")
     out = torch.empty(words, dtype=torch.int64, device=t.device)
     ptr = t.data_ptr() if nbytes else out.data_ptr()  # zero bytes: the address is never read
-    _check(LIB.ms_fingerprint(ptr, nbytes, chunk_bytes, out.data_ptr(), _stream(t.device)), "ms_fingerprint")
+    with _on(t.device):
+        _check(LIB.ms_fingerprint(ptr, nbytes, chunk_bytes, out.data_ptr(), _stream(t.device)), "ms_fingerprint")
     return out
 
 
@@ -297,15 +353,19 @@ def attn_shard_fwd(X, Wqkv_i, Wo_i, b: int, s: int, n: int, d: int, causal: bool
         raise ValueError(f"X has {T} rows, expected b*s = {b * s}")
     bf = torch.bfloat16
     _dev(X, "X", bf, (T, h)); _dev(Wqkv_i, "Wqkv_i", bf, (h, 3 * nd)); _dev(Wo_i, "Wo_i", bf, (nd, h))
+    _same_device(X.device, Wqkv_i=Wqkv_i, Wo_i=Wo_i)
     if out is None:
         QKV = torch.empty((T, 3 * nd), dtype=bf, device=X.device)
         O = torch.empty((T, nd), dtype=bf, device=X.device)
         lse = torch.empty((n, T), dtype=torch.float32, device=X.device)
         Z = torch.empty((T, h), dtype=torch.float32, device=X.device)
     else:
-        QKV, O, lse, Z = out
-    st = LIB.attn_shard_fwd(_ptr(X), _ptr(Wqkv_i), _ptr(Wo_i), b, s, h, n, d, int(bool(causal)), _ptr(QKV), _ptr(O),
-                            _ptr(lse), _ptr(Z), None, 0, _stream(X.device))
+        QKV, O, lse, Z = _outs(out, (("QKV", bf, (T, 3 * nd), False), ("O", bf, (T, nd), False),
+                                     ("lse", torch.float32, (n, T), False), ("Z", torch.float32, (T, h), False)),
+                               X.device)
+    with _on(X.device):
+        st = LIB.attn_shard_fwd(_ptr(X), _ptr(Wqkv_i), _ptr(Wo_i), b, s, h, n, d, int(bool(causal)), _ptr(QKV), _ptr(O),
+                                _ptr(lse), _ptr(Z), None, 0, _stream(X.device))
     _check(st, "attn_shard_fwd")
     return QKV, O, lse, Z
 
@@ -315,21 +375,26 @@ def attn_shard_bwd(X, Wqkv_i, Wo_i, QKV, O, lse, dZ, b: int, s: int, n: int, d: 
     """(dX_i fp32 [T, h], dWqkv_i bf16 [h, 3nd], dWo_i bf16 [nd, h]) = backward of attn_shard_fwd."""
     T, h = X.shape
     nd = n * d
+    if T != b * s:
+        raise ValueError(f"X has {T} rows, expected b*s = {b * s}")
     bf = torch.bfloat16
     for t, nm, shp, dt in ((X, "X", (T, h), bf), (Wqkv_i, "Wqkv_i", (h, 3 * nd), bf), (Wo_i, "Wo_i", (nd, h), bf),
                            (QKV, "QKV", (T, 3 * nd), bf), (O, "O", (T, nd), bf), (lse, "lse", (n, T), torch.float32),
                            (dZ, "dZ", (T, h), bf)):
         _dev(t, nm, dt, shp)
+    _same_device(X.device, Wqkv_i=Wqkv_i, Wo_i=Wo_i, QKV=QKV, O=O, lse=lse, dZ=dZ)
     if out is None:
         dX = torch.empty((T, h), dtype=torch.float32, device=X.device)
         dWqkv = torch.empty((h, 3 * nd), dtype=bf, device=X.device)
         dWo = torch.empty((nd, h), dtype=bf, device=X.device)
     else:
-        dX, dWqkv, dWo = out
+        dX, dWqkv, dWo = _outs(out, (("dX", torch.float32, (T, h), False), ("dWqkv", bf, (h, 3 * nd), False),
+                                     ("dWo", bf, (nd, h), False)), X.device)
     nbytes = attn_shard_workspace_bytes(b, s, h, n, d)
     ws = _workspace(nbytes, X.device, workspace)
-    st = LIB.attn_shard_bwd(_ptr(X), _ptr(Wqkv_i), _ptr(Wo_i), _ptr(QKV), _ptr(O), _ptr(lse), _ptr(dZ), b, s, h, n,
-                            d, int(bool(causal)), _ptr(dX), _ptr(dWqkv), _ptr(dWo), _ptr(ws), nbytes,
-                            _stream(X.device))
+    with _on(X.device):
+        st = LIB.attn_shard_bwd(_ptr(X), _ptr(Wqkv_i), _ptr(Wo_i), _ptr(QKV), _ptr(O), _ptr(lse), _ptr(dZ), b, s, h, n,
+                                d, int(bool(causal)), _ptr(dX), _ptr(dWqkv), _ptr(dWo), _ptr(ws), nbytes,
+                                _stream(X.device))
     _check(st, "attn_shard_bwd")
     return dX, dWqkv, dWo

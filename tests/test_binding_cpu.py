@@ -1,0 +1,143 @@
+"""The Python binding's argument checks, on the CPU.
+
+The library writes every byte of each output and workspace it is handed, so the
+binding must refuse a caller-supplied output of the wrong shape, dtype or
+layout, a workspace that is too small or not contiguous, and tensors on
+different devices, before anything reaches the C entry point.  Here the device
+type the binding requires is switched to "cpu" and the loaded library is
+replaced by a recorder, so no native code runs: the checks are exercised on
+CPU tensors, and a valid call is seen to reach the entry point with the
+tensors' own pointers.
+"""
+import pytest
+import torch
+
+bf, f32 = torch.bfloat16, torch.float32
+
+
+class _Recorder:
+    """Stands in for the ctypes library: records calls, returns MS_OK."""
+
+    def __init__(self):
+        self.calls = []
+
+    def __getattr__(self, name):
+        if name.endswith("workspace_bytes"):
+            return lambda *a: 4096
+        if name == "ms_last_error":
+            return lambda: b""
+
+        def call(*args):
+            self.calls.append((name, args))
+            return 0
+        return call
+
+
+@pytest.fixture()
+def ms(monkeypatch):
+    from megatron_tensor_transformer_mlp_amd import mshard
+    rec = _Recorder()
+    monkeypatch.setattr(mshard, "LIB", rec)
+    monkeypatch.setattr(mshard, "_DEVICE_TYPE", "cpu")
+    monkeypatch.setattr(mshard, "_stream", lambda device: 0)
+    mshard._rec = rec
+    return mshard
+
+
+T, h, f, v = 16, 8, 24, 32
+
+
+def mlp_inputs():
+    return (torch.zeros(T, h, dtype=bf), torch.zeros(h, f, dtype=bf), torch.zeros(f, h, dtype=bf))
+
+
+def test_valid_calls_reach_the_entry_points(ms):
+    X, A, B = mlp_inputs()
+    H, Y, Z = torch.empty(T, f, dtype=bf), torch.empty(T, f, dtype=bf), torch.empty(T, h, dtype=f32)
+    assert ms.mlp_shard_fwd(X, A, B, out=(H, Y, Z)) == (H, Y, Z)
+    name, args = ms._rec.calls[-1]
+    assert name == "mlp_shard_fwd" and args[0] == X.data_ptr() and args[8] == H.data_ptr()
+    dZ = torch.zeros(T, h, dtype=bf)
+    out = (torch.empty(T, h, dtype=f32), torch.empty(h, f, dtype=bf), torch.empty(f, h, dtype=bf), None)
+    ms.mlp_shard_bwd(X, A, B, H, Y, dZ, workspace=torch.empty(4096, dtype=torch.uint8), out=out)
+    assert ms._rec.calls[-1][0] == "mlp_shard_bwd"
+    m = torch.empty(2, T, dtype=f32)
+    ms.ce_combine(m, m.clone(), m.clone(), out=(torch.empty(T, dtype=f32), None))
+    assert ms._rec.calls[-1][0] == "ce_combine"
+
+
+@pytest.mark.parametrize("bad", ["shape", "dtype", "strided", "missing"])
+def test_bad_outputs_are_refused_before_the_call(ms, bad):
+    X, A, B = mlp_inputs()
+    H, Y, Z = torch.empty(T, f, dtype=bf), torch.empty(T, f, dtype=bf), torch.empty(T, h, dtype=f32)
+    if bad == "shape":
+        H = torch.empty(T - 1, f, dtype=bf)
+    elif bad == "dtype":
+        Z = torch.empty(T, h, dtype=bf)
+    elif bad == "strided":
+        Y = torch.empty(f, T, dtype=bf).t()
+    else:
+        Z = None
+    with pytest.raises((ValueError, TypeError)):
+        ms.mlp_shard_fwd(X, A, B, out=(H, Y, Z))
+    assert ms._rec.calls == []
+
+
+def test_output_count_must_match(ms):
+    X, A, B = mlp_inputs()
+    with pytest.raises(ValueError):
+        ms.mlp_shard_fwd(X, A, B, out=(torch.empty(T, f, dtype=bf), torch.empty(T, f, dtype=bf)))
+    assert ms._rec.calls == []
+
+
+@pytest.mark.parametrize("bad", ["small", "strided"])
+def test_bad_workspaces_are_refused(ms, bad):
+    X, A, B = mlp_inputs()
+    H, Y, dZ = torch.zeros(T, f, dtype=bf), torch.zeros(T, f, dtype=bf), torch.zeros(T, h, dtype=bf)
+    ws = torch.empty(4095, dtype=torch.uint8) if bad == "small" else torch.empty(8192, dtype=torch.uint8)[::2]
+    with pytest.raises(ValueError):
+        ms.mlp_shard_bwd(X, A, B, H, Y, dZ, workspace=ws)
+    assert ms._rec.calls == []
+
+
+def test_every_entry_point_checks_its_outputs(ms):
+    X = torch.zeros(T, h, dtype=bf)
+    E, tg = torch.zeros(h, v, dtype=bf), torch.zeros(T, dtype=torch.int64)
+    with pytest.raises(ValueError):
+        ms.vocab_ce_shard_fwd(X, E, tg, 0, out=(torch.empty(T, dtype=f32), torch.empty(T, dtype=f32),
+                                                torch.empty(T + 1, dtype=f32)))
+    m = torch.zeros(1, T, dtype=f32)
+    with pytest.raises(ValueError):
+        ms.vocab_ce_shard_bwd(X, E, tg, m, m.clone(), 0,
+                              out=(torch.empty(T, h, dtype=f32), torch.empty(v, h, dtype=bf)))
+    with pytest.raises(ValueError):
+        ms.ce_combine(m, m.clone(), m.clone(), out=(torch.empty(T, dtype=f32), torch.empty(2, dtype=f32)))
+    b, s, n, d = 2, 8, 2, 16
+    Wqkv, Wo = torch.zeros(h, 3 * n * d, dtype=bf), torch.zeros(n * d, h, dtype=bf)
+    with pytest.raises(ValueError):
+        ms.attn_shard_fwd(X, Wqkv, Wo, b, s, n, d,
+                          out=(torch.empty(T, 3 * n * d, dtype=bf), torch.empty(T, n * d, dtype=bf),
+                               torch.empty(T, n, dtype=f32), torch.empty(T, h, dtype=f32)))
+    QKV, O = torch.zeros(T, 3 * n * d, dtype=bf), torch.zeros(T, n * d, dtype=bf)
+    lse, dZ = torch.zeros(n, T, dtype=f32), torch.zeros(T, h, dtype=bf)
+    with pytest.raises(ValueError):
+        ms.attn_shard_bwd(X, Wqkv, Wo, QKV, O, lse, dZ, b, s, n, d, out=(torch.empty(T, h, dtype=f32),
+                                                                          torch.empty(h, 3 * n * d, dtype=bf),
+                                                                          torch.empty(h, n * d, dtype=bf)))
+    with pytest.raises(ValueError):  # X's rows must be b*s
+        ms.attn_shard_bwd(X, Wqkv, Wo, QKV, O, lse, dZ, b, s + 1, n, d)
+    assert ms._rec.calls == []
+
+
+def test_unknown_gelu_form_is_a_value_error(ms):
+    X, A, B = mlp_inputs()
+    with pytest.raises(ValueError):
+        ms.mlp_shard_fwd(X, A, B, gelu="exact")
+    assert ms._rec.calls == []
+
+
+def test_tensors_on_different_devices_are_refused(ms):
+    # one CPU device only: the cross-device check itself, on a CPU and a meta tensor
+    with pytest.raises(ValueError):
+        ms._same_device(torch.device("cpu"), A_i=torch.zeros(1, device="meta"))
+    ms._same_device(torch.device("cpu"), A_i=torch.zeros(1), b1_i=None)
