@@ -26,6 +26,8 @@ class _Recorder:
             return lambda *a: 4096
         if name == "ms_last_error":
             return lambda: b""
+        if name == "ms_fingerprint_words":
+            return lambda nbytes, chunk: 1 + max(1, -(-nbytes // chunk))
 
         def call(*args):
             self.calls.append((name, args))
@@ -141,3 +143,28 @@ def test_tensors_on_different_devices_are_refused(ms):
     with pytest.raises(ValueError):
         ms._same_device(torch.device("cpu"), A_i=torch.zeros(1, device="meta"))
     ms._same_device(torch.device("cpu"), A_i=torch.zeros(1), b1_i=None)
+
+
+def test_valid_calls_of_every_entry_point(ms):
+    X = torch.zeros(T, h, dtype=bf)
+    E, tg = torch.zeros(h, v, dtype=bf), torch.zeros(T, dtype=torch.int64)
+    ms.vocab_ce_shard_fwd(X, E, tg, 0)
+    ms.vocab_ce_shard_fwd(X, E, tg, 0, workspace=torch.empty(4096, dtype=torch.uint8),
+                          out=tuple(torch.empty(T, dtype=f32) for _ in range(3)))
+    m = torch.zeros(2, T, dtype=f32)
+    ms.vocab_ce_shard_bwd(X, E, tg, m, m.clone(), 0, dloss=torch.ones(T, dtype=f32))
+    ms.vocab_ce_shard_bwd(X, E, tg, m, m.clone(), 0, out=(torch.empty(T, h, dtype=f32), torch.empty(h, v, dtype=bf)))
+    ms.ce_combine(m, m.clone(), m.clone())
+    b, s, n, d = 2, 8, 2, 16
+    Wqkv, Wo = torch.zeros(h, 3 * n * d, dtype=bf), torch.zeros(n * d, h, dtype=bf)
+    QKV, O, lse, Z = ms.attn_shard_fwd(X, Wqkv, Wo, b, s, n, d)
+    ms.attn_shard_fwd(X, Wqkv, Wo, b, s, n, d, out=(QKV, O, lse, Z))
+    dZ = torch.zeros(T, h, dtype=bf)
+    ms.attn_shard_bwd(X, Wqkv, Wo, QKV, O, lse, dZ, b, s, n, d)
+    ms.attn_shard_bwd(X, Wqkv, Wo, QKV, O, lse, dZ, b, s, n, d, workspace=torch.empty(4096, dtype=torch.uint8),
+                      out=(torch.empty(T, h, dtype=f32), torch.empty(h, 3 * n * d, dtype=bf),
+                           torch.empty(n * d, h, dtype=bf)))
+    ms.fingerprint(X)
+    names = [c[0] for c in ms._rec.calls]
+    assert names == ["vocab_ce_shard_fwd"] * 2 + ["vocab_ce_shard_bwd"] * 2 + ["ce_combine"] + \
+        ["attn_shard_fwd"] * 2 + ["attn_shard_bwd"] * 2 + ["ms_fingerprint"]
