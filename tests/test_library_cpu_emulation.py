@@ -226,6 +226,58 @@ def test_emulated_cases_cover_the_plans(lib):
     assert p_small["mlp"]["pair_ax"] == "1" and p_small["ce_bwd"]["paired"] == "1"
 
 
+def _random_case(seed):
+    """A seeded random shape for one of the three sequences: any multiple of 8 for
+    h, f_i and v_i, any token count, any head size the binding accepts."""
+    g = np.random.default_rng(seed)
+    kind = ["mlp", "ce", "attn"][seed % 3]
+    if kind == "mlp":
+        return kind, dict(T=int(g.integers(1, 700)), h=8 * int(g.integers(1, 60)), f=8 * int(g.integers(1, 60)),
+                          gelu=int(g.integers(0, 2)), bias=int(g.integers(0, 2)))
+    if kind == "ce":
+        t = int(g.integers(1, 4))
+        return kind, dict(T=int(g.integers(1, 700)), h=8 * int(g.integers(1, 60)), v=8 * int(g.integers(1, 120)),
+                          t=t, rank=int(g.integers(0, t)))
+    return kind, dict(b=int(g.integers(1, 4)), s=int(g.integers(1, 300)), h=8 * int(g.integers(1, 40)),
+                      n=int(g.integers(1, 4)), hd=int(g.choice([16, 32, 48, 64, 80, 96, 112, 128])),
+                      causal=bool(g.integers(0, 2)))
+
+
+@pytest.mark.parametrize("seed", range(100, 112))
+def test_random_shapes_emulated(lib, seed):
+    """Seeded random shapes through each sequence (the same checks as above): the
+    ragged edges, K tails, splits and pairings they happen to hit."""
+    exe, d = lib
+    kind, p = _random_case(seed)
+    print(kind, p)
+    if kind == "mlp":
+        mlp_case(exe, d, p["T"], p["h"], p["f"], p["gelu"], p["bias"])
+    elif kind == "attn":
+        attn_case(exe, d, p["b"], p["s"], p["h"], p["n"], p["hd"], p["causal"])
+    else:
+        T, h, v, t, r = p["T"], p["h"], p["v"], p["t"], p["rank"]
+        x = inputs.make_inputs(T, h, 8, v, t=t, rank=r, seed=seed)
+        vs = int(x["vocab_start"])
+        case = os.path.join(d, f"rand_ce_{seed}")
+        put(case, X=x["X"], E=x["E"], target=x["targets"])
+        run(exe, case, "ce_fwd", T, h, v, vs)
+        o = oracle.vocab_ce_shard(x["X"], x["E"], x["targets"], vs)
+        m, s, z = (get(case, k, np.float32, (T,)) for k in ("m", "s", "z"))
+        assert np.abs(m - o["m"]).max() <= CE_TOL * np.abs(o["m"]).max()
+        assert np.abs(s / o["s"] - 1).max() <= CE_TOL
+        assert np.abs(z - o["z"]).max() <= CE_TOL * max(np.abs(o["z"]).max(), 1e-30)
+        # the other ranks' partials: this rank's shifted, so the combined statistics differ from the shard's own
+        M = np.stack([m + 0.3 * k for k in range(t)]).astype(np.float32)
+        S = np.stack([s * (1 + k) for k in range(t)]).astype(np.float32)
+        dl = np.random.default_rng(seed).uniform(0, 2, T).astype(np.float32)
+        put(case, m=M, s=S, dloss=dl)
+        scale = float(np.float32(1.0 / T))
+        run(exe, case, "ce_bwd", T, h, v, vs, t, repr(scale), 1)
+        ob = oracle.vocab_ce_shard_bwd(x["X"], x["E"], x["targets"], vs, M, S, scale * dl.astype(np.float64))
+        assert rel_fro(get(case, "dX", np.float32, (T, h)), ob["dX"]) <= TOL
+        assert rel_fro(get(case, "dE", np.uint16, (h, v)), ob["dE"]) <= TOL
+
+
 @pytest.mark.parametrize("nbytes,chunk", [(0, 64), (100, 32), (70000, 4096), (3 * 65536 + 5, 65536)])
 def test_fingerprint_emulated(lib, nbytes, chunk):
     fingerprint_case(*lib, nbytes, chunk)
