@@ -15,6 +15,7 @@ The packed fp32 -> bf16 conversion becomes an explicit round-to-nearest-even
 other builtins included (hip/hip_runtime.h here), is compiled as it is.
 """
 import os
+import re
 import shutil
 
 LDS_SPACE = "__attribute__((address_space(3)))"
@@ -40,7 +41,12 @@ SUBS = {
     "epilogues.hpp": [
         ('asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");', ';'),
         ('asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));', 'r = fmaxf(fmaxf(a, b), c);'),
-        ('asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x) : "a"(acc[mi][ni][r]));', 'x = acc[mi][ni][r];'),
+    ],
+}
+# Substitutions whose operands may be any expression: (regex, replacement), each matching once.
+REGEX_SUBS = {
+    "epilogues.hpp": [
+        (r'asm volatile\("v_accvgpr_read_b32 %0, %1" : "=v"\((\w+)\) : "a"\(([^;]*)\)\);', r'\1 = \2;'),
     ],
 }
 PLAIN = ["kernels.hip", "attention.hip", "fingerprint.hip", "launch.hpp"]
@@ -57,6 +63,9 @@ def prepare(csrc: str, emu_dir: str, out: str) -> None:
         for old, new in SUBS.get(name, []):
             assert text.count(old) == 1, (name, old[:60])
             text = text.replace(old, new)
+        for pattern, repl in REGEX_SUBS.get(name, []):
+            text, n = re.subn(pattern, repl, text)
+            assert n == 1, (name, pattern)
         assert "asm" not in _code(text).replace("#include", ""), name
         open(os.path.join(out, name), "w").write(text)
     shutil.copytree(os.path.join(emu_dir, "hip"), os.path.join(out, "hip"), dirs_exist_ok=True)
