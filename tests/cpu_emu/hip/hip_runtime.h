@@ -359,15 +359,26 @@ struct Rsrc {
   int64_t bytes;
 };
 inline Rsrc make_rsrc(const void* base, int n) { return Rsrc{(char*)base, n}; }
+// The hardware range-checks a multi-dword buffer access dword by dword; an
+// access that straddles the end of its resource would need that, and the
+// kernels never make one, so it is reported instead of emulated.
+inline bool in_range(int64_t off, int64_t size, int64_t bytes) {
+  if (off < 0 || off >= bytes) return false;
+  if (off + size > bytes) {
+    std::fprintf(stderr, "emulation: buffer access straddles the end of its resource\n");
+    std::abort();
+  }
+  return true;
+}
 template <class V>
 inline V rload(Rsrc r, int off) {
   V v{};
-  if (off >= 0 && (int64_t)off + (int64_t)sizeof(V) <= r.bytes) std::memcpy(&v, r.base + off, sizeof(V));
+  if (in_range(off, sizeof(V), r.bytes)) std::memcpy(&v, r.base + off, sizeof(V));
   return v;
 }
 template <class V>
 inline void rstore(V v, Rsrc r, int off) {
-  if (off >= 0 && (int64_t)off + (int64_t)sizeof(V) <= r.bytes) std::memcpy(r.base + off, &v, sizeof(V));
+  if (in_range(off, sizeof(V), r.bytes)) std::memcpy(r.base + off, &v, sizeof(V));
 }
 // Both lanes of each pair (l, l^m) receive (lower lane's value, upper lane's value).
 struct Pair {
@@ -408,7 +419,7 @@ inline void dma16(u32x4 desc, uint32_t off, uint32_t lds_addr) {
   const char* base = (const char*)(uintptr_t)((uint64_t)desc[0] | ((uint64_t)(desc[1] & 0xffffu) << 32));
   PendingDma p;
   p.dst = (char*)(uintptr_t)lds_addr + 16 * (threadIdx.x % 64);
-  if ((uint64_t)off + 16 <= (uint64_t)desc[2]) std::memcpy(p.data, base + off, 16);
+  if (in_range(off, 16, desc[2])) std::memcpy(p.data, base + off, 16);
   else std::memset(p.data, 0, 16);
   cur()->dma.push_back(p);
 }
