@@ -26,6 +26,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
 from megatron_tensor_transformer_mlp_amd import inputs
@@ -419,3 +420,93 @@ def test_full_size_sampled_under_address_sanitizer(lib_asan, name):
                 pairs += 1
     assert pairs > 0
     subprocess.run(["rm", "-rf", case], check=True)
+
+
+def _scaled_bf16(u, k):
+    """bf16 bit patterns times 2**k (exact: only the exponent moves)."""
+    return inputs.round_to_bf16_bits(inputs.bf16_bits_to_f32(u) * np.float32(2.0 ** k))
+
+
+def test_vocab_ce_degenerate_and_extreme_logits(lib):
+    """E = 0: every logit is 0, so m = 0, s = v_i and z = 0 exactly, and the
+    gradient is coef (1/v - one-hot) with dE = X^T dL.  Logits 64 times larger
+    than the workloads' (std about 50): the shard max is subtracted before every
+    exponential, so nothing overflows and the partials keep their relative
+    accuracy."""
+    exe, d = lib
+    T, h, v = 300, 128, 520
+    x = inputs.make_inputs(T, h, 8, v)
+    case = os.path.join(d, "ce_zero")
+    put(case, X=x["X"], E=np.zeros_like(x["E"]), target=x["targets"])
+    run(exe, case, "ce_fwd", T, h, v, 0)
+    m, s, z = (get(case, k, np.float32, (T,)) for k in ("m", "s", "z"))
+    assert (m == 0).all() and (s == v).all() and (z == 0).all()
+    put(case, m=m.astype(np.float32)[None], s=s.astype(np.float32)[None])
+    run(exe, case, "ce_bwd", T, h, v, 0, 1, repr(float(np.float32(1.0 / T))), 0)
+    ob = oracle.vocab_ce_shard_bwd(x["X"], np.zeros_like(x["E"]), x["targets"], 0, m[None], s[None], 1.0 / T)
+    assert rel_fro(get(case, "dE", np.uint16, (h, v)), ob["dE"]) <= TOL
+    assert np.abs(get(case, "dX", np.float32, (T, h))).max() == 0
+
+    Xb = _scaled_bf16(x["X"], 6)
+    case = os.path.join(d, "ce_big")
+    put(case, X=Xb, E=x["E"], target=x["targets"])
+    run(exe, case, "ce_fwd", T, h, v, 0)
+    o = oracle.vocab_ce_shard(Xb, x["E"], x["targets"], 0)
+    m, s, z = (get(case, k, np.float32, (T,)) for k in ("m", "s", "z"))
+    # the max logit's own term is exp of the rounding error of m log2(e) (about 1e-5 here), so s may sit just below 1
+    assert np.isfinite(m).all() and np.isfinite(s).all() and (s > 0.999).all()
+    assert np.abs(m - o["m"]).max() <= CE_TOL * np.abs(o["m"]).max()
+    assert np.abs(s / o["s"] - 1).max() <= CE_TOL
+    put(case, m=m.astype(np.float32)[None], s=s.astype(np.float32)[None])
+    run(exe, case, "ce_bwd", T, h, v, 0, 1, repr(float(np.float32(1.0 / T))), 0)
+    ob = oracle.vocab_ce_shard_bwd(Xb, x["E"], x["targets"], 0, m[None], s[None], 1.0 / T)
+    assert rel_fro(get(case, "dX", np.float32, (T, h)), ob["dX"]) <= TOL
+    assert rel_fro(get(case, "dE", np.uint16, (h, v)), ob["dE"]) <= TOL
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_attention_core_uniform_and_peaked(lib, causal):
+    """Q = 0: every visible key has the same score, so each query's output is the
+    mean of the values it sees and lse = ln(visible keys).  Scores 16 times the
+    usual scale (Q times 16): softmax rows close to one-hot, where the running
+    max of the online softmax matters most."""
+    exe, d = lib
+    b, s, n, hd = 2, 150, 2, 64
+    T, nd = b * s, n * hd
+    g = np.random.default_rng(9)
+    qkv = inputs.round_to_bf16_bits(g.standard_normal((T, 3 * nd)).astype(np.float32))
+    dout = inputs.round_to_bf16_bits(g.standard_normal((T, nd)).astype(np.float32))
+    zero_q = qkv.copy()
+    zero_q[:, :nd] = 0
+    case = os.path.join(d, f"core_uniform_{int(causal)}")
+    put(case, qkv=zero_q, dout=dout)
+    run(exe, case, "attn_core", b, s, n, hd, int(causal))
+    O = get(case, "o", np.uint16, (T, nd))
+    lse = get(case, "lse", np.float32, (n, T))
+    V = f64(zero_q[:, 2 * nd:])
+    want = np.empty((T, nd))
+    vis = np.empty(T)
+    for bi in range(b):
+        for q in range(s):
+            k_end = q + 1 if causal else s
+            want[bi * s + q] = V[bi * s:bi * s + k_end].mean(axis=0)
+            vis[bi * s + q] = k_end
+    assert rel_fro(O, want) <= TOL
+    assert np.abs(lse - np.log(vis)[None, :]).max() <= 1e-5
+
+    peaked = qkv.copy()
+    peaked[:, :nd] = _scaled_bf16(qkv[:, :nd], 4)
+    case = os.path.join(d, f"core_peaked_{int(causal)}")
+    put(case, qkv=peaked, dout=dout)
+    run(exe, case, "attn_core", b, s, n, hd, int(causal))
+    Q, K, V = f64(peaked[:, :nd]), f64(peaked[:, nd:2 * nd]), f64(peaked[:, 2 * nd:])
+    want = attn.attention_core(Q, K, V, n, hd, b, s, causal)
+    assert rel_fro(get(case, "o", np.uint16, (T, nd)), want["O"]) <= TOL
+    assert rel_fro(get(case, "lse", np.float32, (n, T)), want["lse"]) <= 1e-5
+    qt, kt, vt = (torch.tensor(x.reshape(b, s, n, hd).transpose(0, 2, 1, 3).copy(), requires_grad=True)
+                  for x in (Q, K, V))
+    ot = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=causal)
+    (ot * torch.tensor(f64(dout).reshape(b, s, n, hd).transpose(0, 2, 1, 3).copy())).sum().backward()
+    dq = get(case, "dqkv", np.uint16, (T, 3 * nd))
+    for j, t in enumerate((qt, kt, vt)):
+        assert rel_fro(dq[:, j * nd:(j + 1) * nd], t.grad.numpy().transpose(0, 2, 1, 3).reshape(T, nd)) <= TOL

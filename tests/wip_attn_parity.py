@@ -126,3 +126,29 @@ def test_attn_bitwise_determinism(ms):
             hsh.update(t.contiguous().view(torch.uint8).cpu().numpy().tobytes())
         ref = ref or hsh.hexdigest()
         assert hsh.hexdigest() == ref, it
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_attn_uniform_and_peaked_scores(ms, causal):
+    """W_Q = 0: every visible key scores the same, so each query's O row is the mean
+    of the values it sees and lse = ln(visible keys).  W_Q 16 times larger: softmax
+    rows close to one-hot."""
+    b, s, h, n, hd = 2, 150, 128, 2, 64
+    print(f"case attn uniform/peaked causal={causal}", flush=True)
+    d = inputs.make_attn_inputs(b, s, h, n, hd)
+    nd = n * hd
+    W0 = d["Wqkv"].copy()
+    W0[:, :nd] = 0
+    X, Wo, dZ = dev(d["X"]), dev(d["Wo"]), dev(d["dZ"])
+    QKV, O, lse, Z = ms.attn_shard_fwd(X, dev(W0), Wo, b, s, n, hd, causal)
+    torch.cuda.synchronize()
+    V = host(QKV)[:, 2 * nd:]
+    vis = np.array([(q + 1 if causal else s) for _ in range(b) for q in range(s)], dtype=np.float64)
+    want = np.concatenate([np.stack([V[bi * s:bi * s + (q + 1 if causal else s)].mean(axis=0) for q in range(s)])
+                           for bi in range(b)])
+    assert rel_fro(host(O), want) <= TOL
+    assert np.abs(host(lse) - np.log(vis)[None, :]).max() <= 1e-5
+    Wp = d["Wqkv"].copy()
+    Wp[:, :nd] = inputs.round_to_bf16_bits(inputs.bf16_bits_to_f32(d["Wqkv"][:, :nd]) * np.float32(16.0))
+    dp = dict(d, Wqkv=Wp)
+    run_and_check(ms, dp, b, s, n, hd, causal)

@@ -197,3 +197,30 @@ def test_ce_bwd_bitwise_determinism(ms):
             hsh.update(x.contiguous().view(torch.uint8).cpu().numpy().tobytes())
         ref = ref or hsh.hexdigest()
         assert hsh.hexdigest() == ref, it
+
+
+def test_ce_degenerate_and_extreme_logits(ms):
+    """E = 0 (every logit 0: m = 0, s = v_i and z = 0 exactly, dX_i = 0) and logits
+    64 times the workloads' scale (the shard max keeps every exponential finite)."""
+    T, h, v = 300, 128, 520
+    print(f"case ce degenerate T={T} h={h} v={v}", flush=True)
+    d = inputs.make_inputs(T, h, 8, v)
+    tg = torch.from_numpy(d["targets"]).cuda()
+    E0 = np.zeros_like(d["E"])
+    m, s, z = ms.vocab_ce_shard_fwd(dev(d["X"]), dev(E0), tg, 0)
+    torch.cuda.synchronize()
+    assert (host(m) == 0).all() and (host(s) == v).all() and (host(z) == 0).all()
+    dX, dE = run_bwd(ms, d["X"], E0, d["targets"], f32(host(m)[None]), f32(host(s)[None]), 0, v)
+    ob = oracle.vocab_ce_shard_bwd(d["X"], E0, d["targets"], 0, host(m)[None], host(s)[None], 1.0 / T)
+    assert np.abs(host(dX)).max() == 0
+    assert rel_fro(host(dE), ob["dE"]) <= TOL
+    Xb = inputs.round_to_bf16_bits(inputs.bf16_bits_to_f32(d["X"]) * np.float32(64.0))
+    m, s, z = ms.vocab_ce_shard_fwd(dev(Xb), dev(d["E"]), tg, 0)
+    torch.cuda.synchronize()
+    o = oracle.vocab_ce_shard(Xb, d["E"], d["targets"], 0)
+    assert np.abs(host(m) - o["m"]).max() <= 1e-4 * np.abs(o["m"]).max()
+    assert np.abs(host(s) / o["s"] - 1).max() <= 1e-4
+    dX, dE = run_bwd(ms, Xb, d["E"], d["targets"], f32(host(m)[None]), f32(host(s)[None]), 0, v)
+    ob = oracle.vocab_ce_shard_bwd(Xb, d["E"], d["targets"], 0, host(m)[None], host(s)[None], 1.0 / T)
+    assert rel_fro(host(dX), ob["dX"]) <= TOL
+    assert rel_fro(host(dE), ob["dE"]) <= TOL
