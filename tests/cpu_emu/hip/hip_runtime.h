@@ -57,6 +57,20 @@ typedef int hipError_t;
 enum { hipSuccess = 0, hipErrorInvalidValue = 1 };
 typedef void* hipStream_t;
 inline hipError_t hipGetLastError() { return hipSuccess; }
+inline hipError_t hipGetDevice(int* dev) {
+  *dev = 0;
+  return hipSuccess;
+}
+// Device attributes a launcher may size a grid by: the compute-unit count is
+// EMU_CUS (default 8), small enough that a grid sized by it leaves each
+// workgroup several tiles on the small shapes emulated here.
+enum hipDeviceAttribute_t { hipDeviceAttributeMultiprocessorCount = 0 };
+inline hipError_t hipDeviceGetAttribute(int* value, hipDeviceAttribute_t attr, int) {
+  if (attr != hipDeviceAttributeMultiprocessorCount) return hipErrorInvalidValue;
+  const char* e = std::getenv("EMU_CUS");
+  *value = e ? std::atoi(e) : 8;
+  return hipSuccess;
+}
 
 struct dim3 {
   unsigned x, y, z;
