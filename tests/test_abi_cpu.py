@@ -233,3 +233,25 @@ def test_bench_breakdown_arms_only_step_kernels(ms):
     assert len(bench.STEP_KERNELS) == len(set(bench.STEP_KERNELS)) == 7
     assert set(bench.STEP_KERNELS) <= set(ms.KERNELS)
     assert not any(k.startswith(("ce_bwd", "attn")) for k in bench.STEP_KERNELS)
+
+
+def test_library_imports_no_allocation_copy_or_sync(ms):
+    """The built library's undefined HIP symbols are only kernel registration and
+    launch, error strings, the device query of its one-time gfx950 check and the
+    measurement hook's event record: it never allocates, frees, copies, clears
+    memory or synchronises, which is what lets a caller capture its calls in a
+    graph and own every buffer."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not found")
+    out = subprocess.run([nm, "-D", "--undefined-only", ms.LIB_PATH], check=True, capture_output=True,
+                         text=True).stdout
+    hip = {line.split()[-1].split("@")[0] for line in out.splitlines() if "hip" in line.lower()}
+    allowed = {"__hipPopCallConfiguration", "__hipPushCallConfiguration", "__hipRegisterFatBinary",
+               "__hipRegisterFunction", "__hipUnregisterFatBinary", "hipLaunchKernel", "hipGetLastError",
+               "hipGetErrorString", "hipGetDevice", "hipGetDevicePropertiesR0600", "hipGetDeviceProperties",
+               "hipEventRecord"}
+    assert hip <= allowed, sorted(hip - allowed)
+    assert not any(re.search(r"Malloc|Free|Memcpy|Memset|Synchronize|HostRegister", s) for s in hip)
