@@ -510,3 +510,33 @@ def test_attention_core_uniform_and_peaked(lib, causal):
     dq = get(case, "dqkv", np.uint16, (T, 3 * nd))
     for j, t in enumerate((qt, kt, vt)):
         assert rel_fro(dq[:, j * nd:(j + 1) * nd], t.grad.numpy().transpose(0, 2, 1, 3).reshape(T, nd)) <= TOL
+
+
+@pytest.mark.parametrize("gelu", [0, 1])
+def test_mlp_degenerate_and_extreme_inputs(lib, gelu):
+    """A = 0 with a bias: every H row equals b1, so Y rows are GeLU(b1) and
+    dX = dH A^T is exactly 0.  X 1024 times the workloads' scale (|H| in the
+    hundreds): the exponential in GeLU and GeLU' underflows to 0, leaving
+    max(x, 0) and the step function, with no NaN from the products."""
+    exe, d = lib
+    T, h, f = 300, 136, 264
+    x = inputs.make_inputs(T, h, f, 8, bias=True)
+    form = "tanh" if gelu else "erf"
+    for label, X, A in (("zeroA", x["X"], np.zeros_like(x["A"])), ("bigX", _scaled_bf16(x["X"], 10), x["A"])):
+        case = os.path.join(d, f"mlp_{label}_{gelu}")
+        put(case, X=X, A=A, B=x["B"], dZ=x["dZ"], b1=x["b1"])
+        run(exe, case, "mlp_fwd", T, h, f, gelu, 1)
+        run(exe, case, "mlp_bwd", T, h, f, gelu, 1)
+        of = oracle.mlp_shard_fwd(X, A, x["B"], x["b1"], form)
+        ob = oracle.mlp_shard_bwd(X, A, x["B"], x["dZ"], x["b1"], form)
+        got = {"H": get(case, "H", np.uint16, (T, f)), "Y": get(case, "Y", np.uint16, (T, f)),
+               "Z": get(case, "Z", np.float32, (T, h)), "dA": get(case, "dA", np.uint16, (h, f)),
+               "dB": get(case, "dB", np.uint16, (f, h)), "db1": get(case, "db1", np.uint16, (f,))}
+        dX = get(case, "dX", np.float32, (T, h))
+        for k, v in got.items():
+            assert np.isfinite(v).all() and rel_fro(v, {**of, **ob}[k]) <= TOL, (label, k)
+        if label == "zeroA":
+            assert (got["H"] == got["H"][0][None, :]).all()
+            assert np.abs(dX).max() == 0
+        else:
+            assert np.isfinite(dX).all() and rel_fro(dX, ob["dX"]) <= TOL

@@ -1,0 +1,64 @@
+"""GPU parity of the MLP shard on degenerate and extreme inputs, against the fp64 oracle.
+
+Run by naming this file (pytest does not collect it by default):
+    python -u -m pytest tests/wip_mlp_edges_gpu.py -x -v --timeout 300 --timeout-method thread
+
+A = 0 with a bias: every H row equals b1, Y rows are GeLU(b1), dX is exactly 0.
+X 1024 times the workloads' scale: GeLU and GeLU' reduce to max(x, 0) and a
+step, and nothing may turn into NaN.  Tolerance: relative Frobenius 1e-2.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from megatron_tensor_transformer_mlp_amd import inputs
+from tests.conftest import rel_fro
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+
+
+@pytest.fixture(scope="module")
+def ms():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from megatron_tensor_transformer_mlp_amd import mshard
+    return mshard
+
+
+def dev(u16):
+    return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def host(t):
+    if t.dtype == torch.bfloat16:
+        return inputs.bf16_bits_to_f32(t.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+    return t.double().cpu().numpy()
+
+
+@pytest.mark.parametrize("gelu", ["erf", "tanh"])
+@pytest.mark.parametrize("label", ["zeroA", "bigX"])
+def test_mlp_edges(ms, gelu, label):
+    T, h, f = 300, 136, 264
+    print(f"case mlp edges {label} gelu={gelu} T={T} h={h} f={f}", flush=True)
+    x = inputs.make_inputs(T, h, f, 8, bias=True)
+    X, A = x["X"], x["A"]
+    if label == "zeroA":
+        A = np.zeros_like(A)
+    else:
+        X = inputs.round_to_bf16_bits(inputs.bf16_bits_to_f32(X) * np.float32(1024.0))
+    H, Y, Z = ms.mlp_shard_fwd(dev(X), dev(A), dev(x["B"]), dev(x["b1"]), gelu=gelu)
+    dX, dA, dB, db1 = ms.mlp_shard_bwd(dev(X), dev(A), dev(x["B"]), H, Y, dev(x["dZ"]), gelu=gelu, want_db1=True)
+    torch.cuda.synchronize()
+    want = {**oracle.mlp_shard_fwd(X, A, x["B"], x["b1"], gelu), **oracle.mlp_shard_bwd(X, A, x["B"], x["dZ"], x["b1"], gelu)}
+    got = {"H": host(H), "Y": host(Y), "Z": host(Z), "dA": host(dA), "dB": host(dB), "db1": host(db1), "dX": host(dX)}
+    for k, v in got.items():
+        assert np.isfinite(v).all(), k
+    if label == "zeroA":
+        assert np.abs(got["dX"]).max() == 0
+        del got["dX"]
+    errs = {k: rel_fro(v, want[k]) for k, v in got.items()}
+    print("  rel-fro", {k: f"{e:.2e}" for k, e in errs.items()}, flush=True)
+    assert all(e <= TOL for e in errs.values()), errs
