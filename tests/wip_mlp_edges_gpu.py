@@ -52,7 +52,8 @@ def test_mlp_edges(ms, gelu, label):
     H, Y, Z = ms.mlp_shard_fwd(dev(X), dev(A), dev(x["B"]), dev(x["b1"]), gelu=gelu)
     dX, dA, dB, db1 = ms.mlp_shard_bwd(dev(X), dev(A), dev(x["B"]), H, Y, dev(x["dZ"]), gelu=gelu, want_db1=True)
     torch.cuda.synchronize()
-    want = {**oracle.mlp_shard_fwd(X, A, x["B"], x["b1"], gelu), **oracle.mlp_shard_bwd(X, A, x["B"], x["dZ"], x["b1"], gelu)}
+    want = {**oracle.mlp_shard_fwd(X, A, x["B"], x["b1"], gelu),
+            **oracle.mlp_shard_bwd(X, A, x["B"], x["dZ"], x["b1"], gelu)}
     got = {"H": host(H), "Y": host(Y), "Z": host(Z), "dA": host(dA), "dB": host(dB), "db1": host(db1), "dX": host(dX)}
     for k, v in got.items():
         assert np.isfinite(v).all(), k
