@@ -58,7 +58,11 @@ def _args():
     p.add_argument("--rows", default="", help="comma list of further rows timed after the step: ce_bwd, attn")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain device copy of 1 GiB (5 launches) and exit")
-    return p.parse_args()
+    a = p.parse_args()
+    unknown = sorted(set(r for r in a.rows.split(",") if r) - {"ce_bwd", "attn"})
+    if unknown:
+        p.error(f"unknown --rows entries {unknown} (known: ce_bwd, attn)")
+    return a
 
 
 def kernel_sources_sha256() -> str:
@@ -240,9 +244,6 @@ def main():
                       for i, n in enumerate(names)}
 
     rows = [r for r in a.rows.split(",") if r]
-    unknown = sorted(set(rows) - {"ce_bwd", "attn"})
-    if unknown:
-        sys.exit(f"bench.py: unknown --rows entries {unknown} (known: ce_bwd, attn)")
     extra = {}
 
     def timed(fn, reps):
