@@ -323,6 +323,7 @@ def test_library_emulated_under_sanitizer(tmp_path, sanitizer):
         fingerprint_case(exe, d, 0, 64)
     else:
         attn_case(exe, d, 1, 130, 128, 2, 64, False)
+        fingerprint_case(exe, d, 70000, 4096)
 
 
 FULL = os.environ.get("MSHARD_FULL_SIZE_EMULATION") == "1"
