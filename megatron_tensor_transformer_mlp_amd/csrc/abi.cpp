@@ -46,6 +46,7 @@ struct Buf {
   size_t bytes;
   const char* name;
   bool output;
+  bool whole_below_2g31 = true;  // false for a workspace: its regions are checked one by one
 };
 
 constexpr int64_t kMaxBytes = (int64_t)1 << 31;  // every buffer must be smaller than 2^31 bytes
@@ -80,7 +81,7 @@ ms_status check_dims(int64_t T, std::initializer_list<std::pair<const char*, int
 ms_status check_bufs(const std::vector<Buf>& bufs) {
   for (const Buf& b : bufs) {
     if (!b.p) return fail(MS_ERR_NULL, "%s is NULL", b.name);
-    if ((int64_t)b.bytes >= kMaxBytes)
+    if (b.whole_below_2g31 && (int64_t)b.bytes >= kMaxBytes)
       return fail(MS_ERR_SHAPE, "%s is %zu bytes; each buffer must be < 2^31 bytes", b.name, b.bytes);
     if (((uintptr_t)b.p & 15) != 0) return fail(MS_ERR_ALIGN, "%s is not 16-byte aligned", b.name);
   }
@@ -97,12 +98,22 @@ ms_status check_bufs(const std::vector<Buf>& bufs) {
   return MS_OK;
 }
 
-ms_status check_workspace(const void* ws, size_t have, size_t need, std::vector<Buf>& bufs) {
+// The workspace as a whole may exceed 2^31 bytes: the kernels address each of
+// its regions (and each split-K slice) through a resource of its own, so it is
+// the largest region that must stay below 2^31 bytes.
+ms_status check_workspace(const void* ws, size_t have, size_t need, size_t max_region, std::vector<Buf>& bufs) {
   if (need == 0) return MS_OK;
+  if ((int64_t)max_region >= kMaxBytes)
+    return fail(MS_ERR_SHAPE, "a workspace region would be %zu bytes; each must be < 2^31 bytes", max_region);
   if (!ws) return fail(MS_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", need);
   if (have < need) return fail(MS_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", have, need);
-  bufs.push_back(Buf{ws, need, "workspace", true});
+  bufs.push_back(Buf{ws, need, "workspace", true, false});
   return MS_OK;
+}
+
+template <class Layout>
+ms_status check_workspace_layout(const void* ws, size_t have, const Layout& w, std::vector<Buf>& bufs) {
+  return check_workspace(ws, have, w.bytes, w.max_region, bufs);
 }
 
 // One-time (per device) check that the current device is a gfx950.
@@ -200,7 +211,7 @@ ms_status mlp_shard_bwd(const ms_bf16* X, const ms_bf16* A_i, const ms_bf16* B_i
       {dX_i, nbytes(T, h, 4), "dX_i", true},     {dA_i, nbytes(h, f_i, 2), "dA_i", true},
       {dB_i, nbytes(f_i, h, 2), "dB_i", true}};
   if (db1_i) bufs.push_back({db1_i, nbytes(f_i, 1, 2), "db1_i", true});
-  MS_TRY(check_workspace(workspace, workspace_bytes, mshard::mlp_workspace_layout(T, h, f_i).bytes, bufs));
+  MS_TRY(check_workspace_layout(workspace, workspace_bytes, mshard::mlp_workspace_layout(T, h, f_i), bufs));
   MS_TRY(check_bufs(bufs));
   MS_TRY(check_device());
   return launched(mshard::launch_mlp_bwd(X, A_i, B_i, H_i, Y_i, dZ, T, h, f_i, (int)gelu, dX_i, dA_i, dB_i,
@@ -222,7 +233,7 @@ ms_status vocab_ce_shard_fwd(const ms_bf16* X, const ms_bf16* E_i, const int64_t
   std::vector<Buf> bufs = {{X, nbytes(T, h, 2), "X", false},     {E_i, nbytes(h, v_i, 2), "E_i", false},
                            {target, nbytes(T, 1, 8), "target", false}, {m_i, nbytes(T, 1, 4), "m_i", true},
                            {s_i, nbytes(T, 1, 4), "s_i", true},       {z_i, nbytes(T, 1, 4), "z_i", true}};
-  MS_TRY(check_workspace(workspace, workspace_bytes, mshard::ce_workspace_layout(T, v_i).bytes, bufs));
+  MS_TRY(check_workspace_layout(workspace, workspace_bytes, mshard::ce_workspace_layout(T, v_i), bufs));
   MS_TRY(check_bufs(bufs));
   MS_TRY(check_device());
   return launched(mshard::launch_vocab_ce(X, E_i, target, T, h, v_i, vocab_start, m_i, s_i, z_i, workspace,
@@ -267,7 +278,7 @@ ms_status attn_shard_bwd(const ms_bf16* X, const ms_bf16* Wqkv_i, const ms_bf16*
                            {dZ, nbytes(T, h, 2), "dZ", false},        {dX_i, nbytes(T, h, 4), "dX_i", true},
                            {dWqkv_i, nbytes(h, 3 * nd, 2), "dWqkv_i", true},
                            {dWo_i, nbytes(nd, h, 2), "dWo_i", true}};
-  MS_TRY(check_workspace(workspace, workspace_bytes, mshard::attn_workspace_layout(b, s, h, n, d).bytes, bufs));
+  MS_TRY(check_workspace_layout(workspace, workspace_bytes, mshard::attn_workspace_layout(b, s, h, n, d), bufs));
   MS_TRY(check_bufs(bufs));
   MS_TRY(check_device());
   return launched(mshard::launch_attn_bwd(X, Wqkv_i, Wo_i, QKV, O, lse, dZ, b, s, h, n, d, causal == 1, dX_i,
@@ -293,7 +304,7 @@ ms_status vocab_ce_shard_bwd(const ms_bf16* X, const ms_bf16* E_i, const int64_t
                            {s, nbytes(t, T, 4), "s", false},            {dX_i, nbytes(T, h, 4), "dX_i", true},
                            {dE_i, nbytes(h, v_i, 2), "dE_i", true}};
   if (dloss) bufs.push_back({dloss, nbytes(T, 1, 4), "dloss", false});
-  MS_TRY(check_workspace(workspace, workspace_bytes, mshard::ce_bwd_workspace_layout(T, h, v_i).bytes, bufs));
+  MS_TRY(check_workspace_layout(workspace, workspace_bytes, mshard::ce_bwd_workspace_layout(T, h, v_i), bufs));
   MS_TRY(check_bufs(bufs));
   MS_TRY(check_device());
   return launched(mshard::launch_vocab_ce_bwd(X, E_i, target, m, s, (int)t, dloss, grad_scale, T, h, v_i,

@@ -11,6 +11,7 @@
 // private per-writer output space).
 #include "launch.hpp"
 
+#include <algorithm>
 #include <array>
 #include <cmath>
 #include <functional>
@@ -292,6 +293,7 @@ MlpWorkspace mlp_workspace_layout(int64_t T, int64_t h, int64_t f) {
   w.off_splitk = w.off_db1 + align((size_t)w.db1_parts * f * 4);
   const int S = w.plan.splits_dB > w.plan.splits_dA ? w.plan.splits_dB : w.plan.splits_dA;
   w.bytes = w.off_splitk + (S > 1 ? align((size_t)S * h * f * 4) : 0);
+  w.max_region = std::max({(size_t)T * f * 2, (size_t)w.db1_parts * f * 4, S > 1 ? (size_t)h * f * 4 : (size_t)0});
   return w;
 }
 
@@ -304,6 +306,7 @@ CeWorkspace ce_workspace_layout(int64_t T, int64_t v) {
   w.off_s = one;
   w.off_z = 2 * one;
   w.bytes = 3 * one;
+  w.max_region = (size_t)w.parts * T * 4;
   return w;
 }
 
@@ -331,6 +334,7 @@ CeBwdWorkspace ce_bwd_workspace_layout(int64_t T, int64_t h, int64_t v) {
   const BlockList dx{tile_count(T, h), block_cost(v, 1, kEpiF32)};
   plan_pair(h, v, T, dx, w.splits_dE, w.paired, w.dx_first, max_splits);
   w.bytes = w.off_splitk + (w.splits_dE > 1 ? align(slice * w.splits_dE) : 0);
+  w.max_region = std::max({(size_t)T * 16, (size_t)T * v * 2, w.splits_dE > 1 ? slice : (size_t)0});
   std::lock_guard<std::mutex> lock(mu);
   cache.emplace(key, w);
   return w;
@@ -361,6 +365,7 @@ AttnWorkspace attn_workspace_layout(int64_t b, int64_t s, int64_t h, int64_t n, 
   plan_pair(h, 3 * nd, T, dx, w.splits_wqkv, w.pair_x, w.x_first, max_splits);
   const int S = w.splits_wo > w.splits_wqkv ? w.splits_wo : w.splits_wqkv;
   w.bytes = w.off_splitk + (S > 1 ? align(slice * S) : 0);
+  w.max_region = std::max({(size_t)T * nd * 2, (size_t)n * T * 4, (size_t)T * 3 * nd * 2, S > 1 ? slice : (size_t)0});
   std::lock_guard<std::mutex> lock(mu);
   cache.emplace(key, w);
   return w;

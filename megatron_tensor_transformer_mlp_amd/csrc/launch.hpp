@@ -22,6 +22,7 @@ struct MlpWorkspace {
   size_t off_db1;     // fp32 [db1_parts x f]: per-writer bias-gradient column sums
   size_t off_splitk;  // fp32 [S x h*f]: weight-gradient split-K slices
   size_t bytes;
+  size_t max_region;  // largest piece one kernel addresses through one resource (a region or one slice)
   int db1_parts;
   BwdPlan plan;
 };
@@ -29,6 +30,7 @@ struct MlpWorkspace {
 struct CeWorkspace {
   size_t off_m, off_s, off_z;  // fp32 [parts x T] each
   size_t bytes;
+  size_t max_region;
   int parts;
 };
 
@@ -37,6 +39,7 @@ struct CeBwdWorkspace {
   size_t off_dL;      // bf16 [T x v]: the logit gradient
   size_t off_splitk;  // fp32 [S x h*v]: split-K slices of dE
   size_t bytes;
+  size_t max_region;
   int splits_dE;      // K split of dE (1 = none)
   bool paired;        // dE and dX share one launch
   bool dx_first;      // in the paired launch, dX's blocks lead
@@ -59,6 +62,7 @@ struct AttnWorkspace {
   size_t off_dqkv;    // bf16 [T x 3nd]
   size_t off_splitk;  // fp32 slices
   size_t bytes;
+  size_t max_region;
   int splits_wo, splits_wqkv;
   bool pair_o, o_first;   // dW_O with dO in one launch; dO's blocks lead
   bool pair_x, x_first;   // dWqkv with dX in one launch; dX's blocks lead

@@ -91,6 +91,20 @@ def test_bwd_validation(ms):
     assert bwd(gelu=-1) == ms.MS_ERR_ENUM
 
 
+def test_bwd_workspace_above_2g31_with_regions_below(ms):
+    """The workspace as a whole may pass 2^31 bytes when each region stays below:
+    at T = 1040000, h = 8, f = 1024 dH is 2.13e9 bytes and the bias-gradient
+    partials follow it.  The call gets past every size check and stops at the
+    planted overlap, which is checked last."""
+    T, h, f = 1040000, 8, 1024
+    need = ms.mlp_shard_workspace_bytes(T, h, f)
+    assert need > (1 << 31) and T * f * 2 < (1 << 31)
+    p = [FAKE + (i << 33) for i in range(12)]
+    rc = ms.LIB.mlp_shard_bwd(p[0], p[1], p[2], p[3], p[4], p[5], T, h, f, 0, p[6], p[3], p[8], None,
+                              p[10], need, None)
+    assert rc == ms.MS_ERR_ALIAS, ms.LIB.ms_last_error().decode()
+
+
 def test_ce_validation(ms):
     T, h, v = 128, 64, 512
     need = ms.vocab_ce_workspace_bytes(T, h, v)

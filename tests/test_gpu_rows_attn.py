@@ -1,8 +1,5 @@
 """GPU parity of the self-attention shard against the fp64 oracle (oracle/attn.py).
 
-Run by naming this file (pytest does not collect it by default):
-    python -u -m pytest tests/wip_attn_parity.py -x -v --timeout 600 --timeout-method thread
-
 Both sides start from the same seeded bf16 X, Wqkv_i, Wo_i and dZ; the oracle
 stays in fp64 throughout, the GPU rounds QKV, O, dO and dQKV to bf16 between
 steps.  Tolerance: relative Frobenius error <= 1e-2 on every output (QKV, O,

@@ -1,8 +1,5 @@
 """GPU parity of the vocab-parallel cross-entropy backward against the fp64 oracle.
 
-Run by naming this file (pytest does not collect it by default):
-    python -u -m pytest tests/wip_ce_bwd_parity.py -x -v --timeout 300 --timeout-method thread
-
 Both sides take the same inputs: seeded bf16 X, E_i, targets, per-token weights,
 and the forward partials (m, s) of every vocab shard, which the oracle computes
 in fp64 and which are rounded to fp32 for both sides.  Tolerance: relative

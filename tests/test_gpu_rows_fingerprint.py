@@ -1,9 +1,6 @@
 """GPU parity of the library's buffer fingerprints against the plain-Python oracle,
 and the fingerprint tracer on real library calls.
 
-Run by naming this file (pytest does not collect it by default):
-    python -u -m pytest tests/wip_fingerprint_gpu.py -x -v --timeout 300 --timeout-method thread
-
 Fingerprints are integers, so the bar is exact equality.
 """
 import numpy as np

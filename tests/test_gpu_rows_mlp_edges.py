@@ -1,8 +1,5 @@
 """GPU parity of the MLP shard on degenerate and extreme inputs, against the fp64 oracle.
 
-Run by naming this file (pytest does not collect it by default):
-    python -u -m pytest tests/wip_mlp_edges_gpu.py -x -v --timeout 300 --timeout-method thread
-
 A = 0 with a bias: every H row equals b1, Y rows are GeLU(b1), dX is exactly 0.
 X 1024 times the workloads' scale: GeLU and GeLU' reduce to max(x, 0) and a
 step, and nothing may turn into NaN.  Tolerance: relative Frobenius 1e-2.

@@ -351,3 +351,131 @@ def test_pins_catch_wrong_target_offset(rng, monkeypatch):
     monkeypatch.setattr(oracle, "vocab_ce_shard", bad)
     with pytest.raises(AssertionError):
         test_vocab_shard_ce_identity(rng, [48, 48])
+
+
+# ----------------------------------------------------------------------------- input widening
+def _bf16_by_definition(u: int) -> float:
+    """bf16 bit pattern -> value from the format's definition (1 sign bit, 8
+    exponent bits with bias 127, 7 fraction bits; subnormals, infinities, NaN)."""
+    sign = -1.0 if (u >> 15) & 1 else 1.0
+    e = (u >> 7) & 0xFF
+    f = u & 0x7F
+    if e == 0xFF:
+        return math.nan if f else sign * math.inf
+    if e == 0:
+        return sign * math.ldexp(f, -126 - 7)
+    return sign * math.ldexp(128 + f, e - 127 - 7)
+
+
+def test_bf16_widening_every_bit_pattern():
+    """bf16_to_f64 on all 65536 patterns equals the format's definition and
+    torch's bfloat16 -> float64 conversion (NaN patterns stay NaN)."""
+    u = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = oracle.bf16_to_f64(u)
+    assert got.dtype == np.float64 and got.shape == (1 << 16,)
+    want = np.array([_bf16_by_definition(int(x)) for x in u], dtype=np.float64)
+    nan = np.isnan(want)
+    assert nan.sum() == 2 * 127  # both signs, every nonzero fraction
+    np.testing.assert_array_equal(np.isnan(got), nan)
+    np.testing.assert_array_equal(got[~nan], want[~nan])
+    # signed zeros keep their sign
+    assert math.copysign(1.0, got[0x8000]) == -1.0 and math.copysign(1.0, got[0]) == 1.0
+    tv = torch.from_numpy(u.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(np.isnan(tv), nan)
+    np.testing.assert_array_equal(got[~nan], tv[~nan])
+
+
+def test_oracle_entry_points_widen_bf16_inputs(rng):
+    """The oracle's functions take raw bf16 patterns (uint16) and give exactly
+    what they give on the same values already widened to float64."""
+    T, h, f, v = 6, 8, 16, 24
+    bits = lambda *s: (rng.integers(0, 1 << 16, size=s, dtype=np.uint32) & 0x3FFF | 0x3000).astype(np.uint16)
+    X, A, B, E, dZ = bits(T, h), bits(h, f), bits(f, h), bits(h, v), bits(T, h)
+    w = lambda a: torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    y = rng.integers(0, v, size=T)
+    fb, fw = oracle.mlp_shard_fwd(X, A, B), oracle.mlp_shard_fwd(w(X), w(A), w(B))
+    bb, bw = oracle.mlp_shard_bwd(X, A, B, dZ), oracle.mlp_shard_bwd(w(X), w(A), w(B), w(dZ))
+    cb, cw = oracle.vocab_ce_shard(X, E, y, 0), oracle.vocab_ce_shard(w(X), w(E), y, 0)
+    for got, want in [(fb, fw), (bb, bw), (cb, cw)]:
+        for k in want:
+            np.testing.assert_array_equal(got[k], want[k])
+
+
+# ----------------------------------------------------------------------------- CE over several token blocks
+@pytest.mark.parametrize("T", [1100, 1536])
+def test_ce_across_token_blocks(rng, T):
+    """The CE oracle walks tokens 512 at a time (memory only).  At T past two
+    block edges: the combined vocab shards and the unsharded CE equal torch's
+    cross_entropy (fp64) on every token, and a permuted row subset gives the
+    same values as the full evaluation."""
+    h, split = 8, [40, 24, 33]
+    v = sum(split)
+    X = _rand(rng, T, h)
+    E = _rand(rng, h, v, scale=0.8)
+    y = rng.integers(0, v, size=T)
+    offs = np.cumsum([0] + split)
+    parts = [oracle.vocab_ce_shard(X, E[:, offs[r]:offs[r + 1]], y, int(offs[r])) for r in range(len(split))]
+    c = oracle.ce_combine([p["m"] for p in parts], [p["s"] for p in parts], [p["z"] for p in parts])
+    tl = torch.nn.functional.cross_entropy(torch.tensor(X @ E), torch.tensor(y), reduction="none").numpy()
+    np.testing.assert_allclose(c["loss"], tl, rtol=1e-13)
+    np.testing.assert_allclose(oracle.full_vocab_ce(X, E, y), tl, rtol=1e-13)
+    assert abs(c["mean"] - math.fsum(tl.tolist()) / T) <= 1e-13 * abs(tl.mean())
+    R = rng.permutation(T)[: T - 3]
+    np.testing.assert_allclose(oracle.full_vocab_ce(X, E, y, rows=R), tl[R], rtol=1e-13)
+    sub = oracle.vocab_ce_shard(X, E, y, 0, rows=R)
+    np.testing.assert_allclose(sub["m"] + np.log(sub["s"]) - sub["z"], tl[R], rtol=1e-13)
+
+
+def test_pins_catch_bf16_shift_of_15(monkeypatch):
+    def bad(u):
+        u32 = np.ascontiguousarray(u, dtype=np.uint16).astype(np.uint32) << 15
+        return u32.view(np.float32).astype(np.float64)
+
+    monkeypatch.setattr(oracle, "bf16_to_f64", bad)
+    with pytest.raises(AssertionError):
+        test_bf16_widening_every_bit_pattern()
+
+
+def test_pins_catch_token_block_offset(rng, monkeypatch):
+    """A block walk whose second and later blocks start one token late."""
+    def bad_full(X, E, targets, rows=None, block=512):
+        X, E = ref._f64(X), ref._f64(E)
+        targets = np.asarray(targets, dtype=np.int64)
+        R = np.arange(X.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+        out = np.empty(len(R))
+        for b0 in range(0, len(R), block):
+            s0 = b0 + (1 if b0 else 0)
+            rb = R[s0:s0 + block]
+            L = X[rb] @ E
+            val = special.logsumexp(L, axis=1) - L[np.arange(len(rb)), targets[rb]]
+            out[b0:b0 + len(val)] = val
+        return out
+
+    monkeypatch.setattr(oracle, "full_vocab_ce", bad_full)
+    with pytest.raises(AssertionError):
+        test_ce_across_token_blocks(rng, 1100)
+
+
+def test_pins_catch_shard_block_offset(rng, monkeypatch):
+    """The same planted mistake in the shard partials' block walk."""
+    orig = ref.vocab_ce_shard
+
+    def bad(X, E_i, targets, vocab_start, rows=None, block=512):
+        n = np.asarray(X).shape[0]
+        R = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+        R = np.concatenate([R[:block], R[block + 1:], R[-1:]])  # later blocks one token late
+        return orig(X, E_i, targets, vocab_start, rows=R, block=block)
+
+    monkeypatch.setattr(oracle, "vocab_ce_shard", bad)
+    with pytest.raises(AssertionError):
+        test_ce_across_token_blocks(rng, 1100)
+
+
+def test_pins_catch_bf16_shift_inside_entry_points(rng, monkeypatch):
+    def bad(u):
+        u32 = np.ascontiguousarray(u, dtype=np.uint16).astype(np.uint32) << 15
+        return u32.view(np.float32).astype(np.float64)
+
+    monkeypatch.setattr(ref, "bf16_to_f64", bad)
+    with pytest.raises(AssertionError):
+        test_oracle_entry_points_widen_bf16_inputs(rng)
