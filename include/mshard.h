@@ -286,6 +286,15 @@ const char* ms_last_error(void);
 /* Library version string (host pointer, static storage). */
 const char* ms_version(void);
 
+/* Compute units and peak shader clock of HIP device `device`, as the runtime
+ * reports them (hipDeviceAttributeMultiprocessorCount and
+ * hipDeviceAttributeClockRate), so that a caller can state the dense bf16 MFMA
+ * peak of the card it measures on: compute_units x 4096 flop per clock x clock
+ * (gfx950: 4 matrix cores per compute unit, 1024 bf16 flop per clock each).
+ * Outputs are HOST pointers.  Errors: MS_ERR_NULL for a NULL output,
+ * MS_ERR_HIP if the runtime query fails (no device, bad index). */
+ms_status ms_device_info(int32_t device, int32_t* compute_units, int32_t* clock_khz);
+
 #ifdef __cplusplus
 }
 #endif

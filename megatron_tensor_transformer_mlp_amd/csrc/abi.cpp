@@ -370,4 +370,16 @@ const char* ms_last_error(void) { return g_last_error.c_str(); }
 
 const char* ms_version(void) { return "mshard 0.1.0 (gfx950)"; }
 
+ms_status ms_device_info(int32_t device, int32_t* compute_units, int32_t* clock_khz) {
+  if (!compute_units || !clock_khz) return fail(MS_ERR_NULL, "an output pointer is NULL");
+  int cus = 0, khz = 0;
+  hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&khz, hipDeviceAttributeClockRate, device);
+  if (e != hipSuccess) return fail(MS_ERR_HIP, "hipDeviceGetAttribute(device %d): %s", (int)device, hipGetErrorString(e));
+  *compute_units = cus;
+  *clock_khz = khz;
+  g_last_error.clear();
+  return MS_OK;
+}
+
 }  // extern "C"

@@ -144,7 +144,7 @@ __device__ __forceinline__ void map_tile(const GemmGeom& g, int b, int G, int& t
 //
 // Layouts (16-byte slots; a K-major tile is [256 m/n rows][32 k], an
 // M/N-major tile is [32 k rows][256 m/n columns]):
-//   K-major : slot(r, c) = (r/16)*64 + (r%16)*4 + (c ^ ((r%16)/4 % 4))
+//   K-major : slot(r, c) = (r/16)*64 + (r%16)*4 + (c ^ ((r%16)/2 % 4))
 //                                                   c = k/8 (8 k values)
 //   MN-major: slot(k, j) = k*32 + (j ^ 2*((k%4) | 4*((k/8)%2)))
 //                                                   j = col/8 (8 columns)
@@ -152,11 +152,14 @@ __device__ __forceinline__ void map_tile(const GemmGeom& g, int b, int G, int& t
 // instruction's 64 lanes read whole 64-byte row segments or 512-byte k rows:
 // neighbouring lanes read neighbouring 16 bytes and the memory pipeline merges
 // them into full cache-line requests.  The XOR terms only permute slots
-// within a row; they make the fragment reads conflict-free (LDS serves 16
-// lanes x 16 bytes or 32 lanes x 8 bytes, all 64 banks, per cycle): a K-major
-// fragment's 16 rows of one chunk fall in 16 different 4-bank groups, and the
-// 8 k rows x 32 bytes that 32 lanes of an M/N-major transposing read touch
-// fall in 8 different 32-byte windows.
+// within a row; they make the fragment reads conflict-free.  A ds_read_b128
+// is served 8 lanes at a time, whose 16-byte chunks must lie in different
+// 16-byte slots of a 128-byte window: a K-major fragment's 8 consecutive rows
+// of one chunk do (rows r and r+1 sit 64 bytes apart, the XOR of (r%16)/2
+// moves pairs of rows by 16 bytes); with an XOR of (r%16)/4 pairs of rows
+// share a slot and the read runs at half rate (measured on gfx950: 128 versus
+// 250 bytes per clock per CU).  The 8 k rows x 32 bytes that 32 lanes of an
+// M/N-major transposing read touch fall in 8 different 32-byte windows.
 
 typedef __attribute__((address_space(3))) char lds_char;
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -218,9 +221,9 @@ __device__ __forceinline__ DmaLanes dma_lanes(const Operand& op, int mn0, int nm
   const uint32_t ldb = (uint32_t)op.ld * 2u;
   if constexpr (KMAJOR) {
     // instruction 4w + i writes slots (4w + i)*64 + l: row (4w + i)*16 + l/4,
-    // chunk (l%4) ^ (l/16 % 4)
+    // chunk (l%4) ^ (l/8 % 4)
     const uint32_t r = (uint32_t)wave * 64u + (uint32_t)(lane >> 2);
-    const int c = (lane & 3) ^ ((lane >> 4) & 3);
+    const int c = (lane & 3) ^ ((lane >> 3) & 3);
     d.v[0] = r * ldb + (uint32_t)c * 16u;
     const int tail = K & (kBK - 1);
     d.v[1] = (c * 8 < tail) ? d.v[0] : kOOB;
@@ -291,7 +294,7 @@ __device__ __forceinline__ FragBase<KMAJOR> frag_lane_base(int lane) {
   FragBase<KMAJOR> fb;
   if constexpr (KMAJOR) {
     // row l%16 of the block, chunk l/16
-    fb.x[0] = ((lane & 15) * 4 + ((lane >> 4) ^ ((lane >> 2) & 3))) * 16;
+    fb.x[0] = ((lane & 15) * 4 + ((lane >> 4) ^ ((lane >> 1) & 3))) * 16;
   } else {
     // lane x = 4e + q of group g: k row 8g + e (+ 4h), columns 4q..4q+3 of the
     // block; the layout's XOR moves block b to position b ^ F within the row

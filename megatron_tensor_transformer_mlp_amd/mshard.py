@@ -31,7 +31,7 @@ EXPORTED = ("mlp_shard_workspace_bytes", "mlp_shard_fwd", "mlp_shard_bwd", "voca
             "vocab_ce_shard_fwd", "ce_combine_workspace_bytes", "ce_combine", "vocab_ce_bwd_workspace_bytes",
             "vocab_ce_shard_bwd", "attn_shard_workspace_bytes", "attn_shard_fwd", "attn_shard_bwd",
             "ms_fingerprint_words", "ms_fingerprint", "ms_arm_kernel_events",
-            "ms_last_error", "ms_version")
+            "ms_last_error", "ms_version", "ms_device_info")
 
 # ms_kernel ids: the single GEMM launches ms_arm_kernel_events can bracket
 KERNELS = {"ce_gemm": 0, "fwd_h": 1, "fwd_z": 2, "bwd_dh": 3, "bwd_db": 4, "bwd_da": 5, "bwd_dx": 6,
@@ -77,6 +77,7 @@ def _load() -> ctypes.CDLL:
         "ms_arm_kernel_events": (ctypes.c_int, [ctypes.c_int, _vp, _vp]),
         "ms_last_error": (ctypes.c_char_p, []),
         "ms_version": (ctypes.c_char_p, []),
+        "ms_device_info": (ctypes.c_int, [_i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -90,6 +91,13 @@ LIB = _load()
 
 def version() -> str:
     return LIB.ms_version().decode()
+
+
+def device_info(device: int = 0) -> dict:
+    """Compute units and peak shader clock (kHz) of a HIP device, from the runtime."""
+    cus, khz = _i32(0), _i32(0)
+    _check(LIB.ms_device_info(device, ctypes.byref(cus), ctypes.byref(khz)), "ms_device_info")
+    return {"compute_units": cus.value, "clock_khz": khz.value}
 
 
 def arm_kernel_events(kernel: str, before: Optional[torch.cuda.Event], after: Optional[torch.cuda.Event]) -> None:

@@ -6,9 +6,10 @@ CE partials (m, s, z), the per-token loss (max relative) and the mean loss.
 
 Sizes: full comparisons at sizes the oracle finishes in seconds (a tiny layer,
 and ragged shapes spanning several 256-wide tiles, a K tail and split-K weight
-gradients); at the five workloads' full sizes, sampled token rows and FFN
-columns that the oracle evaluates one by one (tile-edge indices always
-included).
+gradients); at the four large workloads' full sizes, sampled token rows and
+FFN columns that the oracle evaluates one by one (tile-edge indices always
+included) for the MLP, and every token for the vocab-parallel CE.  Bitwise
+determinism at the benchmark's shape, with a concurrent stream.
 """
 import hashlib
 
@@ -151,13 +152,13 @@ def test_mlp_full_size_sampled(ms, name):
 
 
 @pytest.mark.parametrize("name", BIG)
-def test_ce_full_size_sampled(ms, name):
-    """All t vocab shards on the GPU, combined on the GPU; the oracle checks shard 0's
-    partials and the combined per-token loss on sampled tokens."""
+def test_ce_full_size(ms, name):
+    """All t vocab shards on the GPU, combined on the GPU.  The oracle evaluates
+    every shard's partials over all T tokens: shard 0's (m, s, z), the per-token
+    loss of every token and the mean over all T tokens are compared with it
+    (at most 1.5e13 fp64 flops, the 176B-scale layer)."""
     c = inputs.CONFIGS[name]
     print(f"case ce {name} T={c.T} h={c.h} v_i={c.v_i} t={c.t}", flush=True)
-    nrows = 64 if c.h * c.v_global > 1e9 else 256
-    rows = inputs.sample_indices(c.T, nrows, 13, [0, 255, 256, c.T - 1])
     base = inputs.make_config_inputs(c, want=("X", "targets"))
     X = dev(base["X"])
     tg = torch.from_numpy(base["targets"]).cuda()
@@ -167,23 +168,25 @@ def test_ce_full_size_sampled(ms, name):
         E = inputs.make_config_inputs(c, rank=r, want=("E",))["E"]
         m, s, z = ms.vocab_ce_shard_fwd(X, dev(E), tg, r * c.v_i)
         ms_.append(m); ss_.append(s); zs_.append(z)
-        o = oracle.vocab_ce_shard(base["X"], E, base["targets"], r * c.v_i, rows=rows)
+        o = oracle.vocab_ce_shard(base["X"], E, base["targets"], r * c.v_i)
         o_m.append(o["m"]); o_s.append(o["s"]); o_z.append(o["z"])
         if r == 0:
             for k, got in (("m", m), ("s", s), ("z", z)):
-                e = rel_fro(host(got)[rows], o[k])
+                e = rel_fro(host(got), o[k])
                 print(f"  shard0 {k} rel-fro {e:.2e}", flush=True)
                 assert e <= CE_TOL, (k, e)
         del E
     loss, mean = ms.ce_combine(torch.stack(ms_), torch.stack(ss_), torch.stack(zs_))
     torch.cuda.synchronize()
-    want = oracle.ce_combine(o_m, o_s, o_z)["loss"]
+    want = oracle.ce_combine(o_m, o_s, o_z)
     gl = host(loss)
-    err = np.max(np.abs(gl[rows] - want) / np.abs(want))
-    print(f"  loss max-rel {err:.2e}; mean {host(mean)[0]:.6f} (ln v = {np.log(c.v_global):.6f})", flush=True)
+    err = np.max(np.abs(gl - want["loss"]) / np.abs(want["loss"]))
+    gmean = host(mean)[0]
+    merr = abs(gmean - want["mean"]) / abs(want["mean"])
+    print(f"  loss max-rel {err:.2e} over {c.T} tokens; mean {gmean:.6f} vs oracle {want['mean']:.6f}"
+          f" (rel {merr:.2e}; ln v = {np.log(c.v_global):.6f})", flush=True)
     assert err <= CE_TOL
-    assert abs(host(mean)[0] - gl.mean()) <= 1e-6 * abs(gl.mean())
-    assert abs(gl[rows].mean() - want.mean()) <= CE_TOL * abs(want.mean())
+    assert merr <= CE_TOL
 
 
 # ----------------------------------------------------------------------------- determinism
@@ -203,6 +206,45 @@ def test_bitwise_determinism(ms):
         h = digest(H, Y, Z, dX, dA, dB, db1, m, s, z, loss, mean)
         ref = ref or h
         assert h == ref, it
+
+
+def test_bitwise_determinism_bench_shape_concurrent(ms):
+    """At the GPT-2 1.5B-like layer, the shape the benchmark times (its backward
+    runs (dB, dH) as one paired launch), every entry point of the step gives
+    identical bytes over 12 runs: dirty workspaces filled differently each run,
+    fresh outputs, and on every other run a stream of unrelated GEMMs running
+    at the same time on a second stream, so the library's workgroups share the
+    CUs with another kernel in a different order each time."""
+    c = inputs.CONFIGS["gpt2_1p5b"]
+    d = inputs.make_config_inputs(c)
+    X, A, B, dZ, E = dev(d["X"]), dev(d["A"]), dev(d["B"]), dev(d["dZ"]), dev(d["E"])
+    tg = torch.from_numpy(d["targets"]).cuda()
+    side = torch.cuda.Stream()
+    busy_a = torch.randn(4096, 4096, device="cuda", dtype=torch.bfloat16)
+    busy_b = torch.randn(4096, 4096, device="cuda", dtype=torch.bfloat16)
+    nbytes = {"mlp": ms.mlp_shard_workspace_bytes(c.T, c.h, c.f_i),
+              "ce": ms.vocab_ce_workspace_bytes(c.T, c.h, c.v_i),
+              "ce_bwd": ms.vocab_ce_bwd_workspace_bytes(c.T, c.h, c.v_i)}
+    ref = None
+    for it in range(12):
+        ws = {k: torch.full((n,), 17 * it + 3, dtype=torch.uint8, device="cuda") for k, n in nbytes.items()}
+        torch.cuda.synchronize()
+        if it % 2:
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                for _ in range(40):
+                    busy_c = busy_a @ busy_b
+        H, Y, Z = ms.mlp_shard_fwd(X, A, B)
+        dX, dA, dB, _ = ms.mlp_shard_bwd(X, A, B, H, Y, dZ, workspace=ws["mlp"])
+        m, s, z = ms.vocab_ce_shard_fwd(X, E, tg, 0, workspace=ws["ce"])
+        loss, mean = ms.ce_combine(m[None], s[None], z[None])
+        cdX, cdE = ms.vocab_ce_shard_bwd(X, E, tg, m[None], s[None], 0, workspace=ws["ce_bwd"])
+        torch.cuda.synchronize()
+        h = digest(H, Y, Z, dX, dA, dB, m, s, z, loss, mean, cdX, cdE)
+        print(f"  run {it} {'with' if it % 2 else 'without'} a concurrent stream: {h[:16]}", flush=True)
+        ref = ref or h
+        assert h == ref, it
+    del busy_c
 
 
 # ----------------------------------------------------------------------------- multi-rank emulation
@@ -253,3 +295,34 @@ def test_ce_target_ownership_edges(ms):
     d2["targets"] = np.zeros(T, dtype=np.int64)  # all owned by rank 0
     _, _, z2 = run_ce(ms, d2)
     assert not host(z2).any()
+
+
+# ----------------------------------------------------------------------------- degenerate and extreme inputs
+# A = 0 with a bias: every H row equals b1, Y rows are GeLU(b1), dX is exactly 0.
+# X 1024 times the workloads' scale: GeLU and GeLU' reduce to max(x, 0) and a
+# step, and nothing may turn into NaN.
+@pytest.mark.parametrize("gelu", ["erf", "tanh"])
+@pytest.mark.parametrize("label", ["zeroA", "bigX"])
+def test_mlp_edges(ms, gelu, label):
+    T, h, f = 300, 136, 264
+    print(f"case mlp edges {label} gelu={gelu} T={T} h={h} f={f}", flush=True)
+    x = inputs.make_inputs(T, h, f, 8, bias=True)
+    X, A = x["X"], x["A"]
+    if label == "zeroA":
+        A = np.zeros_like(A)
+    else:
+        X = inputs.round_to_bf16_bits(inputs.bf16_bits_to_f32(X) * np.float32(1024.0))
+    H, Y, Z = ms.mlp_shard_fwd(dev(X), dev(A), dev(x["B"]), dev(x["b1"]), gelu=gelu)
+    dX, dA, dB, db1 = ms.mlp_shard_bwd(dev(X), dev(A), dev(x["B"]), H, Y, dev(x["dZ"]), gelu=gelu, want_db1=True)
+    torch.cuda.synchronize()
+    want = {**oracle.mlp_shard_fwd(X, A, x["B"], x["b1"], gelu),
+            **oracle.mlp_shard_bwd(X, A, x["B"], x["dZ"], x["b1"], gelu)}
+    got = {"H": host(H), "Y": host(Y), "Z": host(Z), "dA": host(dA), "dB": host(dB), "db1": host(db1), "dX": host(dX)}
+    for k, v in got.items():
+        assert np.isfinite(v).all(), k
+    if label == "zeroA":
+        assert np.abs(got["dX"]).max() == 0
+        del got["dX"]
+    errs = {k: rel_fro(v, want[k]) for k, v in got.items()}
+    print("  rel-fro", {k: f"{e:.2e}" for k, e in errs.items()}, flush=True)
+    assert all(e <= MLP_TOL for e in errs.values()), errs
