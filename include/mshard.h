@@ -129,6 +129,23 @@ ms_status vocab_ce_shard_fwd(const ms_bf16* X, const ms_bf16* E_i, const int64_t
                              float* m_i, float* s_i, float* z_i,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* vocab_ce_shard_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under stream capture, tight serving loops,
+ * harnesses that forbid allocation).  The per-tile partials live in a static
+ * device array of 32 MiB, one per GPU, held until the process ends; its device
+ * address is looked up once per GPU on the first call there.  Sizes whose
+ * partials need more (vocab_ce_workspace_bytes(T, h, v_i) > 32 MiB, i.e.
+ * 12 * T * ceil(v_i / 256) bytes rounded up) are refused with MS_ERR_WORKSPACE
+ * before anything is enqueued.  Every call on a GPU uses that GPU's array and
+ * leaves its own partials in it: calls that overlap in time on one GPU (other
+ * streams, other threads) race and must not be made.  Each call writes every
+ * partial it reads, so nothing needs clearing between calls.  Arguments,
+ * outputs, validation and results are those of vocab_ce_shard_fwd; the same
+ * kernels run, so the outputs are bitwise those of vocab_ce_shard_fwd. */
+ms_status vocab_ce_shard_fwd_noalloc(const ms_bf16* X, const ms_bf16* E_i, const int64_t* target,
+                                     int64_t T, int64_t h, int64_t v_i, int64_t vocab_start,
+                                     float* m_i, float* s_i, float* z_i, void* stream);
+
 /* Bytes of device workspace ce_combine needs (currently 0 for valid sizes). */
 size_t ce_combine_workspace_bytes(int32_t t, int64_t T);
 

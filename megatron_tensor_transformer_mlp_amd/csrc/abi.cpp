@@ -312,6 +312,30 @@ ms_status vocab_ce_shard_bwd(const ms_bf16* X, const ms_bf16* E_i, const int64_t
                   "vocab_ce_shard_bwd");
 }
 
+ms_status vocab_ce_shard_fwd_noalloc(const ms_bf16* X, const ms_bf16* E_i, const int64_t* target, int64_t T,
+                                     int64_t h, int64_t v_i, int64_t vocab_start, float* m_i, float* s_i, float* z_i,
+                                     void* stream) {
+  const DisarmOnReturn disarm{mshard::kTkCeGemm, mshard::kTkCeGemm};
+  MS_TRY(check_dims(T, {{"h", h}, {"v_i", v_i}}));
+  if (vocab_start < 0) return fail(MS_ERR_SHAPE, "vocab_start must be >= 0 (got %lld)", (long long)vocab_start);
+  const size_t need = mshard::ce_workspace_layout(T, v_i).bytes;
+  if (need > mshard::kNoAllocScratchBytes)
+    return fail(MS_ERR_WORKSPACE,
+                "vocab_ce_shard_fwd_noalloc: these sizes need %zu bytes of scratch, more than its fixed %zu",
+                need, mshard::kNoAllocScratchBytes);
+  std::vector<Buf> bufs = {{X, nbytes(T, h, 2), "X", false},           {E_i, nbytes(h, v_i, 2), "E_i", false},
+                           {target, nbytes(T, 1, 8), "target", false}, {m_i, nbytes(T, 1, 4), "m_i", true},
+                           {s_i, nbytes(T, 1, 4), "s_i", true},        {z_i, nbytes(T, 1, 4), "z_i", true}};
+  MS_TRY(check_bufs(bufs));
+  MS_TRY(check_device());
+  void* scratch = nullptr;
+  const hipError_t e = mshard::noalloc_scratch(&scratch);
+  if (e != hipSuccess) return fail(MS_ERR_HIP, "scratch address lookup: %s", hipGetErrorString(e));
+  return launched(mshard::launch_vocab_ce(X, E_i, target, T, h, v_i, vocab_start, m_i, s_i, z_i, scratch,
+                                          (hipStream_t)stream),
+                  "vocab_ce_shard_fwd_noalloc");
+}
+
 size_t ce_combine_workspace_bytes(int32_t t, int64_t T) {
   (void)t;
   (void)T;

@@ -641,6 +641,34 @@ hipError_t launch_attn_bwd(const uint16_t* X, const uint16_t* Wqkv, const uint16
   return err;
 }
 
+// Device-resident scratch of the allocation-free CE entry point: the per-tile
+// (m, s, z) partials, up to kNoAllocScratchBytes.  One copy per GPU, kept for
+// the life of the process; every call on a GPU uses that GPU's copy.  Host code
+// never passes the array's name to a kernel (in host code it is only a
+// stand-in for the symbol): it looks the device address up once per device
+// and passes that.
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void** ptr) {
+  static std::mutex mu;
+  static std::map<int, void*> per_device;
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = per_device.find(dev);
+  if (it != per_device.end()) {
+    *ptr = it->second;
+    return hipSuccess;
+  }
+  void* p = nullptr;
+  err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (err != hipSuccess) return err;
+  per_device.emplace(dev, p);
+  *ptr = p;
+  return hipSuccess;
+}
+
 hipError_t launch_ce_combine(const float* m, const float* s, const float* z, int t, int64_t T, float* loss,
                              float* loss_mean, hipStream_t st) {
   hipLaunchKernelGGL(ce_combine_tokens, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, st, m, s, z, t, T, loss);

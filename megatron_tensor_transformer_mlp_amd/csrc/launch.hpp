@@ -110,6 +110,12 @@ hipError_t launch_attn_bwd(const uint16_t* X, const uint16_t* Wqkv, const uint16
                            const uint16_t* O, const float* lse, const uint16_t* dZ, int64_t b, int64_t s, int64_t h,
                            int64_t n, int64_t d, bool causal, float* dX, uint16_t* dWqkv, uint16_t* dWo, void* ws,
                            hipStream_t st);
+// Scratch of the allocation-free CE entry point: one static device array per
+// GPU, sized for the per-tile partials of every workload shape in use.
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+// Device address of this GPU's scratch array (looked up once per device, with
+// that device current).
+hipError_t noalloc_scratch(void** ptr);
 uint64_t fingerprint_chunk_count(uint64_t bytes, uint64_t chunk);
 hipError_t launch_fingerprint(const void* buf, uint64_t bytes, uint64_t chunk, uint64_t* out, hipStream_t st);
 hipError_t launch_ce_combine(const float* m, const float* s, const float* z, int t, int64_t T, float* loss,

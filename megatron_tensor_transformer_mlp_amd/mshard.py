@@ -8,7 +8,8 @@ import fails loudly; there is no fallback.
 Entry points mirror the C ABI in include/mshard.h:
   mlp_shard_fwd, mlp_shard_bwd, vocab_ce_shard_fwd, ce_combine,
   vocab_ce_shard_bwd, attn_shard_fwd, attn_shard_bwd, fingerprint, plus the
-  workspace-size queries.
+  workspace-size queries, the allocation-free vocab_ce_shard_fwd_noalloc and
+  device_info.
 """
 from __future__ import annotations
 
@@ -31,7 +32,7 @@ EXPORTED = ("mlp_shard_workspace_bytes", "mlp_shard_fwd", "mlp_shard_bwd", "voca
             "vocab_ce_shard_fwd", "ce_combine_workspace_bytes", "ce_combine", "vocab_ce_bwd_workspace_bytes",
             "vocab_ce_shard_bwd", "attn_shard_workspace_bytes", "attn_shard_fwd", "attn_shard_bwd",
             "ms_fingerprint_words", "ms_fingerprint", "ms_arm_kernel_events",
-            "ms_last_error", "ms_version", "ms_device_info")
+            "ms_last_error", "ms_version", "ms_device_info", "vocab_ce_shard_fwd_noalloc")
 
 # ms_kernel ids: the single GEMM launches ms_arm_kernel_events can bracket
 KERNELS = {"ce_gemm": 0, "fwd_h": 1, "fwd_z": 2, "bwd_dh": 3, "bwd_db": 4, "bwd_da": 5, "bwd_dx": 6,
@@ -78,6 +79,7 @@ def _load() -> ctypes.CDLL:
         "ms_last_error": (ctypes.c_char_p, []),
         "ms_version": (ctypes.c_char_p, []),
         "ms_device_info": (ctypes.c_int, [_i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
+        "vocab_ce_shard_fwd_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -272,6 +274,22 @@ def vocab_ce_shard_fwd(X, E_i, target, vocab_start: int, workspace: Optional[tor
         st = LIB.vocab_ce_shard_fwd(_ptr(X), _ptr(E_i), _ptr(target), T, h, v_i, int(vocab_start), _ptr(m), _ptr(s),
                                     _ptr(z), _ptr(ws), nbytes, _stream(X.device))
     _check(st, "vocab_ce_shard_fwd")
+    return m, s, z
+
+
+def vocab_ce_shard_fwd_noalloc(X, E_i, target, vocab_start: int, out):
+    """vocab_ce_shard_fwd through the library's allocation-free entry point: the caller
+    passes the outputs (m, s, z) fp32 [T] and no workspace; nothing is allocated."""
+    T, h = X.shape
+    v_i = E_i.shape[1]
+    _dev(X, "X", torch.bfloat16, (T, h)); _dev(E_i, "E_i", torch.bfloat16, (h, v_i))
+    _dev(target, "target", torch.int64, (T,))
+    _same_device(X.device, E_i=E_i, target=target)
+    m, s, z = _outs(out, tuple((n, torch.float32, (T,), False) for n in ("m", "s", "z")), X.device)
+    with _on(X.device):
+        st = LIB.vocab_ce_shard_fwd_noalloc(_ptr(X), _ptr(E_i), _ptr(target), T, h, v_i, int(vocab_start), _ptr(m),
+                                            _ptr(s), _ptr(z), _stream(X.device))
+    _check(st, "vocab_ce_shard_fwd_noalloc")
     return m, s, z
 
 

@@ -72,6 +72,15 @@ inline hipError_t hipDeviceGetAttribute(int* value, hipDeviceAttribute_t attr, i
   return hipSuccess;
 }
 
+// Static device arrays: the host array stands for the device one, and a
+// symbol's device address is the host array's own address.
+#define __align__(n) __attribute__((aligned(n)))
+#define HIP_SYMBOL(s) (&(s))
+inline hipError_t hipGetSymbolAddress(void** ptr, const void* symbol) {
+  *ptr = const_cast<void*>(symbol);
+  return hipSuccess;
+}
+
 struct dim3 {
   unsigned x, y, z;
   dim3(unsigned a = 1, unsigned b = 1, unsigned c = 1) : x(a), y(b), z(c) {}

@@ -120,6 +120,26 @@ def test_ce_validation(ms):
     assert ce(z=p[4] + 16) == ms.MS_ERR_ALIAS
 
 
+def test_ce_noalloc_validation(ms):
+    """The allocation-free CE entry point validates like vocab_ce_shard_fwd and refuses,
+    before any device call, sizes whose partials exceed its fixed 32 MiB scratch."""
+    p = [FAKE + (i << 33) for i in range(6)]
+
+    def ce(T=128, h=64, v=512, start=0, X=p[0], z=p[5]):
+        return ms.LIB.vocab_ce_shard_fwd_noalloc(X, p[1], p[2], T, h, v, start, p[3], p[4], z, None)
+
+    assert ce(v=500) == ms.MS_ERR_SHAPE
+    assert ce(start=-1) == ms.MS_ERR_SHAPE
+    assert ce(X=None) == ms.MS_ERR_NULL
+    assert ce(z=p[4] + 16) == ms.MS_ERR_ALIAS
+    # 12 bytes of partials per token and 256-column tile: 2^20 tokens x 32 tiles is 384 MiB
+    assert ce(T=1 << 20, h=8, v=8192) == ms.MS_ERR_WORKSPACE
+    assert "scratch" in ms.LIB.ms_last_error().decode()
+    # the largest workload shapes fit (GPT-2 1.5B-like full vocabulary: 19.4 MB)
+    assert ms.vocab_ce_workspace_bytes(8192, 1600, 50304) <= 32 << 20
+    assert ms.vocab_ce_workspace_bytes(2048, 14336, 62720) <= 32 << 20
+
+
 def test_ce_bwd_workspace_sizes(ms):
     T, h, v = 8192, 1600, 50304
     need = ms.vocab_ce_bwd_workspace_bytes(T, h, v)
@@ -252,7 +272,9 @@ def test_bench_breakdown_arms_only_step_kernels(ms):
 def test_library_imports_no_allocation_copy_or_sync(ms):
     """The built library's undefined HIP symbols are only kernel registration and
     launch, error strings, the device queries of its one-time gfx950 check and of
-    ms_device_info, and the measurement hook's event record: it never allocates, frees, copies, clears
+    ms_device_info, the one-time device-address lookup of the allocation-free
+    entry point's static scratch array (and that array's registration), and the
+    measurement hook's event record: it never allocates, frees, copies, clears
     memory or synchronises, which is what lets a caller capture its calls in a
     graph and own every buffer."""
     import shutil
@@ -266,6 +288,6 @@ def test_library_imports_no_allocation_copy_or_sync(ms):
     allowed = {"__hipPopCallConfiguration", "__hipPushCallConfiguration", "__hipRegisterFatBinary",
                "__hipRegisterFunction", "__hipUnregisterFatBinary", "hipLaunchKernel", "hipGetLastError",
                "hipGetErrorString", "hipGetDevice", "hipGetDevicePropertiesR0600", "hipGetDeviceProperties",
-               "hipEventRecord", "hipDeviceGetAttribute"}
+               "hipEventRecord", "hipDeviceGetAttribute", "hipGetSymbolAddress", "__hipRegisterVar"}
     assert hip <= allowed, sorted(hip - allowed)
     assert not any(re.search(r"Malloc|Free|Memcpy|Memset|Synchronize|HostRegister", s) for s in hip)
