@@ -1,13 +1,14 @@
 // epilogues.hpp - what each GEMM does with its fp32 accumulators.
 //
 // Accumulator element acc[mi][ni][r] of wave (wm, wn) in the tile at (m0, n0)
-// is C[m0 + wm*128 + mi*16 + (lane & 15)][n0 + wn*128 + ni*16 + 4*(lane >> 4) + r].
+// is C[m0 + wm*kWaveM + mi*16 + (lane & 15)][n0 + wn*kWaveN + ni*16 + 4*(lane >> 4) + r].
 //
 // Epilogues hand the accumulators over through LDS: each wave writes its
-// 128 x 128 fp32 sub-tile, 64 rows at a time, into a private 32 KiB region
-// (row pitch 512 bytes, 16-byte chunk q of row r at slot q ^ (r & 15), so the
-// 16 rows written or read together hit distinct banks), then reads it back in
-// a row-major lane order.  The accumulators are therefore only ever stored,
+// kWaveM x kWaveN fp32 sub-tile, 64 rows at a time, into a private region of
+// the LDS stages (row pitch 4*kWaveN bytes, 16-byte chunk q of row r at slot
+// q ^ (r & 15), so that every 8 lanes written or read together hit distinct
+// 16-byte slots of a 128-byte window), then reads it back in a row-major lane
+// order.  The accumulators are therefore only ever stored,
 // which keeps them in the accumulation registers through the main loop, and
 // global stores become full 256/512-byte row segments.  N is a multiple of 8,
 // so every 4-column group is entirely inside or outside the matrix; rows are
@@ -87,14 +88,28 @@ __device__ __forceinline__ float gelu_grad_f(float x) {
 // ---------------------------------------------------------------------------
 // LDS hand-over of the accumulators
 
+// Each wave stages 64 rows of its sub-tile at a time: 64 x kWaveN fp32 in a
+// private region of the four LDS stages.
+constexpr int kEpiRows = 64;
+constexpr int kWavesPerStage = kWaves / 4;
+static_assert(kEpiRows * kWaveN * 4 * kWavesPerStage <= kStageBytes, "staging regions fit the LDS stages");
+// The row-major read-back: kLanesPerRow lanes (4 values each) cover one row of
+// the sub-tile, so one read instruction covers kRowsPerRead rows.
+constexpr int kLanesPerRow = kWaveN / 4;
+constexpr int kRowsPerRead = 64 / kLanesPerRow;
+
 __device__ __forceinline__ char* epi_region(const EpiCtx& c) {
-  const int wave = c.wm * 2 + c.wn;
-  return wave == 0 ? c.lds0 : (wave == 1 ? c.lds1 : (wave == 2 ? c.lds2 : c.lds3));
+  const int wave = c.wm * kWavesN + c.wn;
+  const int st = wave / kWavesPerStage;
+  char* base = st == 0 ? c.lds0 : (st == 1 ? c.lds1 : (st == 2 ? c.lds2 : c.lds3));
+  return base + (wave % kWavesPerStage) * (kEpiRows * kWaveN * 4);
 }
 
-__device__ __forceinline__ int epi_slot(int lr, int q) { return lr * 512 + ((q ^ (lr & 15)) << 4); }
+// Row pitch kWaveN * 4 bytes; chunk q of row lr at slot q ^ (lr & 15).
+__device__ __forceinline__ int epi_slot(int lr, int q) { return lr * (kWaveN * 4) + ((q ^ (lr & 15)) << 4); }
 
 // Write rows [64h, 64h + 64) of the wave's sub-tile (row blocks mi = 4h .. 4h+3).
+static_assert(kWaveM == 128, "the sub-tile is staged in two halves of 64 rows");
 __device__ __forceinline__ void epi_stage_half(const AccTile& acc, char* region, int h, int lane) {
   if (h == 0) acc_settle();
 #pragma unroll
@@ -107,30 +122,30 @@ __device__ __forceinline__ void epi_stage_half(const AccTile& acc, char* region,
   __builtin_amdgcn_wave_barrier();
 }
 
-// Local row lr (0..63) of the staged half, columns 4q .. 4q+3 (q = 0..31).
+// Local row lr (0..63) of the staged half, columns 4q .. 4q+3 (q < kLanesPerRow).
 __device__ __forceinline__ f32x4_t epi_read(const char* region, int lr, int q) {
   return *(const f32x4_t*)(region + epi_slot(lr, q));
 }
 
 // Row-major walk of the staged sub-tile: calls f(row, col, v) with tile-local
-// row/col of 4 consecutive values; 32 lanes cover one 128-column row.  Rows
+// row/col of 4 consecutive values; kLanesPerRow lanes cover one row.  Reads
 // are taken 4 at a time with their LDS reads issued together, so the read
 // latency is paid once per group.
 template <class F>
 __device__ __forceinline__ void epi_rows(const AccTile& acc, const EpiCtx& c, F&& f) {
   char* region = epi_region(c);
-  const int q = c.lane & 31;
+  const int q = c.lane % kLanesPerRow, sub = c.lane / kLanesPerRow;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     epi_stage_half(acc, region, h, c.lane);  // h must be a constant: acc is indexed by it
 #pragma unroll 1
-    for (int it0 = 0; it0 < 32; it0 += 4) {
+    for (int it0 = 0; it0 < kEpiRows / kRowsPerRead; it0 += 4) {
       f32x4_t v[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = epi_read(region, (it0 + u) * 2 + (c.lane >> 5), q);
+      for (int u = 0; u < 4; ++u) v[u] = epi_read(region, (it0 + u) * kRowsPerRead + sub, q);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int lr = (it0 + u) * 2 + (c.lane >> 5);
+        const int lr = (it0 + u) * kRowsPerRead + sub;
         f(c.wm * kWaveM + h * 64 + lr, c.wn * kWaveN + q * 4, v[u]);
       }
     }
@@ -207,7 +222,7 @@ struct EpiGeluFwd {
     const rsrc_t ry = make_rsrc(Y + base, bytes);
     const int mrem = M - c.m0, nrem = N - c.n0;
     // this lane always owns the same 4 columns: load their bias once
-    const int col = c.n0 + c.wn * kWaveN + (c.lane & 31) * 4;
+    const int col = c.n0 + c.wn * kWaveN + (c.lane % kLanesPerRow) * 4;
     const rsrc_t rb = make_rsrc(b1, b1 ? (int64_t)N * 2 : 0);
     const u32x2_t bb = buf_load8(rb, col < N ? (uint32_t)col * 2u : kOOB);
     const float bv[4] = {bf16_lo(bb[0]), bf16_hi(bb[0]), bf16_lo(bb[1]), bf16_hi(bb[1])};
@@ -228,7 +243,8 @@ struct EpiGeluFwd {
 
 // Backward epilogue of dY = dZ B_i^T: dH = dY * GeLU'(H) stored as bf16.  If
 // db1_part is set, also writes this wave's column sums of the fp32 dH over its
-// 128 rows to db1_part[(tile_m*2 + wm) * N + col] (one private slot per writer).
+// 128 rows to db1_part[(tile_m*kWavesM + wm) * N + col] (one private slot per
+// writer).
 template <int FORM>
 struct EpiDGelu {
   const uint16_t* H;
@@ -243,18 +259,19 @@ struct EpiDGelu {
     const rsrc_t rd = make_rsrc(dH + base, bytes);
     const int mrem = M - c.m0, nrem = N - c.n0;
     char* region = epi_region(c);
-    const int q = c.lane & 31;
+    const int q = c.lane % kLanesPerRow, sub = c.lane / kLanesPerRow;
     const int cl = c.wn * kWaveN + q * 4;
+    constexpr int kIters = kEpiRows / kRowsPerRead;  // read instructions per staged half
     float csum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       epi_stage_half(acc, region, h, c.lane);  // h must be a constant: acc is indexed by it
-      // H of 8 rows per batch; the next batch's loads are issued before the
+      // H of 8 reads per batch; the next batch's loads are issued before the
       // current batch is processed, so their latency overlaps the arithmetic
       auto load_h = [&](int it0, u32x2_t (&hh)[8]) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int rl = c.wm * kWaveM + h * 64 + (it0 + u) * 2 + (c.lane >> 5);
+          const int rl = c.wm * kWaveM + h * 64 + (it0 + u) * kRowsPerRead + sub;
           const bool ok = rl < mrem && cl < nrem;
           hh[u] = buf_load8(rh, ok ? (uint32_t)(((int64_t)rl * ld + cl) * 2) : kOOB);
         }
@@ -262,11 +279,11 @@ struct EpiDGelu {
       u32x2_t hcur[8], hnext[8];
       load_h(0, hcur);
 #pragma unroll 2
-      for (int it0 = 0; it0 < 32; it0 += 8) {
-        if (it0 + 8 < 32) load_h(it0 + 8, hnext);
+      for (int it0 = 0; it0 < kIters; it0 += 8) {
+        if (it0 + 8 < kIters) load_h(it0 + 8, hnext);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int lr = (it0 + u) * 2 + (c.lane >> 5);
+          const int lr = (it0 + u) * kRowsPerRead + sub;
           const int rl = c.wm * kWaveM + h * 64 + lr;
           const bool ok = rl < mrem && cl < nrem;
           const f32x4_t v = epi_read(region, lr, q);
@@ -286,10 +303,15 @@ struct EpiDGelu {
       __builtin_amdgcn_wave_barrier();
     }
     if (db1_part) {
+      // the lanes holding the same columns (sub = 0 .. kRowsPerRead-1) add their
+      // sums pairwise; each addition is commutative, so every lane of a group
+      // ends with the same bits
 #pragma unroll
-      for (int r = 0; r < 4; ++r) csum[r] += __shfl_xor(csum[r], 32, 64);
-      if ((c.lane >> 5) == 0 && cl < nrem) {
-        const int64_t slot = (int64_t)(c.tm * 2 + c.wm) * N + c.n0 + cl;
+      for (int x = kLanesPerRow; x < 64; x *= 2)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) csum[r] += __shfl_xor(csum[r], x, 64);
+      if (sub == 0 && cl < nrem) {
+        const int64_t slot = (int64_t)(c.tm * kWavesM + c.wm) * N + c.n0 + cl;
         *(f32x4_t*)(db1_part + slot) = f32x4_t{csum[0], csum[1], csum[2], csum[3]};
       }
     }
@@ -300,19 +322,29 @@ struct EpiDGelu {
 // the tile, computes over the tile's valid columns
 //   pm = max L,  ps = sum exp(L - pm),  pz = L at the target column if it lies
 //   in this tile, else 0,
-// straight from the accumulators.  Lane l holds 32 columns of each of its 8
-// rows and 4 lanes (l, l^16, l^32, l^48) share a row: each lane reduces its
-// 32 values to (max, sum of exp(L - max)), then the four are merged by
-// log-sum-exp over two lane-pair exchanges (v_permlane16_swap, then
+// straight from the accumulators.  Lane l holds 4*kSubN columns of each of
+// its kSubM rows and 4 lanes (l, l^16, l^32, l^48) share a row: each lane
+// reduces its values to (max, sum of exp(L - max)), then the four are merged
+// by log-sum-exp over two lane-pair exchanges (v_permlane16_swap, then
 // v_permlane32_swap).  Each exchange hands every lane the pair's two values
 // in the same order, so all four lanes end with bitwise-equal results.  The
-// two column-waves of each row are merged in LDS in fixed order (wn = 0
-// first) and the triple goes to partial slot tile_n of arrays laid out
+// kWavesN column-waves of each row are merged in LDS in fixed order (wn = 0,
+// 1, ...) and the triple goes to partial slot tile_n of arrays laid out
 // [tiles_n][T].
 __device__ __forceinline__ float max3f(float a, float b, float c) {
   float r;
   asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
   return r;
+}
+
+// One accumulator copied to an ordinary register at this point of the program.
+// The copy is an asm statement, so the compiler neither hoists nor merges it:
+// the CE epilogue then holds one 16-row block's values at a time instead of
+// all of them (which left no registers and spilled).
+__device__ __forceinline__ float acc_read(float a) {
+  float x;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x) : "a"(a));
+  return x;
 }
 
 // Both lanes of each exchanged pair receive (value of the lower lane, value of the upper lane).
@@ -327,6 +359,25 @@ __device__ __forceinline__ void xswap32(float x, float& lo, float& hi) {
   hi = __uint_as_float(r[1]);
 }
 
+// Maximum of n values by a fixed tree of v_max3 (exact in any order).
+template <int N>
+__device__ __forceinline__ float max_tree(const float* v) {
+  if constexpr (N == 1) return v[0];
+  else if constexpr (N == 2) return fmaxf(v[0], v[1]);
+  else if constexpr (N == 3) return max3f(v[0], v[1], v[2]);
+  else {
+    constexpr int a = (N + 2) / 3, b = (N - a + 1) / 2;
+    return max3f(max_tree<a>(v), max_tree<b>(v + a), max_tree<N - a - b>(v + a + b));
+  }
+}
+
+// Sum of n values by a fixed pairwise tree.
+template <int N>
+__device__ __forceinline__ float sum_tree(const float* v) {
+  if constexpr (N == 1) return v[0];
+  else return sum_tree<N / 2>(v) + sum_tree<N - N / 2>(v + N / 2);
+}
+
 // (m, s) pairs -> merged pair; m = -inf means an empty set (s = 0).
 __device__ __forceinline__ void lse_pair(float ma, float sa, float mb, float sb, float& m, float& s) {
   m = fmaxf(ma, mb);
@@ -336,6 +387,9 @@ __device__ __forceinline__ void lse_pair(float ma, float sa, float mb, float sb,
 }
 
 struct EpiCE {
+  static constexpr bool kKeepsStages = true;  // uses only the exchange buffer, never the LDS stages
+  // bytes of the small LDS buffer the column-waves' triples are merged through
+  static constexpr int kXchBytes = (kWavesN - 1) * kBM * 3 * 4;
   const int64_t* target;
   int64_t vocab_start;
   float* part;  // pm at part, ps at part + stride, pz at part + 2*stride (floats)
@@ -369,13 +423,11 @@ struct EpiCE {
 #pragma unroll
         for (int ni = 0; ni < kSubN; ++ni)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[ni * 4 + r] = kMasked ? acc[mi][ni][r] + pad[ni] : acc[mi][ni][r];
-        float t[11];
-#pragma unroll
-        for (int k = 0; k < 10; ++k) t[k] = max3f(v[3 * k], v[3 * k + 1], v[3 * k + 2]);
-        t[10] = fmaxf(v[30], v[31]);
-        const float mx = max3f(max3f(t[0], t[1], t[2]), max3f(t[3], t[4], t[5]),
-                               max3f(max3f(t[6], t[7], t[8]), t[9], t[10]));
+          for (int r = 0; r < 4; ++r) {
+            const float a = acc_read(acc[mi][ni][r]);
+            v[ni * 4 + r] = kMasked ? a + pad[ni] : a;
+          }
+        const float mx = max_tree<kSubN * 4>(v);
         const float ml = mx == -INFINITY ? 0.f : mx * kLog2e;  // no valid column: every term is 0
         float e[kSubN];
 #pragma unroll
@@ -386,7 +438,7 @@ struct EpiCE {
           e[ni] = (q[0] + q[1]) + (q[2] + q[3]);
         }
         rm[mi] = mx;
-        rs[mi] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+        rs[mi] = sum_tree<kSubN>(e);
       }
     };
     if (ncol >= kWaveN) rows(std::false_type{});
@@ -424,8 +476,7 @@ struct EpiCE {
         for (int ni = 0; ni < kSubN; ++ni)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            float x;
-            asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x) : "a"(acc[mi][ni][r]));
+            const float x = acc_read(acc[mi][ni][r]);
             zz = (ni * 16 + 4 * g + r) == tl[mi] ? x : zz;
           }
         float za, zb;
@@ -435,13 +486,13 @@ struct EpiCE {
         rz[mi] = za + zb;
       }
     }
-    // merge the two column-waves of each row: wn = 1 hands its triples to
-    // wn = 0 through LDS (the stages are free: the main loop ended with a barrier)
-    float* xch = (float*)c.lds0;  // [wm][128 rows][3]
-    if (c.wn == 1 && g == 0) {
+    // merge the column-waves of each row: waves wn >= 1 hand their triples to
+    // wn = 0 through the exchange buffer, which merges them in ascending wn
+    float* xch = (float*)c.xch;  // [wn - 1][kBM rows][3]
+    if (c.wn > 0 && g == 0) {
 #pragma unroll
       for (int mi = 0; mi < kSubM; ++mi) {
-        float* e = xch + (c.wm * kWaveM + mi * 16 + l16) * 3;
+        float* e = xch + ((c.wn - 1) * kBM + c.wm * kWaveM + mi * 16 + l16) * 3;
         e[0] = rm[mi];
         e[1] = rs[mi];
         e[2] = rz[mi];
@@ -453,13 +504,20 @@ struct EpiCE {
       for (int mi = 0; mi < kSubM; ++mi) {
         const int row = row0 + mi * 16;
         if (row < M) {
-          const float* e = xch + (c.wm * kWaveM + mi * 16 + l16) * 3;
-          float mm, ss;
-          lse_pair(rm[mi], rs[mi], e[0], e[1], mm, ss);
+          float mm = rm[mi], ss = rs[mi], zz = rz[mi];
+#pragma unroll
+          for (int w = 1; w < kWavesN; ++w) {
+            const float* e = xch + ((w - 1) * kBM + c.wm * kWaveM + mi * 16 + l16) * 3;
+            float m2, s2;
+            lse_pair(mm, ss, e[0], e[1], m2, s2);
+            mm = m2;
+            ss = s2;
+            zz += e[2];
+          }
           float* o = part + (int64_t)c.tn * M + row;
           o[0] = mm;
           o[stride] = ss;
-          o[2 * (int64_t)stride] = rz[mi] + e[2];
+          o[2 * (int64_t)stride] = zz;
         }
       }
     }
@@ -486,27 +544,28 @@ struct EpiCEGrad {
     const rsrc_t rs = make_rsrc(stats + c.m0, (int64_t)(M - c.m0) * 16);
     const int mrem = M - c.m0, nrem = N - c.n0;
     char* region = epi_region(c);
-    const int q = c.lane & 31;
+    const int q = c.lane % kLanesPerRow, sub = c.lane / kLanesPerRow;
     const int cl = c.wn * kWaveN + q * 4;
     const int col = c.n0 + cl;  // shard column of this lane's first value
+    constexpr int kIters = kEpiRows / kRowsPerRead;  // read instructions per staged half
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       epi_stage_half(acc, region, h, c.lane);  // h must be a constant: acc is indexed by it
       auto load_s = [&](int it0, u32x4_t (&ss)[8]) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int rl = c.wm * kWaveM + h * 64 + (it0 + u) * 2 + (c.lane >> 5);
+          const int rl = c.wm * kWaveM + h * 64 + (it0 + u) * kRowsPerRead + sub;
           ss[u] = buf_load16(rs, rl < mrem ? (uint32_t)rl * 16u : kOOB);
         }
       };
       u32x4_t scur[8], snext[8];
       load_s(0, scur);
 #pragma unroll 2
-      for (int it0 = 0; it0 < 32; it0 += 8) {
-        if (it0 + 8 < 32) load_s(it0 + 8, snext);
+      for (int it0 = 0; it0 < kIters; it0 += 8) {
+        if (it0 + 8 < kIters) load_s(it0 + 8, snext);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int lr = (it0 + u) * 2 + (c.lane >> 5);
+          const int lr = (it0 + u) * kRowsPerRead + sub;
           const int rl = c.wm * kWaveM + h * 64 + lr;
           const bool ok = rl < mrem && cl < nrem;
           const f32x4_t v = epi_read(region, lr, q);

@@ -59,8 +59,13 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 constexpr int kBM = 256, kBN = 256, kBK = 32;
 constexpr int kStages = 4;  // LDS ring: tiles kt+1..kt+3 in flight while kt is consumed
-constexpr int kThreads = 256;
-constexpr int kWaveM = 128, kWaveN = 128;
+// Wave grid of a workgroup: kWavesM x kWavesN waves, each owning a
+// kWaveM x kWaveN sub-tile of the 256 x 256 tile.
+constexpr int kWavesM = 2, kWavesN = 2;
+constexpr int kWaves = kWavesM * kWavesN;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kWavesPerSimd = kWaves / 4;  // a CU has 4 SIMDs
+constexpr int kWaveM = kBM / kWavesM, kWaveN = kBN / kWavesN;
 constexpr int kSubM = kWaveM / 16, kSubN = kWaveN / 16;  // 16x16 MFMA blocks per wave
 constexpr int kStageBytes = (kBM + kBN) * kBK * 2;  // 32 KiB
 constexpr int kGroupM = 8;
@@ -165,7 +170,8 @@ typedef __attribute__((address_space(3))) char lds_char;
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x8_t __attribute__((ext_vector_type(8)));
 constexpr int kTileBytes = kBM * kBK * 2;  // 16 KiB per operand tile
-constexpr int kDmaPerWave = kTileBytes / 1024 / 4;
+constexpr int kDmaPerWave = kTileBytes / 1024 / kWaves;  // direct-to-LDS instructions per wave per operand tile
+static_assert(kDmaPerWave == 1 || kDmaPerWave == 2 || kDmaPerWave == 4, "layout offsets assume 1, 2 or 4");
 
 // One buffer_load_dwordx4 ... lds: 64 lanes x 16 bytes from the buffer
 // described by `desc` at per-lane byte offsets `off` into 1 KiB of LDS at
@@ -220,22 +226,23 @@ __device__ __forceinline__ DmaLanes dma_lanes(const Operand& op, int mn0, int nm
   DmaLanes d;
   const uint32_t ldb = (uint32_t)op.ld * 2u;
   if constexpr (KMAJOR) {
-    // instruction 4w + i writes slots (4w + i)*64 + l: row (4w + i)*16 + l/4,
-    // chunk (l%4) ^ (l/8 % 4)
-    const uint32_t r = (uint32_t)wave * 64u + (uint32_t)(lane >> 2);
+    // instruction D*w + i (D = kDmaPerWave) writes slots (D*w + i)*64 + l:
+    // row (D*w + i)*16 + l/4, chunk (l%4) ^ (l/8 % 4)
+    const uint32_t r = (uint32_t)wave * (16u * kDmaPerWave) + (uint32_t)(lane >> 2);
     const int c = (lane & 3) ^ ((lane >> 3) & 3);
     d.v[0] = r * ldb + (uint32_t)c * 16u;
     const int tail = K & (kBK - 1);
     d.v[1] = (c * 8 < tail) ? d.v[0] : kOOB;
     d.step = 16u * ldb;
   } else {
-    // instruction 4w + i writes slots (4w + i)*64 + l: k row 8w + 2i + l/32 and
-    // column group (l%32) ^ 2F with F = ((2i + l/32) % 4) | 4*(w%2); F depends
-    // on i only through i%2
-    const uint32_t k = (uint32_t)wave * 8u + (uint32_t)(lane >> 5);
+    // instruction D*w + i (D = kDmaPerWave) writes slots (D*w + i)*64 + l:
+    // k row 2Dw + 2i + l/32 and column group (l%32) ^ 2F with
+    // F = ((2i + l/32) % 4) | 4*((2Dw/8) % 2); F depends on i only through i%2
+    const uint32_t k = (uint32_t)wave * (2u * kDmaPerWave) + (uint32_t)(lane >> 5);
+    const int k8 = ((wave * 2 * kDmaPerWave) >> 3) & 1;
 #pragma unroll
     for (int par = 0; par < 2; ++par) {
-      const int F = ((2 * par + (lane >> 5)) & 3) | ((wave & 1) << 2);
+      const int F = ((2 * par + (lane >> 5)) & 3) | (k8 << 2);
       const int j = (lane & 31) ^ (2 * F);
       d.v[par] = (mn0 + j * 8 < nmn) ? k * ldb + (uint32_t)j * 16u : kOOB;
     }
@@ -284,14 +291,15 @@ __device__ __forceinline__ bf16x8_t frag_value(const Frag& f) {
   return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(f.lo, f.hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-template <bool KMAJOR>
+// SUB: the 16-wide blocks of this operand one wave covers (kSubM for A, kSubN for B).
+template <bool KMAJOR, int SUB>
 struct FragBase {
-  int x[KMAJOR ? 1 : kSubN];  // K-major: one lane base; M/N-major: one per 16-column block
+  int x[KMAJOR ? 1 : SUB];  // K-major: one lane base; M/N-major: one per 16-column block
 };
 
-template <bool KMAJOR>
-__device__ __forceinline__ FragBase<KMAJOR> frag_lane_base(int lane) {
-  FragBase<KMAJOR> fb;
+template <bool KMAJOR, int SUB>
+__device__ __forceinline__ FragBase<KMAJOR, SUB> frag_lane_base(int lane) {
+  FragBase<KMAJOR, SUB> fb;
   if constexpr (KMAJOR) {
     // row l%16 of the block, chunk l/16
     fb.x[0] = ((lane & 15) * 4 + ((lane >> 4) ^ ((lane >> 1) & 3))) * 16;
@@ -302,7 +310,7 @@ __device__ __forceinline__ FragBase<KMAJOR> frag_lane_base(int lane) {
     const int F = e | ((g & 1) << 2);
     const int base = (8 * g + e) * 512 + F * 32 + (q >> 1) * 16 + (q & 1) * 8;
 #pragma unroll
-    for (int blk = 0; blk < kSubN; ++blk) fb.x[blk] = base ^ (blk * 32);
+    for (int blk = 0; blk < SUB; ++blk) fb.x[blk] = base ^ (blk * 32);
   }
   return fb;
 }
@@ -311,16 +319,19 @@ __device__ __forceinline__ FragBase<KMAJOR> frag_lane_base(int lane) {
 template <bool KMAJOR>
 constexpr int kPieces = KMAJOR ? 1 : 2;
 
-// Read piece h of the fragment of block blk (0..7) for wave coordinate w.
-template <bool KMAJOR>
-__device__ __forceinline__ void read_piece(Frag& f, const lds_char* tile, const FragBase<KMAJOR>& fb, int w, int blk,
-                                           int h) {
+// Read piece h of the fragment of block blk (0..SUB-1) for wave coordinate w.
+// M/N-major: the wave's first block is block w*SUB of the 16 in a k row, and
+// the layout's XOR acts on the block index (bits 5-8 of the byte offset), so
+// the wave offset is XORed in too.
+template <bool KMAJOR, int SUB>
+__device__ __forceinline__ void read_piece(Frag& f, const lds_char* tile, const FragBase<KMAJOR, SUB>& fb, int w,
+                                           int blk, int h) {
   if constexpr (KMAJOR) {
-    const s16x8_t v = *(const s16x8_t*)(tile + fb.x[0] + (w * 8 + blk) * 1024);
+    const s16x8_t v = *(const s16x8_t*)(tile + fb.x[0] + (w * SUB + blk) * 1024);
     f.lo = __builtin_shufflevector(v, v, 0, 1, 2, 3);
     f.hi = __builtin_shufflevector(v, v, 4, 5, 6, 7);
   } else {
-    const lds_char* p = tile + fb.x[blk] + h * 2048 + w * 256;
+    const lds_char* p = tile + (fb.x[blk] ^ (w * SUB * 32)) + h * 2048;
     const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p);
     if (h == 0) f.lo = v;
     else f.hi = v;
@@ -333,14 +344,15 @@ struct Frags {
 };
 
 // Order in which the fragments of a tile are read: A block 0, then every B
-// block, then A blocks 1..7 -- the order in which the MFMA sequence (A block
-// outer, B block inner) first needs them.  Piece p of PA + 8*PB + 7*PA pieces.
+// block, then A blocks 1.. -- the order in which the MFMA sequence (A block
+// outer, B block inner) first needs them.
 template <bool AK, bool BK>
 struct ReadOrder {
   static constexpr int PA = kPieces<AK>, PB = kPieces<BK>;
   static constexpr int P = PA * kSubM + PB * kSubN;
-  // piece p is issued right after MFMA number slot(p) of the 64 (spread over the first 48)
-  static constexpr int slot(int p) { return (p * 48) / P; }
+  static constexpr int kMfma = kSubM * kSubN;
+  // piece p is issued right after MFMA number slot(p) (spread over the first 3/4 of them)
+  static constexpr int slot(int p) { return (p * (3 * kMfma / 4)) / P; }
   static constexpr int piece_at(int j) {
     for (int p = 0; p < P; ++p)
       if (slot(p) == j) return p;
@@ -349,17 +361,17 @@ struct ReadOrder {
 };
 
 template <bool AK, bool BK, int p>
-__device__ __forceinline__ void read_piece_p(Frags& f, const lds_char* stage, const FragBase<AK>& fa,
-                                             const FragBase<BK>& fb, int wm, int wn) {
+__device__ __forceinline__ void read_piece_p(Frags& f, const lds_char* stage, const FragBase<AK, kSubM>& fa,
+                                             const FragBase<BK, kSubN>& fb, int wm, int wn) {
   using R = ReadOrder<AK, BK>;
   if constexpr (p < R::PA) {
-    read_piece<AK>(f.a[0], stage, fa, wm, 0, p);
+    read_piece<AK, kSubM>(f.a[0], stage, fa, wm, 0, p);
   } else if constexpr (p < R::PA + kSubN * R::PB) {
     constexpr int q = p - R::PA;
-    read_piece<BK>(f.b[q / R::PB], stage + kTileBytes, fb, wn, q / R::PB, q % R::PB);
+    read_piece<BK, kSubN>(f.b[q / R::PB], stage + kTileBytes, fb, wn, q / R::PB, q % R::PB);
   } else {
     constexpr int q = p - R::PA - kSubN * R::PB;
-    read_piece<AK>(f.a[1 + q / R::PA], stage, fa, wm, 1 + q / R::PA, q % R::PA);
+    read_piece<AK, kSubM>(f.a[1 + q / R::PA], stage, fa, wm, 1 + q / R::PA, q % R::PA);
   }
 }
 
@@ -374,16 +386,16 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 template <bool AK, bool BK>
-__device__ __forceinline__ void read_all(Frags& f, const lds_char* stage, const FragBase<AK>& fa,
-                                         const FragBase<BK>& fb, int wm, int wn) {
+__device__ __forceinline__ void read_all(Frags& f, const lds_char* stage, const FragBase<AK, kSubM>& fa,
+                                         const FragBase<BK, kSubN>& fb, int wm, int wn) {
   static_for<ReadOrder<AK, BK>::P>([&](auto pc) { read_piece_p<AK, BK, decltype(pc)::value>(f, stage, fa, fb, wm, wn); });
 }
 
 // The MFMA is written as inline assembly with accumulation-register operands so
 // that the 256 accumulators are pinned to the accumulation registers for their
 // whole life (compiler-selected forms end up copying them between register
-// files every iteration).  A given accumulator is re-used only after the 63
-// other MFMAs of the tile; fragment registers come from LDS loads, which the
+// files every iteration).  A given accumulator is re-used only after the
+// kSubM*kSubN - 1 other MFMAs of the tile; fragment registers come from LDS loads, which the
 // wait-count pass tracks through the asm operands; the first read of the
 // accumulators after the loop is fenced with explicit wait states.
 template <bool FIRST>
@@ -430,6 +442,7 @@ struct EpiCtx {
   char* lds1;
   char* lds2;
   char* lds3;
+  char* xch;    // small cross-wave exchange buffer (lds0 unless the kernel gives one of its own)
 };
 
 // s_waitcnt with only the vector-memory count: wait until at most n of this
@@ -471,9 +484,9 @@ __device__ __forceinline__ void gemm_tile(const GemmGeom& g, const Operand& a, c
   const int kt_end = (int)(((int64_t)(split + 1) * nk) / g.splits);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // uniform copy for scalar address math
-  const int wm = wave >> 1, wn = wave & 1;
-  const FragBase<A_KMAJOR> fra = frag_lane_base<A_KMAJOR>(lane);
-  const FragBase<B_KMAJOR> frb = frag_lane_base<B_KMAJOR>(lane);
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
+  const FragBase<A_KMAJOR, kSubM> fra = frag_lane_base<A_KMAJOR, kSubM>(lane);
+  const FragBase<B_KMAJOR, kSubN> frb = frag_lane_base<B_KMAJOR, kSubN>(lane);
   const DmaLanes dla = dma_lanes<A_KMAJOR>(a, m0, g.M, g.K, wave_s, lane);
   const DmaLanes dlb = dma_lanes<B_KMAJOR>(b, n0, g.N, g.K, wave_s, lane);
   auto lds_addr = [](const lds_char* p) { return (uint32_t)(uintptr_t)p; };
@@ -485,6 +498,7 @@ __device__ __forceinline__ void gemm_tile(const GemmGeom& g, const Operand& a, c
     dma_tile<B_KMAJOR>(b, dlb, n0, kt * kBK, g.K, lds_addr(stage + kTileBytes), wave_s);
   };
   constexpr int kPerTile = 2 * kDmaPerWave;  // direct-to-LDS instructions per wave per tile
+  static_assert(kSubM * kSubN == 8 * kPerTile, "one direct-to-LDS load per 8 MFMAs");
   using RO = ReadOrder<A_KMAJOR, B_KMAJOR>;
 
   // The 64 MFMAs of k tile kt on fragments fc.  Invariant at entry: tiles kt
@@ -555,8 +569,142 @@ __device__ __forceinline__ void gemm_tile(const GemmGeom& g, const Operand& a, c
     if (kt + 2 < kt_end) step(False{}, True{}, st[0], st[2], kt + 2, f1, f0);
     if (kt + 3 < kt_end) step(False{}, True{}, st[1], st[3], kt + 3, f0, f1);
   }
-  EpiCtx ctx{m0, n0, tm, tn, split, wm, wn, lane, lds0, lds1, lds2, lds3};
+  EpiCtx ctx{m0, n0, tm, tn, split, wm, wn, lane, lds0, lds1, lds2, lds3, lds0};
   epi(acc, ctx);
+}
+
+// Persistent form for epilogues that leave the four LDS stages alone
+// (Epi::kKeepsStages): workgroup p of P walks the blocks p, p + P, p + 2P, ...
+// (P a multiple of 8, so every tile stays on the XCD map_tile gives it).
+// After the last k step of a tile, whose closing barrier ends every read of
+// the stages, the first three k tiles of the next tile are loaded into stages
+// 0-2, and only then does the epilogue run: the loads land while it computes.
+// The next main loop starts by waiting for every outstanding load (count-based,
+// in program order: the epilogue's own loads and stores issued after them only
+// make it wait longer) and a barrier.  The k steps are those of gemm_tile, in
+// the same order of reads, loads, waits and barriers, so the accumulators, and
+// the results, are the same bits.
+template <bool A_KMAJOR, bool B_KMAJOR, class Epi>
+__device__ __forceinline__ void gemm_tiles_persistent(const GemmGeom& g, const Operand& a, const Operand& b,
+                                                      const Epi& epi, int p, int P, int vg, char* lds0, char* lds1,
+                                                      char* lds2, char* lds3, char* xch) {
+  static_assert(Epi::kKeepsStages, "the persistent form needs an epilogue that leaves the LDS stages alone");
+  args_to_sgprs(g);
+  args_to_sgprs(a);
+  args_to_sgprs(b);
+  args_to_sgprs(epi);
+  lds_char* st[kStages] = {(lds_char*)lds0, (lds_char*)lds1, (lds_char*)lds2, (lds_char*)lds3};
+  const int nk = (g.K + kBK - 1) / kBK;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
+  auto lds_addr = [](const lds_char* q) { return (uint32_t)(uintptr_t)q; };
+  constexpr int kPerTile = 2 * kDmaPerWave;
+  using RO = ReadOrder<A_KMAJOR, B_KMAJOR>;
+  using True = std::integral_constant<bool, true>;
+  using False = std::integral_constant<bool, false>;
+
+  struct TileState {
+    int tm, tn, split, m0, n0, kt_beg, kt_end;
+    DmaLanes dla, dlb;
+  };
+  auto setup = [&](int vb) {
+    TileState t;
+    map_tile(g, vb, vg, t.tm, t.tn, t.split);
+    t.m0 = t.tm * kBM;
+    t.n0 = t.tn * kBN;
+    t.kt_beg = (int)(((int64_t)t.split * nk) / g.splits);
+    t.kt_end = (int)(((int64_t)(t.split + 1) * nk) / g.splits);
+    t.dla = dma_lanes<A_KMAJOR>(a, t.m0, g.M, g.K, wave_s, lane);
+    t.dlb = dma_lanes<B_KMAJOR>(b, t.n0, g.N, g.K, wave_s, lane);
+    return t;
+  };
+  auto prologue = [&](const TileState& t) {
+    for (int i = 0; i < 3 && t.kt_beg + i < t.kt_end; ++i) {
+      dma_tile<A_KMAJOR>(a, t.dla, t.m0, (t.kt_beg + i) * kBK, g.K, lds_addr(st[i]), wave_s);
+      dma_tile<B_KMAJOR>(b, t.dlb, t.n0, (t.kt_beg + i) * kBK, g.K, lds_addr(st[i] + kTileBytes), wave_s);
+    }
+  };
+
+  AccTile acc;
+  auto main_loop = [&](const TileState& t) {
+    const int m0 = t.m0, n0 = t.n0, kt_beg = t.kt_beg, kt_end = t.kt_end;
+    const DmaLanes dla = t.dla, dlb = t.dlb;
+    // per tile: nothing per-lane outlives the loop
+    const FragBase<A_KMAJOR, kSubM> fra = frag_lane_base<A_KMAJOR, kSubM>(lane);
+    const FragBase<B_KMAJOR, kSubN> frb = frag_lane_base<B_KMAJOR, kSubN>(lane);
+    auto step = [&](auto first, auto checked, const lds_char* nxt, lds_char* far, int kt, Frags& fc, Frags& fn) {
+      constexpr bool kFirst = decltype(first)::value;
+      constexpr bool kChecked = decltype(checked)::value;
+      const bool issue = !kChecked || kt + 3 < kt_end;
+      const bool next = !kChecked || kt + 1 < kt_end;
+      const int k3 = (kt + 3) * kBK;
+      const u32x4_t da = tile_desc<A_KMAJOR>(a, m0, k3);
+      const u32x4_t db = tile_desc<B_KMAJOR>(b, n0, k3);
+      const bool ktail = k3 + kBK > g.K;
+      const uint32_t fa = lds_addr(far), fb = lds_addr(far + kTileBytes);
+      static_for<kSubM * kSubN>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        constexpr int mi = j / kSubN, ni = j % kSubN;
+        mfma_16x16x32<kFirst>(acc[mi][ni], frag_value(fc.b[ni]), frag_value(fc.a[mi]));
+        constexpr int pc = RO::piece_at(j);
+        if constexpr (pc >= 0) {
+          if (next) read_piece_p<A_KMAJOR, B_KMAJOR, pc>(fn, nxt, fra, frb, wm, wn);
+        }
+        if constexpr (j % 8 == 7) {
+          constexpr int q = j / 8;
+          if (issue) {
+            if constexpr (q < kDmaPerWave) dma_one<A_KMAJOR>(dla, da, ktail, fa, wave_s, q);
+            else dma_one<B_KMAJOR>(dlb, db, ktail, fb, wave_s, q - kDmaPerWave);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      if (issue) wait_vmcnt<kPerTile>();
+      else wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+    };
+    wait_vmcnt<0>();  // the prologue's loads (and anything issued after them)
+    __builtin_amdgcn_s_barrier();
+    Frags f0, f1;
+    read_all<A_KMAJOR, B_KMAJOR>(f0, st[0], fra, frb, wm, wn);
+    step(True{}, True{}, st[1], st[3], kt_beg, f0, f1);
+    int kt = kt_beg + 1;
+    for (; kt + 6 < kt_end; kt += 4) {
+      step(False{}, False{}, st[2], st[0], kt, f1, f0);
+      step(False{}, False{}, st[3], st[1], kt + 1, f0, f1);
+      step(False{}, False{}, st[0], st[2], kt + 2, f1, f0);
+      step(False{}, False{}, st[1], st[3], kt + 3, f0, f1);
+    }
+    for (; kt < kt_end; kt += 4) {
+      step(False{}, True{}, st[2], st[0], kt, f1, f0);
+      if (kt + 1 < kt_end) step(False{}, True{}, st[3], st[1], kt + 1, f0, f1);
+      if (kt + 2 < kt_end) step(False{}, True{}, st[0], st[2], kt + 2, f1, f0);
+      if (kt + 3 < kt_end) step(False{}, True{}, st[1], st[3], kt + 3, f0, f1);
+    }
+  };
+
+  // Tile state is rebuilt from the block index where it is needed (a few
+  // instructions) rather than kept live across the epilogue, which needs
+  // every register it can get.
+  int vb = p;
+  if (vb >= vg) return;
+  prologue(setup(vb));
+  while (true) {
+    {
+      const TileState cur = setup(vb);
+      main_loop(cur);
+    }
+    const int nvb = vb + P;
+    const bool more = nvb < vg;
+    if (more) prologue(setup(nvb));
+    int tm, tn, split;
+    map_tile(g, vb, vg, tm, tn, split);
+    const EpiCtx ctx{tm * kBM, tn * kBN, tm, tn, split, wm, wn, lane, lds0, lds1, lds2, lds3, xch};
+    epi(acc, ctx);
+    if (!more) break;
+    vb = nvb;
+  }
 }
 
 #define MS_DECLARE_LDS_STAGES                                 \
@@ -565,8 +713,21 @@ __device__ __forceinline__ void gemm_tile(const GemmGeom& g, const Operand& a, c
   __shared__ __attribute__((aligned(1024))) char lds2[kStageBytes]; \
   __shared__ __attribute__((aligned(1024))) char lds3[kStageBytes]
 
+// Persistent launch of gemm_tiles_persistent: gridDim.x workgroups (a multiple
+// of 8, at most one per CU) share the vg tiles.
 template <bool A_KMAJOR, bool B_KMAJOR, class Epi>
-__global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+__global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                               amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd)))
+gemm_persistent_kernel(GemmGeom g, Operand a, Operand b, Epi epi, int vg) {
+  MS_DECLARE_LDS_STAGES;
+  __shared__ __attribute__((aligned(16))) char xch[Epi::kXchBytes];
+  gemm_tiles_persistent<A_KMAJOR, B_KMAJOR, Epi>(g, a, b, epi, (int)blockIdx.x, (int)gridDim.x, vg, lds0, lds1, lds2,
+                                                 lds3, xch);
+}
+
+template <bool A_KMAJOR, bool B_KMAJOR, class Epi>
+__global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                               amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd)))
 gemm_kernel(GemmGeom g, Operand a, Operand b, Epi epi) {
   MS_DECLARE_LDS_STAGES;
   gemm_tile<A_KMAJOR, B_KMAJOR, Epi>(g, a, b, epi, (int)blockIdx.x, (int)gridDim.x, lds0, lds1, lds2, lds3);
@@ -579,7 +740,8 @@ gemm_kernel(GemmGeom g, Operand a, Operand b, Epi epi) {
 // GEMM's range is its block count rounded up to a multiple of 8 (the extra
 // blocks exit at once), which keeps the trailing GEMM's first block on XCD 0.
 template <bool AK1, bool BK1, class E1, bool AK2, bool BK2, class E2>
-__global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+__global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                               amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd)))
 gemm_pair_kernel(GemmGeom g1, Operand a1, Operand b1, E1 e1, int blocks1, GemmGeom g2, Operand a2, Operand b2,
                  E2 e2, int blocks2, int second_first) {
   MS_DECLARE_LDS_STAGES;

@@ -162,7 +162,28 @@ __global__ void __launch_bounds__(1024) mean_fixed_tree(const float* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// GEMM launch helper
+// GEMM launch helpers
+
+// Compute units of the current device (queried once per device).
+static hipError_t device_compute_units(int* cus) {
+  static std::mutex mu;
+  static std::map<int, int> per_device;
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = per_device.find(dev);
+  if (it != per_device.end()) {
+    *cus = it->second;
+    return hipSuccess;
+  }
+  int n = 0;
+  err = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (err != hipSuccess) return err;
+  per_device.emplace(dev, n);
+  *cus = n;
+  return hipSuccess;
+}
 
 static GemmGeom make_geom(int64_t M, int64_t N, int64_t K, int splits) {
   GemmGeom g;
@@ -289,7 +310,7 @@ MlpWorkspace mlp_workspace_layout(int64_t T, int64_t h, int64_t f) {
   w.plan = plan_backward(T, h, f);
   w.off_dH = 0;
   w.off_db1 = align((size_t)T * f * 2);
-  w.db1_parts = (int)(tiles_m * 2);
+  w.db1_parts = (int)(tiles_m * kWavesM);
   w.off_splitk = w.off_db1 + align((size_t)w.db1_parts * f * 4);
   const int S = w.plan.splits_dB > w.plan.splits_dA ? w.plan.splits_dB : w.plan.splits_dA;
   w.bytes = w.off_splitk + (S > 1 ? align((size_t)S * h * f * 4) : 0);
@@ -514,7 +535,18 @@ hipError_t launch_vocab_ce(const uint16_t* X, const uint16_t* E, const int64_t* 
   GemmGeom g = make_geom(T, v, h, 1);
   Operand a{X, h, T * h}, b{E, v, h * v};
   EpiCE e{target, vocab_start, pm, (int)((w.off_s - w.off_m) / 4), (int)T, (int)v, 0};
-  hipError_t err = launch_gemm<true, false>(kTkCeGemm, g, a, b, e, st);
+  // persistent: at most one workgroup per CU, a multiple of 8 of them, each walking its tiles
+  int cus = 0;
+  hipError_t err = device_compute_units(&cus);
+  if (err != hipSuccess) return err;
+  const int vg = g.tiles_m * g.tiles_n * g.splits;
+  int P = cus - cus % 8;
+  if (P < 8) P = 8;
+  if (P > vg) P = vg;
+  record_armed_event(kTkCeGemm, false, st);
+  hipLaunchKernelGGL((gemm_persistent_kernel<true, false, EpiCE>), dim3(P), dim3(kThreads), 0, st, g, a, b, e, vg);
+  err = hipGetLastError();
+  record_armed_event(kTkCeGemm, true, st);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(ce_tile_combine, dim3((unsigned)((T + 63) / 64)), dim3(512), 0, st, pm, ps, pz, w.parts,
                      (int)T, m, s, z);

@@ -12,16 +12,16 @@ static const float* g_logits;
 
 static void tile_kernel(mshard::EpiCEGrad epi, int M, int N) {
   using namespace mshard;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave / kWavesN, wn = wave % kWavesN;
   const int tm = blockIdx.x, tn = blockIdx.y, m0 = tm * kBM, n0 = tn * kBN;
   AccTile acc;
   for (int mi = 0; mi < kSubM; ++mi)
     for (int ni = 0; ni < kSubN; ++ni)
       for (int r = 0; r < 4; ++r) {
-        const int row = m0 + wm * 128 + mi * 16 + (lane & 15), col = n0 + wn * 128 + ni * 16 + 4 * (lane >> 4) + r;
+        const int row = m0 + wm * kWaveM + mi * 16 + (lane & 15), col = n0 + wn * kWaveN + ni * 16 + 4 * (lane >> 4) + r;
         acc[mi][ni][r] = (row < M && col < N) ? g_logits[(int64_t)row * N + col] : 0.f;  // as the GEMM leaves them
       }
-  const EpiCtx ctx{m0, n0, tm, tn, 0, wm, wn, lane, g_lds[0], g_lds[1], g_lds[2], g_lds[3]};
+  const EpiCtx ctx{m0, n0, tm, tn, 0, wm, wn, lane, g_lds[0], g_lds[1], g_lds[2], g_lds[3], g_lds[0]};
   epi(acc, ctx);
 }
 
@@ -40,7 +40,7 @@ int main(int argc, char** argv) {
   std::vector<uint16_t> dl((size_t)M * N, 0xffff);
   g_logits = logits.data();
   const mshard::EpiCEGrad epi{stats.data(), dl.data(), N, M, N};
-  emu::launch(dim3((M + 255) / 256, (N + 255) / 256, 1), dim3(256), tile_kernel, epi, M, N);
+  emu::launch(dim3((M + 255) / 256, (N + 255) / 256, 1), dim3(mshard::kThreads), tile_kernel, epi, M, N);
   f = std::fopen((dir + "/dl.bin").c_str(), "wb");
   std::fwrite(dl.data(), 2, dl.size(), f);
   std::fclose(f);

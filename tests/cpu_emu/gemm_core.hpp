@@ -18,9 +18,12 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef char lds_char;
 
 constexpr int kBM = 256, kBN = 256, kBK = 32;
-constexpr int kThreads = 256;
-constexpr int kWaveM = 128, kWaveN = 128;
+constexpr int kWavesM = 2, kWavesN = 2;
+constexpr int kWaves = kWavesM * kWavesN;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kWaveM = kBM / kWavesM, kWaveN = kBN / kWavesN;
 constexpr int kSubM = kWaveM / 16, kSubN = kWaveN / 16;
+constexpr int kStageBytes = (kBM + kBN) * kBK * 2;
 constexpr uint32_t kOOB = 0x80000000u;
 
 struct rsrc_t {
@@ -56,7 +59,7 @@ inline uint32_t pack_bf16x2(float lo, float hi) { return f32_to_bf16_rne(lo) | (
 inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// acc[mi][ni][r] of wave (wm, wn) holds C[wm*128 + mi*16 + (lane & 15)][wn*128 + ni*16 + 4*(lane >> 4) + r]
+// acc[mi][ni][r] of wave (wm, wn) holds C[wm*kWaveM + mi*16 + (lane & 15)][wn*kWaveN + ni*16 + 4*(lane >> 4) + r]
 typedef f32x4_t AccTile[kSubM][kSubN];
 inline void acc_store_lds(char* p, const f32x4_t& a) { std::memcpy(p, &a, 16); }
 inline void acc_settle() {}
@@ -71,6 +74,7 @@ struct EpiCtx {
   char* lds1;
   char* lds2;
   char* lds3;
+  char* xch;
 };
 
 }  // namespace mshard
