@@ -240,10 +240,11 @@ def test_bitwise_determinism_bench_shape_concurrent(ms):
         loss, mean = ms.ce_combine(m[None], s[None], z[None])
         cdX, cdE = ms.vocab_ce_shard_bwd(X, E, tg, m[None], s[None], 0, workspace=ws["ce_bwd"])
         torch.cuda.synchronize()
-        h = digest(H, Y, Z, dX, dA, dB, m, s, z, loss, mean, cdX, cdE)
-        print(f"  run {it} {'with' if it % 2 else 'without'} a concurrent stream: {h[:16]}", flush=True)
+        outs = dict(H=H, Y=Y, Z=Z, dX=dX, dA=dA, dB=dB, m=m, s=s, z=z, loss=loss, mean=mean, ce_dX=cdX, ce_dE=cdE)
+        h = {k: digest(v)[:16] for k, v in outs.items()}
+        print(f"  run {it} {'with' if it % 2 else 'without'} a concurrent stream: {h}", flush=True)
         ref = ref or h
-        assert h == ref, it
+        assert h == ref, (it, sorted(k for k in h if h[k] != ref[k]))
     del busy_c
 
 
