@@ -1,8 +1,5 @@
 """The whole step captured in a HIP graph (through torch.cuda.graphs) and replayed.
 
-Run by naming this file (pytest does not collect it by default):
-    python -u -m pytest tests/wip_graph_capture.py -x -v --timeout 300 --timeout-method thread
-
 The library allocates nothing and clears nothing with memset, so its calls can
 be captured.  The graph is replayed several times with eager work and
 synchronisations in between, and every replay must reproduce the eager
