@@ -176,7 +176,9 @@ size_t attn_shard_workspace_bytes(int64_t b, int64_t s, int64_t h, int64_t n, in
  * pages name heads only); mask: causal (a token sees itself and earlier
  * tokens of its sequence) when `causal` is 1, none when 0.
  * Sizes  : b sequences of s tokens (T = b*s rows, sequence-major), hidden h,
- *          n heads of size d on this rank (d a multiple of 16, 16..128).
+ *          n heads of size d on this rank (d a multiple of 16, 16..128);
+ *          n*b < 2^31 and s <= 4194240 (65535 blocks of 64 rows), else
+ *          MS_ERR_SHAPE.
  * Inputs : X[T x h]; Wqkv_i[h x 3nd] = [W_Q,i | W_K,i | W_V,i], head j at
  *          columns j*d of each block; Wo_i[nd x h] (the matching rows of W_O);
  *          all bf16.
@@ -195,8 +197,9 @@ ms_status attn_shard_fwd(const ms_bf16* X, const ms_bf16* Wqkv_i, const ms_bf16*
  *     dS = P * (dO V^T - delta),  dQ = dS K / sqrt(d),  dK = dS^T Q / sqrt(d);
  *     dWqkv_i = X^T [dQ | dK | dV],  dX_i = [dQ | dK | dV] Wqkv_i^T.
  * The attention core recomputes P from QKV and lse; dO and dQKV are rounded
- * to bf16 in the workspace.  Two kernels (one over key blocks for dK and dV,
- * one over query blocks for dQ) keep every sum in a fixed order.
+ * to bf16 in the workspace.  Two kernels (one over query blocks for dQ, which
+ * also forms delta, then one over key blocks for dK and dV) keep every sum in
+ * a fixed order.
  * Inputs : X, Wqkv_i, Wo_i, dZ[T x h] bf16; QKV, O, lse from the forward.
  * Outputs: dX_i[T x h] fp32 (this rank's partial; f sums it); dWqkv_i[h x 3nd],
  *          dWo_i[nd x h] bf16. */

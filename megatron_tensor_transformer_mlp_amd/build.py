@@ -35,6 +35,14 @@ COMMON_FLAGS = [
     f"-I{CSRC}",
 ]
 
+# Per-source additions.  The attention kernels read every score and update
+# every O accumulator with VALU instructions between their MFMAs; with the
+# MFMA destinations in VGPRs they skip the AGPR-to-VGPR copies and need fewer
+# registers in all (three waves per SIMD for head size 64 instead of two).
+SOURCE_FLAGS = {
+    "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
 
 def _run(cmd, verbose):
     if verbose:
@@ -57,7 +65,7 @@ def build_library(verbose: bool = True, jobs: int = 2) -> str:
         for src in SOURCES:
             obj = os.path.join(tmp, src + ".o")
             objs.append(obj)
-            cmd = [HIPCC, *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [HIPCC, *COMMON_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))

@@ -147,12 +147,15 @@ ms_status launched(hipError_t e, const char* what) {
     if (_st != MS_OK) return _st;   \
   } while (0)
 
-// Attention shard sizes: b, s >= 1 (b*s tokens, grid limits on b and n), h as
-// the other entry points, n >= 1 heads of size d (a multiple of 16, 16..128).
+// Attention shard sizes: b, s >= 1 (b*s tokens), h as the other entry points,
+// n >= 1 heads of size d (a multiple of 16, 16..128).  The core kernels' grids
+// put the (head, sequence) pairs on x and the 64-row blocks of a sequence on y,
+// so n*b < 2^31 and s <= 65535 * 64.
 ms_status check_attn(int64_t b, int64_t s, int64_t h, int64_t n, int64_t d, int32_t causal) {
   if (b < 1 || s < 1 || n < 1) return fail(MS_ERR_SHAPE, "b, s and n must be >= 1 (got %lld, %lld, %lld)",
                                            (long long)b, (long long)s, (long long)n);
-  if (b > 65535 || n > 65535) return fail(MS_ERR_SHAPE, "b and n must be <= 65535");
+  if (n > INT32_MAX / b) return fail(MS_ERR_SHAPE, "n*b too large");
+  if (s > (int64_t)65535 * 64) return fail(MS_ERR_SHAPE, "s must be <= 4194240 (got %lld)", (long long)s);
   if (s > INT32_MAX / b) return fail(MS_ERR_SHAPE, "b*s too large");
   if (d < 16 || d > 128 || d % 16 != 0)
     return fail(MS_ERR_SHAPE, "d must be a multiple of 16 in [16, 128] (got %lld)", (long long)d);

@@ -14,13 +14,19 @@
 // with a 16-byte pad per row, double-buffered, staged through registers).
 //   S = Q K^T: v_mfma_f32_16x16x32_bf16 with the K fragment first, so lane l
 //     holds S[query l%16][key 4(l/16) + r] of each 16-key block; the four
-//     lanes of a query row merge its max and sum over lanes l^16 and l^32.
-//   Online softmax in base 2 (scores scaled by log2(e)/sqrt(d)).
+//     lanes of a query row merge its max over lanes l^16 and l^32.
+//   Online softmax in base 2 (scores scaled by log2(e)/sqrt(d)); the running
+//     max is raised only when a scaled score exceeds it by more than 8, so most
+//     steps skip the merge and the rescale of O; masks are applied only on the
+//     steps that cross the causal diagonal or the sequence end.
 //   O += P V: P stays in registers as the MFMA's second operand.  A lane's
 //     8 keys of a 32-key step are {4g..4g+3, 16+4g..16+4g+3} (g = l/16), the
 //     keys its S registers hold; the V fragment is gathered in the same key
 //     order with two transposing LDS reads (ds_read_b64_tr_b16), so the
 //     contraction pairs every key with itself.
+// Grids put the (head, sequence) pairs on x and a sequence's row blocks on y,
+// so that under a causal mask every block with the most work is dispatched
+// before any block with less (the last blocks to start are the shortest).
 #include <type_traits>
 
 #include "epilogues.hpp"
@@ -108,6 +114,56 @@ __device__ __forceinline__ float row_sum4(float x) {
   return a + b;
 }
 
+// One query-row group's softmax step over the 64 keys whose raw scores sacc
+// holds (lane l: query l%16, keys 16kb16 + 4(l/16) + r).  The running max m
+// is kept in the scaled (base-2) domain and only raised when some row of the
+// wave sees a score more than kRescaleSlack above it, so the common step needs
+// no cross-lane merge and no rescale of O; the exponents then stay at most
+// 2^kRescaleSlack, which bf16 P and the fp32 sums hold exactly as well as 1.
+// The row sum is kept per lane (the lane's 16 keys of each step) and merged
+// over the row's four lanes once, after the last step.
+constexpr float kRescaleSlack = 8.f;
+
+template <int ND, bool MASK, bool CAUSAL>
+__device__ __forceinline__ void attn_softmax_step(const f32x4_t (&sacc)[4], f32x4_t (&o)[ND], float& m, float& nm,
+                                                  float& l, bf16x8_t (&pf)[2], float scale, int key0, int q, int s) {
+  float sv[4][4];
+  float lm = -INFINITY;
+  // key key0 + off is valid when off <= lim (before the sequence end and, causal, not after the query)
+  const int lim = (CAUSAL ? min(q, s - 1) : s - 1) - key0;
+#pragma unroll
+  for (int kb16 = 0; kb16 < 4; ++kb16)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sv[kb16][r] = sacc[kb16][r];
+      if (MASK && kb16 * 16 + r > lim) sv[kb16][r] = -INFINITY;
+      lm = fmaxf(lm, sv[kb16][r]);
+    }
+  lm *= scale;  // scale > 0, so the max commutes with it exactly
+  if (__any(lm > m + kRescaleSlack)) {
+    const float mnew = fmaxf(m, row_max4(lm));
+    const float corr = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - mnew);
+    l *= corr;
+#pragma unroll
+    for (int nb = 0; nb < ND; ++nb) o[nb] *= corr;
+    m = mnew;
+    nm = mnew == -INFINITY ? 0.f : -mnew;
+  }
+  float p[4][4];
+#pragma unroll
+  for (int kb16 = 0; kb16 < 4; ++kb16)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p[kb16][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[kb16][r], scale, nm));
+      l += p[kb16][r];
+    }
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+    pf[c] = as_bf16x8(u32x4_t{pack_bf16x2(p[2 * c][0], p[2 * c][1]), pack_bf16x2(p[2 * c][2], p[2 * c][3]),
+                              pack_bf16x2(p[2 * c + 1][0], p[2 * c + 1][1]),
+                              pack_bf16x2(p[2 * c + 1][2], p[2 * c + 1][3])});
+}
+
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnGeom g, const uint16_t* __restrict__ qkv,
                                                        uint16_t* __restrict__ out, float* __restrict__ lse) {
@@ -115,8 +171,11 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnGeom g, const uint16_
   using Tile = AttnTile<D>;
   __shared__ __attribute__((aligned(16))) char kt[2][Tile::kBytes];
   __shared__ __attribute__((aligned(16))) char vt[2][Tile::kBytes];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g4 = lane >> 4, l16 = lane & 15;
-  const int q0 = blockIdx.x * kAttnBM, j = blockIdx.y, bi = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so the mask test is a scalar branch
+  // grid x: (head, sequence) pairs; y: query blocks, the ones that see the most keys (causal) dispatched first
+  const int qblk = CAUSAL ? (int)gridDim.y - 1 - (int)blockIdx.y : (int)blockIdx.y;
+  const int q0 = qblk * kAttnBM, j = (int)blockIdx.x % g.n, bi = (int)blockIdx.x / g.n;
   const int64_t tok0 = (int64_t)bi * g.s;
   const int64_t ld = g.ld_qkv;
   const uint16_t* Qb = qkv + tok0 * ld + (int64_t)j * g.d;
@@ -135,10 +194,11 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnGeom g, const uint16_
     }
   }
   f32x4_t o[2][ND];
-  float m[2], l[2];
+  float m[2], nm[2], l[2];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     m[rb] = -INFINITY;
+    nm[rb] = 0.f;
     l[rb] = 0.f;
 #pragma unroll
     for (int nb = 0; nb < ND; ++nb) o[rb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -151,6 +211,7 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnGeom g, const uint16_
   tile_swrite<D>(kt[0], kr, tid);
   tile_swrite<D>(vt[0], vr, tid);
   __syncthreads();
+  const int vrow = 4 * g4 + (l16 >> 2), vcol = 4 * (l16 & 3);
   for (int kb = 0; kb < nkb; ++kb) {
     const int cur = kb & 1;
     const bool more = kb + 1 < nkb;
@@ -160,56 +221,32 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnGeom g, const uint16_
     }
     const char* K = kt[cur];
     const char* V = vt[cur];
+    const int kbase = kb * kAttnBN;
+    f32x4_t sacc[2][4];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const int q = q0 + 32 * w + 16 * rb + l16;  // this lane's query position
-      f32x4_t sacc[4];
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int kb16 = 0; kb16 < 4; ++kb16) {
-        sacc[kb16] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        sacc[rb][kb16] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < KD; ++kk)
-          sacc[kb16] = mfma16(lds_read_b128(K + (kb16 * 16 + l16) * Tile::kPitch + (kk * 4 + g4) * 16), qf[rb][kk],
-                              sacc[kb16]);
+          sacc[rb][kb16] = mfma16(lds_read_b128(K + (kb16 * 16 + l16) * Tile::kPitch + (kk * 4 + g4) * 16),
+                                  qf[rb][kk], sacc[rb][kb16]);
       }
-      float t[4][4];
-      float mx = -INFINITY;
 #pragma unroll
-      for (int kb16 = 0; kb16 < 4; ++kb16)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = kb * kAttnBN + kb16 * 16 + 4 * g4 + r;
-          const bool valid = key < g.s && (!CAUSAL || key <= q);
-          t[kb16][r] = valid ? sacc[kb16][r] * g.scale_log2 : -INFINITY;
-          mx = fmaxf(mx, t[kb16][r]);
-        }
-      mx = row_max4(mx);
-      const float mnew = fmaxf(m[rb], mx);
-      const float msub = mnew == -INFINITY ? 0.f : mnew;
-      const float corr = __builtin_amdgcn_exp2f(m[rb] - msub);
-      float p[4][4];
-      float ps = 0.f;
-#pragma unroll
-      for (int kb16 = 0; kb16 < 4; ++kb16)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          p[kb16][r] = __builtin_amdgcn_exp2f(t[kb16][r] - msub);
-          ps += p[kb16][r];
-        }
-      ps = row_sum4(ps);
-      l[rb] = l[rb] * corr + ps;
-      m[rb] = mnew;
-#pragma unroll
-      for (int nb = 0; nb < ND; ++nb) o[rb][nb] *= corr;
+    for (int rb = 0; rb < 2; ++rb) {
+      const int qw = q0 + 32 * w + 16 * rb;  // first query row of this group
+      // keys past the sequence end, or (causal) after some row of the group, need the mask
+      const bool masked = kbase + kAttnBN > g.s || (CAUSAL && kbase + kAttnBN - 1 > qw);
       bf16x8_t pf[2];
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-        pf[c] = as_bf16x8(u32x4_t{pack_bf16x2(p[2 * c][0], p[2 * c][1]), pack_bf16x2(p[2 * c][2], p[2 * c][3]),
-                                  pack_bf16x2(p[2 * c + 1][0], p[2 * c + 1][1]),
-                                  pack_bf16x2(p[2 * c + 1][2], p[2 * c + 1][3])});
+      if (masked)
+        attn_softmax_step<ND, true, CAUSAL>(sacc[rb], o[rb], m[rb], nm[rb], l[rb], pf, g.scale_log2,
+                                            kbase + 4 * g4, qw + l16, g.s);
+      else
+        attn_softmax_step<ND, false, CAUSAL>(sacc[rb], o[rb], m[rb], nm[rb], l[rb], pf, g.scale_log2,
+                                             kbase + 4 * g4, qw + l16, g.s);
       // source lane 16G + s of a transposing read addresses key 4G + s/4 (+ 16 for the second half)
       // and columns 16nb + 4(s%4) .. +3
-      const int vrow = 4 * g4 + (l16 >> 2), vcol = 4 * (l16 & 3);
 #pragma unroll
       for (int nb = 0; nb < ND; ++nb)
 #pragma unroll
@@ -229,8 +266,9 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnGeom g, const uint16_
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     const int q = q0 + 32 * w + 16 * rb + l16;
+    const float lrow = row_sum4(l[rb]);  // every lane joins the merge before the row test
     if (q >= g.s) continue;
-    const float inv = l[rb] > 0.f ? 1.f / l[rb] : 0.f;
+    const float inv = lrow > 0.f ? 1.f / lrow : 0.f;
     uint16_t* orow = out + (tok0 + q) * (int64_t)g.ld_o + (int64_t)j * g.d;
 #pragma unroll
     for (int nb = 0; nb < ND; ++nb) {
@@ -240,13 +278,13 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnGeom g, const uint16_
         *(u32x2_t*)(orow + col) = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
       }
     }
-    if (g4 == 0) lse[(int64_t)j * T + tok0 + q] = (m[rb] + __builtin_log2f(l[rb])) * kLn2;
+    if (g4 == 0) lse[(int64_t)j * T + tok0 + q] = (m[rb] + __builtin_log2f(lrow)) * kLn2;
   }
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch_attn_fwd_t(const AttnGeom& g, const uint16_t* qkv, uint16_t* out, float* lse, hipStream_t st) {
-  const dim3 grid((unsigned)((g.s + kAttnBM - 1) / kAttnBM), (unsigned)g.n, (unsigned)g.b);
+  const dim3 grid((unsigned)(g.n * g.b), (unsigned)((g.s + kAttnBM - 1) / kAttnBM));
   hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL>), grid, dim3(256), 0, st, g, qkv, out, lse);
   return hipGetLastError();
 }
@@ -257,38 +295,53 @@ hipError_t launch_attn_fwd_d(const AttnGeom& g, bool causal, const uint16_t* qkv
   return causal ? launch_attn_fwd_t<D, true>(g, qkv, out, lse, st) : launch_attn_fwd_t<D, false>(g, qkv, out, lse, st);
 }
 
-// Backward: delta[j][t] = sum over the head's columns of dO * O (fp32, in
-// column order), the row term of dS = P * (dP - delta).
-__global__ void __launch_bounds__(256) attn_bwd_delta(AttnGeom g, const uint16_t* __restrict__ o,
-                                                      const uint16_t* __restrict__ dout, float* __restrict__ delta) {
-  const int64_t T = (int64_t)g.b * g.s;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= T * g.n) return;
-  const int j = (int)(i / T);
-  const int64_t t = i - (int64_t)j * T;
-  const uint16_t* a = o + t * g.ld_o + (int64_t)j * g.d;
-  const uint16_t* b = dout + t * g.ld_o + (int64_t)j * g.d;
-  float acc = 0.f;
-  for (int c = 0; c < g.d; c += 8) {
-    const u32x4_t x = *(const u32x4_t*)(a + c), y = *(const u32x4_t*)(b + c);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      acc += bf16_lo(x[k]) * bf16_lo(y[k]);
-      acc += bf16_hi(x[k]) * bf16_hi(y[k]);
-    }
-  }
-  delta[(int64_t)j * T + t] = acc;
-}
-
 // Backward, dK and dV: one workgroup per (64 keys, head, sequence); wave w owns
 // keys k0 + 16w .. +15 and loops over the query blocks that see them (64
-// queries per step, through LDS: the Q and dO tiles plus each query's lse
-// and delta).  With the Q fragment as the MFMA's first operand, lane l holds
-// S[query 4(l/16) + r][key l%16] of each 16-query block: the transposed
-// layout, so P^T and dS^T stay in registers as the second operand of
+// queries per step, through LDS: the Q and dO tiles plus each query's
+// -lse*log2(e) and delta).  With the Q fragment as the MFMA's first operand,
+// lane l holds S[query 4(l/16) + r][key l%16] of each 16-query block: the
+// transposed layout, so P^T and dS^T stay in registers as the second operand of
 //   dV += P^T dO  and  dK += dS^T Q,
 // whose first operands (dO and Q gathered per column) come from transposing
-// LDS reads, and dP^T = V dO^T takes the wave's V rows from registers.
+// LDS reads, and dP^T = V dO^T takes the wave's V rows from registers.  Only
+// the steps that cross the causal diagonal or the sequence end are masked.
+template <int KD, bool MASK>
+__device__ __forceinline__ void dkdv_group_ds(const char* Q, const char* dO, const float* nl, const float* dl,
+                                              const bf16x8_t (&kf)[KD], const bf16x8_t (&vf)[KD], float scale,
+                                              int lo, int hi, int l16, int g4, int pitch, bf16x8_t (&pf)[2],
+                                              bf16x8_t (&dsf)[2]) {
+  float p[4][4], ds[4][4];
+#pragma unroll
+  for (int qb16 = 0; qb16 < 4; ++qb16) {
+    f32x4_t sacc = f32x4_t{0.f, 0.f, 0.f, 0.f}, dpacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KD; ++kk) {
+      const int off = (qb16 * 16 + l16) * pitch + (kk * 4 + g4) * 16;
+      sacc = mfma16(lds_read_b128(Q + off), kf[kk], sacc);
+      dpacc = mfma16(lds_read_b128(dO + off), vf[kk], dpacc);
+    }
+    // the lane's four queries qb16*16 + 4(l/16) + r are consecutive: one 16-byte read each
+    const f32x4_t nl4 = *(const f32x4_t*)(nl + qb16 * 16 + 4 * g4);
+    const f32x4_t dl4 = *(const f32x4_t*)(dl + qb16 * 16 + 4 * g4);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], scale, nl4[r]));
+      if (MASK && !(qb16 * 16 + r >= lo && qb16 * 16 + r < hi)) pv = 0.f;
+      p[qb16][r] = pv;
+      ds[qb16][r] = pv * (dpacc[r] - dl4[r]);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    pf[c] = as_bf16x8(u32x4_t{pack_bf16x2(p[2 * c][0], p[2 * c][1]), pack_bf16x2(p[2 * c][2], p[2 * c][3]),
+                              pack_bf16x2(p[2 * c + 1][0], p[2 * c + 1][1]),
+                              pack_bf16x2(p[2 * c + 1][2], p[2 * c + 1][3])});
+    dsf[c] = as_bf16x8(u32x4_t{pack_bf16x2(ds[2 * c][0], ds[2 * c][1]), pack_bf16x2(ds[2 * c][2], ds[2 * c][3]),
+                               pack_bf16x2(ds[2 * c + 1][0], ds[2 * c + 1][1]),
+                               pack_bf16x2(ds[2 * c + 1][2], ds[2 * c + 1][3])});
+  }
+}
+
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnGeom g, const uint16_t* __restrict__ qkv,
                                                             const uint16_t* __restrict__ dout,
@@ -299,9 +352,12 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnGeom g, const ui
   using Tile = AttnTile<D>;
   __shared__ __attribute__((aligned(16))) char qt[2][Tile::kBytes];
   __shared__ __attribute__((aligned(16))) char dt[2][Tile::kBytes];
-  __shared__ float sl[2][kAttnBN], sd[2][kAttnBN];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g4 = lane >> 4, l16 = lane & 15;
-  const int k0 = blockIdx.x * kAttnBN, j = blockIdx.y, bi = blockIdx.z;
+  // per query of the block: -lse*log2(e) at [0, 64), delta at [64, 128)
+  __shared__ __attribute__((aligned(16))) float srow[2][2 * kAttnBN];
+  const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so the mask test is a scalar branch
+  // grid x: (head, sequence) pairs; y: key blocks, the first (causal: seen by the most queries) dispatched first
+  const int k0 = (int)blockIdx.y * kAttnBN, j = (int)blockIdx.x % g.n, bi = (int)blockIdx.x / g.n;
   const int64_t tok0 = (int64_t)bi * g.s, T = (int64_t)g.b * g.s;
   const int64_t ld = g.ld_qkv;
   const uint16_t* Qb = qkv + tok0 * ld + (int64_t)j * g.d;
@@ -325,19 +381,18 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnGeom g, const ui
   const int qstart = CAUSAL ? k0 : 0;  // causal: only queries at or after the block's first key
   const int nqb = qstart < g.s ? (g.s - qstart + kAttnBN - 1) / kAttnBN : 0;
   TileRegs<D> qr, dr;
-  float lr = 0.f, dl = 0.f;
+  float rt = 0.f;  // threads [0, 128): their query's row term
   auto gload = [&](int qb) {
     const int r0 = qstart + qb * kAttnBN;
     tile_gload<D>(qr, Qb, ld, r0, g.s, g.d, tid);
     tile_gload<D>(dr, dOb, g.ld_o, r0, g.s, g.d, tid);
-    if (tid < kAttnBN) lr = r0 + tid < g.s ? lseb[r0 + tid] * kLog2e : 0.f;
-    else if (tid < 2 * kAttnBN) dl = r0 + tid - kAttnBN < g.s ? delb[r0 + tid - kAttnBN] : 0.f;
+    const int q = r0 + (tid & (kAttnBN - 1));
+    if (tid < 2 * kAttnBN) rt = q >= g.s ? 0.f : tid < kAttnBN ? -lseb[q] * kLog2e : delb[q];
   };
   auto swrite = [&](int buf) {
     tile_swrite<D>(qt[buf], qr, tid);
     tile_swrite<D>(dt[buf], dr, tid);
-    if (tid < kAttnBN) sl[buf][tid] = lr;
-    else if (tid < 2 * kAttnBN) sd[buf][tid - kAttnBN] = dl;
+    if (tid < 2 * kAttnBN) srow[buf][tid] = rt;
   };
   if (nqb > 0) {
     gload(0);
@@ -352,35 +407,16 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnGeom g, const ui
     const char* Q = qt[cur];
     const char* dO = dt[cur];
     const int qbase = qstart + qb * kAttnBN;
-    float p[4][4], ds[4][4];
-#pragma unroll
-    for (int qb16 = 0; qb16 < 4; ++qb16) {
-      f32x4_t sacc = f32x4_t{0.f, 0.f, 0.f, 0.f}, dpacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < KD; ++kk) {
-        const int off = (qb16 * 16 + l16) * Tile::kPitch + (kk * 4 + g4) * 16;
-        sacc = mfma16(lds_read_b128(Q + off), kf[kk], sacc);
-        dpacc = mfma16(lds_read_b128(dO + off), vf[kk], dpacc);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int ql = qb16 * 16 + 4 * g4 + r;  // query within the block
-        const int q = qbase + ql;
-        const bool valid = q < g.s && key < g.s && (!CAUSAL || key <= q);
-        p[qb16][r] = valid ? __builtin_amdgcn_exp2f(sacc[r] * g.scale_log2 - sl[cur][ql]) : 0.f;
-        ds[qb16][r] = p[qb16][r] * (dpacc[r] - sd[cur][ql]);
-      }
-    }
+    // query qbase + 4(l/16) + off is valid for this lane's key when lo <= off < hi
+    const int lo = CAUSAL ? key - qbase - 4 * g4 : 0, hi = g.s - qbase - 4 * g4;
+    const bool masked = qbase + kAttnBN > g.s || (CAUSAL && qbase < k0 + 16 * w + 15);
     bf16x8_t pf[2], dsf[2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      pf[c] = as_bf16x8(u32x4_t{pack_bf16x2(p[2 * c][0], p[2 * c][1]), pack_bf16x2(p[2 * c][2], p[2 * c][3]),
-                                pack_bf16x2(p[2 * c + 1][0], p[2 * c + 1][1]),
-                                pack_bf16x2(p[2 * c + 1][2], p[2 * c + 1][3])});
-      dsf[c] = as_bf16x8(u32x4_t{pack_bf16x2(ds[2 * c][0], ds[2 * c][1]), pack_bf16x2(ds[2 * c][2], ds[2 * c][3]),
-                                 pack_bf16x2(ds[2 * c + 1][0], ds[2 * c + 1][1]),
-                                 pack_bf16x2(ds[2 * c + 1][2], ds[2 * c + 1][3])});
-    }
+    if (masked)
+      dkdv_group_ds<KD, true>(Q, dO, srow[cur], srow[cur] + kAttnBN, kf, vf, g.scale_log2, lo, hi, l16, g4,
+                              Tile::kPitch, pf, dsf);
+    else
+      dkdv_group_ds<KD, false>(Q, dO, srow[cur], srow[cur] + kAttnBN, kf, vf, g.scale_log2, lo, hi, l16, g4,
+                               Tile::kPitch, pf, dsf);
 #pragma unroll
     for (int nb = 0; nb < ND; ++nb)
 #pragma unroll
@@ -409,45 +445,90 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnGeom g, const ui
   }
 }
 
-// Backward, dQ: one workgroup per (128 queries, head, sequence), 4 waves of 32
-// query rows, keys 64 at a time through LDS as in the forward.  S and dP
-// (= dO V^T, V rows as the first operand) come out in the forward's layout;
-// dS = P * (dP - delta) stays in registers for dQ += dS K, whose first
-// operand (K gathered per column) comes from transposing LDS reads.
+// Backward, dQ, launched before dK/dV: one workgroup per (128 queries, head,
+// sequence), 4 waves of 32 query rows, keys 64 at a time through LDS as in the
+// forward.  The prologue forms each query's delta = sum over the head's
+// columns of dO * O (fp32; the lane's own columns, then its row's four lanes
+// in a fixed tree), the row term of dS = P * (dP - delta), and stores it for
+// the dK/dV kernel.  S and dP (= dO V^T, V rows as the first operand) come out
+// in the forward's layout; dS stays in registers for dQ += dS K, whose first
+// operand (K gathered per column) comes from transposing LDS reads.  Only the
+// steps that cross the causal diagonal or the sequence end are masked.
+template <int KD, bool MASK>
+__device__ __forceinline__ void dq_group_ds(const char* K, const char* V, const bf16x8_t (&qf)[KD],
+                                            const bf16x8_t (&df)[KD], float nlq, float del, float scale, int lim,
+                                            int l16, int g4, int pitch, bf16x8_t (&dsf)[2]) {
+  float ds[4][4];
+#pragma unroll
+  for (int kb16 = 0; kb16 < 4; ++kb16) {
+    f32x4_t sacc = f32x4_t{0.f, 0.f, 0.f, 0.f}, dpacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KD; ++kk) {
+      const int off = (kb16 * 16 + l16) * pitch + (kk * 4 + g4) * 16;
+      sacc = mfma16(lds_read_b128(K + off), qf[kk], sacc);
+      dpacc = mfma16(lds_read_b128(V + off), df[kk], dpacc);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], scale, nlq));
+      if (MASK && kb16 * 16 + r > lim) p = 0.f;
+      ds[kb16][r] = p * (dpacc[r] - del);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+    dsf[c] = as_bf16x8(u32x4_t{pack_bf16x2(ds[2 * c][0], ds[2 * c][1]), pack_bf16x2(ds[2 * c][2], ds[2 * c][3]),
+                               pack_bf16x2(ds[2 * c + 1][0], ds[2 * c + 1][1]),
+                               pack_bf16x2(ds[2 * c + 1][2], ds[2 * c + 1][3])});
+}
+
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(AttnGeom g, const uint16_t* __restrict__ qkv,
+                                                          const uint16_t* __restrict__ out,
                                                           const uint16_t* __restrict__ dout,
-                                                          const float* __restrict__ lse,
-                                                          const float* __restrict__ delta,
+                                                          const float* __restrict__ lse, float* __restrict__ delta,
                                                           uint16_t* __restrict__ dqkv) {
   constexpr int KD = D / 32, ND = D / 16;
   using Tile = AttnTile<D>;
   __shared__ __attribute__((aligned(16))) char kt[2][Tile::kBytes];
   __shared__ __attribute__((aligned(16))) char vt[2][Tile::kBytes];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g4 = lane >> 4, l16 = lane & 15;
-  const int q0 = blockIdx.x * kAttnBM, j = blockIdx.y, bi = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so the mask test is a scalar branch
+  // grid x: (head, sequence) pairs; y: query blocks, the ones that see the most keys (causal) dispatched first
+  const int qblk = CAUSAL ? (int)gridDim.y - 1 - (int)blockIdx.y : (int)blockIdx.y;
+  const int q0 = qblk * kAttnBM, j = (int)blockIdx.x % g.n, bi = (int)blockIdx.x / g.n;
   const int64_t tok0 = (int64_t)bi * g.s, T = (int64_t)g.b * g.s;
   const int64_t ld = g.ld_qkv;
   const uint16_t* Qb = qkv + tok0 * ld + (int64_t)j * g.d;
   const uint16_t* Kb = Qb + (int64_t)g.n * g.d;
   const uint16_t* Vb = Qb + 2 * (int64_t)g.n * g.d;
+  const uint16_t* Ob = out + tok0 * (int64_t)g.ld_o + (int64_t)j * g.d;
   const uint16_t* dOb = dout + tok0 * (int64_t)g.ld_o + (int64_t)j * g.d;
   bf16x8_t qf[2][KD], df[2][KD];
-  float lq[2], dq_del[2];
+  float nlq[2], del[2];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     const int row = q0 + 32 * w + 16 * rb + l16;
     const bool in = row < g.s;
+    float part = 0.f;
 #pragma unroll
     for (int kk = 0; kk < KD; ++kk) {
       const int c = kk * 4 + g4;
       const bool ok = in && c * 8 < g.d;
-      qf[rb][kk] = as_bf16x8(ok ? *(const u32x4_t*)(Qb + (int64_t)row * ld + c * 8) : u32x4_t{0u, 0u, 0u, 0u});
-      df[rb][kk] =
-          as_bf16x8(ok ? *(const u32x4_t*)(dOb + (int64_t)row * g.ld_o + c * 8) : u32x4_t{0u, 0u, 0u, 0u});
+      const u32x4_t zero = u32x4_t{0u, 0u, 0u, 0u};
+      qf[rb][kk] = as_bf16x8(ok ? *(const u32x4_t*)(Qb + (int64_t)row * ld + c * 8) : zero);
+      const u32x4_t dv = ok ? *(const u32x4_t*)(dOb + (int64_t)row * g.ld_o + c * 8) : zero;
+      const u32x4_t ov = ok ? *(const u32x4_t*)(Ob + (int64_t)row * g.ld_o + c * 8) : zero;
+      df[rb][kk] = as_bf16x8(dv);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        part += bf16_lo(dv[k]) * bf16_lo(ov[k]);
+        part += bf16_hi(dv[k]) * bf16_hi(ov[k]);
+      }
     }
-    lq[rb] = in ? lse[(int64_t)j * T + tok0 + row] * kLog2e : 0.f;
-    dq_del[rb] = in ? delta[(int64_t)j * T + tok0 + row] : 0.f;
+    del[rb] = row_sum4(part);  // every lane joins the merge; rows past the end sum zeros
+    nlq[rb] = in ? -lse[(int64_t)j * T + tok0 + row] * kLog2e : 0.f;
+    if (in && g4 == 0) delta[(int64_t)j * T + tok0 + row] = del[rb];
   }
   f32x4_t dq[2][ND];
 #pragma unroll
@@ -472,33 +553,19 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(AttnGeom g, const uint
     }
     const char* K = kt[cur];
     const char* V = vt[cur];
+    const int kbase = kb * kAttnBN;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      const int q = q0 + 32 * w + 16 * rb + l16;
-      float ds[4][4];
-#pragma unroll
-      for (int kb16 = 0; kb16 < 4; ++kb16) {
-        f32x4_t sacc = f32x4_t{0.f, 0.f, 0.f, 0.f}, dpacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KD; ++kk) {
-          const int off = (kb16 * 16 + l16) * Tile::kPitch + (kk * 4 + g4) * 16;
-          sacc = mfma16(lds_read_b128(K + off), qf[rb][kk], sacc);
-          dpacc = mfma16(lds_read_b128(V + off), df[rb][kk], dpacc);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = kb * kAttnBN + kb16 * 16 + 4 * g4 + r;
-          const bool valid = q < g.s && key < g.s && (!CAUSAL || key <= q);
-          const float p = valid ? __builtin_amdgcn_exp2f(sacc[r] * g.scale_log2 - lq[rb]) : 0.f;
-          ds[kb16][r] = p * (dpacc[r] - dq_del[rb]);
-        }
-      }
+      const int qw = q0 + 32 * w + 16 * rb;  // first query row of this group
+      const bool masked = kbase + kAttnBN > g.s || (CAUSAL && kbase + kAttnBN - 1 > qw);
+      // key kbase + 4(l/16) + off is valid for this lane's query when off <= lim
+      const int lim = (CAUSAL ? min(qw + l16, g.s - 1) : g.s - 1) - kbase - 4 * g4;
       bf16x8_t dsf[2];
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-        dsf[c] = as_bf16x8(u32x4_t{pack_bf16x2(ds[2 * c][0], ds[2 * c][1]), pack_bf16x2(ds[2 * c][2], ds[2 * c][3]),
-                                   pack_bf16x2(ds[2 * c + 1][0], ds[2 * c + 1][1]),
-                                   pack_bf16x2(ds[2 * c + 1][2], ds[2 * c + 1][3])});
+      if (masked)
+        dq_group_ds<KD, true>(K, V, qf[rb], df[rb], nlq[rb], del[rb], g.scale_log2, lim, l16, g4, Tile::kPitch, dsf);
+      else
+        dq_group_ds<KD, false>(K, V, qf[rb], df[rb], nlq[rb], del[rb], g.scale_log2, lim, l16, g4, Tile::kPitch,
+                               dsf);
 #pragma unroll
       for (int nb = 0; nb < ND; ++nb)
 #pragma unroll
@@ -532,22 +599,23 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(AttnGeom g, const uint
 }
 
 template <int D, bool CAUSAL>
-hipError_t launch_attn_bwd_t(const AttnGeom& g, const uint16_t* qkv, const uint16_t* dout, const float* lse,
-                             const float* delta, uint16_t* dqkv, hipStream_t st) {
-  const dim3 gk((unsigned)((g.s + kAttnBN - 1) / kAttnBN), (unsigned)g.n, (unsigned)g.b);
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL>), gk, dim3(256), 0, st, g, qkv, dout, lse, delta, dqkv);
+hipError_t launch_attn_bwd_t(const AttnGeom& g, const uint16_t* qkv, const uint16_t* out, const uint16_t* dout,
+                             const float* lse, float* delta, uint16_t* dqkv, hipStream_t st) {
+  const dim3 gq((unsigned)(g.n * g.b), (unsigned)((g.s + kAttnBM - 1) / kAttnBM));
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL>), gq, dim3(256), 0, st, g, qkv, out, dout, lse, delta, dqkv);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const dim3 gq((unsigned)((g.s + kAttnBM - 1) / kAttnBM), (unsigned)g.n, (unsigned)g.b);
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL>), gq, dim3(256), 0, st, g, qkv, dout, lse, delta, dqkv);
+  const dim3 gk((unsigned)(g.n * g.b), (unsigned)((g.s + kAttnBN - 1) / kAttnBN));
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL>), gk, dim3(256), 0, st, g, qkv, dout, lse,
+                     (const float*)delta, dqkv);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_attn_bwd_d(const AttnGeom& g, bool causal, const uint16_t* qkv, const uint16_t* dout,
-                             const float* lse, const float* delta, uint16_t* dqkv, hipStream_t st) {
-  return causal ? launch_attn_bwd_t<D, true>(g, qkv, dout, lse, delta, dqkv, st)
-                : launch_attn_bwd_t<D, false>(g, qkv, dout, lse, delta, dqkv, st);
+hipError_t launch_attn_bwd_d(const AttnGeom& g, bool causal, const uint16_t* qkv, const uint16_t* out,
+                             const uint16_t* dout, const float* lse, float* delta, uint16_t* dqkv, hipStream_t st) {
+  return causal ? launch_attn_bwd_t<D, true>(g, qkv, out, dout, lse, delta, dqkv, st)
+                : launch_attn_bwd_t<D, false>(g, qkv, out, dout, lse, delta, dqkv, st);
 }
 
 }  // namespace
@@ -557,15 +625,11 @@ int attn_padded_dim(int d) { return ((d + 31) / 32) * 32; }
 hipError_t launch_attn_core_bwd(const AttnGeom& g, bool causal, const uint16_t* qkv, const uint16_t* out,
                                 const uint16_t* dout, const float* lse, float* delta, uint16_t* dqkv,
                                 hipStream_t st) {
-  const int64_t rows = (int64_t)g.b * g.s * g.n;
-  hipLaunchKernelGGL(attn_bwd_delta, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, g, out, dout, delta);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
   switch (attn_padded_dim(g.d)) {
-    case 32: return launch_attn_bwd_d<32>(g, causal, qkv, dout, lse, delta, dqkv, st);
-    case 64: return launch_attn_bwd_d<64>(g, causal, qkv, dout, lse, delta, dqkv, st);
-    case 96: return launch_attn_bwd_d<96>(g, causal, qkv, dout, lse, delta, dqkv, st);
-    case 128: return launch_attn_bwd_d<128>(g, causal, qkv, dout, lse, delta, dqkv, st);
+    case 32: return launch_attn_bwd_d<32>(g, causal, qkv, out, dout, lse, delta, dqkv, st);
+    case 64: return launch_attn_bwd_d<64>(g, causal, qkv, out, dout, lse, delta, dqkv, st);
+    case 96: return launch_attn_bwd_d<96>(g, causal, qkv, out, dout, lse, delta, dqkv, st);
+    case 128: return launch_attn_bwd_d<128>(g, causal, qkv, out, dout, lse, delta, dqkv, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -206,7 +206,8 @@ def test_attn_validation(ms):
     assert fwd(d_=24) == ms.MS_ERR_SHAPE
     assert fwd(d_=0) == ms.MS_ERR_SHAPE
     assert fwd(n_=0) == ms.MS_ERR_SHAPE
-    assert fwd(b_=70000) == ms.MS_ERR_SHAPE
+    assert fwd(b_=1 << 16, n_=1 << 15) == ms.MS_ERR_SHAPE   # n*b = 2^31 grid columns
+    assert fwd(b_=1, s_=65535 * 64 + 1) == ms.MS_ERR_SHAPE  # more than 65535 row blocks of 64
     assert fwd(causal=2) == ms.MS_ERR_ENUM
     assert fwd(O=p[3] + 64) == ms.MS_ERR_ALIAS        # O on top of QKV
     assert fwd(lse=p[5] + 4) == ms.MS_ERR_ALIGN

@@ -72,7 +72,7 @@ def bf16r(x):
     return inputs.bf16_bits_to_f32(inputs.round_to_bf16_bits(np.asarray(x, np.float32))).astype(np.float64)
 
 
-def model_fwd(QKV, b, s, n, d, causal, round_p=True):
+def model_fwd(QKV, b, s, n, d, causal, round_p=True, stats=None):
     D = ((d + 31) // 32) * 32
     KD, ND = D // 32, D // 16
     pitch = 2 * D + 16
@@ -106,11 +106,13 @@ def model_fwd(QKV, b, s, n, d, causal, round_p=True):
                                 c = kk * 4 + l // 16
                                 if row < s and c * 8 < d:
                                     qf[rb, kk, l] = QKV[bi * s + row, j * d + c * 8: j * d + c * 8 + 8]
-                    o = np.zeros((2, ND, 64, 4)); m = np.full((2, 64), -np.inf); lsum = np.zeros((2, 64))
+                    o = np.zeros((2, ND, 64, 4)); m = np.full((2, 64), -np.inf); nm = np.zeros((2, 64))
+                    lsum = np.zeros((2, 64))  # per lane: its own keys only, merged over the row after the last step
                     for kb in range(nkb):
                         kt, vt = Lds(BN * pitch), Lds(BN * pitch)
                         tile_load(kt, n * d + j * d, bi, kb * BN)
                         tile_load(vt, 2 * n * d + j * d, bi, kb * BN)
+                        kbase = kb * BN
                         for rb in range(2):
                             sacc = np.zeros((4, 64, 4))
                             for kb16 in range(4):
@@ -118,26 +120,38 @@ def model_fwd(QKV, b, s, n, d, causal, round_p=True):
                                     kfrag = np.array([kt.read_b128((kb16 * 16 + l % 16) * pitch + (kk * 4 + l // 16) * 16)
                                                       for l in range(64)])
                                     sacc[kb16] = mfma(kfrag, qf[rb, kk], sacc[kb16])
-                            t = np.zeros((4, 64, 4))
+                            qw = q0 + 32 * w + 16 * rb
+                            masked = kbase + BN > s or (causal and kbase + BN - 1 > qw)
+                            sv = sacc.copy()
                             for l in range(64):
-                                q = q0 + 32 * w + 16 * rb + l % 16
+                                q = qw + l % 16
+                                key0 = kbase + 4 * (l // 16)
+                                lim = (min(q, s - 1) if causal else s - 1) - key0
                                 for kb16 in range(4):
                                     for r in range(4):
-                                        key = kb * BN + kb16 * 16 + 4 * (l // 16) + r
+                                        key = key0 + kb16 * 16 + r
                                         valid = key < s and (not causal or key <= q)
-                                        t[kb16, l, r] = sacc[kb16, l, r] * scale_log2 if valid else -np.inf
-                            mx = t.max(axis=(0, 2))  # per lane
-                            # merge over the 4 lanes of a row: l, l^16, l^32, l^48
-                            mxr = np.array([max(mx[l], mx[l ^ 16], mx[l ^ 32], mx[l ^ 48]) for l in range(64)])
-                            mnew = np.maximum(m[rb], mxr)
-                            msub = np.where(mnew == -np.inf, 0.0, mnew)
-                            corr = np.exp2(m[rb] - msub)
-                            p = np.exp2(t - msub[None, :, None])
-                            ps = p.sum(axis=(0, 2))
-                            psr = np.array([ps[l] + ps[l ^ 16] + ps[l ^ 32] + ps[l ^ 48] for l in range(64)])
-                            lsum[rb] = lsum[rb] * corr + psr
-                            m[rb] = mnew
-                            o[rb] *= corr[None, :, None]
+                                        assert valid == (kb16 * 16 + r <= lim)
+                                        # a step the kernel runs unmasked has every key valid for every row
+                                        assert masked or valid
+                                        if masked and not valid:
+                                            sv[kb16, l, r] = -np.inf
+                            lm = sv.max(axis=(0, 2)) * scale_log2  # per lane
+                            if np.any(lm > m[rb] + 8.0):  # one decision for the whole wave
+                                if stats is not None and kb > 0:
+                                    stats["late_rescales"] = stats.get("late_rescales", 0) + 1
+                                mxr = np.array([max(lm[l], lm[l ^ 16], lm[l ^ 32], lm[l ^ 48]) for l in range(64)])
+                                mnew = np.maximum(m[rb], mxr)
+                                corr = np.where(mnew == -np.inf, 1.0, np.exp2(m[rb] - mnew))
+                                lsum[rb] *= corr
+                                o[rb] *= corr[None, :, None]
+                                m[rb] = mnew
+                                nm[rb] = np.where(mnew == -np.inf, 0.0, -mnew)
+                            p = np.exp2(sv * scale_log2 + nm[rb][None, :, None])
+                            assert p.max() <= 2.0 ** 8
+                            if stats is not None:
+                                stats["max_p"] = max(stats.get("max_p", 0.0), float(p.max()))
+                            lsum[rb] += p.sum(axis=(0, 2))
                             pr = bf16r(p) if round_p else p
                             pf = np.zeros((2, 64, 8))
                             for c in range(2):
@@ -152,17 +166,19 @@ def model_fwd(QKV, b, s, n, d, causal, round_p=True):
                                     vf = np.concatenate([lo, hi], axis=1)
                                     o[rb, nb] = mfma(vf, pf[c], o[rb, nb])
                     for rb in range(2):
+                        lrow = np.array([lsum[rb, l] + lsum[rb, l ^ 16] + lsum[rb, l ^ 32] + lsum[rb, l ^ 48]
+                                         for l in range(64)])
                         for l in range(64):
                             q = q0 + 32 * w + 16 * rb + l % 16
                             if q >= s:
                                 continue
-                            inv = 1.0 / lsum[rb, l]
+                            inv = 1.0 / lrow[l]
                             for nb in range(ND):
                                 col = 16 * nb + 4 * (l // 16)
                                 if col < d:
                                     O[bi * s + q, j * d + col:j * d + col + 4] = o[rb, nb, l] * inv
                             if l // 16 == 0:
-                                lse[j, bi * s + q] = (m[rb, l] + math.log2(lsum[rb, l])) * math.log(2)
+                                lse[j, bi * s + q] = (m[rb, l] + math.log2(lrow[l])) * math.log(2)
     return O, lse
 
 
@@ -209,6 +225,7 @@ def dkdv(Qs, Ks, Vs, dOs, lse, delta, s, d, causal, rnd):
                 sl = np.array([lse[qbase + i] * math.log2(math.e) if qbase + i < s else 0 for i in range(BN)])
                 sd = np.array([delta[qbase + i] if qbase + i < s else 0 for i in range(BN)])
                 p = np.zeros((4, 64, 4)); ds = np.zeros((4, 64, 4))
+                masked = qbase + BN > s or (causal and qbase < k0 + 16 * w + 15)
                 for qb16 in range(4):
                     sacc = np.zeros((64, 4)); dpacc = np.zeros((64, 4))
                     for kk in range(KD):
@@ -217,11 +234,17 @@ def dkdv(Qs, Ks, Vs, dOs, lse, delta, s, d, causal, rnd):
                         dpacc = mfma(np.array([Dt.read_b128(o) for o in offs]), vf[kk], dpacc)
                     for l in range(64):
                         key = key_of(l)
+                        lo = key - qbase - 4 * (l // 16) if causal else 0
+                        hi = s - qbase - 4 * (l // 16)
                         for r in range(4):
                             ql = qb16 * 16 + 4 * (l // 16) + r
                             q = qbase + ql
-                            valid = q < s and key < s and (not causal or key <= q)
-                            p[qb16, l, r] = 2.0 ** (sacc[l, r] * scale_log2 - sl[ql]) if valid else 0.0
+                            ok = lo <= qb16 * 16 + r < hi  # the kernel's test; keys past the end are not stored
+                            if key < s:
+                                assert ok == (q < s and (not causal or key <= q))
+                            assert masked or ok  # a step the kernel runs unmasked has every element valid
+                            pv = 2.0 ** (sacc[l, r] * scale_log2 - sl[ql])
+                            p[qb16, l, r] = 0.0 if masked and not ok else pv
                             ds[qb16, l, r] = p[qb16, l, r] * (dpacc[l, r] - sd[ql])
                 pr, dsr = (bf16r(p), bf16r(ds)) if rnd else (p, ds)
                 pf = np.zeros((2, 64, 8)); dsf = np.zeros((2, 64, 8))
@@ -246,7 +269,9 @@ def dkdv(Qs, Ks, Vs, dOs, lse, delta, s, d, causal, rnd):
     return dK, dV
 
 
-def dq(Qs, Ks, Vs, dOs, lse, delta, s, d, causal, rnd):
+def dq(Qs, Ks, Vs, dOs, Os, lse, delta, s, d, causal, rnd):
+    """delta is formed here as the dQ kernel forms it (per-lane partial dot products of dO and O over the
+    lane's columns, merged over the row's four lanes) and checked against the one given."""
     D = ((d + 31) // 32) * 32; KD, ND = D // 32, D // 16; pitch = 2 * D + 16
     scale_log2 = math.log2(math.e) / math.sqrt(d)
     dQ = np.full((s, d), np.nan)
@@ -261,11 +286,21 @@ def dq(Qs, Ks, Vs, dOs, lse, delta, s, d, causal, rnd):
                 qf = [kfrag_rows(Qs, row_of, kk, s, d) for kk in range(KD)]
                 df = [kfrag_rows(dOs, row_of, kk, s, d) for kk in range(KD)]
                 lq = np.array([lse[row_of(l)] * math.log2(math.e) if row_of(l) < s else 0 for l in range(64)])
-                dl = np.array([delta[row_of(l)] if row_of(l) < s else 0 for l in range(64)])
+                of = [kfrag_rows(Os, row_of, kk, s, d) for kk in range(KD)]
+                part = sum((df[kk] * of[kk]).sum(axis=1) for kk in range(KD))
+                dl = np.array([part[l] + part[l ^ 16] + part[l ^ 32] + part[l ^ 48] for l in range(64)])
+                for l in range(64):
+                    if row_of(l) < s:
+                        assert abs(dl[l] - delta[row_of(l)]) <= 1e-12 * (1 + abs(delta[row_of(l)]))
+                    else:
+                        assert dl[l] == 0.0
                 for kb in range(nkb):
                     Kt, Vt = Lds(BN * pitch), Lds(BN * pitch)
                     tile_load(Kt, Ks, s, d, D, pitch, kb * BN); tile_load(Vt, Vs, s, d, D, pitch, kb * BN)
                     ds = np.zeros((4, 64, 4))
+                    kbase = kb * BN
+                    qw = q0 + 32 * w + 16 * rb
+                    masked = kbase + BN > s or (causal and kbase + BN - 1 > qw)
                     for kb16 in range(4):
                         sacc = np.zeros((64, 4)); dpacc = np.zeros((64, 4))
                         for kk in range(KD):
@@ -274,10 +309,16 @@ def dq(Qs, Ks, Vs, dOs, lse, delta, s, d, causal, rnd):
                             dpacc = mfma(np.array([Vt.read_b128(o) for o in offs]), df[kk], dpacc)
                         for l in range(64):
                             q = row_of(l)
+                            lim = (min(q, s - 1) if causal else s - 1) - kbase - 4 * (l // 16)
                             for r in range(4):
-                                key = kb * BN + kb16 * 16 + 4 * (l // 16) + r
-                                valid = q < s and key < s and (not causal or key <= q)
-                                pv = 2.0 ** (sacc[l, r] * scale_log2 - lq[l]) if valid else 0.0
+                                key = kbase + kb16 * 16 + 4 * (l // 16) + r
+                                ok = kb16 * 16 + r <= lim  # the kernel's test; rows past the end are not stored
+                                if q < s:
+                                    assert ok == (key < s and (not causal or key <= q))
+                                assert masked or ok  # a step the kernel runs unmasked has every element valid
+                                pv = 2.0 ** (sacc[l, r] * scale_log2 - lq[l])
+                                if masked and not ok:
+                                    pv = 0.0
                                 ds[kb16, l, r] = pv * (dpacc[l, r] - dl[l])
                     dsr = bf16r(ds) if rnd else ds
                     dsf = np.zeros((2, 64, 8))
@@ -301,12 +342,26 @@ def dq(Qs, Ks, Vs, dOs, lse, delta, s, d, causal, rnd):
 
 
 
-@pytest.mark.parametrize("b,s,n,d,causal", [(2, 70, 2, 32, True), (1, 130, 1, 64, False), (1, 64, 1, 16, True),
-                                            (1, 96, 1, 96, True), (1, 64, 1, 128, False)])
-def test_forward_model_is_exact(b, s, n, d, causal):
+def growing_keys(QKV, b, s, n, d, rate):
+    """K rows scaled by 1 + rate * position: later key blocks score far above the first, so the running max
+    must be raised (and O rescaled) after the first step, while other steps stay within the slack."""
+    X = QKV.copy()
+    f = np.tile(1.0 + rate * np.arange(s), b)[:, None]
+    X[:, n * d:2 * n * d] = bf16r(X[:, n * d:2 * n * d] * f)
+    return X
+
+
+@pytest.mark.parametrize("b,s,n,d,causal,rate", [(2, 70, 2, 32, True, 0), (1, 130, 1, 64, False, 0),
+                                                 (1, 64, 1, 16, True, 0), (1, 96, 1, 96, True, 0),
+                                                 (1, 64, 1, 128, False, 0), (1, 200, 1, 64, True, 0.02),
+                                                 (1, 200, 1, 32, False, 0.125)])
+def test_forward_model_is_exact(b, s, n, d, causal, rate):
     rng = np.random.default_rng(s * d)
-    QKV = bf16r(rng.standard_normal((b * s, 3 * n * d)))
-    O, lse = model_fwd(QKV, b, s, n, d, causal, round_p=False)
+    QKV = growing_keys(bf16r(rng.standard_normal((b * s, 3 * n * d))), b, s, n, d, rate)
+    stats = {}
+    O, lse = model_fwd(QKV, b, s, n, d, causal, round_p=False, stats=stats)
+    if rate:  # both branches of the lazy rescale are taken
+        assert stats["late_rescales"] > 0 and stats["max_p"] > 1.0
     want = attn.attention_core(QKV[:, :n * d], QKV[:, n * d:2 * n * d], QKV[:, 2 * n * d:], n, d, b, s, causal)
     np.testing.assert_allclose(O, want["O"], rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(lse, want["lse"], rtol=1e-13, atol=1e-13)
@@ -323,6 +378,6 @@ def test_backward_model_is_exact(s, d, causal):
     w = attn.attention_core(Q, K, V, 1, d, 1, s, causal)
     delta = (dO * w["O"]).sum(axis=1)
     dK, dV = dkdv(Q, K, V, dO, w["lse"][0], delta, s, d, causal, False)
-    dQ = dq(Q, K, V, dO, w["lse"][0], delta, s, d, causal, False)
+    dQ = dq(Q, K, V, dO, w["O"], w["lse"][0], delta, s, d, causal, False)
     for got, want in ((dQ, Qt.grad), (dK, Kt.grad), (dV, Vt.grad)):
         np.testing.assert_allclose(got, want.numpy(), rtol=1e-11, atol=1e-12)

@@ -80,16 +80,22 @@ def _f64(u):
     return inputs.bf16_bits_to_f32(u).astype(np.float64)
 
 
-@pytest.mark.parametrize("b,s,n,d,causal", [(1, 64, 1, 16, True), (2, 70, 2, 32, True), (1, 130, 1, 64, False),
-                                            (1, 96, 1, 96, True), (1, 64, 1, 128, False), (3, 1, 2, 32, True),
-                                            (1, 200, 1, 64, True)])
-def test_attention_kernels_emulated(drivers, b, s, n, d, causal):
+@pytest.mark.parametrize("b,s,n,d,causal,rate", [(1, 64, 1, 16, True, 0), (2, 70, 2, 32, True, 0),
+                                                 (1, 130, 1, 64, False, 0), (1, 96, 1, 96, True, 0),
+                                                 (1, 64, 1, 128, False, 0), (3, 1, 2, 32, True, 0),
+                                                 (1, 200, 1, 64, True, 0), (1, 200, 1, 64, True, 0.02),
+                                                 (2, 200, 1, 32, False, 0.125)])
+def test_attention_kernels_emulated(drivers, b, s, n, d, causal, rate):
+    """rate > 0 scales key row t by 1 + rate * t, so later key steps raise the running max (and rescale O)
+    while others stay within the forward's rescale slack."""
     exes, tmp = drivers
     rng = np.random.default_rng(b * 1000 + s * 10 + d)
     T, nd = b * s, n * d
-    qkv = inputs.round_to_bf16_bits(rng.standard_normal((T, 3 * nd)).astype(np.float32))
+    x = rng.standard_normal((T, 3 * nd)).astype(np.float32)
+    x[:, nd:2 * nd] *= np.tile(1.0 + rate * np.arange(s), b)[:, None].astype(np.float32)
+    qkv = inputs.round_to_bf16_bits(x)
     dout = inputs.round_to_bf16_bits(rng.standard_normal((T, nd)).astype(np.float32))
-    case = os.path.join(tmp, f"attn_{b}_{s}_{n}_{d}_{int(causal)}")
+    case = os.path.join(tmp, f"attn_{b}_{s}_{n}_{d}_{int(causal)}_{rate}")
     os.makedirs(case, exist_ok=True)
     qkv.tofile(os.path.join(case, "qkv.bin"))
     dout.tofile(os.path.join(case, "dout.bin"))

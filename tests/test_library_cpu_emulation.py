@@ -195,9 +195,18 @@ def test_attn_shard_emulated(lib, b, s, h, n, hd, causal):
     attn_case(*lib, b, s, h, n, hd, causal)
 
 
-def attn_case(exe, d, b, s, h, n, hd, causal):
+@pytest.mark.parametrize("causal", [True, False])
+def test_attn_growing_scores_emulated(lib, causal):
+    """X row t scaled by 1 + t/32 (as in the GPU test): later key steps raise the forward's running max."""
+    attn_case(*lib, 2, 300, 128, 2, 64, causal, grow=1 / 32)
+
+
+def attn_case(exe, d, b, s, h, n, hd, causal, grow=0.0):
     a = inputs.make_attn_inputs(b, s, h, n, hd)
-    case = os.path.join(d, f"attn_{b}_{s}_{h}_{n}_{hd}_{int(causal)}")
+    if grow:
+        f = np.tile(1.0 + grow * np.arange(s), b)[:, None].astype(np.float32)
+        a = dict(a, X=inputs.round_to_bf16_bits(inputs.bf16_bits_to_f32(a["X"]) * f))
+    case = os.path.join(d, f"attn_{b}_{s}_{h}_{n}_{hd}_{int(causal)}_{grow}")
     put(case, X=a["X"], Wqkv=a["Wqkv"], Wo=a["Wo"], dZ=a["dZ"])
     run(exe, case, "attn_fwd", b, s, h, n, hd, int(causal))
     run(exe, case, "attn_bwd", b, s, h, n, hd, int(causal))
