@@ -38,17 +38,33 @@ namespace {
 
 constexpr int kAttnBM = 128;  // query rows per workgroup
 constexpr int kAttnBN = 64;   // keys per step
+
+// Waves per SIMD each kernel is compiled for (at most 512 / waves registers a
+// lane): every head size keeps its fragments and accumulators without spills.
+constexpr int attn_waves_per_simd(int d) { return d <= 32 ? 4 : d <= 64 ? 3 : 1; }
 constexpr float kLn2 = 0.69314718055994530942f;
 
 typedef short s16x8_t __attribute__((ext_vector_type(8)));
 
-// LDS tile of 64 rows x D columns (bf16), row pitch 2D + 16 bytes.
+// LDS tile of 64 rows x D columns (bf16), rows padded by 16 bytes (pitch = 16
+// mod 128 at every head size).  The kernels read it two ways: a 16-byte read
+// per lane of one chunk from 8 consecutive rows per 128-byte bank cycle
+// (ds_read_b128), which the pad spreads over 8 distinct 16-byte slots; and an
+// 8-byte transposing read per lane of 32 consecutive bytes from 4 consecutive
+// rows per cycle (ds_read_b64_tr_b16), where neighbouring rows share one slot.
+// A layout free of both conflicts (32-byte pad, chunk pairs swapped on rows
+// 4..7 of each 8) measured slower: the forward and dQ cores took 6% and 5%
+// longer on the same GPU, the dK/dV core the same time.
 template <int D>
 struct AttnTile {
+  static constexpr int kChunks = D / 8;  // 16-byte chunks per row
   static constexpr int kPitch = 2 * D + 16;
   static constexpr int kBytes = kAttnBN * kPitch;
-  static constexpr int kChunks = D / 8;             // 16-byte chunks per row
   static constexpr int kPerThread = 64 * kChunks / 256;  // = D / 32
+  // byte offset of chunk c (columns 8c .. 8c+7) of row r
+  __device__ static __forceinline__ int chunk(int r, int c) { return r * kPitch + 16 * c; }
+  // byte offset of columns col .. col+3 of row r (col a multiple of 4)
+  __device__ static __forceinline__ int quad(int r, int col) { return chunk(r, col >> 3) + ((col & 4) << 1); }
 };
 
 // Registers staging one tile: chunk i = tid + 256u is row i / (D/8), chunk i % (D/8).
@@ -77,7 +93,7 @@ __device__ __forceinline__ void tile_swrite(char* lds, const TileRegs<D>& t, int
   for (int u = 0; u < AttnTile<D>::kPerThread; ++u) {
     const int i = tid + 256 * u;
     const int row = i / AttnTile<D>::kChunks, c = i % AttnTile<D>::kChunks;
-    *(u32x4_t*)(lds + row * AttnTile<D>::kPitch + c * 16) = t.v[u];
+    *(u32x4_t*)(lds + AttnTile<D>::chunk(row, c)) = t.v[u];
   }
 }
 
@@ -114,58 +130,66 @@ __device__ __forceinline__ float row_sum4(float x) {
   return a + b;
 }
 
-// One query-row group's softmax step over the 64 keys whose raw scores sacc
-// holds (lane l: query l%16, keys 16kb16 + 4(l/16) + r).  The running max m
-// is kept in the scaled (base-2) domain and only raised when some row of the
-// wave sees a score more than kRescaleSlack above it, so the common step needs
-// no cross-lane merge and no rescale of O; the exponents then stay at most
-// 2^kRescaleSlack, which bf16 P and the fp32 sums hold exactly as well as 1.
-// The row sum is kept per lane (the lane's 16 keys of each step) and merged
-// over the row's four lanes once, after the last step.
+// The softmax step of a wave's two 16-query groups over the 64 keys whose raw
+// scores sacc holds (lane l: query l%16 of group rb, keys 16kb16 + 4(l/16) + r).
+// The running max m is kept in the scaled (base-2) domain and only raised when
+// some row of the group sees a score more than kRescaleSlack above it (a
+// wave-uniform test per group), so the common step needs no cross-lane
+// merge and no rescale of O; the exponents then stay at most 2^kRescaleSlack,
+// which bf16 P and the fp32 sums hold exactly as well as 1.  The row sum is kept
+// per lane (the lane's 16 keys of each step) and merged over the row's four
+// lanes once, after the last step.  MASK: key key0 + off of group rb is valid
+// when off <= lim[rb].
 constexpr float kRescaleSlack = 8.f;
 
-template <int ND, bool MASK, bool CAUSAL>
-__device__ __forceinline__ void attn_softmax_step(const f32x4_t (&sacc)[4], f32x4_t (&o)[ND], float& m, float& nm,
-                                                  float& l, bf16x8_t (&pf)[2], float scale, int key0, int q, int s) {
-  float sv[4][4];
-  float lm = -INFINITY;
-  // key key0 + off is valid when off <= lim (before the sequence end and, causal, not after the query)
-  const int lim = (CAUSAL ? min(q, s - 1) : s - 1) - key0;
+template <int ND, bool MASK>
+__device__ __forceinline__ void attn_softmax_step(const f32x4_t (&sacc)[2][4], f32x4_t (&o)[2][ND], float (&m)[2],
+                                                  float (&nm)[2], float (&l)[2], bf16x8_t (&pf)[2][2], float scale,
+                                                  const int (&lim)[2]) {
+  float sv[2][4][4];
 #pragma unroll
-  for (int kb16 = 0; kb16 < 4; ++kb16)
+  for (int rb = 0; rb < 2; ++rb) {
+    float lm = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      sv[kb16][r] = sacc[kb16][r];
-      if (MASK && kb16 * 16 + r > lim) sv[kb16][r] = -INFINITY;
-      lm = fmaxf(lm, sv[kb16][r]);
+    for (int kb16 = 0; kb16 < 4; ++kb16)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sv[rb][kb16][r] = sacc[rb][kb16][r];
+        if (MASK && kb16 * 16 + r > lim[rb]) sv[rb][kb16][r] = -INFINITY;
+        lm = fmaxf(lm, sv[rb][kb16][r]);
+      }
+    lm *= scale;  // scale > 0, so the max commutes with it exactly
+    if (__any(lm > m[rb] + kRescaleSlack)) {
+      const float mnew = fmaxf(m[rb], row_max4(lm));
+      const float corr = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[rb] - mnew);
+      l[rb] *= corr;
+#pragma unroll
+      for (int nb = 0; nb < ND; ++nb) o[rb][nb] *= corr;
+      m[rb] = mnew;
+      nm[rb] = mnew == -INFINITY ? 0.f : -mnew;
     }
-  lm *= scale;  // scale > 0, so the max commutes with it exactly
-  if (__any(lm > m + kRescaleSlack)) {
-    const float mnew = fmaxf(m, row_max4(lm));
-    const float corr = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - mnew);
-    l *= corr;
-#pragma unroll
-    for (int nb = 0; nb < ND; ++nb) o[nb] *= corr;
-    m = mnew;
-    nm = mnew == -INFINITY ? 0.f : -mnew;
   }
-  float p[4][4];
 #pragma unroll
-  for (int kb16 = 0; kb16 < 4; ++kb16)
+  for (int rb = 0; rb < 2; ++rb) {
+    float p[4][4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      p[kb16][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[kb16][r], scale, nm));
-      l += p[kb16][r];
-    }
+    for (int kb16 = 0; kb16 < 4; ++kb16)
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
-    pf[c] = as_bf16x8(u32x4_t{pack_bf16x2(p[2 * c][0], p[2 * c][1]), pack_bf16x2(p[2 * c][2], p[2 * c][3]),
-                              pack_bf16x2(p[2 * c + 1][0], p[2 * c + 1][1]),
-                              pack_bf16x2(p[2 * c + 1][2], p[2 * c + 1][3])});
+      for (int r = 0; r < 4; ++r) {
+        p[kb16][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[rb][kb16][r], scale, nm[rb]));
+        l[rb] += p[kb16][r];
+      }
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      pf[rb][c] = as_bf16x8(u32x4_t{pack_bf16x2(p[2 * c][0], p[2 * c][1]), pack_bf16x2(p[2 * c][2], p[2 * c][3]),
+                                    pack_bf16x2(p[2 * c + 1][0], p[2 * c + 1][1]),
+                                    pack_bf16x2(p[2 * c + 1][2], p[2 * c + 1][3])});
+  }
 }
 
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256) attn_fwd_kernel(AttnGeom g, const uint16_t* __restrict__ qkv,
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_waves_per_simd(D))))
+attn_fwd_kernel(AttnGeom g, const uint16_t* __restrict__ qkv,
                                                        uint16_t* __restrict__ out, float* __restrict__ lse) {
   constexpr int KD = D / 32, ND = D / 16;
   using Tile = AttnTile<D>;
@@ -222,40 +246,43 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnGeom g, const uint16_
     const char* K = kt[cur];
     const char* V = vt[cur];
     const int kbase = kb * kAttnBN;
+    // every K fragment is read once and serves both query groups
     f32x4_t sacc[2][4];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int kb16 = 0; kb16 < 4; ++kb16) {
+      sacc[0][kb16] = sacc[1][kb16] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb16 = 0; kb16 < 4; ++kb16) {
-        sacc[rb][kb16] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KD; ++kk)
-          sacc[rb][kb16] = mfma16(lds_read_b128(K + (kb16 * 16 + l16) * Tile::kPitch + (kk * 4 + g4) * 16),
-                                  qf[rb][kk], sacc[rb][kb16]);
+      for (int kk = 0; kk < KD; ++kk) {
+        const bf16x8_t kfrag = lds_read_b128(K + Tile::chunk(kb16 * 16 + l16, kk * 4 + g4));
+        sacc[0][kb16] = mfma16(kfrag, qf[0][kk], sacc[0][kb16]);
+        sacc[1][kb16] = mfma16(kfrag, qf[1][kk], sacc[1][kb16]);
       }
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const int qw = q0 + 32 * w + 16 * rb;  // first query row of this group
-      // keys past the sequence end, or (causal) after some row of the group, need the mask
-      const bool masked = kbase + kAttnBN > g.s || (CAUSAL && kbase + kAttnBN - 1 > qw);
-      bf16x8_t pf[2];
-      if (masked)
-        attn_softmax_step<ND, true, CAUSAL>(sacc[rb], o[rb], m[rb], nm[rb], l[rb], pf, g.scale_log2,
-                                            kbase + 4 * g4, qw + l16, g.s);
-      else
-        attn_softmax_step<ND, false, CAUSAL>(sacc[rb], o[rb], m[rb], nm[rb], l[rb], pf, g.scale_log2,
-                                             kbase + 4 * g4, qw + l16, g.s);
-      // source lane 16G + s of a transposing read addresses key 4G + s/4 (+ 16 for the second half)
-      // and columns 16nb + 4(s%4) .. +3
-#pragma unroll
-      for (int nb = 0; nb < ND; ++nb)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const s16x4_t lo = lds_read_tr(V + (32 * c + vrow) * Tile::kPitch + (16 * nb + vcol) * 2);
-          const s16x4_t hi = lds_read_tr(V + (32 * c + 16 + vrow) * Tile::kPitch + (16 * nb + vcol) * 2);
-          o[rb][nb] = mfma16(concat_bf16(lo, hi), pf[c], o[rb][nb]);
-        }
     }
+    // keys past the sequence end, or (causal) after some row of the wave, need the mask
+    const int qw = q0 + 32 * w;  // the wave's first query row
+    const bool masked = kbase + kAttnBN > g.s || (CAUSAL && kbase + kAttnBN - 1 > qw);
+    bf16x8_t pf[2][2];
+    if (masked) {
+      int lim[2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+        lim[rb] = (CAUSAL ? min(qw + 16 * rb + l16, g.s - 1) : g.s - 1) - kbase - 4 * g4;
+      attn_softmax_step<ND, true>(sacc, o, m, nm, l, pf, g.scale_log2, lim);
+    } else {
+      const int lim[2] = {0, 0};
+      attn_softmax_step<ND, false>(sacc, o, m, nm, l, pf, g.scale_log2, lim);
+    }
+    // source lane 16G + s of a transposing read addresses key 4G + s/4 (+ 16 for the second half)
+    // and columns 16nb + 4(s%4) .. +3; every V fragment serves both query groups
+#pragma unroll
+    for (int nb = 0; nb < ND; ++nb)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const bf16x8_t vfrag = concat_bf16(lds_read_tr(V + Tile::quad(32 * c + vrow, 16 * nb + vcol)),
+                                           lds_read_tr(V + Tile::quad(32 * c + 16 + vrow, 16 * nb + vcol)));
+        o[0][nb] = mfma16(vfrag, pf[0][c], o[0][nb]);
+        o[1][nb] = mfma16(vfrag, pf[1][c], o[1][nb]);
+      }
     if (more) {
       tile_swrite<D>(kt[cur ^ 1], kr, tid);
       tile_swrite<D>(vt[cur ^ 1], vr, tid);
@@ -305,18 +332,20 @@ hipError_t launch_attn_fwd_d(const AttnGeom& g, bool causal, const uint16_t* qkv
 // whose first operands (dO and Q gathered per column) come from transposing
 // LDS reads, and dP^T = V dO^T takes the wave's V rows from registers.  Only
 // the steps that cross the causal diagonal or the sequence end are masked.
-template <int KD, bool MASK>
+template <int D, bool MASK>
 __device__ __forceinline__ void dkdv_group_ds(const char* Q, const char* dO, const float* nl, const float* dl,
-                                              const bf16x8_t (&kf)[KD], const bf16x8_t (&vf)[KD], float scale,
-                                              int lo, int hi, int l16, int g4, int pitch, bf16x8_t (&pf)[2],
+                                              const bf16x8_t (&kf)[D / 32], const bf16x8_t (&vf)[D / 32],
+                                              float scale, int lo, int hi, int l16, int g4, bf16x8_t (&pf)[2],
                                               bf16x8_t (&dsf)[2]) {
+  constexpr int KD = D / 32;
+  using Tile = AttnTile<D>;
   float p[4][4], ds[4][4];
 #pragma unroll
   for (int qb16 = 0; qb16 < 4; ++qb16) {
     f32x4_t sacc = f32x4_t{0.f, 0.f, 0.f, 0.f}, dpacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KD; ++kk) {
-      const int off = (qb16 * 16 + l16) * pitch + (kk * 4 + g4) * 16;
+      const int off = Tile::chunk(qb16 * 16 + l16, kk * 4 + g4);
       sacc = mfma16(lds_read_b128(Q + off), kf[kk], sacc);
       dpacc = mfma16(lds_read_b128(dO + off), vf[kk], dpacc);
     }
@@ -343,7 +372,8 @@ __device__ __forceinline__ void dkdv_group_ds(const char* Q, const char* dO, con
 }
 
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnGeom g, const uint16_t* __restrict__ qkv,
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_waves_per_simd(D))))
+attn_bwd_dkdv_kernel(AttnGeom g, const uint16_t* __restrict__ qkv,
                                                             const uint16_t* __restrict__ dout,
                                                             const float* __restrict__ lse,
                                                             const float* __restrict__ delta,
@@ -412,17 +442,17 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnGeom g, const ui
     const bool masked = qbase + kAttnBN > g.s || (CAUSAL && qbase < k0 + 16 * w + 15);
     bf16x8_t pf[2], dsf[2];
     if (masked)
-      dkdv_group_ds<KD, true>(Q, dO, srow[cur], srow[cur] + kAttnBN, kf, vf, g.scale_log2, lo, hi, l16, g4,
-                              Tile::kPitch, pf, dsf);
+      dkdv_group_ds<D, true>(Q, dO, srow[cur], srow[cur] + kAttnBN, kf, vf, g.scale_log2, lo, hi, l16, g4, pf,
+                             dsf);
     else
-      dkdv_group_ds<KD, false>(Q, dO, srow[cur], srow[cur] + kAttnBN, kf, vf, g.scale_log2, lo, hi, l16, g4,
-                               Tile::kPitch, pf, dsf);
+      dkdv_group_ds<D, false>(Q, dO, srow[cur], srow[cur] + kAttnBN, kf, vf, g.scale_log2, lo, hi, l16, g4, pf,
+                              dsf);
 #pragma unroll
     for (int nb = 0; nb < ND; ++nb)
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const int off0 = (32 * c + vrow) * Tile::kPitch + (16 * nb + vcol) * 2;
-        const int off1 = (32 * c + 16 + vrow) * Tile::kPitch + (16 * nb + vcol) * 2;
+        const int off0 = Tile::quad(32 * c + vrow, 16 * nb + vcol);
+        const int off1 = Tile::quad(32 * c + 16 + vrow, 16 * nb + vcol);
         dv[nb] = mfma16(concat_bf16(lds_read_tr(dO + off0), lds_read_tr(dO + off1)), pf[c], dv[nb]);
         dk[nb] = mfma16(concat_bf16(lds_read_tr(Q + off0), lds_read_tr(Q + off1)), dsf[c], dk[nb]);
       }
@@ -454,36 +484,52 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnGeom g, const ui
 // in the forward's layout; dS stays in registers for dQ += dS K, whose first
 // operand (K gathered per column) comes from transposing LDS reads.  Only the
 // steps that cross the causal diagonal or the sequence end are masked.
-template <int KD, bool MASK>
-__device__ __forceinline__ void dq_group_ds(const char* K, const char* V, const bf16x8_t (&qf)[KD],
-                                            const bf16x8_t (&df)[KD], float nlq, float del, float scale, int lim,
-                                            int l16, int g4, int pitch, bf16x8_t (&dsf)[2]) {
-  float ds[4][4];
+template <int D, bool MASK>
+__device__ __forceinline__ void dq_step_ds(const char* K, const char* V, const bf16x8_t (&qf)[2][D / 32],
+                                           const bf16x8_t (&df)[2][D / 32], const float (&nlq)[2],
+                                           const float (&del)[2], float scale, const int (&lim)[2], int l16, int g4,
+                                           bf16x8_t (&dsf)[2][2]) {
+  constexpr int KD = D / 32;
+  using Tile = AttnTile<D>;
+  float ds[2][4][4];
 #pragma unroll
   for (int kb16 = 0; kb16 < 4; ++kb16) {
-    f32x4_t sacc = f32x4_t{0.f, 0.f, 0.f, 0.f}, dpacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // every K and V fragment is read once and serves both query groups
+    f32x4_t sacc[2], dpacc[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) sacc[rb] = dpacc[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KD; ++kk) {
-      const int off = (kb16 * 16 + l16) * pitch + (kk * 4 + g4) * 16;
-      sacc = mfma16(lds_read_b128(K + off), qf[kk], sacc);
-      dpacc = mfma16(lds_read_b128(V + off), df[kk], dpacc);
+      const int off = Tile::chunk(kb16 * 16 + l16, kk * 4 + g4);
+      const bf16x8_t kfrag = lds_read_b128(K + off), vfrag = lds_read_b128(V + off);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        sacc[rb] = mfma16(kfrag, qf[rb][kk], sacc[rb]);
+        dpacc[rb] = mfma16(vfrag, df[rb][kk], dpacc[rb]);
+      }
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], scale, nlq));
-      if (MASK && kb16 * 16 + r > lim) p = 0.f;
-      ds[kb16][r] = p * (dpacc[r] - del);
-    }
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[rb][r], scale, nlq[rb]));
+        if (MASK && kb16 * 16 + r > lim[rb]) p = 0.f;
+        ds[rb][kb16][r] = p * (dpacc[rb][r] - del[rb]);
+      }
   }
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
-    dsf[c] = as_bf16x8(u32x4_t{pack_bf16x2(ds[2 * c][0], ds[2 * c][1]), pack_bf16x2(ds[2 * c][2], ds[2 * c][3]),
-                               pack_bf16x2(ds[2 * c + 1][0], ds[2 * c + 1][1]),
-                               pack_bf16x2(ds[2 * c + 1][2], ds[2 * c + 1][3])});
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      dsf[rb][c] = as_bf16x8(u32x4_t{pack_bf16x2(ds[rb][2 * c][0], ds[rb][2 * c][1]),
+                                     pack_bf16x2(ds[rb][2 * c][2], ds[rb][2 * c][3]),
+                                     pack_bf16x2(ds[rb][2 * c + 1][0], ds[rb][2 * c + 1][1]),
+                                     pack_bf16x2(ds[rb][2 * c + 1][2], ds[rb][2 * c + 1][3])});
 }
 
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256) attn_bwd_dq_kernel(AttnGeom g, const uint16_t* __restrict__ qkv,
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_waves_per_simd(D))))
+attn_bwd_dq_kernel(AttnGeom g, const uint16_t* __restrict__ qkv,
                                                           const uint16_t* __restrict__ out,
                                                           const uint16_t* __restrict__ dout,
                                                           const float* __restrict__ lse, float* __restrict__ delta,
@@ -554,27 +600,29 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(AttnGeom g, const uint
     const char* K = kt[cur];
     const char* V = vt[cur];
     const int kbase = kb * kAttnBN;
+    const int qw = q0 + 32 * w;  // the wave's first query row
+    const bool masked = kbase + kAttnBN > g.s || (CAUSAL && kbase + kAttnBN - 1 > qw);
+    bf16x8_t dsf[2][2];
+    if (masked) {
+      // key kbase + 4(l/16) + off is valid for this lane's query of group rb when off <= lim[rb]
+      int lim[2];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const int qw = q0 + 32 * w + 16 * rb;  // first query row of this group
-      const bool masked = kbase + kAttnBN > g.s || (CAUSAL && kbase + kAttnBN - 1 > qw);
-      // key kbase + 4(l/16) + off is valid for this lane's query when off <= lim
-      const int lim = (CAUSAL ? min(qw + l16, g.s - 1) : g.s - 1) - kbase - 4 * g4;
-      bf16x8_t dsf[2];
-      if (masked)
-        dq_group_ds<KD, true>(K, V, qf[rb], df[rb], nlq[rb], del[rb], g.scale_log2, lim, l16, g4, Tile::kPitch, dsf);
-      else
-        dq_group_ds<KD, false>(K, V, qf[rb], df[rb], nlq[rb], del[rb], g.scale_log2, lim, l16, g4, Tile::kPitch,
-                               dsf);
-#pragma unroll
-      for (int nb = 0; nb < ND; ++nb)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const s16x4_t lo = lds_read_tr(K + (32 * c + vrow) * Tile::kPitch + (16 * nb + vcol) * 2);
-          const s16x4_t hi = lds_read_tr(K + (32 * c + 16 + vrow) * Tile::kPitch + (16 * nb + vcol) * 2);
-          dq[rb][nb] = mfma16(concat_bf16(lo, hi), dsf[c], dq[rb][nb]);
-        }
+      for (int rb = 0; rb < 2; ++rb)
+        lim[rb] = (CAUSAL ? min(qw + 16 * rb + l16, g.s - 1) : g.s - 1) - kbase - 4 * g4;
+      dq_step_ds<D, true>(K, V, qf, df, nlq, del, g.scale_log2, lim, l16, g4, dsf);
+    } else {
+      const int lim[2] = {0, 0};
+      dq_step_ds<D, false>(K, V, qf, df, nlq, del, g.scale_log2, lim, l16, g4, dsf);
     }
+#pragma unroll
+    for (int nb = 0; nb < ND; ++nb)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const bf16x8_t kfrag = concat_bf16(lds_read_tr(K + Tile::quad(32 * c + vrow, 16 * nb + vcol)),
+                                           lds_read_tr(K + Tile::quad(32 * c + 16 + vrow, 16 * nb + vcol)));
+        dq[0][nb] = mfma16(kfrag, dsf[0][c], dq[0][nb]);
+        dq[1][nb] = mfma16(kfrag, dsf[1][c], dq[1][nb]);
+      }
     if (more) {
       tile_swrite<D>(kt[cur ^ 1], kr, tid);
       tile_swrite<D>(vt[cur ^ 1], vr, tid);

@@ -10,7 +10,7 @@ The attention core kernels (attention.hip) rest on three facts about gfx950:
   * bf16 operands, fp32 accumulation.
 This test re-enacts, lane by lane, the forward kernel and the two backward
 kernels (dK/dV over key blocks, dQ over query blocks) with those semantics:
-the same fragment addresses, padded LDS pitch, key permutation of P and dS,
+the same fragment addresses, LDS tile layout, key permutation of P and dS,
 masks and online softmax.  With exact arithmetic the model must reproduce
 the oracle's attention and torch's attention gradients to rounding, for
 every head size the kernels are built for, causal and not, with ragged
@@ -68,6 +68,20 @@ class Lds:
         return out
 
 
+def chunk_off(r, c, pitch):
+    """Byte offset of 16-byte chunk c of tile row r (rows padded to `pitch`)."""
+    return r * pitch + 16 * c
+
+
+def quad_off(r, col, pitch):
+    """Byte offset of columns col..col+3 (col a multiple of 4) of tile row r."""
+    return chunk_off(r, col >> 3, pitch) + 2 * (col & 7)
+
+
+def tile_pitch(D):
+    return 2 * D + 16
+
+
 def bf16r(x):
     return inputs.bf16_bits_to_f32(inputs.round_to_bf16_bits(np.asarray(x, np.float32))).astype(np.float64)
 
@@ -75,7 +89,7 @@ def bf16r(x):
 def model_fwd(QKV, b, s, n, d, causal, round_p=True, stats=None):
     D = ((d + 31) // 32) * 32
     KD, ND = D // 32, D // 16
-    pitch = 2 * D + 16
+    pitch = tile_pitch(D)
     ld = 3 * n * d
     T = b * s
     O = np.full((T, n * d), np.nan)
@@ -89,7 +103,7 @@ def model_fwd(QKV, b, s, n, d, causal, round_p=True, stats=None):
                 row, c = i // (D // 8), i % (D // 8)
                 ok = row0 + row < s and c * 8 < d
                 vals = QKV[bi * s + row0 + row, base_col + c * 8: base_col + c * 8 + 8] if ok else np.zeros(8)
-                lds.write16(row * pitch + c * 16, vals)
+                lds.write16(chunk_off(row, c, pitch), vals)
 
     for bi in range(b):
         for j in range(n):
@@ -117,7 +131,7 @@ def model_fwd(QKV, b, s, n, d, causal, round_p=True, stats=None):
                             sacc = np.zeros((4, 64, 4))
                             for kb16 in range(4):
                                 for kk in range(KD):
-                                    kfrag = np.array([kt.read_b128((kb16 * 16 + l % 16) * pitch + (kk * 4 + l // 16) * 16)
+                                    kfrag = np.array([kt.read_b128(chunk_off(kb16 * 16 + l % 16, kk * 4 + l // 16, pitch))
                                                       for l in range(64)])
                                     sacc[kb16] = mfma(kfrag, qf[rb, kk], sacc[kb16])
                             qw = q0 + 32 * w + 16 * rb
@@ -159,10 +173,10 @@ def model_fwd(QKV, b, s, n, d, causal, round_p=True, stats=None):
                                 pf[c, :, 4:8] = pr[2 * c + 1]
                             for nb in range(ND):
                                 for c in range(2):
-                                    lo = vt.read_tr([(32 * c + 0 + 4 * (l // 16) + ((l % 16) >> 2)) * pitch
-                                                     + (16 * nb + 4 * ((l % 16) & 3)) * 2 for l in range(64)])
-                                    hi = vt.read_tr([(32 * c + 16 + 4 * (l // 16) + ((l % 16) >> 2)) * pitch
-                                                     + (16 * nb + 4 * ((l % 16) & 3)) * 2 for l in range(64)])
+                                    lo = vt.read_tr([quad_off(32 * c + 4 * (l // 16) + ((l % 16) >> 2),
+                                                              16 * nb + 4 * ((l % 16) & 3), pitch) for l in range(64)])
+                                    hi = vt.read_tr([quad_off(32 * c + 16 + 4 * (l // 16) + ((l % 16) >> 2),
+                                                              16 * nb + 4 * ((l % 16) & 3), pitch) for l in range(64)])
                                     vf = np.concatenate([lo, hi], axis=1)
                                     o[rb, nb] = mfma(vf, pf[c], o[rb, nb])
                     for rb in range(2):
@@ -191,7 +205,7 @@ def tile_load(lds, src, s, d, D, pitch, row0):
             row, c = i // (D // 8), i % (D // 8)
             ok = row0 + row < s and c * 8 < d
             vals = src[row0 + row, c * 8:c * 8 + 8] if ok else np.zeros(8)
-            lds.write16(row * pitch + c * 16, vals)
+            lds.write16(chunk_off(row, c, pitch), vals)
 
 
 def kfrag_rows(src, rows_fn, kk, s, d):
@@ -206,7 +220,7 @@ def kfrag_rows(src, rows_fn, kk, s, d):
 
 def dkdv(Qs, Ks, Vs, dOs, lse, delta, s, d, causal, rnd):
     """One (sequence, head): returns dK, dV [s, d]."""
-    D = ((d + 31) // 32) * 32; KD, ND = D // 32, D // 16; pitch = 2 * D + 16
+    D = ((d + 31) // 32) * 32; KD, ND = D // 32, D // 16; pitch = tile_pitch(D)
     scale_log2 = math.log2(math.e) / math.sqrt(d)
     dK = np.full((s, d), np.nan); dV = np.full((s, d), np.nan)
     for kb in range((s + BN - 1) // BN):
@@ -229,7 +243,7 @@ def dkdv(Qs, Ks, Vs, dOs, lse, delta, s, d, causal, rnd):
                 for qb16 in range(4):
                     sacc = np.zeros((64, 4)); dpacc = np.zeros((64, 4))
                     for kk in range(KD):
-                        offs = [(qb16 * 16 + l % 16) * pitch + (kk * 4 + l // 16) * 16 for l in range(64)]
+                        offs = [chunk_off(qb16 * 16 + l % 16, kk * 4 + l // 16, pitch) for l in range(64)]
                         sacc = mfma(np.array([Qt.read_b128(o) for o in offs]), kf[kk], sacc)
                         dpacc = mfma(np.array([Dt.read_b128(o) for o in offs]), vf[kk], dpacc)
                     for l in range(64):
@@ -253,8 +267,8 @@ def dkdv(Qs, Ks, Vs, dOs, lse, delta, s, d, causal, rnd):
                     dsf[c, :, :4], dsf[c, :, 4:] = dsr[2 * c], dsr[2 * c + 1]
                 for nb in range(ND):
                     for c in range(2):
-                        a0 = [(32 * c + 4 * (l // 16) + ((l % 16) >> 2)) * pitch + (16 * nb + 4 * ((l % 16) & 3)) * 2 for l in range(64)]
-                        a1 = [(32 * c + 16 + 4 * (l // 16) + ((l % 16) >> 2)) * pitch + (16 * nb + 4 * ((l % 16) & 3)) * 2 for l in range(64)]
+                        a0 = [quad_off(32 * c + 4 * (l // 16) + ((l % 16) >> 2), 16 * nb + 4 * ((l % 16) & 3), pitch) for l in range(64)]
+                        a1 = [quad_off(32 * c + 16 + 4 * (l // 16) + ((l % 16) >> 2), 16 * nb + 4 * ((l % 16) & 3), pitch) for l in range(64)]
                         dv[nb] = mfma(np.concatenate([Dt.read_tr(a0), Dt.read_tr(a1)], axis=1), pf[c], dv[nb])
                         dk[nb] = mfma(np.concatenate([Qt.read_tr(a0), Qt.read_tr(a1)], axis=1), dsf[c], dk[nb])
             for l in range(64):
@@ -272,7 +286,7 @@ def dkdv(Qs, Ks, Vs, dOs, lse, delta, s, d, causal, rnd):
 def dq(Qs, Ks, Vs, dOs, Os, lse, delta, s, d, causal, rnd):
     """delta is formed here as the dQ kernel forms it (per-lane partial dot products of dO and O over the
     lane's columns, merged over the row's four lanes) and checked against the one given."""
-    D = ((d + 31) // 32) * 32; KD, ND = D // 32, D // 16; pitch = 2 * D + 16
+    D = ((d + 31) // 32) * 32; KD, ND = D // 32, D // 16; pitch = tile_pitch(D)
     scale_log2 = math.log2(math.e) / math.sqrt(d)
     dQ = np.full((s, d), np.nan)
     for qbk in range((s + BM - 1) // BM):
@@ -304,7 +318,7 @@ def dq(Qs, Ks, Vs, dOs, Os, lse, delta, s, d, causal, rnd):
                     for kb16 in range(4):
                         sacc = np.zeros((64, 4)); dpacc = np.zeros((64, 4))
                         for kk in range(KD):
-                            offs = [(kb16 * 16 + l % 16) * pitch + (kk * 4 + l // 16) * 16 for l in range(64)]
+                            offs = [chunk_off(kb16 * 16 + l % 16, kk * 4 + l // 16, pitch) for l in range(64)]
                             sacc = mfma(np.array([Kt.read_b128(o) for o in offs]), qf[kk], sacc)
                             dpacc = mfma(np.array([Vt.read_b128(o) for o in offs]), df[kk], dpacc)
                         for l in range(64):
@@ -326,8 +340,8 @@ def dq(Qs, Ks, Vs, dOs, Os, lse, delta, s, d, causal, rnd):
                         dsf[c, :, :4], dsf[c, :, 4:] = dsr[2 * c], dsr[2 * c + 1]
                     for nb in range(ND):
                         for c in range(2):
-                            a0 = [(32 * c + 4 * (l // 16) + ((l % 16) >> 2)) * pitch + (16 * nb + 4 * ((l % 16) & 3)) * 2 for l in range(64)]
-                            a1 = [(32 * c + 16 + 4 * (l // 16) + ((l % 16) >> 2)) * pitch + (16 * nb + 4 * ((l % 16) & 3)) * 2 for l in range(64)]
+                            a0 = [quad_off(32 * c + 4 * (l // 16) + ((l % 16) >> 2), 16 * nb + 4 * ((l % 16) & 3), pitch) for l in range(64)]
+                            a1 = [quad_off(32 * c + 16 + 4 * (l // 16) + ((l % 16) >> 2), 16 * nb + 4 * ((l % 16) & 3), pitch) for l in range(64)]
                             accs[rb, nb] = mfma(np.concatenate([Kt.read_tr(a0), Kt.read_tr(a1)], axis=1), dsf[c], accs[rb, nb])
                 for l in range(64):
                     q = row_of(l)
@@ -381,3 +395,35 @@ def test_backward_model_is_exact(s, d, causal):
     dQ = dq(Q, K, V, dO, w["O"], w["lse"][0], delta, s, d, causal, False)
     for got, want in ((dQ, Qt.grad), (dK, Kt.grad), (dV, Vt.grad)):
         np.testing.assert_allclose(got, want.numpy(), rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("D", [32, 64, 96, 128])
+def test_tile_layout_banks(D):
+    """The kernels' LDS accesses of a tile under the bank model of gfx950's LDS (128 bytes per cycle: a
+    16-byte access serves 8 lanes per cycle, an 8-byte access 16).  The layout is a bijection of the
+    tile's chunks; the 16-byte fragment reads touch distinct bytes modulo 128 in every cycle; the
+    transposing reads touch each byte at most twice (neighbouring rows share one 16-byte slot)."""
+    pitch = tile_pitch(D)
+    chunks = D // 8
+    offs = {chunk_off(r, c, pitch) for r in range(BN) for c in range(chunks)}
+    assert len(offs) == BN * chunks and max(offs) + 16 <= BN * pitch
+
+    def most_shared(addrs, width):
+        count = np.zeros(128, int)
+        for a in addrs:
+            assert a % 128 + width <= 128
+            count[a % 128:a % 128 + width] += 1
+        return count.max()
+
+    for base in range(0, BN, 16):  # 16-byte reads: lane l reads row base + l%16, chunk 4kk + l/16
+        for kk in range(D // 32):
+            addrs = [chunk_off(base + l % 16, 4 * kk + l // 16, pitch) for l in range(64)]
+            for grp in range(0, 64, 8):
+                assert most_shared(addrs[grp:grp + 8], 16) == 1, (base, kk, grp)
+    for c in range(2):  # transposing reads: lane l reads row 32c (+16) + 4(l/16) + (l%16)/4, columns 16nb + 4(l%4)
+        for half in (0, 16):
+            for nb in range(D // 16):
+                addrs = [quad_off(32 * c + half + 4 * (l // 16) + ((l % 16) >> 2), 16 * nb + 4 * ((l % 16) & 3), pitch)
+                         for l in range(64)]
+                for grp in range(0, 64, 16):
+                    assert most_shared(addrs[grp:grp + 16], 8) <= 2, (c, half, nb, grp)
