@@ -24,7 +24,8 @@ workload on the host cores.
 After the headline workload, the same step is timed on the three rank-shard
 workloads (8.3B-GPT-like t=8, 3.9B-BERT-like t=4, 176B-scale t=4) and reported
 under ``shard_configs``; the CE backward and the attention shard of the headline
-workload are timed under ``ce_bwd`` and ``attn``.  ``peak_box`` restates the
+workload are timed under ``ce_bwd`` and ``attn``, and each shard workload's
+attention shard under its own ``attn``.  ``peak_box`` restates the
 bf16 peak from the compute-unit count and peak clock the HIP runtime reports
 (compute units x 4096 flop/clock x clock).
 
@@ -277,6 +278,42 @@ def step_summary(cfg, t):
     return {"value": value, "mlp_tflops": mlp_tflops, "ce_tflops": ce_tflops, "gemm_tflops": gemm_tflops}
 
 
+def attn_row(torch, mshard, run, cfg, dev, steps, warmup):
+    """Times this workload's attention shard (forward, then backward) on the runner's stream."""
+    from megatron_tensor_transformer_mlp_amd import inputs
+    bf = torch.bfloat16
+    T, h = cfg.T, cfg.h
+    ac = inputs.ATTN_CONFIGS[cfg.name]
+    assert ac.b * ac.s == T and ac.h == h, (ac, cfg)
+    ad = inputs.make_attn_config_inputs(ac)
+    up = run.up
+    Xa, Wqkv, Wo, dZa = up(ad["X"]), up(ad["Wqkv"]), up(ad["Wo"]), up(ad["dZ"])
+    nd = ac.n * ac.d
+    QKV = torch.empty((T, 3 * nd), dtype=bf, device=dev)
+    Oa = torch.empty((T, nd), dtype=bf, device=dev)
+    lse = torch.empty((ac.n, T), dtype=torch.float32, device=dev)
+    Za = torch.empty((T, h), dtype=torch.float32, device=dev)
+    dXa = torch.empty((T, h), dtype=torch.float32, device=dev)
+    dWqkv = torch.empty((h, 3 * nd), dtype=bf, device=dev)
+    dWo = torch.empty((nd, h), dtype=bf, device=dev)
+    attn_ws = torch.empty(max(mshard.attn_shard_workspace_bytes(ac.b, ac.s, h, ac.n, ac.d), 1), dtype=torch.uint8,
+                          device=dev)
+    fwd = lambda: mshard.attn_shard_fwd(Xa, Wqkv, Wo, ac.b, ac.s, ac.n, ac.d, ac.causal, out=(QKV, Oa, lse, Za))
+    bwd = lambda: mshard.attn_shard_bwd(Xa, Wqkv, Wo, QKV, Oa, lse, dZa, ac.b, ac.s, ac.n, ac.d, ac.causal,
+                                        workspace=attn_ws, out=(dXa, dWqkv, dWo))
+    ms_f = run.timed(fwd, steps, warmup)
+    ms_b = run.timed(bwd, steps, warmup)
+    pairs = ac.b * ac.n * (ac.s * (ac.s + 1) // 2 if ac.causal else ac.s * ac.s)  # visible (query, key) pairs
+    proj = 2 * T * h * 3 * nd + 2 * T * nd * h
+    f_flop = proj + 4 * pairs * ac.d            # projections; S and P V
+    b_flop = 2 * proj + 8 * pairs * ac.d        # their gradients; dV, dP, dQ, dK (recompute not counted)
+    return {"config": f"b={ac.b} s={ac.s} h={h} n={ac.n} d={ac.d} causal={ac.causal}",
+            "fwd_ms": round(ms_f, 4), "bwd_ms": round(ms_b, 4),
+            "fwd_tflops": round(f_flop / (ms_f * 1e-3) / 1e12, 2),
+            "bwd_tflops": round(b_flop / (ms_b * 1e-3) / 1e12, 2),
+            "algorithmic_flop": {"fwd": f_flop, "bwd": b_flop}}
+
+
 def main():
     a = _args()
     if a.gpus != 1:
@@ -323,35 +360,7 @@ def main():
                            "tokens_per_s": round(T / (ms_ce * 1e-3), 1), "algorithmic_flop": flop}
         del ce_bwd_ws, dXc, dEc
     if "attn" in rows:
-        ac = inputs.ATTN_CONFIGS[cfg.name]
-        ad = inputs.make_attn_config_inputs(ac)
-        up = run.up
-        Xa, Wqkv, Wo, dZa = up(ad["X"]), up(ad["Wqkv"]), up(ad["Wo"]), up(ad["dZ"])
-        nd = ac.n * ac.d
-        QKV = torch.empty((T, 3 * nd), dtype=bf, device=dev)
-        Oa = torch.empty((T, nd), dtype=bf, device=dev)
-        lse = torch.empty((ac.n, T), dtype=torch.float32, device=dev)
-        Za = torch.empty((T, h), dtype=torch.float32, device=dev)
-        dXa = torch.empty((T, h), dtype=torch.float32, device=dev)
-        dWqkv = torch.empty((h, 3 * nd), dtype=bf, device=dev)
-        dWo = torch.empty((nd, h), dtype=bf, device=dev)
-        attn_ws = torch.empty(max(mshard.attn_shard_workspace_bytes(ac.b, ac.s, h, ac.n, ac.d), 1), dtype=torch.uint8,
-                              device=dev)
-        fwd = lambda: mshard.attn_shard_fwd(Xa, Wqkv, Wo, ac.b, ac.s, ac.n, ac.d, ac.causal, out=(QKV, Oa, lse, Za))
-        bwd = lambda: mshard.attn_shard_bwd(Xa, Wqkv, Wo, QKV, Oa, lse, dZa, ac.b, ac.s, ac.n, ac.d, ac.causal,
-                                            workspace=attn_ws, out=(dXa, dWqkv, dWo))
-        ms_f = run.timed(fwd, a.steps, a.warmup)
-        ms_b = run.timed(bwd, a.steps, a.warmup)
-        pairs = ac.b * ac.n * (ac.s * (ac.s + 1) // 2 if ac.causal else ac.s * ac.s)  # visible (query, key) pairs
-        proj = 2 * T * h * 3 * nd + 2 * T * nd * h
-        f_flop = proj + 4 * pairs * ac.d            # projections; S and P V
-        b_flop = 2 * proj + 8 * pairs * ac.d        # their gradients; dV, dP, dQ, dK (recompute not counted)
-        extra["attn"] = {"config": f"b={ac.b} s={ac.s} h={h} n={ac.n} d={ac.d} causal={ac.causal}",
-                         "fwd_ms": round(ms_f, 4), "bwd_ms": round(ms_b, 4),
-                         "fwd_tflops": round(f_flop / (ms_f * 1e-3) / 1e12, 2),
-                         "bwd_tflops": round(b_flop / (ms_b * 1e-3) / 1e12, 2),
-                         "algorithmic_flop": {"fwd": f_flop, "bwd": b_flop}}
-        del Xa, Wqkv, Wo, dZa, QKV, Oa, lse, Za, dXa, dWqkv, dWo, attn_ws
+        extra["attn"] = attn_row(torch, mshard, run, cfg, dev, a.steps, a.warmup)
 
     info = mshard.device_info(0)
     box_peak = info["compute_units"] * FLOP_PER_CU_CLOCK * info["clock_khz"] * 1e3 / 1e12
@@ -410,6 +419,8 @@ def main():
             "ce_pct_of_peak": round(100 * s2["ce_tflops"] / PEAK_BF16_TFLOPS, 2),
             "ce_gemm_tflops": round(s2["gemm_tflops"], 2),
             "kernels_us": None if a.no_breakdown else r2.breakdown()}
+        if "attn" in rows:
+            shards[name]["attn"] = attn_row(torch, mshard, r2, c2, dev, a.steps, a.warmup)
         del r2
         torch.cuda.empty_cache()
     if shards:
