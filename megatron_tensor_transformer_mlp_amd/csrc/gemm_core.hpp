@@ -15,10 +15,13 @@
 //   * One workgroup = 256 threads = 4 wave64s computes a 256 x 256 tile of C.
 //     The waves form a 2 x 2 grid, each owning a 128 x 128 sub-tile held as
 //     8 x 8 fp32 16x16 MFMA accumulators (256 accumulation registers per lane).
-//   * K advances in steps of 32.  A ring of 4 LDS stages (32 KiB each: the A
-//     and B tiles of one step) holds step kt being consumed, kt+1 and kt+2
-//     resident or landing, and kt+3 being loaded; the loads of kt+3 are
-//     interleaved with the MFMAs of kt.  One barrier per step.
+//   * K advances in steps of 32.  Each operand has a ring in LDS (128 KiB in
+//     all): an M/N-major operand four 16 KiB stages, one k tile each; a
+//     K-major operand two 32 KiB pair slots, two k tiles each, so that its
+//     loads read whole 128-byte rows.  Step kt consumes tile kt while kt+1 and
+//     kt+2 are resident or landing and the loads of kt+3 (M/N-major), or on
+//     every other step of the pair kt+3, kt+4 (K-major), run interleaved with
+//     its MFMAs.  One barrier per step.
 //   * Global -> LDS moves use direct-to-LDS buffer loads (no staging
 //     registers); the layouts (see below) make every fragment read
 //     conflict-free: K-major tiles are read with ds_read_b128, M/N-major tiles
@@ -58,7 +61,6 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 constexpr int kBM = 256, kBN = 256, kBK = 32;
-constexpr int kStages = 4;  // LDS ring: tiles kt+1..kt+3 in flight while kt is consumed
 // Wave grid of a workgroup: kWavesM x kWavesN waves, each owning a
 // kWaveM x kWaveN sub-tile of the 256 x 256 tile.
 constexpr int kWavesM = 2, kWavesN = 2;
@@ -145,31 +147,40 @@ __device__ __forceinline__ void map_tile(const GemmGeom& g, int b, int G, int& t
 // contiguous LDS (lane l -> byte 16*l); each lane chooses which 16-byte global
 // chunk lands in its slot, so the LDS layout is free at 16-byte granularity.
 // Out-of-range lanes (edge tiles) get an offset beyond the resource and write
-// zeros.  A 16 KiB operand tile = 1024 slots = 16 instructions, 4 per wave.
+// zeros.
 //
-// Layouts (16-byte slots; a K-major tile is [256 m/n rows][32 k], an
-// M/N-major tile is [32 k rows][256 m/n columns]):
-//   K-major : slot(r, c) = (r/16)*64 + (r%16)*4 + (c ^ ((r%16)/2 % 4))
-//                                                   c = k/8 (8 k values)
-//   MN-major: slot(k, j) = k*32 + (j ^ 2*((k%4) | 4*((k/8)%2)))
-//                                                   j = col/8 (8 columns)
+// An operand stored K-major is loaded two k tiles at a time: a pair of k
+// tiles is [256 m/n rows][64 k], whose 128-byte rows are whole cache lines
+// (one k tile's 64-byte rows would each be half a line, fetched twice, and
+// the memory path pays per request, not per byte: loading whole lines made
+// the CE GEMM about 5% faster).  Pairs live in two 32 KiB pair slots.  An
+// operand stored M/N-major is loaded one k tile ([32 k rows][256 m/n]) per
+// step into four 16 KiB stages; its 512-byte k rows are whole lines already.
+// The four 32 KiB LDS arrays hold, in order, the pair slots of each K-major
+// operand (A first) and then the stages of each M/N-major one, two 16 KiB
+// stages per array; with both operands M/N-major, array s holds stage s of A
+// then stage s of B.
+//
+// Layouts (16-byte slots):
+//   K-major pair : slot(r, c) = r*8 + (c ^ (r % 8))     c = k/8 (0..7 over the pair's 64 k)
+//   MN-major tile: slot(k, j) = k*32 + (j ^ 2*((k%4) | 4*((k/8)%2)))
+//                                                       j = col/8 (8 columns)
 // Rows (K-major) and k rows (M/N-major) are contiguous, so each load
-// instruction's 64 lanes read whole 64-byte row segments or 512-byte k rows:
-// neighbouring lanes read neighbouring 16 bytes and the memory pipeline merges
-// them into full cache-line requests.  The XOR terms only permute slots
-// within a row; they make the fragment reads conflict-free.  A ds_read_b128
-// is served 8 lanes at a time, whose 16-byte chunks must lie in different
-// 16-byte slots of a 128-byte window: a K-major fragment's 8 consecutive rows
-// of one chunk do (rows r and r+1 sit 64 bytes apart, the XOR of (r%16)/2
-// moves pairs of rows by 16 bytes); with an XOR of (r%16)/4 pairs of rows
-// share a slot and the read runs at half rate (measured on gfx950: 128 versus
-// 250 bytes per clock per CU).  The 8 k rows x 32 bytes that 32 lanes of an
-// M/N-major transposing read touch fall in 8 different 32-byte windows.
+// instruction's 64 lanes read 8 whole 128-byte rows or 2 whole 512-byte k
+// rows.  The XOR terms only permute slots within a row; they make the
+// fragment reads conflict-free.  A ds_read_b128 is served 8 lanes at a time,
+// whose 16-byte chunks must lie in different 16-byte slots of a 128-byte
+// window: a K-major fragment reads one chunk of 8 consecutive rows, which the
+// XOR with r % 8 spreads over the 8 slots of the window (with two rows per
+// slot the read runs at half rate: measured on gfx950, 128 versus 250 bytes
+// per clock per CU).  The 8 k rows x 32 bytes that 32 lanes of an M/N-major
+// transposing read touch fall in 8 different 32-byte windows.
 
 typedef __attribute__((address_space(3))) char lds_char;
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x8_t __attribute__((ext_vector_type(8)));
 constexpr int kTileBytes = kBM * kBK * 2;  // 16 KiB per operand tile
+constexpr int kPairBytes = 2 * kTileBytes;  // a K-major operand's pair slot: two k tiles
 constexpr int kDmaPerWave = kTileBytes / 1024 / kWaves;  // direct-to-LDS instructions per wave per operand tile
 static_assert(kDmaPerWave == 1 || kDmaPerWave == 2 || kDmaPerWave == 4, "layout offsets assume 1, 2 or 4");
 
@@ -209,12 +220,13 @@ __device__ __forceinline__ u32x4_t tile_desc(const Operand& op, int mn0, int k0)
 }
 
 // Loop-invariant per-lane byte offsets of one operand's direct-to-LDS loads,
-// relative to the tile origin, for this wave's kDmaPerWave instructions
-// (which rows, k rows and chunks each lane loads is fixed by the LDS layout):
-//   K-major:   offset = v[0 or 1] + i * step    (v[1]: k chunks past K masked)
-//   M/N-major: offset = v[i % 2] + i * step     (columns past M/N masked)
+// relative to the tile (K-major: pair) origin:
+//   K-major:   instruction i of this wave (0 .. 2*kDmaPerWave-1) at offset
+//              v[0] + i * step, or kOOB when the lane's k chunk (k offset v[1]
+//              within the pair) lies past K;
+//   M/N-major: instruction i at v[i % 2] + i * step    (columns past M/N masked).
 // The host keeps every leading dimension below 2^22 elements, so no offset of
-// a 256-row tile wraps 32 bits and a masked offset (kOOB + up to 3 steps)
+// a 256-row tile wraps 32 bits and a masked offset (kOOB + up to 7 steps)
 // stays out of range.
 struct DmaLanes {
   uint32_t v[2];
@@ -226,14 +238,13 @@ __device__ __forceinline__ DmaLanes dma_lanes(const Operand& op, int mn0, int nm
   DmaLanes d;
   const uint32_t ldb = (uint32_t)op.ld * 2u;
   if constexpr (KMAJOR) {
-    // instruction D*w + i (D = kDmaPerWave) writes slots (D*w + i)*64 + l:
-    // row (D*w + i)*16 + l/4, chunk (l%4) ^ (l/8 % 4)
-    const uint32_t r = (uint32_t)wave * (16u * kDmaPerWave) + (uint32_t)(lane >> 2);
-    const int c = (lane & 3) ^ ((lane >> 3) & 3);
+    // instruction 2D*w + i (D = kDmaPerWave) writes slots (2D*w + i)*64 + l:
+    // row (2D*w + i)*8 + l/8, chunk (l%8) ^ (l/8)  (the row's index mod 8 is l/8)
+    const uint32_t r = (uint32_t)wave * (16u * kDmaPerWave) + (uint32_t)(lane >> 3);
+    const int c = (lane & 7) ^ (lane >> 3);
     d.v[0] = r * ldb + (uint32_t)c * 16u;
-    const int tail = K & (kBK - 1);
-    d.v[1] = (c * 8 < tail) ? d.v[0] : kOOB;
-    d.step = 16u * ldb;
+    d.v[1] = (uint32_t)c * 8u;
+    d.step = 8u * ldb;
   } else {
     // instruction D*w + i (D = kDmaPerWave) writes slots (D*w + i)*64 + l:
     // k row 2Dw + 2i + l/32 and column group (l%32) ^ 2F with
@@ -251,25 +262,32 @@ __device__ __forceinline__ DmaLanes dma_lanes(const Operand& op, int mn0, int nm
   return d;
 }
 
-// Direct-to-LDS instruction i of this wave's share of one operand tile.
-// `ktail` (K-major only): the tile is the last one and K is not a multiple of
-// 32.  `tile` is the tile's LDS address; `wave_s` the wave index (uniform).
-template <bool KMAJOR>
-__device__ __forceinline__ void dma_one(const DmaLanes& d, u32x4_t desc, bool ktail, uint32_t tile, int wave_s,
-                                        int i) {
-  uint32_t off;
-  if constexpr (KMAJOR) off = (ktail ? d.v[1] : d.v[0]) + (uint32_t)i * d.step;
-  else off = d.v[i & 1] + (uint32_t)i * d.step;
-  dma16(desc, off, tile + (uint32_t)wave_s * (kDmaPerWave * 1024u) + (uint32_t)i * 1024u);
+// K-major: the lane's base offset for the pair whose first k is k0 (masked when
+// its chunk lies past K).  Computed once per pair.
+__device__ __forceinline__ uint32_t dma_pair_base(const DmaLanes& d, int k0, int K) {
+  return (int)d.v[1] < K - k0 ? d.v[0] : kOOB;
 }
 
+// Direct-to-LDS instruction i of this wave's share of one pair (K-major, `base`
+// from dma_pair_base) or one tile (M/N-major).  `dst` is the pair slot's or the
+// stage's LDS address; `wave_s` the wave index (uniform).
 template <bool KMAJOR>
-__device__ __forceinline__ void dma_tile(const Operand& op, const DmaLanes& d, int mn0, int k0, int K,
-                                         uint32_t tile, int wave_s) {
+__device__ __forceinline__ void dma_one(const DmaLanes& d, u32x4_t desc, uint32_t base, uint32_t dst, int wave_s,
+                                        int i) {
+  if constexpr (KMAJOR)
+    dma16(desc, base + (uint32_t)i * d.step, dst + (uint32_t)wave_s * (2 * kDmaPerWave * 1024u) + (uint32_t)i * 1024u);
+  else
+    dma16(desc, d.v[i & 1] + (uint32_t)i * d.step, dst + (uint32_t)wave_s * (kDmaPerWave * 1024u) + (uint32_t)i * 1024u);
+}
+
+// All of this wave's loads of one pair (K-major, first k at k0) or one tile.
+template <bool KMAJOR>
+__device__ __forceinline__ void dma_unit(const Operand& op, const DmaLanes& d, int mn0, int k0, int K, uint32_t dst,
+                                         int wave_s) {
   const u32x4_t desc = tile_desc<KMAJOR>(op, mn0, k0);
-  const bool ktail = k0 + kBK > K;
+  const uint32_t base = KMAJOR ? dma_pair_base(d, k0, K) : 0u;
 #pragma unroll
-  for (int i = 0; i < kDmaPerWave; ++i) dma_one<KMAJOR>(d, desc, ktail, tile, wave_s, i);
+  for (int i = 0; i < (KMAJOR ? 2 : 1) * kDmaPerWave; ++i) dma_one<KMAJOR>(d, desc, base, dst, wave_s, i);
 }
 
 // Fragments for v_mfma_f32_16x16x32_bf16.  Lane l holds 8 bf16 values of one
@@ -277,8 +295,9 @@ __device__ __forceinline__ void dma_tile(const Operand& op, const DmaLanes& d, i
 // for e = 0..7, as two 4-value halves (k 8g..8g+3 and 8g+4..8g+7, g = l/16).
 // Both operands use the same lane -> k assignment, which is all the product
 // over k requires.
-//   K-major tile: a block's fragment is 1 KiB of contiguous slots (its 16 rows
-//     x 4 chunks): one ds_read_b128 per fragment.
+//   K-major pair: a block's fragment for one k tile of the pair is its 16
+//     rows x 4 chunks (chunks 4h..4h+3 of each row for k tile h of the pair):
+//     one ds_read_b128 per fragment.
 //   M/N-major tile: each half is one ds_read_b64_tr_b16.  Within a 16-lane
 //     group, lane x = 4e + q supplies the address of k row 8g + 4h + e,
 //     columns 4q..4q+3 of the block, and the instruction hands lane i the
@@ -294,15 +313,17 @@ __device__ __forceinline__ bf16x8_t frag_value(const Frag& f) {
 // SUB: the 16-wide blocks of this operand one wave covers (kSubM for A, kSubN for B).
 template <bool KMAJOR, int SUB>
 struct FragBase {
-  int x[KMAJOR ? 1 : SUB];  // K-major: one lane base; M/N-major: one per 16-column block
+  int x[KMAJOR ? 2 : SUB];  // K-major: a lane base per k tile of the pair; M/N-major: one per 16-column block
 };
 
 template <bool KMAJOR, int SUB>
 __device__ __forceinline__ FragBase<KMAJOR, SUB> frag_lane_base(int lane) {
   FragBase<KMAJOR, SUB> fb;
   if constexpr (KMAJOR) {
-    // row l%16 of the block, chunk l/16
-    fb.x[0] = ((lane & 15) * 4 + ((lane >> 4) ^ ((lane >> 1) & 3))) * 16;
+    // row l%16 of the block (its index mod 8 is (l%16)%8), chunk 4h + l/16 of the pair
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      fb.x[h] = (lane & 15) * 128 + ((4 * h + (lane >> 4)) ^ (lane & 7)) * 16;
   } else {
     // lane x = 4e + q of group g: k row 8g + e (+ 4h), columns 4q..4q+3 of the
     // block; the layout's XOR moves block b to position b ^ F within the row
@@ -319,15 +340,16 @@ __device__ __forceinline__ FragBase<KMAJOR, SUB> frag_lane_base(int lane) {
 template <bool KMAJOR>
 constexpr int kPieces = KMAJOR ? 1 : 2;
 
-// Read piece h of the fragment of block blk (0..SUB-1) for wave coordinate w.
+// Read piece h of the fragment of block blk (0..SUB-1) for wave coordinate w;
+// `half` (K-major): which k tile of the pair in `tile` (a pair slot).
 // M/N-major: the wave's first block is block w*SUB of the 16 in a k row, and
 // the layout's XOR acts on the block index (bits 5-8 of the byte offset), so
 // the wave offset is XORed in too.
 template <bool KMAJOR, int SUB>
-__device__ __forceinline__ void read_piece(Frag& f, const lds_char* tile, const FragBase<KMAJOR, SUB>& fb, int w,
-                                           int blk, int h) {
+__device__ __forceinline__ void read_piece(Frag& f, const lds_char* tile, int half, const FragBase<KMAJOR, SUB>& fb,
+                                           int w, int blk, int h) {
   if constexpr (KMAJOR) {
-    const s16x8_t v = *(const s16x8_t*)(tile + fb.x[0] + (w * SUB + blk) * 1024);
+    const s16x8_t v = *(const s16x8_t*)(tile + fb.x[half] + (w * SUB + blk) * 2048);
     f.lo = __builtin_shufflevector(v, v, 0, 1, 2, 3);
     f.hi = __builtin_shufflevector(v, v, 4, 5, 6, 7);
   } else {
@@ -360,18 +382,26 @@ struct ReadOrder {
   }
 };
 
+// Where one k tile of each operand sits in LDS: the pair slot and half
+// (K-major) or the stage (M/N-major, half 0).
+struct TileSrc {
+  const lds_char* a;
+  const lds_char* b;
+  int ha, hb;
+};
+
 template <bool AK, bool BK, int p>
-__device__ __forceinline__ void read_piece_p(Frags& f, const lds_char* stage, const FragBase<AK, kSubM>& fa,
+__device__ __forceinline__ void read_piece_p(Frags& f, const TileSrc& t, const FragBase<AK, kSubM>& fa,
                                              const FragBase<BK, kSubN>& fb, int wm, int wn) {
   using R = ReadOrder<AK, BK>;
   if constexpr (p < R::PA) {
-    read_piece<AK, kSubM>(f.a[0], stage, fa, wm, 0, p);
+    read_piece<AK, kSubM>(f.a[0], t.a, t.ha, fa, wm, 0, p);
   } else if constexpr (p < R::PA + kSubN * R::PB) {
     constexpr int q = p - R::PA;
-    read_piece<BK, kSubN>(f.b[q / R::PB], stage + kTileBytes, fb, wn, q / R::PB, q % R::PB);
+    read_piece<BK, kSubN>(f.b[q / R::PB], t.b, t.hb, fb, wn, q / R::PB, q % R::PB);
   } else {
     constexpr int q = p - R::PA - kSubN * R::PB;
-    read_piece<AK, kSubM>(f.a[1 + q / R::PA], stage, fa, wm, 1 + q / R::PA, q % R::PA);
+    read_piece<AK, kSubM>(f.a[1 + q / R::PA], t.a, t.ha, fa, wm, 1 + q / R::PA, q % R::PA);
   }
 }
 
@@ -386,9 +416,9 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 template <bool AK, bool BK>
-__device__ __forceinline__ void read_all(Frags& f, const lds_char* stage, const FragBase<AK, kSubM>& fa,
+__device__ __forceinline__ void read_all(Frags& f, const TileSrc& t, const FragBase<AK, kSubM>& fa,
                                          const FragBase<BK, kSubN>& fb, int wm, int wn) {
-  static_for<ReadOrder<AK, BK>::P>([&](auto pc) { read_piece_p<AK, BK, decltype(pc)::value>(f, stage, fa, fb, wm, wn); });
+  static_for<ReadOrder<AK, BK>::P>([&](auto pc) { read_piece_p<AK, BK, decltype(pc)::value>(f, t, fa, fb, wm, wn); });
 }
 
 // The MFMA is written as inline assembly with accumulation-register operands so
@@ -465,9 +495,188 @@ __device__ __forceinline__ void args_to_sgprs(const T& t) {
   for (int i = 0; i < (int)(sizeof(T) / 4); ++i) asm volatile("" ::"s"(w[i]));
 }
 
+// The LDS homes of the two operands (see the layout notes above): K-major
+// operands have two 32 KiB pair slots p[0..1], M/N-major ones four 16 KiB
+// stages p[0..3].
+template <bool AK, bool BK>
+struct LdsRing {
+  lds_char* a[4];
+  lds_char* b[4];
+};
+
+template <bool AK, bool BK>
+__device__ __forceinline__ LdsRing<AK, BK> lds_ring(char* lds0, char* lds1, char* lds2, char* lds3) {
+  lds_char* l[4] = {(lds_char*)lds0, (lds_char*)lds1, (lds_char*)lds2, (lds_char*)lds3};
+  LdsRing<AK, BK> r;
+  if constexpr (!AK && !BK) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      r.a[i] = l[i];
+      r.b[i] = l[i] + kTileBytes;
+    }
+  } else {
+    // pair slots of the K-major operand(s) first, then the stages of an M/N-major one
+    lds_char** kop = AK ? r.a : r.b;  // A if it is K-major, else B
+    kop[0] = l[0];
+    kop[1] = l[1];
+    kop[2] = kop[3] = nullptr;
+    lds_char** other = AK ? r.b : r.a;
+    if constexpr (AK && BK) {
+      other[0] = l[2];
+      other[1] = l[3];
+      other[2] = other[3] = nullptr;
+    } else {
+      other[0] = l[2];
+      other[1] = l[2] + kTileBytes;
+      other[2] = l[3];
+      other[3] = l[3] + kTileBytes;
+    }
+  }
+  return r;
+}
+
+// Direct-to-LDS instructions per wave one operand issues at a k step of the
+// given parity (of the step's index counted from the tile's first k step):
+// a K-major operand loads a pair on odd steps, an M/N-major one a tile on every step.
+template <bool KMAJOR>
+constexpr int dma_count(bool odd) { return KMAJOR ? (odd ? 2 * kDmaPerWave : 0) : kDmaPerWave; }
+
+// The q-th of cnt direct-to-LDS instructions of a step is issued after MFMA
+// number ((q + 1) * 64) / cnt - 1; returns the q issued after MFMA j, or -1.
+constexpr int dma_at(int j, int cnt, int nmfma) {
+  for (int q = 0; q < cnt; ++q)
+    if (((q + 1) * nmfma) / cnt - 1 == j) return q;
+  return -1;
+}
+
+// The k loop of one tile (or K split), shared by the per-tile and the
+// persistent kernels: local k step i = 0 .. n-1 (global kt_beg + i).
+//
+// Ring: local k tile t sits in pair slot (t/2)%2, half t%2 (K-major operand)
+// or stage t%4 (M/N-major).  Step i runs the 64 MFMAs of tile i on fragments
+// fc, reads the fragments of tile i+1 into fn, and issues the loads of tile
+// i+3 (M/N-major) and, on odd i, of the pair of tiles i+3 and i+4 (K-major).
+// Each slot or stage it loads into was last read in step i-2 or earlier (as
+// fragments of tiles i-1 or i).  It then waits until only its own loads are
+// outstanding, so tile i+2 has landed, and the barrier publishes it; the
+// barrier also orders every read of a slot or stage before the step that
+// loads into it again.  At entry: tiles 0 and 1 are published and tile 2
+// (with the rest of its pair) may be landing.
+template <bool AK, bool BK>
+__device__ __forceinline__ void tile_k_loop(AccTile& acc, const GemmGeom& g, const Operand& a, const Operand& b,
+                                            int m0, int n0, int kt_beg, int n, const DmaLanes& dla,
+                                            const DmaLanes& dlb, const LdsRing<AK, BK>& R, int wave_s, int wm, int wn,
+                                            int lane) {
+  const FragBase<AK, kSubM> fra = frag_lane_base<AK, kSubM>(lane);
+  const FragBase<BK, kSubN> frb = frag_lane_base<BK, kSubN>(lane);
+  using RO = ReadOrder<AK, BK>;
+  constexpr int kMfma = kSubM * kSubN;
+  auto lds_addr = [](const lds_char* q) { return (uint32_t)(uintptr_t)q; };
+  // LDS home of local tile t, for t with t % 4 == T4 (compile time)
+  auto src = [&](auto t4) {
+    constexpr int T4 = decltype(t4)::value;
+    TileSrc ts;
+    ts.a = AK ? R.a[(T4 >> 1) & 1] : R.a[T4 & 3];
+    ts.b = BK ? R.b[(T4 >> 1) & 1] : R.b[T4 & 3];
+    ts.ha = AK ? (T4 & 1) : 0;
+    ts.hb = BK ? (T4 & 1) : 0;
+    return ts;
+  };
+  // step i with i % 4 == POS (compile time)
+  auto step = [&](auto first, auto checked, auto posc, int i, Frags& fc, Frags& fn) {
+    constexpr bool kFirst = decltype(first)::value;
+    constexpr bool kChecked = decltype(checked)::value;
+    constexpr int POS = decltype(posc)::value;
+    constexpr bool kOdd = (POS & 1) != 0;
+    constexpr int cA = dma_count<AK>(kOdd), cB = dma_count<BK>(kOdd), cnt = cA + cB;
+    const bool issue = !kChecked || i + 3 < n;
+    const bool next = !kChecked || i + 1 < n;
+    const TileSrc nx = src(std::integral_constant<int, (POS + 1) & 3>{});
+    const int k3 = (kt_beg + i + 3) * kBK;
+    u32x4_t da = {0u, 0u, 0u, 0u}, db = {0u, 0u, 0u, 0u};
+    uint32_t baseA = 0u, baseB = 0u, dstA = 0u, dstB = 0u;
+    if constexpr (cA > 0) {
+      da = tile_desc<AK>(a, m0, k3);
+      if constexpr (AK) baseA = dma_pair_base(dla, k3, g.K);
+      dstA = lds_addr(AK ? R.a[((POS + 3) >> 1) & 1] : R.a[(POS + 3) & 3]);
+    }
+    if constexpr (cB > 0) {
+      db = tile_desc<BK>(b, n0, k3);
+      if constexpr (BK) baseB = dma_pair_base(dlb, k3, g.K);
+      dstB = lds_addr(BK ? R.b[((POS + 3) >> 1) & 1] : R.b[(POS + 3) & 3]);
+    }
+    static_for<kMfma>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      constexpr int mi = j / kSubN, ni = j % kSubN;
+      mfma_16x16x32<kFirst>(acc[mi][ni], frag_value(fc.b[ni]), frag_value(fc.a[mi]));
+      constexpr int p = RO::piece_at(j);
+      if constexpr (p >= 0) {
+        if (next) read_piece_p<AK, BK, p>(fn, nx, fra, frb, wm, wn);
+      }
+      constexpr int q = dma_at(j, cnt, kMfma);
+      if constexpr (q >= 0) {
+        if (issue) {
+          if constexpr (q < cA) dma_one<AK>(dla, da, baseA, dstA, wave_s, q);
+          else dma_one<BK>(dlb, db, baseB, dstB, wave_s, q - cA);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if (issue) wait_vmcnt<cnt>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+  };
+  using True = std::integral_constant<bool, true>;
+  using False = std::integral_constant<bool, false>;
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  using P2 = std::integral_constant<int, 2>;
+  using P3 = std::integral_constant<int, 3>;
+
+  Frags f0, f1;
+  read_all<AK, BK>(f0, src(P0{}), fra, frb, wm, wn);
+  step(True{}, True{}, P0{}, 0, f0, f1);
+  int i = 1;
+  // steady state: every step of the group reads its next tile and issues its loads
+  for (; i + 6 < n; i += 4) {
+    step(False{}, False{}, P1{}, i, f1, f0);
+    step(False{}, False{}, P2{}, i + 1, f0, f1);
+    step(False{}, False{}, P3{}, i + 2, f1, f0);
+    step(False{}, False{}, P0{}, i + 3, f0, f1);
+  }
+  for (; i < n; i += 4) {
+    step(False{}, True{}, P1{}, i, f1, f0);
+    if (i + 1 < n) step(False{}, True{}, P2{}, i + 1, f0, f1);
+    if (i + 2 < n) step(False{}, True{}, P3{}, i + 2, f1, f0);
+    if (i + 3 < n) step(False{}, True{}, P0{}, i + 3, f0, f1);
+  }
+}
+
+// The loads of local k tiles 0, 1 and 2 (K-major: pairs 0 and 1), in an order
+// that lets the caller wait for tiles 0 and 1 alone: tile 2's loads
+// (dma_count<AK>(true) + dma_count<BK>(true) per wave when n > 2) are last.
+template <bool AK, bool BK>
+__device__ __forceinline__ void tile_first_loads(const GemmGeom& g, const Operand& a, const Operand& b, int m0, int n0,
+                                                 int kt_beg, int n, const DmaLanes& dla, const DmaLanes& dlb,
+                                                 const LdsRing<AK, BK>& R, int wave_s) {
+  auto lds_addr = [](const lds_char* q) { return (uint32_t)(uintptr_t)q; };
+  const int k0 = kt_beg * kBK;
+  dma_unit<AK>(a, dla, m0, k0, g.K, lds_addr(R.a[0]), wave_s);
+  dma_unit<BK>(b, dlb, n0, k0, g.K, lds_addr(R.b[0]), wave_s);
+  if (n > 1) {
+    if constexpr (!AK) dma_unit<false>(a, dla, m0, k0 + kBK, g.K, lds_addr(R.a[1]), wave_s);
+    if constexpr (!BK) dma_unit<false>(b, dlb, n0, k0 + kBK, g.K, lds_addr(R.b[1]), wave_s);
+  }
+  if (n > 2) {
+    // K-major: the pair of tiles 2 and 3 into slot 1; M/N-major: tile 2 into stage 2
+    dma_unit<AK>(a, dla, m0, k0 + 2 * kBK, g.K, lds_addr(R.a[AK ? 1 : 2]), wave_s);
+    dma_unit<BK>(b, dlb, n0, k0 + 2 * kBK, g.K, lds_addr(R.b[BK ? 1 : 2]), wave_s);
+  }
+}
+
 // One 256 x 256 output tile (or one K split of it): block `vb` of the `vg`
-// blocks this GEMM has in the launch.  lds0..lds3 are the kernel's four LDS
-// stages (A tile then B tile in each).
+// blocks this GEMM has in the launch.  lds0..lds3 are the kernel's four
+// 32 KiB LDS arrays (the operands' pair slots and stages).
 template <bool A_KMAJOR, bool B_KMAJOR, class Epi>
 __device__ __forceinline__ void gemm_tile(const GemmGeom& g, const Operand& a, const Operand& b, const Epi& epi,
                                           int vb, int vg, char* lds0, char* lds1, char* lds2, char* lds3) {
@@ -475,115 +684,43 @@ __device__ __forceinline__ void gemm_tile(const GemmGeom& g, const Operand& a, c
   args_to_sgprs(a);
   args_to_sgprs(b);
   args_to_sgprs(epi);
-  lds_char* st[kStages] = {(lds_char*)lds0, (lds_char*)lds1, (lds_char*)lds2, (lds_char*)lds3};
+  const LdsRing<A_KMAJOR, B_KMAJOR> R = lds_ring<A_KMAJOR, B_KMAJOR>(lds0, lds1, lds2, lds3);
   int tm, tn, split;
   map_tile(g, vb, vg, tm, tn, split);
   const int m0 = tm * kBM, n0 = tn * kBN;
   const int nk = (g.K + kBK - 1) / kBK;
   const int kt_beg = (int)(((int64_t)split * nk) / g.splits);
   const int kt_end = (int)(((int64_t)(split + 1) * nk) / g.splits);
+  const int n = kt_end - kt_beg;  // >= 1 (the host guarantees kt_beg < kt_end)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // uniform copy for scalar address math
   const int wm = wave / kWavesN, wn = wave % kWavesN;
-  const FragBase<A_KMAJOR, kSubM> fra = frag_lane_base<A_KMAJOR, kSubM>(lane);
-  const FragBase<B_KMAJOR, kSubN> frb = frag_lane_base<B_KMAJOR, kSubN>(lane);
   const DmaLanes dla = dma_lanes<A_KMAJOR>(a, m0, g.M, g.K, wave_s, lane);
   const DmaLanes dlb = dma_lanes<B_KMAJOR>(b, n0, g.N, g.K, wave_s, lane);
-  auto lds_addr = [](const lds_char* p) { return (uint32_t)(uintptr_t)p; };
 
   AccTile acc;
-
-  auto dma = [&](int kt, lds_char* stage) {
-    dma_tile<A_KMAJOR>(a, dla, m0, kt * kBK, g.K, lds_addr(stage), wave_s);
-    dma_tile<B_KMAJOR>(b, dlb, n0, kt * kBK, g.K, lds_addr(stage + kTileBytes), wave_s);
-  };
-  constexpr int kPerTile = 2 * kDmaPerWave;  // direct-to-LDS instructions per wave per tile
-  static_assert(kSubM * kSubN == 8 * kPerTile, "one direct-to-LDS load per 8 MFMAs");
-  using RO = ReadOrder<A_KMAJOR, B_KMAJOR>;
-
-  // The 64 MFMAs of k tile kt on fragments fc.  Invariant at entry: tiles kt
-  // and kt+1 are published (complete in LDS for every wave) and fc holds tile
-  // kt's fragments.  Interleaved with the MFMAs, in a fixed order: the
-  // fragments of tile kt+1 are read from stage `nxt` into fn (when NEXT,
-  // i.e. kt+1 < kt_end), one LDS read every 1.5-3 MFMAs over the first 48, in
-  // the order the next tile's MFMAs need them; and the loads of tile kt+3 go
-  // into the stage consumed at kt-1 (when ISSUE, i.e. kt+3 < kt_end), one after
-  // every 8 MFMAs.  NEXT/ISSUE are compile-time in the steady-state loop.
-  // Then this wave waits for its share of tile kt+2 (tile kt+3 may stay in
-  // flight) and the barrier publishes it; that barrier also orders every read
-  // of stage kt+1 before its reuse at kt+2.  The host guarantees kt_beg < kt_end.
-  auto step = [&](auto first, auto checked, const lds_char* nxt, lds_char* far, int kt, Frags& fc, Frags& fn) {
-    constexpr bool kFirst = decltype(first)::value;
-    constexpr bool kChecked = decltype(checked)::value;
-    const bool issue = !kChecked || kt + 3 < kt_end;
-    const bool next = !kChecked || kt + 1 < kt_end;
-    const int k3 = (kt + 3) * kBK;
-    const u32x4_t da = tile_desc<A_KMAJOR>(a, m0, k3);
-    const u32x4_t db = tile_desc<B_KMAJOR>(b, n0, k3);
-    const bool ktail = k3 + kBK > g.K;
-    const uint32_t fa = lds_addr(far), fb = lds_addr(far + kTileBytes);
-    static_for<kSubM * kSubN>([&](auto jc) {
-      constexpr int j = decltype(jc)::value;
-      constexpr int mi = j / kSubN, ni = j % kSubN;
-      mfma_16x16x32<kFirst>(acc[mi][ni], frag_value(fc.b[ni]), frag_value(fc.a[mi]));
-      constexpr int p = RO::piece_at(j);
-      if constexpr (p >= 0) {
-        if (next) read_piece_p<A_KMAJOR, B_KMAJOR, p>(fn, nxt, fra, frb, wm, wn);
-      }
-      if constexpr (j % 8 == 7) {
-        constexpr int q = j / 8;
-        if (issue) {
-          if constexpr (q < kDmaPerWave) dma_one<A_KMAJOR>(dla, da, ktail, fa, wave_s, q);
-          else dma_one<B_KMAJOR>(dlb, db, ktail, fb, wave_s, q - kDmaPerWave);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    });
-    if (issue) wait_vmcnt<kPerTile>();
-    else wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-  };
-  using True = std::integral_constant<bool, true>;
-  using False = std::integral_constant<bool, false>;
-
-  dma(kt_beg, st[0]);
-  if (kt_beg + 1 < kt_end) dma(kt_beg + 1, st[1]);
-  if (kt_beg + 2 < kt_end) dma(kt_beg + 2, st[2]);
-  if (kt_beg + 2 < kt_end) wait_vmcnt<kPerTile>();  // tiles kt_beg, kt_beg+1 done
+  tile_first_loads<A_KMAJOR, B_KMAJOR>(g, a, b, m0, n0, kt_beg, n, dla, dlb, R, wave_s);
+  constexpr int kLate = dma_count<A_KMAJOR>(true) + dma_count<B_KMAJOR>(true);
+  if (n > 2) wait_vmcnt<kLate>();  // tiles 0 and 1 landed; tile 2 may still be in flight
   else wait_vmcnt<0>();
   __builtin_amdgcn_s_barrier();
-  Frags f0, f1;
-  read_all<A_KMAJOR, B_KMAJOR>(f0, st[0], fra, frb, wm, wn);
-  step(True{}, True{}, st[1], st[3], kt_beg, f0, f1);
-  int kt = kt_beg + 1;
-  // steady state: every step of the group reads its next tile and issues the loads of tile kt+3
-  for (; kt + 6 < kt_end; kt += 4) {
-    step(False{}, False{}, st[2], st[0], kt, f1, f0);
-    step(False{}, False{}, st[3], st[1], kt + 1, f0, f1);
-    step(False{}, False{}, st[0], st[2], kt + 2, f1, f0);
-    step(False{}, False{}, st[1], st[3], kt + 3, f0, f1);
-  }
-  for (; kt < kt_end; kt += 4) {
-    step(False{}, True{}, st[2], st[0], kt, f1, f0);
-    if (kt + 1 < kt_end) step(False{}, True{}, st[3], st[1], kt + 1, f0, f1);
-    if (kt + 2 < kt_end) step(False{}, True{}, st[0], st[2], kt + 2, f1, f0);
-    if (kt + 3 < kt_end) step(False{}, True{}, st[1], st[3], kt + 3, f0, f1);
-  }
+  tile_k_loop<A_KMAJOR, B_KMAJOR>(acc, g, a, b, m0, n0, kt_beg, n, dla, dlb, R, wave_s, wm, wn, lane);
   EpiCtx ctx{m0, n0, tm, tn, split, wm, wn, lane, lds0, lds1, lds2, lds3, lds0};
   epi(acc, ctx);
 }
 
-// Persistent form for epilogues that leave the four LDS stages alone
+// Persistent form for epilogues that leave the four LDS arrays alone
 // (Epi::kKeepsStages): workgroup p of P walks the blocks p, p + P, p + 2P, ...
 // (P a multiple of 8, so every tile stays on the XCD map_tile gives it).
 // After the last k step of a tile, whose closing barrier ends every read of
-// the stages, the first three k tiles of the next tile are loaded into stages
-// 0-2, and only then does the epilogue run: the loads land while it computes.
-// The next main loop starts by waiting for every outstanding load (count-based,
-// in program order: the epilogue's own loads and stores issued after them only
-// make it wait longer) and a barrier.  The k steps are those of gemm_tile, in
-// the same order of reads, loads, waits and barriers, so the accumulators, and
-// the results, are the same bits.
+// the slots and stages, the first k tiles of the next tile (0, 1 and 2, with 3
+// for a K-major operand's second pair) are loaded, and only then does the
+// epilogue run: the loads land while it computes.  The next k loop starts by
+// waiting for every outstanding load (count-based, in program order: the
+// epilogue's own loads and stores issued after them only make it wait longer)
+// and a barrier.  The k steps are those of gemm_tile, in the same order of
+// reads, loads, waits and barriers, so the accumulators, and the results, are
+// the same bits.
 template <bool A_KMAJOR, bool B_KMAJOR, class Epi>
 __device__ __forceinline__ void gemm_tiles_persistent(const GemmGeom& g, const Operand& a, const Operand& b,
                                                       const Epi& epi, int p, int P, int vg, char* lds0, char* lds1,
@@ -593,19 +730,14 @@ __device__ __forceinline__ void gemm_tiles_persistent(const GemmGeom& g, const O
   args_to_sgprs(a);
   args_to_sgprs(b);
   args_to_sgprs(epi);
-  lds_char* st[kStages] = {(lds_char*)lds0, (lds_char*)lds1, (lds_char*)lds2, (lds_char*)lds3};
+  const LdsRing<A_KMAJOR, B_KMAJOR> R = lds_ring<A_KMAJOR, B_KMAJOR>(lds0, lds1, lds2, lds3);
   const int nk = (g.K + kBK - 1) / kBK;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const int wm = wave / kWavesN, wn = wave % kWavesN;
-  auto lds_addr = [](const lds_char* q) { return (uint32_t)(uintptr_t)q; };
-  constexpr int kPerTile = 2 * kDmaPerWave;
-  using RO = ReadOrder<A_KMAJOR, B_KMAJOR>;
-  using True = std::integral_constant<bool, true>;
-  using False = std::integral_constant<bool, false>;
 
   struct TileState {
-    int tm, tn, split, m0, n0, kt_beg, kt_end;
+    int tm, tn, split, m0, n0, kt_beg, n;
     DmaLanes dla, dlb;
   };
   auto setup = [&](int vb) {
@@ -614,90 +746,33 @@ __device__ __forceinline__ void gemm_tiles_persistent(const GemmGeom& g, const O
     t.m0 = t.tm * kBM;
     t.n0 = t.tn * kBN;
     t.kt_beg = (int)(((int64_t)t.split * nk) / g.splits);
-    t.kt_end = (int)(((int64_t)(t.split + 1) * nk) / g.splits);
+    t.n = (int)(((int64_t)(t.split + 1) * nk) / g.splits) - t.kt_beg;
     t.dla = dma_lanes<A_KMAJOR>(a, t.m0, g.M, g.K, wave_s, lane);
     t.dlb = dma_lanes<B_KMAJOR>(b, t.n0, g.N, g.K, wave_s, lane);
     return t;
   };
-  auto prologue = [&](const TileState& t) {
-    for (int i = 0; i < 3 && t.kt_beg + i < t.kt_end; ++i) {
-      dma_tile<A_KMAJOR>(a, t.dla, t.m0, (t.kt_beg + i) * kBK, g.K, lds_addr(st[i]), wave_s);
-      dma_tile<B_KMAJOR>(b, t.dlb, t.n0, (t.kt_beg + i) * kBK, g.K, lds_addr(st[i] + kTileBytes), wave_s);
-    }
+  auto first_loads = [&](const TileState& t) {
+    tile_first_loads<A_KMAJOR, B_KMAJOR>(g, a, b, t.m0, t.n0, t.kt_beg, t.n, t.dla, t.dlb, R, wave_s);
   };
 
   AccTile acc;
-  auto main_loop = [&](const TileState& t) {
-    const int m0 = t.m0, n0 = t.n0, kt_beg = t.kt_beg, kt_end = t.kt_end;
-    const DmaLanes dla = t.dla, dlb = t.dlb;
-    // per tile: nothing per-lane outlives the loop
-    const FragBase<A_KMAJOR, kSubM> fra = frag_lane_base<A_KMAJOR, kSubM>(lane);
-    const FragBase<B_KMAJOR, kSubN> frb = frag_lane_base<B_KMAJOR, kSubN>(lane);
-    auto step = [&](auto first, auto checked, const lds_char* nxt, lds_char* far, int kt, Frags& fc, Frags& fn) {
-      constexpr bool kFirst = decltype(first)::value;
-      constexpr bool kChecked = decltype(checked)::value;
-      const bool issue = !kChecked || kt + 3 < kt_end;
-      const bool next = !kChecked || kt + 1 < kt_end;
-      const int k3 = (kt + 3) * kBK;
-      const u32x4_t da = tile_desc<A_KMAJOR>(a, m0, k3);
-      const u32x4_t db = tile_desc<B_KMAJOR>(b, n0, k3);
-      const bool ktail = k3 + kBK > g.K;
-      const uint32_t fa = lds_addr(far), fb = lds_addr(far + kTileBytes);
-      static_for<kSubM * kSubN>([&](auto jc) {
-        constexpr int j = decltype(jc)::value;
-        constexpr int mi = j / kSubN, ni = j % kSubN;
-        mfma_16x16x32<kFirst>(acc[mi][ni], frag_value(fc.b[ni]), frag_value(fc.a[mi]));
-        constexpr int pc = RO::piece_at(j);
-        if constexpr (pc >= 0) {
-          if (next) read_piece_p<A_KMAJOR, B_KMAJOR, pc>(fn, nxt, fra, frb, wm, wn);
-        }
-        if constexpr (j % 8 == 7) {
-          constexpr int q = j / 8;
-          if (issue) {
-            if constexpr (q < kDmaPerWave) dma_one<A_KMAJOR>(dla, da, ktail, fa, wave_s, q);
-            else dma_one<B_KMAJOR>(dlb, db, ktail, fb, wave_s, q - kDmaPerWave);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      });
-      if (issue) wait_vmcnt<kPerTile>();
-      else wait_vmcnt<0>();
-      __builtin_amdgcn_s_barrier();
-    };
-    wait_vmcnt<0>();  // the prologue's loads (and anything issued after them)
-    __builtin_amdgcn_s_barrier();
-    Frags f0, f1;
-    read_all<A_KMAJOR, B_KMAJOR>(f0, st[0], fra, frb, wm, wn);
-    step(True{}, True{}, st[1], st[3], kt_beg, f0, f1);
-    int kt = kt_beg + 1;
-    for (; kt + 6 < kt_end; kt += 4) {
-      step(False{}, False{}, st[2], st[0], kt, f1, f0);
-      step(False{}, False{}, st[3], st[1], kt + 1, f0, f1);
-      step(False{}, False{}, st[0], st[2], kt + 2, f1, f0);
-      step(False{}, False{}, st[1], st[3], kt + 3, f0, f1);
-    }
-    for (; kt < kt_end; kt += 4) {
-      step(False{}, True{}, st[2], st[0], kt, f1, f0);
-      if (kt + 1 < kt_end) step(False{}, True{}, st[3], st[1], kt + 1, f0, f1);
-      if (kt + 2 < kt_end) step(False{}, True{}, st[0], st[2], kt + 2, f1, f0);
-      if (kt + 3 < kt_end) step(False{}, True{}, st[1], st[3], kt + 3, f0, f1);
-    }
-  };
-
   // Tile state is rebuilt from the block index where it is needed (a few
   // instructions) rather than kept live across the epilogue, which needs
   // every register it can get.
   int vb = p;
   if (vb >= vg) return;
-  prologue(setup(vb));
+  first_loads(setup(vb));
   while (true) {
     {
       const TileState cur = setup(vb);
-      main_loop(cur);
+      wait_vmcnt<0>();  // the first loads (and anything issued after them)
+      __builtin_amdgcn_s_barrier();
+      tile_k_loop<A_KMAJOR, B_KMAJOR>(acc, g, a, b, cur.m0, cur.n0, cur.kt_beg, cur.n, cur.dla, cur.dlb, R, wave_s,
+                                      wm, wn, lane);
     }
     const int nvb = vb + P;
     const bool more = nvb < vg;
-    if (more) prologue(setup(nvb));
+    if (more) first_loads(setup(nvb));
     int tm, tn, split;
     map_tile(g, vb, vg, tm, tn, split);
     const EpiCtx ctx{tm * kBM, tn * kBN, tm, tn, split, wm, wn, lane, lds0, lds1, lds2, lds3, xch};
