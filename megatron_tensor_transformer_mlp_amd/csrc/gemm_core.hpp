@@ -15,13 +15,13 @@
 //   * One workgroup = 256 threads = 4 wave64s computes a 256 x 256 tile of C.
 //     The waves form a 2 x 2 grid, each owning a 128 x 128 sub-tile held as
 //     8 x 8 fp32 16x16 MFMA accumulators (256 accumulation registers per lane).
-//   * K advances in steps of 32.  Each operand has a ring in LDS: an
-//     M/N-major operand four 16 KiB stages, one k tile each; a K-major operand
-//     32 KiB pair slots, two k tiles each, so that its loads read whole
-//     128-byte rows (three slots beside an M/N-major operand, 160 KiB in all;
-//     two each when both are K-major).  Step kt consumes tile kt while kt+1
-//     and kt+2 are resident or landing; the loads of later tiles (kt+3, or
-//     half a pair) run interleaved with its MFMAs.  One barrier per step.
+//   * K advances in steps of 32.  Each operand has a ring in LDS (128 KiB in
+//     all): an M/N-major operand four 16 KiB stages, one k tile each; a
+//     K-major operand two 32 KiB pair slots, two k tiles each, so that its
+//     loads read whole 128-byte rows.  Step kt consumes tile kt while kt+1 and
+//     kt+2 are resident or landing and the loads of kt+3 (M/N-major), or on
+//     every other step of the pair kt+3, kt+4 (K-major), run interleaved with
+//     its MFMAs.  One barrier per step.
 //   * Global -> LDS moves use direct-to-LDS buffer loads (no staging
 //     registers); the layouts (see below) make every fragment read
 //     conflict-free: K-major tiles are read with ds_read_b128, M/N-major tiles
@@ -156,10 +156,10 @@ __device__ __forceinline__ void map_tile(const GemmGeom& g, int b, int G, int& t
 // the CE GEMM about 5% faster).  Pairs live in two 32 KiB pair slots.  An
 // operand stored M/N-major is loaded one k tile ([32 k rows][256 m/n]) per
 // step into four 16 KiB stages; its 512-byte k rows are whole lines already.
-// The kernel's 32 KiB LDS arrays hold the pair slots of the K-major operands
-// and the stages of the M/N-major ones, two 16 KiB stages per array; with
-// both operands M/N-major, array s holds stage s of A then stage s of B (see
-// lds_ring).
+// The four 32 KiB LDS arrays hold, in order, the pair slots of each K-major
+// operand (A first) and then the stages of each M/N-major one, two 16 KiB
+// stages per array; with both operands M/N-major, array s holds stage s of A
+// then stage s of B.
 //
 // Layouts (16-byte slots):
 //   K-major pair : slot(r, c) = r*8 + (c ^ (r % 8))     c = k/8 (0..7 over the pair's 64 k)
@@ -495,16 +495,9 @@ __device__ __forceinline__ void args_to_sgprs(const T& t) {
   for (int i = 0; i < (int)(sizeof(T) / 4); ++i) asm volatile("" ::"s"(w[i]));
 }
 
-// The LDS homes of the two operands (see the layout notes above).  An
-// M/N-major operand has four 16 KiB stages.  A K-major operand has three
-// 32 KiB pair slots when the other operand is M/N-major (160 KiB of LDS in
-// all, the kernel's fifth array lds4 included), two when both are K-major
-// (128 KiB).
-template <bool AK, bool BK>
-constexpr int kPairSlots = (AK && BK) ? 2 : 3;
-template <bool AK, bool BK>
-constexpr bool kUsesLds4 = AK != BK;
-
+// The LDS homes of the two operands (see the layout notes above): K-major
+// operands have two 32 KiB pair slots p[0..1], M/N-major ones four 16 KiB
+// stages p[0..3].
 template <bool AK, bool BK>
 struct LdsRing {
   lds_char* a[4];
@@ -512,8 +505,8 @@ struct LdsRing {
 };
 
 template <bool AK, bool BK>
-__device__ __forceinline__ LdsRing<AK, BK> lds_ring(char* lds0, char* lds1, char* lds2, char* lds3, char* lds4) {
-  lds_char* l[5] = {(lds_char*)lds0, (lds_char*)lds1, (lds_char*)lds2, (lds_char*)lds3, (lds_char*)lds4};
+__device__ __forceinline__ LdsRing<AK, BK> lds_ring(char* lds0, char* lds1, char* lds2, char* lds3) {
+  lds_char* l[4] = {(lds_char*)lds0, (lds_char*)lds1, (lds_char*)lds2, (lds_char*)lds3};
   LdsRing<AK, BK> r;
   if constexpr (!AK && !BK) {
 #pragma unroll
@@ -521,35 +514,32 @@ __device__ __forceinline__ LdsRing<AK, BK> lds_ring(char* lds0, char* lds1, char
       r.a[i] = l[i];
       r.b[i] = l[i] + kTileBytes;
     }
-  } else if constexpr (AK && BK) {
-    r.a[0] = l[0];
-    r.a[1] = l[1];
-    r.b[0] = l[2];
-    r.b[1] = l[3];
-    r.a[2] = r.a[3] = r.b[2] = r.b[3] = nullptr;
   } else {
-    lds_char** kop = AK ? r.a : r.b;  // the K-major operand: three pair slots
+    // pair slots of the K-major operand(s) first, then the stages of an M/N-major one
+    lds_char** kop = AK ? r.a : r.b;  // A if it is K-major, else B
     kop[0] = l[0];
     kop[1] = l[1];
-    kop[2] = l[4];
-    kop[3] = nullptr;
-    lds_char** other = AK ? r.b : r.a;  // the M/N-major one: four stages
-    other[0] = l[2];
-    other[1] = l[2] + kTileBytes;
-    other[2] = l[3];
-    other[3] = l[3] + kTileBytes;
+    kop[2] = kop[3] = nullptr;
+    lds_char** other = AK ? r.b : r.a;
+    if constexpr (AK && BK) {
+      other[0] = l[2];
+      other[1] = l[3];
+      other[2] = other[3] = nullptr;
+    } else {
+      other[0] = l[2];
+      other[1] = l[2] + kTileBytes;
+      other[2] = l[3];
+      other[3] = l[3] + kTileBytes;
+    }
   }
   return r;
 }
 
-// Direct-to-LDS instructions per wave an operand issues at a k step of the
-// given parity (of the step's index counted from the tile's first k step).
-// M/N-major: one tile per step.  K-major with two pair slots: a whole pair on
-// odd steps.  K-major with three slots: half a pair on every step.
-template <bool KMAJOR, int SLOTS>
-constexpr int dma_count(bool odd) {
-  return !KMAJOR ? kDmaPerWave : SLOTS == 2 ? (odd ? 2 * kDmaPerWave : 0) : kDmaPerWave;
-}
+// Direct-to-LDS instructions per wave one operand issues at a k step of the
+// given parity (of the step's index counted from the tile's first k step):
+// a K-major operand loads a pair on odd steps, an M/N-major one a tile on every step.
+template <bool KMAJOR>
+constexpr int dma_count(bool odd) { return KMAJOR ? (odd ? 2 * kDmaPerWave : 0) : kDmaPerWave; }
 
 // The q-th of cnt direct-to-LDS instructions of a step is issued after MFMA
 // number ((q + 1) * 64) / cnt - 1; returns the q issued after MFMA j, or -1.
@@ -562,82 +552,35 @@ constexpr int dma_at(int j, int cnt, int nmfma) {
 // The k loop of one tile (or K split), shared by the per-tile and the
 // persistent kernels: local k step i = 0 .. n-1 (global kt_beg + i).
 //
-// Ring: local k tile t sits in stage t%4 (M/N-major operand) or in pair slot
-// (t/2) % S, half t%2 (K-major operand with S pair slots).  Step i runs the 64
-// MFMAs of tile i on fragments fc, reads the fragments of tile i+1 into fn,
-// and issues loads:
-//   M/N-major:             tile i+3;
-//   K-major, two slots:    on odd i, the pair of tiles i+3 and i+4;
-//   K-major, three slots:  on even i, the first half of the pair i+4, i+5;
-//                          on odd i, the second half of the pair i+3, i+4.
-// Each stage or slot it loads into was last read in step i-2 or earlier (as
-// fragments of tiles i-1 or i, or older).  It then waits until only its own
-// loads are outstanding, so tile i+2 has landed, and the barrier publishes
-// it; the barrier also orders every read of a slot or stage before the step
-// that loads into it again.  At entry: tiles 0 and 1 are published and tile 2
+// Ring: local k tile t sits in pair slot (t/2)%2, half t%2 (K-major operand)
+// or stage t%4 (M/N-major).  Step i runs the 64 MFMAs of tile i on fragments
+// fc, reads the fragments of tile i+1 into fn, and issues the loads of tile
+// i+3 (M/N-major) and, on odd i, of the pair of tiles i+3 and i+4 (K-major).
+// Each slot or stage it loads into was last read in step i-2 or earlier (as
+// fragments of tiles i-1 or i).  It then waits until only its own loads are
+// outstanding, so tile i+2 has landed, and the barrier publishes it; the
+// barrier also orders every read of a slot or stage before the step that
+// loads into it again.  At entry: tiles 0 and 1 are published and tile 2
 // (with the rest of its pair) may be landing.
 template <bool AK, bool BK>
 __device__ __forceinline__ void tile_k_loop(AccTile& acc, const GemmGeom& g, const Operand& a, const Operand& b,
                                             int m0, int n0, int kt_beg, int n, const DmaLanes& dla,
                                             const DmaLanes& dlb, const LdsRing<AK, BK>& R, int wave_s, int wm, int wn,
                                             int lane) {
-  constexpr int S = kPairSlots<AK, BK>;
   const FragBase<AK, kSubM> fra = frag_lane_base<AK, kSubM>(lane);
   const FragBase<BK, kSubN> frb = frag_lane_base<BK, kSubN>(lane);
   using RO = ReadOrder<AK, BK>;
   constexpr int kMfma = kSubM * kSubN;
-  constexpr int D = kDmaPerWave;
   auto lds_addr = [](const lds_char* q) { return (uint32_t)(uintptr_t)q; };
-  // pair slot of local tile t when there are three slots (run time; s_cselect)
-  auto slot3 = [](lds_char* const* p, int t) {
-    const int k = (t >> 1) % 3;
-    return k == 0 ? p[0] : k == 1 ? p[1] : p[2];
-  };
-  // LDS home of local tile t, t % 4 == T4
-  auto src = [&](auto t4, int t) {
+  // LDS home of local tile t, for t with t % 4 == T4 (compile time)
+  auto src = [&](auto t4) {
     constexpr int T4 = decltype(t4)::value;
     TileSrc ts;
-    if constexpr (AK) ts.a = S == 2 ? R.a[(T4 >> 1) & 1] : slot3(R.a, t);
-    else ts.a = R.a[T4 & 3];
-    if constexpr (BK) ts.b = S == 2 ? R.b[(T4 >> 1) & 1] : slot3(R.b, t);
-    else ts.b = R.b[T4 & 3];
+    ts.a = AK ? R.a[(T4 >> 1) & 1] : R.a[T4 & 3];
+    ts.b = BK ? R.b[(T4 >> 1) & 1] : R.b[T4 & 3];
     ts.ha = AK ? (T4 & 1) : 0;
     ts.hb = BK ? (T4 & 1) : 0;
     return ts;
-  };
-  // this step's loads of one operand: descriptor, lane base, destination,
-  // first instruction index within the pair or tile
-  struct StepLoads {
-    u32x4_t desc;
-    uint32_t base, dst;
-    int i0;
-    bool on;
-  };
-  auto plan = [&](auto kmaj, auto posc, const Operand& op, const DmaLanes& dl, lds_char* const* ring, int mn0,
-                  int i) {
-    constexpr bool KM = decltype(kmaj)::value;
-    constexpr int POS = decltype(posc)::value;
-    constexpr bool kOdd = (POS & 1) != 0;
-    StepLoads L;
-    L.base = 0u;
-    L.i0 = 0;
-    int t;  // first k tile of the unit loaded
-    if constexpr (!KM) {
-      t = i + 3;
-      L.dst = lds_addr(ring[(POS + 3) & 3]);
-    } else if constexpr (S == 2) {
-      t = i + 3;
-      L.dst = lds_addr(ring[((POS + 3) >> 1) & 1]);
-    } else {
-      t = kOdd ? i + 3 : i + 4;
-      L.i0 = kOdd ? D : 0;
-      L.dst = lds_addr(slot3(ring, t));
-    }
-    L.on = t < n;
-    const int k0 = (kt_beg + t) * kBK;
-    L.desc = tile_desc<KM>(op, mn0, k0);
-    if constexpr (KM) L.base = dma_pair_base(dl, k0, g.K);
-    return L;
   };
   // step i with i % 4 == POS (compile time)
   auto step = [&](auto first, auto checked, auto posc, int i, Frags& fc, Frags& fn) {
@@ -645,17 +588,22 @@ __device__ __forceinline__ void tile_k_loop(AccTile& acc, const GemmGeom& g, con
     constexpr bool kChecked = decltype(checked)::value;
     constexpr int POS = decltype(posc)::value;
     constexpr bool kOdd = (POS & 1) != 0;
-    constexpr int cA = dma_count<AK, S>(kOdd), cB = dma_count<BK, S>(kOdd), cnt = cA + cB;
+    constexpr int cA = dma_count<AK>(kOdd), cB = dma_count<BK>(kOdd), cnt = cA + cB;
+    const bool issue = !kChecked || i + 3 < n;
     const bool next = !kChecked || i + 1 < n;
-    const TileSrc nx = src(std::integral_constant<int, (POS + 1) & 3>{}, i + 1);
-    StepLoads LA{}, LB{};
+    const TileSrc nx = src(std::integral_constant<int, (POS + 1) & 3>{});
+    const int k3 = (kt_beg + i + 3) * kBK;
+    u32x4_t da = {0u, 0u, 0u, 0u}, db = {0u, 0u, 0u, 0u};
+    uint32_t baseA = 0u, baseB = 0u, dstA = 0u, dstB = 0u;
     if constexpr (cA > 0) {
-      LA = plan(std::integral_constant<bool, AK>{}, posc, a, dla, R.a, m0, i);
-      if constexpr (!kChecked) LA.on = true;
+      da = tile_desc<AK>(a, m0, k3);
+      if constexpr (AK) baseA = dma_pair_base(dla, k3, g.K);
+      dstA = lds_addr(AK ? R.a[((POS + 3) >> 1) & 1] : R.a[(POS + 3) & 3]);
     }
     if constexpr (cB > 0) {
-      LB = plan(std::integral_constant<bool, BK>{}, posc, b, dlb, R.b, n0, i);
-      if constexpr (!kChecked) LB.on = true;
+      db = tile_desc<BK>(b, n0, k3);
+      if constexpr (BK) baseB = dma_pair_base(dlb, k3, g.K);
+      dstB = lds_addr(BK ? R.b[((POS + 3) >> 1) & 1] : R.b[(POS + 3) & 3]);
     }
     static_for<kMfma>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
@@ -667,24 +615,15 @@ __device__ __forceinline__ void tile_k_loop(AccTile& acc, const GemmGeom& g, con
       }
       constexpr int q = dma_at(j, cnt, kMfma);
       if constexpr (q >= 0) {
-        if constexpr (q < cA) {
-          if (LA.on) dma_one<AK>(dla, LA.desc, LA.base, LA.dst, wave_s, LA.i0 + q);
-        } else {
-          if (LB.on) dma_one<BK>(dlb, LB.desc, LB.base, LB.dst, wave_s, LB.i0 + q - cA);
+        if (issue) {
+          if constexpr (q < cA) dma_one<AK>(dla, da, baseA, dstA, wave_s, q);
+          else dma_one<BK>(dlb, db, baseB, dstB, wave_s, q - cA);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
     });
-    // wait until only this step's own loads are outstanding
-    if constexpr (!kChecked) {
-      wait_vmcnt<cnt>();
-    } else {
-      const bool onA = cA > 0 && LA.on, onB = cB > 0 && LB.on;
-      if (onA && onB) wait_vmcnt<cnt>();
-      else if (onA) wait_vmcnt<cA>();
-      else if (onB) wait_vmcnt<cB>();
-      else wait_vmcnt<0>();
-    }
+    if (issue) wait_vmcnt<cnt>();
+    else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
   };
   using True = std::integral_constant<bool, true>;
@@ -695,11 +634,11 @@ __device__ __forceinline__ void tile_k_loop(AccTile& acc, const GemmGeom& g, con
   using P3 = std::integral_constant<int, 3>;
 
   Frags f0, f1;
-  read_all<AK, BK>(f0, src(P0{}, 0), fra, frb, wm, wn);
+  read_all<AK, BK>(f0, src(P0{}), fra, frb, wm, wn);
   step(True{}, True{}, P0{}, 0, f0, f1);
   int i = 1;
-  // steady state: every step of the group reads its next tile and issues all its loads
-  for (; i + 7 < n; i += 4) {
+  // steady state: every step of the group reads its next tile and issues its loads
+  for (; i + 6 < n; i += 4) {
     step(False{}, False{}, P1{}, i, f1, f0);
     step(False{}, False{}, P2{}, i + 1, f0, f1);
     step(False{}, False{}, P3{}, i + 2, f1, f0);
@@ -713,14 +652,9 @@ __device__ __forceinline__ void tile_k_loop(AccTile& acc, const GemmGeom& g, con
   }
 }
 
-// Direct-to-LDS instructions per wave of one operand's tile 2 in tile_first_loads
-// (K-major: the whole pair of tiles 2 and 3).
-template <bool KMAJOR>
-constexpr int kFirstLate = KMAJOR ? 2 * kDmaPerWave : kDmaPerWave;
-
 // The loads of local k tiles 0, 1 and 2 (K-major: pairs 0 and 1), in an order
 // that lets the caller wait for tiles 0 and 1 alone: tile 2's loads
-// (kFirstLate<AK> + kFirstLate<BK> per wave when n > 2) are last.
+// (dma_count<AK>(true) + dma_count<BK>(true) per wave when n > 2) are last.
 template <bool AK, bool BK>
 __device__ __forceinline__ void tile_first_loads(const GemmGeom& g, const Operand& a, const Operand& b, int m0, int n0,
                                                  int kt_beg, int n, const DmaLanes& dla, const DmaLanes& dlb,
@@ -741,18 +675,16 @@ __device__ __forceinline__ void tile_first_loads(const GemmGeom& g, const Operan
 }
 
 // One 256 x 256 output tile (or one K split of it): block `vb` of the `vg`
-// blocks this GEMM has in the launch.  lds0..lds4 are the kernel's 32 KiB LDS
-// arrays (the operands' pair slots and stages; lds4 only when exactly one
-// operand is K-major).
+// blocks this GEMM has in the launch.  lds0..lds3 are the kernel's four
+// 32 KiB LDS arrays (the operands' pair slots and stages).
 template <bool A_KMAJOR, bool B_KMAJOR, class Epi>
 __device__ __forceinline__ void gemm_tile(const GemmGeom& g, const Operand& a, const Operand& b, const Epi& epi,
-                                          int vb, int vg, char* lds0, char* lds1, char* lds2, char* lds3,
-                                          char* lds4) {
+                                          int vb, int vg, char* lds0, char* lds1, char* lds2, char* lds3) {
   args_to_sgprs(g);
   args_to_sgprs(a);
   args_to_sgprs(b);
   args_to_sgprs(epi);
-  const LdsRing<A_KMAJOR, B_KMAJOR> R = lds_ring<A_KMAJOR, B_KMAJOR>(lds0, lds1, lds2, lds3, lds4);
+  const LdsRing<A_KMAJOR, B_KMAJOR> R = lds_ring<A_KMAJOR, B_KMAJOR>(lds0, lds1, lds2, lds3);
   int tm, tn, split;
   map_tile(g, vb, vg, tm, tn, split);
   const int m0 = tm * kBM, n0 = tn * kBN;
@@ -768,7 +700,7 @@ __device__ __forceinline__ void gemm_tile(const GemmGeom& g, const Operand& a, c
 
   AccTile acc;
   tile_first_loads<A_KMAJOR, B_KMAJOR>(g, a, b, m0, n0, kt_beg, n, dla, dlb, R, wave_s);
-  constexpr int kLate = kFirstLate<A_KMAJOR> + kFirstLate<B_KMAJOR>;
+  constexpr int kLate = dma_count<A_KMAJOR>(true) + dma_count<B_KMAJOR>(true);
   if (n > 2) wait_vmcnt<kLate>();  // tiles 0 and 1 landed; tile 2 may still be in flight
   else wait_vmcnt<0>();
   __builtin_amdgcn_s_barrier();
@@ -789,22 +721,16 @@ __device__ __forceinline__ void gemm_tile(const GemmGeom& g, const Operand& a, c
 // and a barrier.  The k steps are those of gemm_tile, in the same order of
 // reads, loads, waits and barriers, so the accumulators, and the results, are
 // the same bits.
-// With three pair slots the exchange buffer is the K-major operand's slot 2:
-// the next tile's first loads fill slots 0 and 1 during the epilogue, and slot
-// 2 is loaded again only in the next tile's first k step, after the barrier
-// that follows every wave's epilogue.
 template <bool A_KMAJOR, bool B_KMAJOR, class Epi>
 __device__ __forceinline__ void gemm_tiles_persistent(const GemmGeom& g, const Operand& a, const Operand& b,
                                                       const Epi& epi, int p, int P, int vg, char* lds0, char* lds1,
-                                                      char* lds2, char* lds3, char* lds4, char* xch_own) {
+                                                      char* lds2, char* lds3, char* xch) {
   static_assert(Epi::kKeepsStages, "the persistent form needs an epilogue that leaves the LDS stages alone");
-  static_assert(Epi::kXchBytes <= kPairBytes, "the exchange buffer fits a pair slot");
   args_to_sgprs(g);
   args_to_sgprs(a);
   args_to_sgprs(b);
   args_to_sgprs(epi);
-  const LdsRing<A_KMAJOR, B_KMAJOR> R = lds_ring<A_KMAJOR, B_KMAJOR>(lds0, lds1, lds2, lds3, lds4);
-  char* xch = kUsesLds4<A_KMAJOR, B_KMAJOR> ? (char*)(A_KMAJOR ? R.a[2] : R.b[2]) : xch_own;
+  const LdsRing<A_KMAJOR, B_KMAJOR> R = lds_ring<A_KMAJOR, B_KMAJOR>(lds0, lds1, lds2, lds3);
   const int nk = (g.K + kBK - 1) / kBK;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
@@ -856,14 +782,11 @@ __device__ __forceinline__ void gemm_tiles_persistent(const GemmGeom& g, const O
   }
 }
 
-// The kernel's LDS arrays; the fifth only when some GEMM of the kernel has
-// exactly one K-major operand (USES4).
-#define MS_DECLARE_LDS_STAGES(USES4)                                   \
-  __shared__ __attribute__((aligned(1024))) char lds0[kStageBytes];    \
-  __shared__ __attribute__((aligned(1024))) char lds1[kStageBytes];    \
-  __shared__ __attribute__((aligned(1024))) char lds2[kStageBytes];    \
-  __shared__ __attribute__((aligned(1024))) char lds3[kStageBytes];    \
-  __shared__ __attribute__((aligned(1024))) char lds4[(USES4) ? kStageBytes : 16]
+#define MS_DECLARE_LDS_STAGES                                 \
+  __shared__ __attribute__((aligned(1024))) char lds0[kStageBytes]; \
+  __shared__ __attribute__((aligned(1024))) char lds1[kStageBytes]; \
+  __shared__ __attribute__((aligned(1024))) char lds2[kStageBytes]; \
+  __shared__ __attribute__((aligned(1024))) char lds3[kStageBytes]
 
 // Persistent launch of gemm_tiles_persistent: gridDim.x workgroups (a multiple
 // of 8, at most one per CU) share the vg tiles.
@@ -871,19 +794,18 @@ template <bool A_KMAJOR, bool B_KMAJOR, class Epi>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                                amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd)))
 gemm_persistent_kernel(GemmGeom g, Operand a, Operand b, Epi epi, int vg) {
-  constexpr bool k4 = kUsesLds4<A_KMAJOR, B_KMAJOR>;
-  MS_DECLARE_LDS_STAGES(k4);
-  __shared__ __attribute__((aligned(16))) char xch[k4 ? 16 : Epi::kXchBytes];  // with lds4: a pair slot serves
+  MS_DECLARE_LDS_STAGES;
+  __shared__ __attribute__((aligned(16))) char xch[Epi::kXchBytes];
   gemm_tiles_persistent<A_KMAJOR, B_KMAJOR, Epi>(g, a, b, epi, (int)blockIdx.x, (int)gridDim.x, vg, lds0, lds1, lds2,
-                                                 lds3, lds4, xch);
+                                                 lds3, xch);
 }
 
 template <bool A_KMAJOR, bool B_KMAJOR, class Epi>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                                amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd)))
 gemm_kernel(GemmGeom g, Operand a, Operand b, Epi epi) {
-  MS_DECLARE_LDS_STAGES((kUsesLds4<A_KMAJOR, B_KMAJOR>));
-  gemm_tile<A_KMAJOR, B_KMAJOR, Epi>(g, a, b, epi, (int)blockIdx.x, (int)gridDim.x, lds0, lds1, lds2, lds3, lds4);
+  MS_DECLARE_LDS_STAGES;
+  gemm_tile<A_KMAJOR, B_KMAJOR, Epi>(g, a, b, epi, (int)blockIdx.x, (int)gridDim.x, lds0, lds1, lds2, lds3);
 }
 
 // Two independent GEMMs in one launch, so that the blocks of one fill the CUs
@@ -897,7 +819,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                                amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd)))
 gemm_pair_kernel(GemmGeom g1, Operand a1, Operand b1, E1 e1, int blocks1, GemmGeom g2, Operand a2, Operand b2,
                  E2 e2, int blocks2, int second_first) {
-  MS_DECLARE_LDS_STAGES((kUsesLds4<AK1, BK1> || kUsesLds4<AK2, BK2>));
+  MS_DECLARE_LDS_STAGES;
   const int bid = (int)blockIdx.x;
   const int lead = second_first ? blocks2 : blocks1;
   const int lead_pad = (lead + 7) & ~7;
@@ -905,9 +827,9 @@ gemm_pair_kernel(GemmGeom g1, Operand a1, Operand b1, E1 e1, int blocks1, GemmGe
   if (in_lead && bid >= lead) return;
   const int vb = in_lead ? bid : bid - lead_pad;
   if (in_lead != (second_first != 0)) {
-    gemm_tile<AK1, BK1, E1>(g1, a1, b1, e1, vb, blocks1, lds0, lds1, lds2, lds3, lds4);
+    gemm_tile<AK1, BK1, E1>(g1, a1, b1, e1, vb, blocks1, lds0, lds1, lds2, lds3);
   } else {
-    gemm_tile<AK2, BK2, E2>(g2, a2, b2, e2, vb, blocks2, lds0, lds1, lds2, lds3, lds4);
+    gemm_tile<AK2, BK2, E2>(g2, a2, b2, e2, vb, blocks2, lds0, lds1, lds2, lds3);
   }
 }
 
