@@ -10,7 +10,9 @@ in HBM before the timed region.  Prints one JSON line.
 
 value = algorithmic TFLOP/s of the whole step: (12*T*h*f_i + 2*T*h*v_i) / step time.
 The MLP fwd+bwd TFLOP/s, the CE tokens/s and their fractions of the bf16 MFMA peak
-are reported alongside.  ``roofline`` covers the dominant kernel, the logits GEMM
+are reported alongside.  ``ms_per_step`` is host wall time over the K timed steps;
+``step_ms_events`` gives the median, minimum and 90th percentile of the same steps
+timed one by one with HIP events.  ``roofline`` covers the dominant kernel, the logits GEMM
 with the fused CE epilogue: the library records a pair of HIP events on its launch
 stream around that one launch in every timed step (ms_arm_kernel_events), and
 ``achieved`` = 2*T*h*v_i / the mean of those durations.  ``traffic`` is the HBM
@@ -240,7 +242,11 @@ class StepRunner:
             self.step(phases[k], arm=[("ce_gemm", gemm_ev[k])])
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        per_step = np.array([e[0].elapsed_time(e[2]) for e in phases])
         return {"ms_step": wall * 1e3 / steps,
+                "step_stats": {"median": round(float(np.median(per_step)), 4),
+                               "min": round(float(per_step.min()), 4),
+                               "p90": round(float(np.percentile(per_step, 90)), 4)},
                 "mlp_ms": float(np.mean([e[0].elapsed_time(e[1]) for e in phases])),
                 "ce_ms": float(np.mean([e[1].elapsed_time(e[2]) for e in phases])),
                 "gemm_ms": float(np.mean([e0.elapsed_time(e1) for e0, e1 in gemm_ev]))}
@@ -373,6 +379,7 @@ def main():
         "steps": a.steps,
         "warmup": a.warmup,
         "ms_per_step": round(ms_step, 4),
+        "step_ms_events": t["step_stats"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -411,7 +418,8 @@ def main():
         s2 = step_summary(c2, t2)
         shards[name] = {
             "workload": f"T={c2.T}, h={c2.h}, f_i={c2.f_i}, v_i={c2.v_i}, t={c2.t}",
-            "ms_per_step": round(t2["ms_step"], 4), "tflops": round(s2["value"], 2),
+            "ms_per_step": round(t2["ms_step"], 4), "step_ms_events": t2["step_stats"],
+            "tflops": round(s2["value"], 2),
             "pct_of_bf16_peak": round(100 * s2["value"] / PEAK_BF16_TFLOPS, 2),
             "mlp_fwd_bwd_tflops": round(s2["mlp_tflops"], 2),
             "mlp_pct_of_peak": round(100 * s2["mlp_tflops"] / PEAK_BF16_TFLOPS, 2),

@@ -457,27 +457,23 @@ struct EpiCE {
       xswap32(rs[mi], sa, sb);
       lse_pair(ma, sa, mb, sb, rm[mi], rs[mi]);
     }
-    // the target logit: only in the tiles that hold some row's target (about
-    // one in N/256); at most one lane of a row's four holds it
-    int tl[kSubM];
-    bool any = false;
+    // the target logit: searched only in the 16-row blocks that hold some
+    // row's target in this wave's 128 columns (one block in 25 at v_i = 50304),
+    // so waves do not wait at the barrier below for a search over all their
+    // accumulators; at most one lane of a row's four holds it
 #pragma unroll
     for (int mi = 0; mi < kSubM; ++mi) {
       const int64_t t = (int64_t)(((uint64_t)tw[mi][1] << 32) | tw[mi][0]) - vocab_start - col0;
-      tl[mi] = (t >= 0 && t < ncol) ? (int)t : -1;
-      any |= tl[mi] >= 0;
+      const int tl = (t >= 0 && t < ncol) ? (int)t : -1;
       rz[mi] = 0.f;
-    }
-    if (__any(any)) {
-#pragma unroll
-      for (int mi = 0; mi < kSubM; ++mi) {
+      if (__any(tl >= 0)) {
         float zz = 0.f;
 #pragma unroll
         for (int ni = 0; ni < kSubN; ++ni)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float x = acc_read(acc[mi][ni][r]);
-            zz = (ni * 16 + 4 * g + r) == tl[mi] ? x : zz;
+            zz = (ni * 16 + 4 * g + r) == tl ? x : zz;
           }
         float za, zb;
         xswap16(zz, za, zb);

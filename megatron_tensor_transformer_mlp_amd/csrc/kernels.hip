@@ -75,38 +75,74 @@ __device__ __forceinline__ void lse_merge(float& M, float& S, float m2, float s2
 }
 
 // Per token row: merge the P tile partials of the logits GEMM into the shard's
-// (m, s, z).  A block covers 64 rows with 8 waves; wave w merges partials
-// [w*P/8, (w+1)*P/8) in ascending order (one row per lane, coalesced over
-// rows), then wave 0 merges the 8 wave results in ascending wave order.
+// (m, s, z).  A block covers 32 rows with 16 groups of 32 lanes (two per wave,
+// one row per lane, 128-byte loads); group g takes partials
+// [g*P/16, (g+1)*P/16) in ascending chunks of 8: a chunk's loads are issued
+// together, its maximum raises the running maximum (rescaling the running sum
+// once), and its terms s_p exp(m_p - max) are added in ascending p.  Group 0
+// then merges the 16 group results in ascending g.  T/32 blocks fill the chip
+// at the workloads' token counts.
+constexpr int kCombineRows = 32, kCombineGroups = 16, kCombineChunk = 8;
 __global__ void __launch_bounds__(512) ce_tile_combine(const float* __restrict__ pm, const float* __restrict__ ps,
                                                        const float* __restrict__ pz, int P, int T,
                                                        float* __restrict__ m, float* __restrict__ s,
                                                        float* __restrict__ z) {
-  __shared__ float xm[8][64], xs[8][64], xz[8][64];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int row = blockIdx.x * 64 + lane;
-  const int p0 = (int)(((int64_t)w * P) / 8), p1 = (int)(((int64_t)(w + 1) * P) / 8);
+  __shared__ float xm[kCombineGroups][kCombineRows], xs[kCombineGroups][kCombineRows],
+      xz[kCombineGroups][kCombineRows];
+  const int r = threadIdx.x % kCombineRows, gi = threadIdx.x / kCombineRows;
+  const int row = blockIdx.x * kCombineRows + r;
+  const int p0 = (int)(((int64_t)gi * P) / kCombineGroups), p1 = (int)(((int64_t)(gi + 1) * P) / kCombineGroups);
   float M = -INFINITY, S = 0.f, Z = 0.f;
   if (row < T) {
-    for (int p = p0; p < p1; ++p) {
-      const int64_t o = (int64_t)p * T + row;
-      lse_merge(M, S, pm[o], ps[o]);
-      Z += pz[o];
+    for (int p = p0; p < p1; p += kCombineChunk) {
+      float cm[kCombineChunk], cs[kCombineChunk], cz[kCombineChunk];
+#pragma unroll
+      for (int j = 0; j < kCombineChunk; ++j) {
+        const bool in = p + j < p1;
+        const int64_t o = (int64_t)(p + j) * T + row;
+        cm[j] = in ? pm[o] : -INFINITY;
+        cs[j] = in ? ps[o] : 0.f;
+        cz[j] = in ? pz[o] : 0.f;
+      }
+      float mx = cm[0];
+#pragma unroll
+      for (int j = 1; j < kCombineChunk; ++j) mx = fmaxf(mx, cm[j]);
+      if (mx > M) {
+        S = S > 0.f ? S * expf(M - mx) : 0.f;
+        M = mx;
+      }
+#pragma unroll
+      for (int j = 0; j < kCombineChunk; ++j) {
+        S += cs[j] > 0.f ? cs[j] * expf(cm[j] - M) : 0.f;  // empty parts and padding add nothing
+        Z += cz[j];
+      }
     }
   }
-  xm[w][lane] = M;
-  xs[w][lane] = S;
-  xz[w][lane] = Z;
+  xm[gi][r] = M;
+  xs[gi][r] = S;
+  xz[gi][r] = Z;
   __syncthreads();
-  if (w == 0 && row < T) {
-    for (int q = 1; q < 8; ++q) {
-      lse_merge(M, S, xm[q][lane], xs[q][lane]);
-      Z += xz[q][lane];
+  if (gi == 0 && row < T) {
+    for (int q = 1; q < kCombineGroups; ++q) {
+      lse_merge(M, S, xm[q][r], xs[q][r]);
+      Z += xz[q][r];
     }
     m[row] = M;
     s[row] = S;
     z[row] = Z;
   }
+}
+
+// Loss of token i: the t shards' partials merged in ascending rank order.
+__device__ __forceinline__ float token_loss(const float* __restrict__ m, const float* __restrict__ s,
+                                            const float* __restrict__ z, int t, int64_t T, int64_t i) {
+  float M = -INFINITY, S = 0.f, Z = 0.f;
+  for (int r = 0; r < t; ++r) {
+    const int64_t o = (int64_t)r * T + i;
+    lse_merge(M, S, m[o], s[o]);
+    Z += z[o];
+  }
+  return logf(S) + M - Z;
 }
 
 // Per token: merge t shards' partials in ascending rank order into the loss.
@@ -115,13 +151,7 @@ __global__ void __launch_bounds__(256) ce_combine_tokens(const float* __restrict
                                                          float* __restrict__ loss) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= T) return;
-  float M = -INFINITY, S = 0.f, Z = 0.f;
-  for (int r = 0; r < t; ++r) {
-    const int64_t o = (int64_t)r * T + i;
-    lse_merge(M, S, m[o], s[o]);
-    Z += z[o];
-  }
-  loss[i] = logf(S) + M - Z;
+  loss[i] = token_loss(m, s, z, t, T, i);
 }
 
 // Per token, the record the cross-entropy backward's epilogue reads: the
@@ -145,13 +175,9 @@ __global__ void __launch_bounds__(256) ce_bwd_rowstats(const float* __restrict__
   out[i] = f32x4_t{M * kLog2e, coef / S, coef, __int_as_float(col)};
 }
 
-// Mean of loss[0..T): thread j sums j, j+1024, ... in order, then a fixed
-// binary tree over the 1024 thread sums.  One workgroup.
-__global__ void __launch_bounds__(1024) mean_fixed_tree(const float* __restrict__ x, int64_t T,
-                                                        float* __restrict__ out) {
+// The fixed binary tree over the 1024 per-thread sums of one workgroup: out = sum / T.
+__device__ __forceinline__ void mean_tree_1024(float acc, int64_t T, float* __restrict__ out) {
   __shared__ float red[1024];
-  float acc = 0.f;
-  for (int64_t i = threadIdx.x; i < T; i += 1024) acc += x[i];
   red[threadIdx.x] = acc;
   __syncthreads();
   for (int w = 512; w > 0; w >>= 1) {
@@ -159,6 +185,45 @@ __global__ void __launch_bounds__(1024) mean_fixed_tree(const float* __restrict_
     __syncthreads();
   }
   if (threadIdx.x == 0) out[0] = red[0] / (float)T;
+}
+
+// Mean of loss[0..T): thread j sums j, j+1024, ... in order, then a fixed
+// binary tree over the 1024 thread sums.  One workgroup.
+__global__ void __launch_bounds__(1024) mean_fixed_tree(const float* __restrict__ x, int64_t T,
+                                                        float* __restrict__ out) {
+  float acc = 0.f;
+  for (int64_t i = threadIdx.x; i < T; i += 1024) acc += x[i];
+  mean_tree_1024(acc, T, out);
+}
+
+// Largest t*T that ce_combine_mean_small takes (64 partials per thread).
+constexpr int64_t kCombineSmall = 65536;
+
+// ce_combine_tokens followed by mean_fixed_tree in one workgroup, for small
+// t*T: thread j forms the losses of tokens j, j+1024, ... and sums them in that
+// order, so loss and mean are the same bits as the two-kernel path's.
+__global__ void __launch_bounds__(1024) ce_combine_mean_small(const float* __restrict__ m,
+                                                              const float* __restrict__ s,
+                                                              const float* __restrict__ z, int t, int64_t T,
+                                                              float* __restrict__ loss, float* __restrict__ out) {
+  float acc = 0.f;
+  for (int64_t i0 = threadIdx.x; i0 < T; i0 += 8 * 1024) {
+    float l[8];  // eight tokens' losses formed together, then summed in token order
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t i = i0 + (int64_t)j * 1024;
+      l[j] = i < T ? token_loss(m, s, z, t, T, i) : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t i = i0 + (int64_t)j * 1024;
+      if (i < T) {
+        loss[i] = l[j];
+        acc += l[j];
+      }
+    }
+  }
+  mean_tree_1024(acc, T, out);
 }
 
 // ---------------------------------------------------------------------------
@@ -273,7 +338,7 @@ void plan_pair(int64_t M, int64_t N, int64_t T, BlockList p, int& S_out, bool& p
       paired = false;
       partner_first = false;
     }
-    if (par < best) {
+    if (par <= best) {  // on a tie the paired launch saves a launch
       best = par;
       S_out = S;
       paired = true;
@@ -548,8 +613,8 @@ hipError_t launch_vocab_ce(const uint16_t* X, const uint16_t* E, const int64_t* 
   err = hipGetLastError();
   record_armed_event(kTkCeGemm, true, st);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(ce_tile_combine, dim3((unsigned)((T + 63) / 64)), dim3(512), 0, st, pm, ps, pz, w.parts,
-                     (int)T, m, s, z);
+  hipLaunchKernelGGL(ce_tile_combine, dim3((unsigned)((T + kCombineRows - 1) / kCombineRows)),
+                     dim3(kCombineRows * kCombineGroups), 0, st, pm, ps, pz, w.parts, (int)T, m, s, z);
   return hipGetLastError();
 }
 
@@ -703,6 +768,10 @@ hipError_t noalloc_scratch(void** ptr) {
 
 hipError_t launch_ce_combine(const float* m, const float* s, const float* z, int t, int64_t T, float* loss,
                              float* loss_mean, hipStream_t st) {
+  if (loss_mean && (int64_t)t * T <= kCombineSmall) {
+    hipLaunchKernelGGL(ce_combine_mean_small, dim3(1), dim3(1024), 0, st, m, s, z, t, T, loss, loss_mean);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(ce_combine_tokens, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, st, m, s, z, t, T, loss);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || !loss_mean) return err;

@@ -9,6 +9,7 @@
 //   lib_driver ce_fwd   T h v vstart dir    : X E target              -> m s z
 //   lib_driver ce_bwd   T h v vstart t scale dloss dir : X E target m s [dloss] -> dX dE
 //   lib_driver combine  t T dir             : m s z                   -> loss mean
+//   lib_driver combine_nomean t T dir       : m s z                   -> loss_only (no mean asked)
 //   lib_driver attn_fwd b s h n d causal dir: X Wqkv Wo               -> QKV O lse Z
 //   lib_driver attn_bwd b s h n d causal dir: X Wqkv Wo QKV O lse dZ  -> dX dWqkv dWo
 //   lib_driver attn_core b s n d causal dir : qkv dout                -> o lse dqkv (the core alone)
@@ -110,14 +111,16 @@ int main(int argc, char** argv) {
                            ws.begin() + mshard::ce_bwd_workspace_layout(T, h, v).off_dL + T * v * 2);
       wr("dL", dL, T * v * 2);
     }
-  } else if (op == "combine") {
+  } else if (op == "combine" || op == "combine_nomean") {
     const int64_t t = I(0), T = I(1);
+    const bool mean_too = op == "combine";
     auto m = rd("m", t * T * 4), s = rd("s", t * T * 4), z = rd("z", t * T * 4);
     auto loss = out(T * 4), mean = out(4);
-    ok(mshard::launch_ce_combine(C<float>(m), C<float>(s), C<float>(z), (int)t, T, P<float>(loss), P<float>(mean),
-                                 nullptr),
+    ok(mshard::launch_ce_combine(C<float>(m), C<float>(s), C<float>(z), (int)t, T, P<float>(loss),
+                                 mean_too ? P<float>(mean) : nullptr, nullptr),
        "launch_ce_combine");
-    wr("loss", loss, T * 4), wr("mean", mean, 4);
+    wr(mean_too ? "loss" : "loss_only", loss, T * 4);
+    if (mean_too) wr("mean", mean, 4);
   } else if (op == "attn_fwd" || op == "attn_bwd") {
     const int64_t b = I(0), s = I(1), h = I(2), n = I(3), d = I(4), causal = I(5);
     const int64_t T = b * s, nd = n * d;

@@ -189,6 +189,52 @@ def test_ce_full_size(ms, name):
     assert merr <= CE_TOL
 
 
+def combine_partials(rng, t, T):
+    """Shard partials shaped like real ones: each token's target logit sits in one
+    rank's shard and is at most that shard's maximum, and every shard's sum of
+    exponentials is at least 2, so each loss is at least ln 2."""
+    M = rng.normal(0, 3, (t, T)).astype(np.float32)
+    S = rng.uniform(2, 500, (t, T)).astype(np.float32)
+    owner = rng.integers(0, t, T)
+    Z = np.zeros((t, T), np.float32)
+    Z[owner, np.arange(T)] = M[owner, np.arange(T)] - np.abs(rng.normal(0, 3, T)).astype(np.float32)
+    return M, S, Z
+
+
+def fixed_order_mean(loss: np.ndarray) -> np.float32:
+    """The combine's mean in float32: per-thread sums over tokens j, j+1024, ... in
+    ascending order, then a binary tree over the 1024 sums, divided by T."""
+    T = loss.shape[0]
+    acc = np.zeros(1024, np.float32)
+    for k in range(0, T, 1024):
+        c = loss[k:k + 1024]
+        acc[:c.shape[0]] += c
+    w = 512
+    while w > 0:
+        acc[:w] += acc[w:2 * w]
+        w //= 2
+    return np.float32(acc[0] / np.float32(T))
+
+
+@pytest.mark.parametrize("t,T", [(1, 8192), (8, 8192), (2, 33000), (3, 100000)])
+def test_combine_paths(ms, t, T):
+    """ce_combine at and above the one-workgroup limit (t*T <= 65536): the loss has the
+    same bits with and without the mean, it matches the oracle, and the mean is the
+    fixed-order float32 sum of those losses, bit for bit."""
+    M, S, Z = combine_partials(np.random.default_rng(17 + t), t, T)
+    print(f"  ce_combine t={t} T={T}", flush=True)
+    m, s, z = (torch.from_numpy(a).cuda() for a in (M, S, Z))
+    loss, mean = ms.ce_combine(m, s, z)
+    loss_only, none = ms.ce_combine(m, s, z, want_mean=False)
+    torch.cuda.synchronize()
+    assert none is None
+    gl = loss.cpu().numpy()
+    assert torch.equal(loss.view(torch.int32), loss_only.view(torch.int32))
+    want = oracle.ce_combine(M, S, Z)
+    assert np.max(np.abs(gl / want["loss"] - 1)) <= CE_TOL
+    assert mean.cpu().numpy()[0].view(np.uint32) == fixed_order_mean(gl).view(np.uint32)
+
+
 # ----------------------------------------------------------------------------- determinism
 def test_bitwise_determinism(ms):
     """Repeated calls on identical inputs give identical output bytes, also with

@@ -127,6 +127,53 @@ def mlp_case(exe, d, T, h, f, gelu, bias):
     assert all(e <= TOL for e in errs.values()), errs
 
 
+def combine_partials(rng, t, T):
+    """Shard partials shaped like real ones: each token's target logit sits in one
+    rank's shard and is at most that shard's maximum, and every shard's sum of
+    exponentials is at least 2, so each loss is at least ln 2."""
+    M = rng.normal(0, 3, (t, T)).astype(np.float32)
+    S = rng.uniform(2, 500, (t, T)).astype(np.float32)
+    owner = rng.integers(0, t, T)
+    Z = np.zeros((t, T), np.float32)
+    Z[owner, np.arange(T)] = M[owner, np.arange(T)] - np.abs(rng.normal(0, 3, T)).astype(np.float32)
+    return M, S, Z
+
+
+def fixed_order_mean(loss):
+    """The combine's mean in float32: per-thread sums over tokens j, j+1024, ... in
+    ascending order, then a binary tree over the 1024 sums, divided by T."""
+    T = loss.shape[0]
+    acc = np.zeros(1024, np.float32)
+    for k in range(0, T, 1024):
+        c = loss[k:k + 1024]
+        acc[:c.shape[0]] += c
+    w = 512
+    while w > 0:
+        acc[:w] += acc[w:2 * w]
+        w //= 2
+    return np.float32(acc[0] / np.float32(T))
+
+
+@pytest.mark.parametrize("T", [3000, 33000])
+def test_combine_paths_emulated(lib, T):
+    """ce_combine below and above the one-workgroup limit (t*T <= 65536): the loss has
+    the same bits whether or not the mean is asked for, and the mean is the fixed-order
+    float32 sum of those losses."""
+    exe, d = lib
+    t = 2
+    M, S, Z = combine_partials(np.random.default_rng(11), t, T)
+    case = os.path.join(d, f"comb{T}")
+    put(case, m=M, s=S, z=Z)
+    run(exe, case, "combine", t, T)
+    run(exe, case, "combine_nomean", t, T)
+    loss = np.fromfile(os.path.join(case, "loss.bin"), np.float32)
+    assert np.array_equal(loss.view(np.uint32), np.fromfile(os.path.join(case, "loss_only.bin"), np.uint32))
+    oc = oracle.ce_combine(M, S, Z)
+    assert np.abs(loss / oc["loss"] - 1).max() <= CE_TOL
+    mean = np.fromfile(os.path.join(case, "mean.bin"), np.float32)[0]
+    assert mean.view(np.uint32) == fixed_order_mean(loss).view(np.uint32)
+
+
 def test_vocab_ce_two_shards_emulated(lib):
     """Both ranks' forward partials, the fixed-order combine, and rank 0's backward
     with a per-token upstream gradient (every seventh token weighted 0)."""
