@@ -11,8 +11,8 @@ in HBM before the timed region.  Prints one JSON line.
 value = algorithmic TFLOP/s of the whole step: (12*T*h*f_i + 2*T*h*v_i) / step time.
 The MLP fwd+bwd TFLOP/s, the CE tokens/s and their fractions of the bf16 MFMA peak
 are reported alongside.  ``ms_per_step`` is host wall time over the K timed steps;
-``step_ms_events`` gives the median, minimum and 90th percentile of the same steps
-timed one by one with HIP events.  ``roofline`` covers the dominant kernel, the logits GEMM
+``step_ms_events`` gives the median, minimum and 90th percentile of K further steps
+timed one by one with HIP events (the MLP and CE phase times come from those too).  ``roofline`` covers the dominant kernel, the logits GEMM
 with the fused CE epilogue: the library records a pair of HIP events on its launch
 stream around that one launch in every timed step (ms_arm_kernel_events), and
 ``achieved`` = 2*T*h*v_i / the mean of those durations.  ``traffic`` is the HBM
@@ -229,8 +229,11 @@ class StepRunner:
             phase[2].record(self.stream)
 
     def timed_steps(self, steps, warmup):
-        """Wall time per step over `steps` steps (after `warmup`), the MLP and CE phase
-        times from events, and the CE GEMM's own launch time from the library's hook."""
+        """Wall time per step over `steps` steps (after `warmup`), with the CE GEMM's
+        own launch time from the library's hook on each of them; then the same number
+        of steps again with events at the phase boundaries, for the MLP and CE phase
+        times and the per-step spread (kept out of the timed steps, whose only events
+        are the CE GEMM's)."""
         torch = self.torch
         for _ in range(warmup):
             self.step()
@@ -239,9 +242,12 @@ class StepRunner:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for k in range(steps):
-            self.step(phases[k], arm=[("ce_gemm", gemm_ev[k])])
+            self.step(arm=[("ce_gemm", gemm_ev[k])])
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        for k in range(steps):
+            self.step(phases[k])
+        torch.cuda.synchronize()
         per_step = np.array([e[0].elapsed_time(e[2]) for e in phases])
         return {"ms_step": wall * 1e3 / steps,
                 "step_stats": {"median": round(float(np.median(per_step)), 4),
