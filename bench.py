@@ -217,7 +217,7 @@ class StepRunner:
             ms.arm_kernel_events(name, e0, e1)
         if phase is not None:
             phase[0].record(self.stream)
-        ms.mlp_shard_fwd(self.X, self.A, self.B, None, out=(self.H, self.Y, self.Z))
+        ms.mlp_shard_fwd(self.X, self.A, self.B, None, out=(self.H, self.Y, self.Z), workspace=self.mlp_ws)
         ms.mlp_shard_bwd(self.X, self.A, self.B, self.H, self.Y, self.dZ, workspace=self.mlp_ws,
                          out=(self.dX, self.dA, self.dB, None))
         if phase is not None:

@@ -81,6 +81,13 @@ typedef enum { MS_GELU_ERF = 0, MS_GELU_TANH = 1 } ms_gelu;
  * sizes (one number covers both).  Returns 0 for invalid sizes. */
 size_t mlp_shard_workspace_bytes(int64_t T, int64_t h, int64_t f_i);
 
+/* Bytes of workspace mlp_shard_fwd itself needs: 0 when its launch plan uses
+ * none (then its workspace may be NULL), else mlp_shard_workspace_bytes.  The
+ * forward uses a workspace when the tiles of X A_i leave the GPU's last round
+ * of workgroups mostly idle: it then splits the contraction of the last tile
+ * columns into slices there, summed in slice order.  Returns 0 for invalid sizes. */
+size_t mlp_shard_fwd_workspace_bytes(int64_t T, int64_t h, int64_t f_i);
+
 /* Forward of one rank's MLP shard (explainer, "core idea"; paper notes, "MLP
  * block split"):
  *     H_i = X A_i (+ b1_i),   Y_i = GeLU(H_i),   Z_i = Y_i B_i.
@@ -89,7 +96,9 @@ size_t mlp_shard_workspace_bytes(int64_t T, int64_t h, int64_t f_i);
  * Outputs: H_i[T x f_i] and Y_i[T x f_i] bf16 (saved for the backward; Y_i is
  *          GeLU of the fp32 pre-activation, then rounded); Z_i[T x h] fp32,
  *          this rank's partial of YB (g would sum it over ranks; the second
- *          bias and dropout act after that sum and are not applied here). */
+ *          bias and dropout act after that sum and are not applied here).
+ * Workspace: mlp_shard_fwd_workspace_bytes(T, h, f_i) bytes, or NULL when that
+ *          is 0; too small or NULL when needed -> MS_ERR_WORKSPACE. */
 ms_status mlp_shard_fwd(const ms_bf16* X, const ms_bf16* A_i, const ms_bf16* b1_i, const ms_bf16* B_i,
                         int64_t T, int64_t h, int64_t f_i, ms_gelu gelu,
                         ms_bf16* H_i, ms_bf16* Y_i, float* Z_i,

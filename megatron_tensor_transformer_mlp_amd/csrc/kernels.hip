@@ -49,6 +49,51 @@ __global__ void __launch_bounds__(256) splitk_reduce_bf16(const float* __restric
   *(u32x4_t*)(out + i) = o;
 }
 
+// The forward's tail columns: for element (t, c) of [T x tn], the
+// pre-activation is the sum of the S split slices ws[s*T*tn + t*tn + c] in
+// ascending s, plus the bias b1[c] when there is one, as the GeLU epilogue
+// forms it; H and GeLU(H) are stored in bf16 at row t, column c of H and Y
+// (row pitch ld).  8 elements per thread.
+template <int FORM>
+__global__ void __launch_bounds__(256) splitk_gelu_reduce(const float* __restrict__ ws, int S, int64_t T, int tn,
+                                                          const uint16_t* __restrict__ b1, int64_t ld,
+                                                          uint16_t* __restrict__ H, uint16_t* __restrict__ Y) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  const int64_t n = T * tn;
+  if (i >= n) return;
+  const int64_t t = i / tn;
+  const int c = (int)(i - t * tn);
+  float acc[8];
+  const f32x4_t* p = (const f32x4_t*)(ws + i);
+  f32x4_t a = p[0], b = p[1];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) { acc[r] = a[r]; acc[4 + r] = b[r]; }
+  for (int sl = 1; sl < S; ++sl) {
+    const f32x4_t* q = (const f32x4_t*)(ws + (int64_t)sl * n + i);
+    a = q[0];
+    b = q[1];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) { acc[r] += a[r]; acc[4 + r] += b[r]; }
+  }
+  float bv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (b1) {
+    const u32x4_t w = *(const u32x4_t*)(b1 + c);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) { bv[2 * r] = bf16_lo(w[r]); bv[2 * r + 1] = bf16_hi(w[r]); }
+  }
+  float hv[8], yv[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    hv[r] = acc[r] + bv[r];
+    yv[r] = gelu_f<FORM>(hv[r]);
+  }
+  const int64_t o = t * ld + c;
+  *(u32x4_t*)(H + o) = u32x4_t{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]), pack_bf16x2(hv[4], hv[5]),
+                               pack_bf16x2(hv[6], hv[7])};
+  *(u32x4_t*)(Y + o) = u32x4_t{pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3]), pack_bf16x2(yv[4], yv[5]),
+                               pack_bf16x2(yv[6], yv[7])};
+}
+
 // db1[j] = bf16( sum_{p = 0..P-1} part[p*N + j] ), p ascending.
 __global__ void __launch_bounds__(256) colsum_reduce_bf16(const float* __restrict__ part, int P, int N,
                                                           uint16_t* __restrict__ out) {
@@ -286,7 +331,7 @@ static hipError_t launch_gemm(int id, const GemmGeom& g, const Operand& a, const
 namespace {
 constexpr int kModelCUs = 256;
 constexpr double kCyclesPerKStep = 1400.0, kFillCycles = 4000.0, kCyclesPerUs = 2000.0;
-constexpr double kEpiDGelu = 40000.0, kEpiF32 = 12000.0, kEpiBF16 = 10000.0;
+constexpr double kEpiDGelu = 40000.0, kEpiF32 = 12000.0, kEpiBF16 = 10000.0, kEpiGelu = 29000.0;
 
 struct BlockList {
   int64_t n;
@@ -368,6 +413,43 @@ BwdPlan plan_backward(int64_t T, int64_t h, int64_t f) {
   return pl;
 }
 
+// Forward plan: the plain launch of X A_i with GeLU, or its last tile columns
+// split over K (see FwdPlan), whichever the same model gives the shorter time,
+// the split only when it wins by at least 3%.  Its reduction is charged its
+// bytes (S fp32 slices read, H and Y written) at ~4 TB/s plus a launch.
+// Considered only where the plain launch has more tiles than CUs and at most
+// 16 rounds of them (beyond that the last round's idle share is small).
+FwdPlan plan_forward(int64_t T, int64_t h, int64_t f) {
+  static std::mutex mu;
+  static std::map<std::array<int64_t, 3>, FwdPlan> cache;
+  const std::array<int64_t, 3> key{T, h, f};
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+  }
+  FwdPlan pl{0, 1};
+  const int64_t tm = (T + kBM - 1) / kBM, tn = (f + kBN - 1) / kBN, nk = (h + kBK - 1) / kBK;
+  if (tm * tn > kModelCUs && tm * tn <= 16 * kModelCUs && nk >= 8) {
+    double best = 0.97 * makespan_us({BlockList{tm * tn, block_cost(h, 1, kEpiGelu)}});
+    for (int64_t nc = 1; nc < tn && nc <= 32; ++nc) {
+      const int64_t tail_n = f - (tn - nc) * kBN;
+      for (int S = 2; S <= 8 && nk / S >= 4; S *= 2) {
+        const double t = makespan_us({BlockList{tm * (tn - nc), block_cost(h, 1, kEpiGelu)},
+                                      BlockList{tm * nc * S, block_cost(h, S, kEpiF32)}}) +
+                         (double)(4 * S + 4) * (double)T * (double)tail_n / 4e6 + 3.0;
+        if (t < best) {
+          best = t;
+          pl = FwdPlan{(int)tail_n, S};
+        }
+      }
+    }
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  cache.emplace(key, pl);
+  return pl;
+}
+
 MlpWorkspace mlp_workspace_layout(int64_t T, int64_t h, int64_t f) {
   MlpWorkspace w;
   auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -380,6 +462,13 @@ MlpWorkspace mlp_workspace_layout(int64_t T, int64_t h, int64_t f) {
   const int S = w.plan.splits_dB > w.plan.splits_dA ? w.plan.splits_dB : w.plan.splits_dA;
   w.bytes = w.off_splitk + (S > 1 ? align((size_t)S * h * f * 4) : 0);
   w.max_region = std::max({(size_t)T * f * 2, (size_t)w.db1_parts * f * 4, S > 1 ? (size_t)h * f * 4 : (size_t)0});
+  w.fwd = plan_forward(T, h, f);
+  w.off_fwd_tail = 0;
+  if (w.fwd.tail_n > 0) {
+    const size_t slice = (size_t)T * w.fwd.tail_n * 4;
+    w.bytes = std::max(w.bytes, align(slice * w.fwd.tail_splits));
+    w.max_region = std::max(w.max_region, slice);
+  }
   return w;
 }
 
@@ -462,14 +551,40 @@ AttnWorkspace attn_workspace_layout(int64_t b, int64_t s, int64_t h, int64_t n, 
 
 template <int FORM>
 static hipError_t mlp_fwd_impl(const uint16_t* X, const uint16_t* A, const uint16_t* b1, const uint16_t* B,
-                               int64_t T, int64_t h, int64_t f, uint16_t* H, uint16_t* Y, float* Z,
+                               int64_t T, int64_t h, int64_t f, uint16_t* H, uint16_t* Y, float* Z, char* ws,
                                hipStream_t st) {
   // H = X A (+ b1), Y = GeLU(H):  NN, M = T, N = f, K = h
-  {
+  const FwdPlan pl = plan_forward(T, h, f);
+  const Operand a{X, h, T * h};
+  if (pl.tail_n == 0) {
     GemmGeom g = make_geom(T, f, h, 1);
-    Operand a{X, h, T * h}, b{A, f, h * f};
+    Operand b{A, f, h * f};
     EpiGeluFwd<FORM> e{H, Y, b1, f, (int)T, (int)f};
     hipError_t err = launch_gemm<true, false>(kTkFwdH, g, a, b, e, st);
+    if (err != hipSuccess) return err;
+  } else {
+    // columns [0, n1) with the GeLU epilogue, and the tail columns [n1, f) split
+    // over K into fp32 slices, in one launch (the full tiles first); then the
+    // slices are summed with the bias and GeLU
+    const int64_t n1 = f - pl.tail_n;
+    float* slices = (float*)(ws + mlp_workspace_layout(T, h, f).off_fwd_tail);
+    const GemmGeom g1 = make_geom(T, n1, h, 1);
+    const Operand b1o{A, f, h * f};
+    const EpiGeluFwd<FORM> e1{H, Y, b1, f, (int)T, (int)n1};
+    const GemmGeom g2 = make_geom(T, pl.tail_n, h, pl.tail_splits);
+    const Operand b2o{A + n1, f, h * f - n1};
+    const EpiStoreF32 e2{slices, pl.tail_n, (int)T, (int)pl.tail_n, T * pl.tail_n};
+    const int nb1 = g1.tiles_m * g1.tiles_n * g1.splits, nb2 = g2.tiles_m * g2.tiles_n * g2.splits;
+    record_armed_event(kTkFwdH, false, st);
+    hipLaunchKernelGGL((gemm_pair_kernel<true, false, EpiGeluFwd<FORM>, true, false, EpiStoreF32>),
+                       dim3(((nb1 + 7) & ~7) + nb2), dim3(kThreads), 0, st, g1, a, b1o, e1, nb1, g2, a, b2o, e2, nb2, 0);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int64_t n8 = T * pl.tail_n / 8;
+    hipLaunchKernelGGL((splitk_gelu_reduce<FORM>), dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, slices,
+                       g2.splits, T, pl.tail_n, b1 ? b1 + n1 : nullptr, f, H + n1, Y + n1);
+    err = hipGetLastError();
+    record_armed_event(kTkFwdH, true, st);
     if (err != hipSuccess) return err;
   }
   // Z = Y B:  NN, M = T, N = h, K = f
@@ -482,10 +597,10 @@ static hipError_t mlp_fwd_impl(const uint16_t* X, const uint16_t* A, const uint1
 }
 
 hipError_t launch_mlp_fwd(const uint16_t* X, const uint16_t* A, const uint16_t* b1, const uint16_t* B,
-                          int64_t T, int64_t h, int64_t f, int gelu, uint16_t* H, uint16_t* Y, float* Z,
+                          int64_t T, int64_t h, int64_t f, int gelu, uint16_t* H, uint16_t* Y, float* Z, void* ws,
                           hipStream_t st) {
-  return gelu == kGeluErf ? mlp_fwd_impl<kGeluErf>(X, A, b1, B, T, h, f, H, Y, Z, st)
-                          : mlp_fwd_impl<kGeluTanh>(X, A, b1, B, T, h, f, H, Y, Z, st);
+  return gelu == kGeluErf ? mlp_fwd_impl<kGeluErf>(X, A, b1, B, T, h, f, H, Y, Z, (char*)ws, st)
+                          : mlp_fwd_impl<kGeluTanh>(X, A, b1, B, T, h, f, H, Y, Z, (char*)ws, st);
 }
 
 // Two independent GEMMs as one launch (see gemm_pair_kernel); both kernel ids'

@@ -17,14 +17,27 @@ struct BwdPlan {
   bool dh_first, dx_first;   // in a paired launch, the partner's blocks lead
 };
 
+// Launch plan of the forward's first GEMM (X A_i with GeLU): when its tiles
+// leave the last round of workgroups mostly idle, the last tile columns
+// (tail_n columns) are computed apart, their contraction split tail_splits
+// ways into workspace slices that a second kernel sums, in slice order, before
+// the bias and GeLU.  tail_n = 0: one plain launch.
+struct FwdPlan {
+  int tail_n;
+  int tail_splits;
+};
+
 struct MlpWorkspace {
   size_t off_dH;      // bf16 [T x f]: dH, consumed by the dA and dX GEMMs
   size_t off_db1;     // fp32 [db1_parts x f]: per-writer bias-gradient column sums
   size_t off_splitk;  // fp32 [S x h*f]: weight-gradient split-K slices
+  size_t off_fwd_tail;  // fp32 [tail_splits x T x tail_n]: the forward's tail slices (the forward
+                        // and the backward never use one workspace at the same time)
   size_t bytes;
   size_t max_region;  // largest piece one kernel addresses through one resource (a region or one slice)
   int db1_parts;
   BwdPlan plan;
+  FwdPlan fwd;
 };
 
 struct CeWorkspace {
@@ -80,13 +93,14 @@ enum TimedKernel {
 void record_armed_event(int id, bool after, hipStream_t st);
 
 BwdPlan plan_backward(int64_t T, int64_t h, int64_t f);
+FwdPlan plan_forward(int64_t T, int64_t h, int64_t f);
 MlpWorkspace mlp_workspace_layout(int64_t T, int64_t h, int64_t f);
 CeWorkspace ce_workspace_layout(int64_t T, int64_t v);
 CeBwdWorkspace ce_bwd_workspace_layout(int64_t T, int64_t h, int64_t v);
 AttnWorkspace attn_workspace_layout(int64_t b, int64_t s, int64_t h, int64_t n, int64_t d);
 
 hipError_t launch_mlp_fwd(const uint16_t* X, const uint16_t* A, const uint16_t* b1, const uint16_t* B,
-                          int64_t T, int64_t h, int64_t f, int gelu, uint16_t* H, uint16_t* Y, float* Z,
+                          int64_t T, int64_t h, int64_t f, int gelu, uint16_t* H, uint16_t* Y, float* Z, void* ws,
                           hipStream_t st);
 hipError_t launch_mlp_bwd(const uint16_t* X, const uint16_t* A, const uint16_t* B, const uint16_t* H,
                           const uint16_t* Y, const uint16_t* dZ, int64_t T, int64_t h, int64_t f, int gelu,

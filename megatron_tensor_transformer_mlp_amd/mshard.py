@@ -28,7 +28,8 @@ STATUS_NAMES = ["MS_OK", "MS_ERR_NULL", "MS_ERR_SHAPE", "MS_ERR_ALIGN", "MS_ERR_
                 "MS_ERR_ENUM", "MS_ERR_HIP"]
 GELU = {"erf": 0, "tanh": 1}
 
-EXPORTED = ("mlp_shard_workspace_bytes", "mlp_shard_fwd", "mlp_shard_bwd", "vocab_ce_workspace_bytes",
+EXPORTED = ("mlp_shard_workspace_bytes", "mlp_shard_fwd_workspace_bytes", "mlp_shard_fwd", "mlp_shard_bwd",
+            "vocab_ce_workspace_bytes",
             "vocab_ce_shard_fwd", "ce_combine_workspace_bytes", "ce_combine", "vocab_ce_bwd_workspace_bytes",
             "vocab_ce_shard_bwd", "attn_shard_workspace_bytes", "attn_shard_fwd", "attn_shard_bwd",
             "ms_fingerprint_words", "ms_fingerprint", "ms_arm_kernel_events",
@@ -57,6 +58,7 @@ def _load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     sig = {
         "mlp_shard_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+        "mlp_shard_fwd_workspace_bytes": (_sz, [_i64, _i64, _i64]),
         "mlp_shard_fwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_int, _vp, _vp, _vp, _vp,
                                          _sz, _vp]),
         "mlp_shard_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_int, _vp, _vp,
@@ -183,6 +185,10 @@ def mlp_shard_workspace_bytes(T: int, h: int, f_i: int) -> int:
     return int(LIB.mlp_shard_workspace_bytes(T, h, f_i))
 
 
+def mlp_shard_fwd_workspace_bytes(T: int, h: int, f_i: int) -> int:
+    return int(LIB.mlp_shard_fwd_workspace_bytes(T, h, f_i))
+
+
 def vocab_ce_workspace_bytes(T: int, h: int, v_i: int) -> int:
     return int(LIB.vocab_ce_workspace_bytes(T, h, v_i))
 
@@ -207,8 +213,12 @@ def _workspace(nbytes: int, device, given: Optional[torch.Tensor]) -> Optional[t
 
 
 def mlp_shard_fwd(X: torch.Tensor, A_i: torch.Tensor, B_i: torch.Tensor, b1_i: Optional[torch.Tensor] = None,
-                  gelu: str = "erf", out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
-    """(H_i, Y_i, Z_i) = forward of one rank's MLP shard (bf16 H, Y; fp32 partial Z)."""
+                  gelu: str = "erf", out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
+                  workspace: Optional[torch.Tensor] = None):
+    """(H_i, Y_i, Z_i) = forward of one rank's MLP shard (bf16 H, Y; fp32 partial Z).
+
+    A workspace is allocated when the launch plan needs one and none is given
+    (mlp_shard_fwd_workspace_bytes; the backward's workspace is large enough)."""
     T, h = X.shape
     f_i = A_i.shape[1]
     bf = torch.bfloat16
@@ -223,9 +233,11 @@ def mlp_shard_fwd(X: torch.Tensor, A_i: torch.Tensor, B_i: torch.Tensor, b1_i: O
     else:
         H, Y, Z = _outs(out, (("H", bf, (T, f_i), False), ("Y", bf, (T, f_i), False),
                               ("Z", torch.float32, (T, h), False)), X.device)
+    nbytes = mlp_shard_fwd_workspace_bytes(T, h, f_i)
+    ws = _workspace(nbytes, X.device, workspace) if nbytes else None
     with _on(X.device):
         st = LIB.mlp_shard_fwd(_ptr(X), _ptr(A_i), _ptr(b1_i), _ptr(B_i), T, h, f_i, _gelu(gelu),
-                               _ptr(H), _ptr(Y), _ptr(Z), None, 0, _stream(X.device))
+                               _ptr(H), _ptr(Y), _ptr(Z), _ptr(ws), nbytes, _stream(X.device))
     _check(st, "mlp_shard_fwd")
     return H, Y, Z
 

@@ -68,8 +68,9 @@ int main(int argc, char** argv) {
     auto X = rd("X", T * h * 2), A = rd("A", h * f * 2), B = rd("B", f * h * 2);
     std::vector<char> b1 = bias ? rd("b1", f * 2) : std::vector<char>();
     auto H = out(T * f * 2), Y = out(T * f * 2), Z = out(T * h * 4);
+    auto ws = out(mshard::mlp_workspace_layout(T, h, f).bytes);
     ok(mshard::launch_mlp_fwd(C<uint16_t>(X), C<uint16_t>(A), bias ? C<uint16_t>(b1) : nullptr, C<uint16_t>(B), T, h,
-                              f, (int)gelu, P<uint16_t>(H), P<uint16_t>(Y), P<float>(Z), nullptr),
+                              f, (int)gelu, P<uint16_t>(H), P<uint16_t>(Y), P<float>(Z), ws.data(), nullptr),
        "launch_mlp_fwd");
     wr("H", H, T * f * 2), wr("Y", Y, T * f * 2), wr("Z", Z, T * h * 4);
   } else if (op == "mlp_bwd") {
@@ -166,9 +167,10 @@ int main(int argc, char** argv) {
     const mshard::MlpWorkspace mw = mshard::mlp_workspace_layout(T, h, f);
     const mshard::CeBwdWorkspace cw = mshard::ce_bwd_workspace_layout(T, h, v);
     const mshard::AttnWorkspace aw = mshard::attn_workspace_layout(b, s, h, n, d);
-    std::printf("mlp splits_dB=%d splits_dA=%d pair_bh=%d pair_ax=%d dh_first=%d dx_first=%d db1_parts=%d\n",
+    std::printf("mlp splits_dB=%d splits_dA=%d pair_bh=%d pair_ax=%d dh_first=%d dx_first=%d db1_parts=%d "
+                "fwd_tail_n=%d fwd_tail_splits=%d\n",
                 mw.plan.splits_dB, mw.plan.splits_dA, (int)mw.plan.pair_bh, (int)mw.plan.pair_ax,
-                (int)mw.plan.dh_first, (int)mw.plan.dx_first, mw.db1_parts);
+                (int)mw.plan.dh_first, (int)mw.plan.dx_first, mw.db1_parts, mw.fwd.tail_n, mw.fwd.tail_splits);
     std::printf("ce_bwd splits_dE=%d paired=%d dx_first=%d\n", cw.splits_dE, (int)cw.paired, (int)cw.dx_first);
     std::printf("attn splits_wo=%d splits_wqkv=%d pair_o=%d o_first=%d pair_x=%d x_first=%d\n", aw.splits_wo,
                 aw.splits_wqkv, (int)aw.pair_o, (int)aw.o_first, (int)aw.pair_x, (int)aw.x_first);

@@ -51,6 +51,23 @@ def test_workspace_sizes(ms):
 FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced
 
 
+def test_forward_workspace(ms):
+    """The forward needs a workspace only where its plan splits the last tile
+    columns (the GPT-2 layer: 800 tiles on 256 CUs); there a NULL or short one is
+    refused before anything is launched, and the backward's size covers it."""
+    assert ms.mlp_shard_fwd_workspace_bytes(64, 64, 256) == 0
+    assert ms.mlp_shard_fwd_workspace_bytes(4100, 392, 776) == 0
+    need = ms.mlp_shard_fwd_workspace_bytes(8192, 1600, 6400)
+    assert need == ms.mlp_shard_workspace_bytes(8192, 1600, 6400) > 0
+    assert ms.mlp_shard_fwd_workspace_bytes(64, 60, 256) == 0
+    T, h, f = 8192, 1600, 6400
+    args = (FAKE, FAKE + (1 << 30), None, FAKE + (2 << 30), T, h, f, 0, FAKE + (3 << 30), FAKE + (4 << 30),
+            FAKE + (5 << 30))
+    assert ms.LIB.mlp_shard_fwd(*args, None, 0, None) == ms.MS_ERR_WORKSPACE
+    assert ms.LIB.mlp_shard_fwd(*args, FAKE + (6 << 30), need - 256, None) == ms.MS_ERR_WORKSPACE
+    assert ms.LIB.mlp_shard_fwd(*args, FAKE + (5 << 30), need, None) == ms.MS_ERR_ALIAS  # workspace on Z
+
+
 def _fwd(ms, X=FAKE, A=FAKE + (1 << 30), b1=None, B=FAKE + (2 << 30), T=64, h=64, f=256, gelu=0,
          H=FAKE + (3 << 30), Y=FAKE + (4 << 30), Z=FAKE + (5 << 30)):
     return ms.LIB.mlp_shard_fwd(X, A, b1, B, T, h, f, gelu, H, Y, Z, None, 0, None)

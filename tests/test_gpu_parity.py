@@ -201,6 +201,31 @@ def combine_partials(rng, t, T):
     return M, S, Z
 
 
+@pytest.mark.parametrize("gelu", ["erf", "tanh"])
+def test_forward_tail_split(ms, gelu):
+    """A shape whose forward splits its last tile columns over K (264 tiles on 256
+    CUs): H, Y and Z against the oracle, the split columns on their own, the
+    backward from those H and Y, and the same bits on a second call."""
+    T, h, f = 2048, 512, 8448
+    assert ms.mlp_shard_fwd_workspace_bytes(T, h, f) > 0
+    print(f"case forward tail split gelu={gelu} T={T} h={h} f={f}", flush=True)
+    d = inputs.make_inputs(T, h, f, 8, bias=True)
+    X, A, B, dZ, b1 = dev(d["X"]), dev(d["A"]), dev(d["B"]), dev(d["dZ"]), dev(d["b1"])
+    H, Y, Z = ms.mlp_shard_fwd(X, A, B, b1, gelu=gelu)
+    H2, Y2, Z2 = ms.mlp_shard_fwd(X, A, B, b1, gelu=gelu)
+    dX, dA, dB, db1 = ms.mlp_shard_bwd(X, A, B, H, Y, dZ, gelu=gelu, want_db1=True)
+    torch.cuda.synchronize()
+    assert digest(H, Y, Z) == digest(H2, Y2, Z2)
+    want = {**oracle.mlp_shard_fwd(d["X"], d["A"], d["B"], d["b1"], gelu),
+            **oracle.mlp_shard_bwd(d["X"], d["A"], d["B"], d["dZ"], d["b1"], gelu)}
+    got = {"H": host(H), "Y": host(Y), "Z": host(Z), "dX": host(dX), "dA": host(dA), "dB": host(dB),
+           "db1": host(db1)}
+    errs = {k: rel_fro(v, want[k]) for k, v in got.items()}
+    errs.update({k + "_tail": rel_fro(got[k][:, -256:], want[k][:, -256:]) for k in ("H", "Y")})
+    print("  rel-fro", {k: f"{e:.2e}" for k, e in errs.items()}, flush=True)
+    assert all(e <= MLP_TOL for e in errs.values()), errs
+
+
 def fixed_order_mean(loss: np.ndarray) -> np.float32:
     """The combine's mean in float32: per-thread sums over tokens j, j+1024, ... in
     ascending order, then a binary tree over the 1024 sums, divided by T."""

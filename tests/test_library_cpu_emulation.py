@@ -107,6 +107,32 @@ def test_mlp_shard_emulated(lib, T, h, f, gelu, bias):
     mlp_case(*lib, T, h, f, gelu, bias)
 
 
+@pytest.mark.parametrize("gelu", [0, 1])
+def test_mlp_forward_tail_split_emulated(lib, gelu):
+    """The forward plan that splits the last tile columns over K: 257 column tiles
+    (one more than the CUs), the last one ragged (136 columns), with a bias; H, Y
+    and Z against the oracle, and the split columns on their own."""
+    mlp_tail_case(*lib, gelu)
+
+
+def mlp_tail_case(exe, d, gelu):
+    T, h, f = 200, 256, 256 * 256 + 136
+    p = plan(exe, d, T, h, f, 64, 1, 64, 1, 64)["mlp"]
+    tn = int(p["fwd_tail_n"])
+    assert tn > 0 and tn % 256 == 136 and int(p["fwd_tail_splits"]) > 1, p  # the ragged tile is in the tail
+    x = inputs.make_inputs(T, h, f, 64, bias=True)
+    case = os.path.join(d, f"mlp_tail_{gelu}")
+    put(case, X=x["X"], A=x["A"], B=x["B"], b1=x["b1"])
+    run(exe, case, "mlp_fwd", T, h, f, gelu, 1)
+    of = oracle.mlp_shard_fwd(x["X"], x["A"], x["B"], x["b1"], "tanh" if gelu else "erf")
+    got = {"H": get(case, "H", np.uint16, (T, f)), "Y": get(case, "Y", np.uint16, (T, f)),
+           "Z": get(case, "Z", np.float32, (T, h))}
+    errs = {k: rel_fro(v, of[k]) for k, v in got.items()}
+    tail = {k: rel_fro(got[k][:, -tn:], of[k][:, -tn:]) for k in ("H", "Y")}
+    print(case, errs, tail)
+    assert all(e <= TOL for e in list(errs.values()) + list(tail.values())), (errs, tail)
+
+
 def mlp_case(exe, d, T, h, f, gelu, bias):
     x = inputs.make_inputs(T, h, f, 64, bias=True)
     case = os.path.join(d, f"mlp_{T}_{h}_{f}_{gelu}_{bias}")
@@ -383,6 +409,13 @@ def test_library_emulated_under_sanitizer(tmp_path, sanitizer):
 
 
 FULL = os.environ.get("MSHARD_FULL_SIZE_EMULATION") == "1"
+
+
+@pytest.mark.skipif(not FULL, reason="about a minute; set MSHARD_FULL_SIZE_EMULATION=1")
+def test_mlp_forward_tail_split_under_address_sanitizer(lib_asan):
+    """The forward's split tail (GEMM slices and their GeLU reduction) with every
+    access checked against its allocation."""
+    mlp_tail_case(*lib_asan, 0)
 
 
 @pytest.fixture(scope="module")
