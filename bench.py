@@ -1,7 +1,7 @@
 """Benchmark: one step = the whole per-rank hot path on one batch of synthetic input:
 mlp_shard_fwd + mlp_shard_bwd + vocab_ce_shard_fwd + ce_combine.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W (default 50)] [--workload NAME] [--no-cpu-baseline]
                     [--rows ce_bwd,attn|none] [--shards NAME,...|none]
 
 Default workload: the GPT-2 1.5B-like full layer (t=1): T = 8*1024 tokens, h = 1600,
@@ -64,7 +64,7 @@ def _args():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--workload", default="gpt2_1p5b")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle CPU time")
