@@ -226,18 +226,23 @@ struct EpiGeluFwd {
     const rsrc_t rb = make_rsrc(b1, b1 ? (int64_t)N * 2 : 0);
     const u32x2_t bb = buf_load8(rb, col < N ? (uint32_t)col * 2u : kOOB);
     const float bv[4] = {bf16_lo(bb[0]), bf16_hi(bb[0]), bf16_lo(bb[1]), bf16_hi(bb[1])};
-    epi_rows(acc, c, [&](int rl, int cl, f32x4_t v) {
-      const bool ok = rl < mrem && cl < nrem;
-      const uint32_t off = ok ? (uint32_t)(((int64_t)rl * ld + cl) * 2) : kOOB;
-      float hv[4], yv[4];
+    // without a bias the pre-activation is the accumulator itself (no addition)
+    auto body = [&](auto with_bias) {
+      epi_rows(acc, c, [&](int rl, int cl, f32x4_t v) {
+        const bool ok = rl < mrem && cl < nrem;
+        const uint32_t off = ok ? (uint32_t)(((int64_t)rl * ld + cl) * 2) : kOOB;
+        float hv[4], yv[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        hv[r] = v[r] + bv[r];
-        yv[r] = gelu_f<FORM>(hv[r]);
-      }
-      buf_store8(u32x2_t{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])}, rh, off);
-      buf_store8(u32x2_t{pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3])}, ry, off);
-    });
+        for (int r = 0; r < 4; ++r) {
+          hv[r] = decltype(with_bias)::value ? v[r] + bv[r] : v[r];
+          yv[r] = gelu_f<FORM>(hv[r]);
+        }
+        buf_store8(u32x2_t{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])}, rh, off);
+        buf_store8(u32x2_t{pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3])}, ry, off);
+      });
+    };
+    if (b1) body(std::true_type{});
+    else body(std::false_type{});
   }
 };
 
@@ -263,44 +268,59 @@ struct EpiDGelu {
     const int cl = c.wn * kWaveN + q * 4;
     constexpr int kIters = kEpiRows / kRowsPerRead;  // read instructions per staged half
     float csum[4] = {0.f, 0.f, 0.f, 0.f};
+    // compile-time paths: column sums only with a bias gradient to form, and no
+    // per-row bounds tests for tiles wholly inside the matrix
+    auto body = [&](auto with_db1, auto interior) {
+      constexpr bool kDb1 = decltype(with_db1)::value, kInterior = decltype(interior)::value;
+      auto in = [&](int rl) { return kInterior || (rl < mrem && cl < nrem); };
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      epi_stage_half(acc, region, h, c.lane);  // h must be a constant: acc is indexed by it
-      // H of 8 reads per batch; the next batch's loads are issued before the
-      // current batch is processed, so their latency overlaps the arithmetic
-      auto load_h = [&](int it0, u32x2_t (&hh)[8]) {
+      for (int h = 0; h < 2; ++h) {
+        epi_stage_half(acc, region, h, c.lane);  // h must be a constant: acc is indexed by it
+        // H of 8 reads per batch; the next batch's loads are issued before the
+        // current batch is processed, so their latency overlaps the arithmetic
+        auto load_h = [&](int it0, u32x2_t (&hh)[8]) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int rl = c.wm * kWaveM + h * 64 + (it0 + u) * kRowsPerRead + sub;
-          const bool ok = rl < mrem && cl < nrem;
-          hh[u] = buf_load8(rh, ok ? (uint32_t)(((int64_t)rl * ld + cl) * 2) : kOOB);
-        }
-      };
-      u32x2_t hcur[8], hnext[8];
-      load_h(0, hcur);
-#pragma unroll 2
-      for (int it0 = 0; it0 < kIters; it0 += 8) {
-        if (it0 + 8 < kIters) load_h(it0 + 8, hnext);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int lr = (it0 + u) * kRowsPerRead + sub;
-          const int rl = c.wm * kWaveM + h * 64 + lr;
-          const bool ok = rl < mrem && cl < nrem;
-          const f32x4_t v = epi_read(region, lr, q);
-          const float hv[4] = {bf16_lo(hcur[u][0]), bf16_hi(hcur[u][0]), bf16_lo(hcur[u][1]), bf16_hi(hcur[u][1])};
-          float dv[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            dv[r] = ok ? v[r] * gelu_grad_f<FORM>(hv[r]) : 0.0f;
-            csum[r] += dv[r];
+          for (int u = 0; u < 8; ++u) {
+            const int rl = c.wm * kWaveM + h * 64 + (it0 + u) * kRowsPerRead + sub;
+            hh[u] = buf_load8(rh, in(rl) ? (uint32_t)(((int64_t)rl * ld + cl) * 2) : kOOB);
           }
-          buf_store8(u32x2_t{pack_bf16x2(dv[0], dv[1]), pack_bf16x2(dv[2], dv[3])}, rd,
-                     ok ? (uint32_t)(((int64_t)rl * ld + cl) * 2) : kOOB);
-        }
+        };
+        u32x2_t hcur[8], hnext[8];
+        load_h(0, hcur);
+#pragma unroll 2
+        for (int it0 = 0; it0 < kIters; it0 += 8) {
+          if (it0 + 8 < kIters) load_h(it0 + 8, hnext);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) hcur[u] = hnext[u];
+          for (int u = 0; u < 8; ++u) {
+            const int lr = (it0 + u) * kRowsPerRead + sub;
+            const int rl = c.wm * kWaveM + h * 64 + lr;
+            const bool ok = in(rl);
+            const f32x4_t v = epi_read(region, lr, q);
+            const float hv[4] = {bf16_lo(hcur[u][0]), bf16_hi(hcur[u][0]), bf16_lo(hcur[u][1]),
+                                 bf16_hi(hcur[u][1])};
+            float dv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              dv[r] = v[r] * gelu_grad_f<FORM>(hv[r]);
+              if constexpr (!kInterior) dv[r] = ok ? dv[r] : 0.0f;
+              if constexpr (kDb1) csum[r] += dv[r];
+            }
+            buf_store8(u32x2_t{pack_bf16x2(dv[0], dv[1]), pack_bf16x2(dv[2], dv[3])}, rd,
+                       ok ? (uint32_t)(((int64_t)rl * ld + cl) * 2) : kOOB);
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) hcur[u] = hnext[u];
+        }
+        __builtin_amdgcn_wave_barrier();
       }
-      __builtin_amdgcn_wave_barrier();
+    };
+    const bool interior = mrem >= kBM && nrem >= kBN;
+    if (db1_part) {
+      if (interior) body(std::true_type{}, std::true_type{});
+      else body(std::true_type{}, std::false_type{});
+    } else {
+      if (interior) body(std::false_type{}, std::true_type{});
+      else body(std::false_type{}, std::false_type{});
     }
     if (db1_part) {
       // the lanes holding the same columns (sub = 0 .. kRowsPerRead-1) add their

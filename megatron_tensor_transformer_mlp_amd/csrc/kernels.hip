@@ -51,8 +51,8 @@ __global__ void __launch_bounds__(256) splitk_reduce_bf16(const float* __restric
 
 // The forward's tail columns: for element (t, c) of [T x tn], the
 // pre-activation is the sum of the S split slices ws[s*T*tn + t*tn + c] in
-// ascending s, plus the bias b1[c] when there is one, as the GeLU epilogue
-// forms it; H and GeLU(H) are stored in bf16 at row t, column c of H and Y
+// ascending s, plus the bias b1[c] when there is one (with none, no addition),
+// as the GeLU epilogue forms it; H and GeLU(H) are stored in bf16 at row t, column c of H and Y
 // (row pitch ld).  8 elements per thread.
 template <int FORM>
 __global__ void __launch_bounds__(256) splitk_gelu_reduce(const float* __restrict__ ws, int S, int64_t T, int tn,
@@ -75,18 +75,19 @@ __global__ void __launch_bounds__(256) splitk_gelu_reduce(const float* __restric
 #pragma unroll
     for (int r = 0; r < 4; ++r) { acc[r] += a[r]; acc[4 + r] += b[r]; }
   }
-  float bv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (b1) {
-    const u32x4_t w = *(const u32x4_t*)(b1 + c);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) { bv[2 * r] = bf16_lo(w[r]); bv[2 * r + 1] = bf16_hi(w[r]); }
-  }
   float hv[8], yv[8];
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    hv[r] = acc[r] + bv[r];
-    yv[r] = gelu_f<FORM>(hv[r]);
+  for (int r = 0; r < 8; ++r) hv[r] = acc[r];
+  if (b1) {  // without a bias, the sum itself (no addition), as in the epilogue
+    const u32x4_t w = *(const u32x4_t*)(b1 + c);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      hv[2 * r] += bf16_lo(w[r]);
+      hv[2 * r + 1] += bf16_hi(w[r]);
+    }
   }
+#pragma unroll
+  for (int r = 0; r < 8; ++r) yv[r] = gelu_f<FORM>(hv[r]);
   const int64_t o = t * ld + c;
   *(u32x4_t*)(H + o) = u32x4_t{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]), pack_bf16x2(hv[4], hv[5]),
                                pack_bf16x2(hv[6], hv[7])};
