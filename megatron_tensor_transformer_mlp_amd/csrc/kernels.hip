@@ -436,8 +436,8 @@ FwdPlan plan_forward(int64_t T, int64_t h, int64_t f) {
     for (int64_t nc = 1; nc < tn && nc <= 32; ++nc) {
       const int64_t tail_n = f - (tn - nc) * kBN;
       for (int S = 2; S <= 8 && nk / S >= 4; S *= 2) {
-        const double t = makespan_us({BlockList{tm * (tn - nc), block_cost(h, 1, kEpiGelu)},
-                                      BlockList{tm * nc * S, block_cost(h, S, kEpiF32)}}) +
+        const double t = makespan_us({BlockList{tm * nc * S, block_cost(h, S, kEpiF32)},
+                                      BlockList{tm * (tn - nc), block_cost(h, 1, kEpiGelu)}}) +
                          (double)(4 * S + 4) * (double)T * (double)tail_n / 4e6 + 3.0;
         if (t < best) {
           best = t;
@@ -565,8 +565,11 @@ static hipError_t mlp_fwd_impl(const uint16_t* X, const uint16_t* A, const uint1
     if (err != hipSuccess) return err;
   } else {
     // columns [0, n1) with the GeLU epilogue, and the tail columns [n1, f) split
-    // over K into fp32 slices, in one launch (the full tiles first); then the
-    // slices are summed with the bias and GeLU
+    // over K into fp32 slices, in one launch; then the slices are summed with
+    // the bias and GeLU.  The short split blocks are dispatched first: the CUs
+    // that take them start their full tiles a fraction of a tile later, so the
+    // full tiles' store-heavy GeLU epilogues fall at two different times instead
+    // of on every CU at once (measured about 3% faster than the full tiles first)
     const int64_t n1 = f - pl.tail_n;
     float* slices = (float*)(ws + mlp_workspace_layout(T, h, f).off_fwd_tail);
     const GemmGeom g1 = make_geom(T, n1, h, 1);
@@ -578,7 +581,7 @@ static hipError_t mlp_fwd_impl(const uint16_t* X, const uint16_t* A, const uint1
     const int nb1 = g1.tiles_m * g1.tiles_n * g1.splits, nb2 = g2.tiles_m * g2.tiles_n * g2.splits;
     record_armed_event(kTkFwdH, false, st);
     hipLaunchKernelGGL((gemm_pair_kernel<true, false, EpiGeluFwd<FORM>, true, false, EpiStoreF32>),
-                       dim3(((nb1 + 7) & ~7) + nb2), dim3(kThreads), 0, st, g1, a, b1o, e1, nb1, g2, a, b2o, e2, nb2, 0);
+                       dim3(((nb2 + 7) & ~7) + nb1), dim3(kThreads), 0, st, g1, a, b1o, e1, nb1, g2, a, b2o, e2, nb2, 1);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int64_t n8 = T * pl.tail_n / 8;
