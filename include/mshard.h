@@ -83,9 +83,10 @@ size_t mlp_shard_workspace_bytes(int64_t T, int64_t h, int64_t f_i);
 
 /* Bytes of workspace mlp_shard_fwd itself needs: 0 when its launch plan uses
  * none (then its workspace may be NULL), else mlp_shard_workspace_bytes.  The
- * forward uses a workspace when the tiles of X A_i leave the GPU's last round
- * of workgroups mostly idle: it then splits the contraction of the last tile
- * columns into slices there, summed in slice order.  Returns 0 for invalid sizes. */
+ * forward uses a workspace when the tiles of X A_i or of Y_i B_i leave the
+ * GPU's last round of workgroups mostly idle: it then splits the contraction
+ * of that GEMM's last tile columns into slices there, summed in slice order.
+ * Returns 0 for invalid sizes. */
 size_t mlp_shard_fwd_workspace_bytes(int64_t T, int64_t h, int64_t f_i);
 
 /* Forward of one rank's MLP shard (explainer, "core idea"; paper notes, "MLP

@@ -183,7 +183,7 @@ size_t mlp_shard_workspace_bytes(int64_t T, int64_t h, int64_t f_i) {
 size_t mlp_shard_fwd_workspace_bytes(int64_t T, int64_t h, int64_t f_i) {
   if (check_dims(T, {{"h", h}, {"f_i", f_i}}) != MS_OK) return 0;
   const mshard::MlpWorkspace w = mshard::mlp_workspace_layout(T, h, f_i);
-  return w.fwd.tail_n > 0 ? w.bytes : 0;
+  return (w.fwd.tail_n > 0 || w.fwd.z_tail_n > 0) ? w.bytes : 0;
 }
 
 ms_status mlp_shard_fwd(const ms_bf16* X, const ms_bf16* A_i, const ms_bf16* b1_i, const ms_bf16* B_i,
@@ -197,9 +197,10 @@ ms_status mlp_shard_fwd(const ms_bf16* X, const ms_bf16* A_i, const ms_bf16* b1_
       {B_i, nbytes(f_i, h, 2), "B_i", false},   {H_i, nbytes(T, f_i, 2), "H_i", true},
       {Y_i, nbytes(T, f_i, 2), "Y_i", true},    {Z_i, nbytes(T, h, 4), "Z_i", true}};
   if (b1_i) bufs.push_back({b1_i, nbytes(f_i, 1, 2), "b1_i", false});
-  // the workspace is used only when the plan splits the last tile columns
+  // the workspace is used only when the plan splits the last tile columns of a GEMM
   const mshard::MlpWorkspace layout = mshard::mlp_workspace_layout(T, h, f_i);
-  if (layout.fwd.tail_n > 0) MS_TRY(check_workspace_layout(workspace, workspace_bytes, layout, bufs));
+  if (layout.fwd.tail_n > 0 || layout.fwd.z_tail_n > 0)
+    MS_TRY(check_workspace_layout(workspace, workspace_bytes, layout, bufs));
   MS_TRY(check_bufs(bufs));
   MS_TRY(check_device());
   return launched(mshard::launch_mlp_fwd(X, A_i, b1_i, B_i, T, h, f_i, (int)gelu, H_i, Y_i, Z_i, workspace,

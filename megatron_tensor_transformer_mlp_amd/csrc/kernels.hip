@@ -95,6 +95,28 @@ __global__ void __launch_bounds__(256) splitk_gelu_reduce(const float* __restric
                                pack_bf16x2(yv[6], yv[7])};
 }
 
+// The second forward GEMM's tail columns: element (t, c) of [T x tn] is the
+// sum of the S split slices ws[s*T*tn + t*tn + c] in ascending s, stored in
+// fp32 at row t, column c of Z (row pitch ld).  8 elements per thread.
+__global__ void __launch_bounds__(256) splitk_reduce_f32(const float* __restrict__ ws, int S, int64_t T, int tn,
+                                                         int64_t ld, float* __restrict__ Z) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  const int64_t n = T * tn;
+  if (i >= n) return;
+  const int64_t t = i / tn;
+  const int c = (int)(i - t * tn);
+  const f32x4_t* p = (const f32x4_t*)(ws + i);
+  f32x4_t a = p[0], b = p[1];
+  for (int sl = 1; sl < S; ++sl) {
+    const f32x4_t* q = (const f32x4_t*)(ws + (int64_t)sl * n + i);
+    a += q[0];
+    b += q[1];
+  }
+  f32x4_t* o = (f32x4_t*)(Z + t * ld + c);
+  o[0] = a;
+  o[1] = b;
+}
+
 // db1[j] = bf16( sum_{p = 0..P-1} part[p*N + j] ), p ascending.
 __global__ void __launch_bounds__(256) colsum_reduce_bf16(const float* __restrict__ part, int P, int N,
                                                           uint16_t* __restrict__ out) {
@@ -414,12 +436,37 @@ BwdPlan plan_backward(int64_t T, int64_t h, int64_t f) {
   return pl;
 }
 
-// Forward plan: the plain launch of X A_i with GeLU, or its last tile columns
-// split over K (see FwdPlan), whichever the same model gives the shorter time,
-// the split only when it wins by at least 3%.  Its reduction is charged its
-// bytes (S fp32 slices read, H and Y written) at ~4 TB/s plus a launch.
-// Considered only where the plain launch has more tiles than CUs and at most
-// 16 rounds of them (beyond that the last round's idle share is small).
+// Forward plan: for each GEMM of the forward, the plain launch or its last
+// tile columns split over K (see FwdPlan), whichever the same model gives the
+// shorter time, the split only when it wins by at least 3%.  The split blocks
+// are dispatched first (see mlp_fwd_impl).  The reduction is charged its bytes
+// (S fp32 slices read, 4 bytes per element written: H and Y, or Z) at ~4 TB/s
+// plus a launch.  Considered only where the plain launch has more tiles than
+// CUs and at most 16 rounds of them (beyond that the last round's idle share is
+// small).
+namespace {
+void plan_tail(int64_t M, int64_t N, int64_t K, double epi, int& tail_n, int& tail_splits) {
+  tail_n = 0;
+  tail_splits = 1;
+  const int64_t tm = (M + kBM - 1) / kBM, tn = (N + kBN - 1) / kBN, nk = (K + kBK - 1) / kBK;
+  if (tm * tn <= kModelCUs || tm * tn > 16 * kModelCUs || nk < 8) return;
+  double best = 0.97 * makespan_us({BlockList{tm * tn, block_cost(K, 1, epi)}});
+  for (int64_t nc = 1; nc < tn && nc <= 32; ++nc) {
+    const int64_t tail = N - (tn - nc) * kBN;
+    for (int S = 2; S <= 8 && nk / S >= 4; S *= 2) {
+      const double t = makespan_us({BlockList{tm * nc * S, block_cost(K, S, kEpiF32)},
+                                    BlockList{tm * (tn - nc), block_cost(K, 1, epi)}}) +
+                       (double)(4 * S + 4) * (double)M * (double)tail / 4e6 + 3.0;
+      if (t < best) {
+        best = t;
+        tail_n = (int)tail;
+        tail_splits = S;
+      }
+    }
+  }
+}
+}  // namespace
+
 FwdPlan plan_forward(int64_t T, int64_t h, int64_t f) {
   static std::mutex mu;
   static std::map<std::array<int64_t, 3>, FwdPlan> cache;
@@ -429,23 +476,9 @@ FwdPlan plan_forward(int64_t T, int64_t h, int64_t f) {
     auto it = cache.find(key);
     if (it != cache.end()) return it->second;
   }
-  FwdPlan pl{0, 1};
-  const int64_t tm = (T + kBM - 1) / kBM, tn = (f + kBN - 1) / kBN, nk = (h + kBK - 1) / kBK;
-  if (tm * tn > kModelCUs && tm * tn <= 16 * kModelCUs && nk >= 8) {
-    double best = 0.97 * makespan_us({BlockList{tm * tn, block_cost(h, 1, kEpiGelu)}});
-    for (int64_t nc = 1; nc < tn && nc <= 32; ++nc) {
-      const int64_t tail_n = f - (tn - nc) * kBN;
-      for (int S = 2; S <= 8 && nk / S >= 4; S *= 2) {
-        const double t = makespan_us({BlockList{tm * nc * S, block_cost(h, S, kEpiF32)},
-                                      BlockList{tm * (tn - nc), block_cost(h, 1, kEpiGelu)}}) +
-                         (double)(4 * S + 4) * (double)T * (double)tail_n / 4e6 + 3.0;
-        if (t < best) {
-          best = t;
-          pl = FwdPlan{(int)tail_n, S};
-        }
-      }
-    }
-  }
+  FwdPlan pl;
+  plan_tail(T, f, h, kEpiGelu, pl.tail_n, pl.tail_splits);    // H = X A_i: M = T, N = f, K = h
+  plan_tail(T, h, f, kEpiF32, pl.z_tail_n, pl.z_tail_splits);  // Z = Y B_i: M = T, N = h, K = f
   std::lock_guard<std::mutex> lock(mu);
   cache.emplace(key, pl);
   return pl;
@@ -468,6 +501,11 @@ MlpWorkspace mlp_workspace_layout(int64_t T, int64_t h, int64_t f) {
   if (w.fwd.tail_n > 0) {
     const size_t slice = (size_t)T * w.fwd.tail_n * 4;
     w.bytes = std::max(w.bytes, align(slice * w.fwd.tail_splits));
+    w.max_region = std::max(w.max_region, slice);
+  }
+  if (w.fwd.z_tail_n > 0) {
+    const size_t slice = (size_t)T * w.fwd.z_tail_n * 4;
+    w.bytes = std::max(w.bytes, align(slice * w.fwd.z_tail_splits));
     w.max_region = std::max(w.max_region, slice);
   }
   return w;
@@ -592,12 +630,35 @@ static hipError_t mlp_fwd_impl(const uint16_t* X, const uint16_t* A, const uint1
     if (err != hipSuccess) return err;
   }
   // Z = Y B:  NN, M = T, N = h, K = f
-  {
+  const Operand ay{Y, f, T * f};
+  if (pl.z_tail_n == 0) {
     GemmGeom g = make_geom(T, h, f, 1);
-    Operand a{Y, f, T * f}, b{B, h, f * h};
+    Operand b{B, h, f * h};
     EpiStoreF32 e{Z, h, (int)T, (int)h, 0};
-    return launch_gemm<true, false>(kTkFwdZ, g, a, b, e, st);
+    return launch_gemm<true, false>(kTkFwdZ, g, ay, b, e, st);
   }
+  // columns [0, n1) stored straight into Z, and the tail columns [n1, h) split
+  // over K into fp32 slices (those blocks first, as above), then summed into Z
+  const int64_t n1 = h - pl.z_tail_n;
+  float* slices = (float*)(ws + mlp_workspace_layout(T, h, f).off_fwd_tail);
+  const GemmGeom g1 = make_geom(T, n1, f, 1);
+  const Operand b1o{B, h, f * h};
+  const EpiStoreF32 e1{Z, h, (int)T, (int)n1, 0};
+  const GemmGeom g2 = make_geom(T, pl.z_tail_n, f, pl.z_tail_splits);
+  const Operand b2o{B + n1, h, f * h - n1};
+  const EpiStoreF32 e2{slices, pl.z_tail_n, (int)T, (int)pl.z_tail_n, T * pl.z_tail_n};
+  const int nb1 = g1.tiles_m * g1.tiles_n * g1.splits, nb2 = g2.tiles_m * g2.tiles_n * g2.splits;
+  record_armed_event(kTkFwdZ, false, st);
+  hipLaunchKernelGGL((gemm_pair_kernel<true, false, EpiStoreF32, true, false, EpiStoreF32>),
+                     dim3(((nb2 + 7) & ~7) + nb1), dim3(kThreads), 0, st, g1, ay, b1o, e1, nb1, g2, ay, b2o, e2, nb2, 1);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int64_t n8 = T * pl.z_tail_n / 8;
+  hipLaunchKernelGGL(splitk_reduce_f32, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, slices, g2.splits, T,
+                     pl.z_tail_n, h, Z + n1);
+  err = hipGetLastError();
+  record_armed_event(kTkFwdZ, true, st);
+  return err;
 }
 
 hipError_t launch_mlp_fwd(const uint16_t* X, const uint16_t* A, const uint16_t* b1, const uint16_t* B,

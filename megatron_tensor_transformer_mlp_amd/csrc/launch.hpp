@@ -17,22 +17,26 @@ struct BwdPlan {
   bool dh_first, dx_first;   // in a paired launch, the partner's blocks lead
 };
 
-// Launch plan of the forward's first GEMM (X A_i with GeLU): when its tiles
-// leave the last round of workgroups mostly idle, the last tile columns
-// (tail_n columns) are computed apart, their contraction split tail_splits
-// ways into workspace slices that a second kernel sums, in slice order, before
-// the bias and GeLU.  tail_n = 0: one plain launch.
+// Launch plan of the forward's two GEMMs: when a GEMM's tiles leave the last
+// round of workgroups mostly idle, its last tile columns are computed apart,
+// their contraction split into workspace slices that a second kernel sums, in
+// slice order.  X A_i with GeLU: tail_n columns split tail_splits ways, summed
+// before the bias and GeLU.  Z = Y B_i: z_tail_n columns split z_tail_splits
+// ways, summed into Z.  A tail of 0 columns: one plain launch.
 struct FwdPlan {
   int tail_n;
   int tail_splits;
+  int z_tail_n;
+  int z_tail_splits;
 };
 
 struct MlpWorkspace {
   size_t off_dH;      // bf16 [T x f]: dH, consumed by the dA and dX GEMMs
   size_t off_db1;     // fp32 [db1_parts x f]: per-writer bias-gradient column sums
   size_t off_splitk;  // fp32 [S x h*f]: weight-gradient split-K slices
-  size_t off_fwd_tail;  // fp32 [tail_splits x T x tail_n]: the forward's tail slices (the forward
-                        // and the backward never use one workspace at the same time)
+  size_t off_fwd_tail;  // fp32 [tail_splits x T x tail_n], then [z_tail_splits x T x z_tail_n]: the
+                        // forward's tail slices, one GEMM's after the other's (the forward and the
+                        // backward never use one workspace at the same time)
   size_t bytes;
   size_t max_region;  // largest piece one kernel addresses through one resource (a region or one slice)
   int db1_parts;

@@ -168,9 +168,10 @@ int main(int argc, char** argv) {
     const mshard::CeBwdWorkspace cw = mshard::ce_bwd_workspace_layout(T, h, v);
     const mshard::AttnWorkspace aw = mshard::attn_workspace_layout(b, s, h, n, d);
     std::printf("mlp splits_dB=%d splits_dA=%d pair_bh=%d pair_ax=%d dh_first=%d dx_first=%d db1_parts=%d "
-                "fwd_tail_n=%d fwd_tail_splits=%d\n",
+                "fwd_tail_n=%d fwd_tail_splits=%d z_tail_n=%d z_tail_splits=%d\n",
                 mw.plan.splits_dB, mw.plan.splits_dA, (int)mw.plan.pair_bh, (int)mw.plan.pair_ax,
-                (int)mw.plan.dh_first, (int)mw.plan.dx_first, mw.db1_parts, mw.fwd.tail_n, mw.fwd.tail_splits);
+                (int)mw.plan.dh_first, (int)mw.plan.dx_first, mw.db1_parts, mw.fwd.tail_n, mw.fwd.tail_splits,
+                mw.fwd.z_tail_n, mw.fwd.z_tail_splits);
     std::printf("ce_bwd splits_dE=%d paired=%d dx_first=%d\n", cw.splits_dE, (int)cw.paired, (int)cw.dx_first);
     std::printf("attn splits_wo=%d splits_wqkv=%d pair_o=%d o_first=%d pair_x=%d x_first=%d\n", aw.splits_wo,
                 aw.splits_wqkv, (int)aw.pair_o, (int)aw.o_first, (int)aw.pair_x, (int)aw.x_first);

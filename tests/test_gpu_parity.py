@@ -226,6 +226,27 @@ def test_forward_tail_split(ms, gelu):
     assert all(e <= MLP_TOL for e in errs.values()), errs
 
 
+def test_forward_z_tail_split(ms):
+    """A shape whose forward splits the last tile columns of Z = Y B_i over K
+    (264 tiles of Z on 256 CUs): H, Y and Z against the oracle, Z's split
+    columns on their own, and the same bits on a second call."""
+    T, h, f = 2048, 8448, 512
+    assert ms.mlp_shard_fwd_workspace_bytes(T, h, f) > 0
+    print(f"case forward Z tail split T={T} h={h} f={f}", flush=True)
+    d = inputs.make_inputs(T, h, f, 8, bias=True)
+    X, A, B, b1 = dev(d["X"]), dev(d["A"]), dev(d["B"]), dev(d["b1"])
+    H, Y, Z = ms.mlp_shard_fwd(X, A, B, b1)
+    H2, Y2, Z2 = ms.mlp_shard_fwd(X, A, B, b1)
+    torch.cuda.synchronize()
+    assert digest(H, Y, Z) == digest(H2, Y2, Z2)
+    want = oracle.mlp_shard_fwd(d["X"], d["A"], d["B"], d["b1"], "erf")
+    got = {"H": host(H), "Y": host(Y), "Z": host(Z)}
+    errs = {k: rel_fro(v, want[k]) for k, v in got.items()}
+    errs["Z_tail"] = rel_fro(got["Z"][:, -256:], want["Z"][:, -256:])
+    print("  rel-fro", {k: f"{e:.2e}" for k, e in errs.items()}, flush=True)
+    assert all(e <= MLP_TOL for e in errs.values()), errs
+
+
 def fixed_order_mean(loss: np.ndarray) -> np.float32:
     """The combine's mean in float32: per-thread sums over tokens j, j+1024, ... in
     ascending order, then a binary tree over the 1024 sums, divided by T."""

@@ -115,6 +115,33 @@ def test_mlp_forward_tail_split_emulated(lib, gelu):
     mlp_tail_case(*lib, gelu)
 
 
+@pytest.mark.parametrize("gelu", [0])
+def test_mlp_forward_z_tail_split_emulated(lib, gelu):
+    """The forward plan that splits the last tile columns of Z = Y B_i over K:
+    257 column tiles of Z (one more than the CUs), the last one ragged (136
+    columns); H, Y and Z against the oracle, and Z's split columns on their own."""
+    mlp_z_tail_case(*lib, gelu)
+
+
+def mlp_z_tail_case(exe, d, gelu):
+    T, h, f = 200, 256 * 256 + 136, 512
+    p = plan(exe, d, T, h, f, 64, 1, 64, 1, 64)["mlp"]
+    tn = int(p["z_tail_n"])
+    assert tn > 0 and tn % 256 == 136 and int(p["z_tail_splits"]) > 1, p  # the ragged tile is in the tail
+    assert p["fwd_tail_n"] == "0", p  # X A_i (two tiles) stays one plain launch
+    x = inputs.make_inputs(T, h, f, 64, bias=True)
+    case = os.path.join(d, f"mlp_ztail_{gelu}")
+    put(case, X=x["X"], A=x["A"], B=x["B"], b1=x["b1"])
+    run(exe, case, "mlp_fwd", T, h, f, gelu, 1)
+    of = oracle.mlp_shard_fwd(x["X"], x["A"], x["B"], x["b1"], "tanh" if gelu else "erf")
+    got = {"H": get(case, "H", np.uint16, (T, f)), "Y": get(case, "Y", np.uint16, (T, f)),
+           "Z": get(case, "Z", np.float32, (T, h))}
+    errs = {k: rel_fro(v, of[k]) for k, v in got.items()}
+    tail = rel_fro(got["Z"][:, -tn:], of["Z"][:, -tn:])
+    print(case, errs, tail)
+    assert all(e <= TOL for e in list(errs.values()) + [tail]), (errs, tail)
+
+
 def mlp_tail_case(exe, d, gelu):
     T, h, f = 200, 256, 256 * 256 + 136
     p = plan(exe, d, T, h, f, 64, 1, 64, 1, 64)["mlp"]
@@ -413,9 +440,10 @@ FULL = os.environ.get("MSHARD_FULL_SIZE_EMULATION") == "1"
 
 @pytest.mark.skipif(not FULL, reason="about a minute; set MSHARD_FULL_SIZE_EMULATION=1")
 def test_mlp_forward_tail_split_under_address_sanitizer(lib_asan):
-    """The forward's split tail (GEMM slices and their GeLU reduction) with every
-    access checked against its allocation."""
+    """The forward's split tails (GEMM slices and their GeLU and fp32 reductions)
+    with every access checked against its allocation."""
     mlp_tail_case(*lib_asan, 0)
+    mlp_z_tail_case(*lib_asan, 0)
 
 
 @pytest.fixture(scope="module")
