@@ -53,8 +53,9 @@ FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced
 
 def test_forward_workspace(ms):
     """The forward needs a workspace only where its plan splits the last tile
-    columns (the GPT-2 layer: 800 tiles on 256 CUs); there a NULL or short one is
-    refused before anything is launched, and the backward's size covers it."""
+    columns of a GEMM (the GPT-2 layer's X A_i: 800 tiles on 256 CUs); there a
+    NULL or short one is refused before anything is launched, and the backward's
+    size covers it."""
     assert ms.mlp_shard_fwd_workspace_bytes(64, 64, 256) == 0
     assert ms.mlp_shard_fwd_workspace_bytes(4100, 392, 776) == 0
     need = ms.mlp_shard_fwd_workspace_bytes(8192, 1600, 6400)
@@ -66,6 +67,9 @@ def test_forward_workspace(ms):
     assert ms.LIB.mlp_shard_fwd(*args, None, 0, None) == ms.MS_ERR_WORKSPACE
     assert ms.LIB.mlp_shard_fwd(*args, FAKE + (6 << 30), need - 256, None) == ms.MS_ERR_WORKSPACE
     assert ms.LIB.mlp_shard_fwd(*args, FAKE + (5 << 30), need, None) == ms.MS_ERR_ALIAS  # workspace on Z
+    # a shape where only Z = Y B_i splits its last tile columns (264 tiles of Z on 256 CUs)
+    assert ms.mlp_shard_fwd_workspace_bytes(2048, 8448, 512) == ms.mlp_shard_workspace_bytes(2048, 8448, 512) > 0
+    assert _fwd(ms, T=2048, h=8448, f=512) == ms.MS_ERR_WORKSPACE
 
 
 def _fwd(ms, X=FAKE, A=FAKE + (1 << 30), b1=None, B=FAKE + (2 << 30), T=64, h=64, f=256, gelu=0,
