@@ -167,26 +167,28 @@ struct EpiStoreF32 {
     const int mrem = M - c.m0, nrem = N - c.n0;
     epi_rows(acc, c, [&](int rl, int cl, f32x4_t v) {
       const bool ok = rl < mrem && cl < nrem;
-      buf_store16(__builtin_bit_cast(u32x4_t, v), rs, ok ? (uint32_t)(((int64_t)rl * ld + cl) * 4) : kOOB);
+      buf_store16<kStreamStore>(__builtin_bit_cast(u32x4_t, v), rs, ok ? (uint32_t)(((int64_t)rl * ld + cl) * 4) : kOOB);
     });
   }
 };
 
-// bf16 store of C.
+// bf16 store of C (store cache policy POLICY; the call operator: the default).
 struct EpiStoreBF16 {
   uint16_t* C;
   int64_t ld;
   int M, N;
-  __device__ void operator()(AccTile& acc, const EpiCtx& c) const {
+  template <int POLICY>
+  __device__ void store(AccTile& acc, const EpiCtx& c) const {
     const int64_t base = (int64_t)c.m0 * ld + c.n0;
     const rsrc_t rs = make_rsrc(C + base, ((int64_t)M * ld - base) * 2);
     const int mrem = M - c.m0, nrem = N - c.n0;
     epi_rows(acc, c, [&](int rl, int cl, f32x4_t v) {
       const bool ok = rl < mrem && cl < nrem;
-      buf_store8(u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}, rs,
-                 ok ? (uint32_t)(((int64_t)rl * ld + cl) * 2) : kOOB);
+      buf_store8<POLICY>(u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}, rs,
+                         ok ? (uint32_t)(((int64_t)rl * ld + cl) * 2) : kOOB);
     });
   }
+  __device__ void operator()(AccTile& acc, const EpiCtx& c) const { store<0>(acc, c); }
 };
 
 // Weight-gradient store for the paired launches: the bf16 result when the
@@ -199,7 +201,7 @@ struct EpiStoreWGrad {
   int64_t slice_stride;  // elements between fp32 slices; 0: bf16 output
   __device__ void operator()(AccTile& acc, const EpiCtx& c) const {
     if (slice_stride == 0) {
-      EpiStoreBF16{(uint16_t*)C, ld, M, N}(acc, c);
+      EpiStoreBF16{(uint16_t*)C, ld, M, N}.store<kStreamStore>(acc, c);
     } else {
       EpiStoreF32{(float*)C, ld, M, N, slice_stride}(acc, c);
     }
@@ -595,8 +597,8 @@ struct EpiCEGrad {
             const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(v[r], kLog2e, -ml));
             d[r] = __builtin_fmaf(e, cs, col + r == tcol ? -cf : 0.0f);
           }
-          buf_store8(u32x2_t{pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3])}, rd,
-                     ok ? (uint32_t)(((int64_t)rl * ld + cl) * 2) : kOOB);
+          buf_store8<kStreamStore>(u32x2_t{pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3])}, rd,
+                                   ok ? (uint32_t)(((int64_t)rl * ld + cl) * 2) : kOOB);
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) scur[u] = snext[u];
