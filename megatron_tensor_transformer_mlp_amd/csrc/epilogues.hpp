@@ -167,7 +167,7 @@ struct EpiStoreF32 {
     const int mrem = M - c.m0, nrem = N - c.n0;
     epi_rows(acc, c, [&](int rl, int cl, f32x4_t v) {
       const bool ok = rl < mrem && cl < nrem;
-      buf_store16<kStreamStore>(__builtin_bit_cast(u32x4_t, v), rs, ok ? (uint32_t)(((int64_t)rl * ld + cl) * 4) : kOOB);
+      buf_store16<kNonTemporal>(__builtin_bit_cast(u32x4_t, v), rs, ok ? (uint32_t)(((int64_t)rl * ld + cl) * 4) : kOOB);
     });
   }
 };
@@ -201,7 +201,7 @@ struct EpiStoreWGrad {
   int64_t slice_stride;  // elements between fp32 slices; 0: bf16 output
   __device__ void operator()(AccTile& acc, const EpiCtx& c) const {
     if (slice_stride == 0) {
-      EpiStoreBF16{(uint16_t*)C, ld, M, N}.store<kStreamStore>(acc, c);
+      EpiStoreBF16{(uint16_t*)C, ld, M, N}.store<kNonTemporal>(acc, c);
     } else {
       EpiStoreF32{(float*)C, ld, M, N, slice_stride}(acc, c);
     }
@@ -284,7 +284,7 @@ struct EpiDGelu {
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
             const int rl = c.wm * kWaveM + h * 64 + (it0 + u) * kRowsPerRead + sub;
-            hh[u] = buf_load8(rh, in(rl) ? (uint32_t)(((int64_t)rl * ld + cl) * 2) : kOOB);
+            hh[u] = buf_load8<kNonTemporal>(rh, in(rl) ? (uint32_t)(((int64_t)rl * ld + cl) * 2) : kOOB);
           }
         };
         u32x2_t hcur[8], hnext[8];
@@ -597,7 +597,7 @@ struct EpiCEGrad {
             const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(v[r], kLog2e, -ml));
             d[r] = __builtin_fmaf(e, cs, col + r == tcol ? -cf : 0.0f);
           }
-          buf_store8<kStreamStore>(u32x2_t{pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3])}, rd,
+          buf_store8<kNonTemporal>(u32x2_t{pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3])}, rd,
                                    ok ? (uint32_t)(((int64_t)rl * ld + cl) * 2) : kOOB);
         }
 #pragma unroll

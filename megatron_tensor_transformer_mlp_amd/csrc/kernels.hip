@@ -28,25 +28,27 @@ namespace mshard {
 // Small kernels
 
 // out[i] = bf16( sum_{s = 0..S-1} ws[s*stride + i] ), s ascending; 8 elements per thread.
+// The slices are read once and the result is not read back soon: both
+// non-temporal (see the cache-policy note in gemm_core.hpp).
 __global__ void __launch_bounds__(256) splitk_reduce_bf16(const float* __restrict__ ws, int64_t stride, int S,
                                                           int64_t n, uint16_t* __restrict__ out) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
   if (i >= n) return;
   float acc[8];
   const f32x4_t* p = (const f32x4_t*)(ws + i);
-  f32x4_t a = p[0], b = p[1];
+  f32x4_t a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
 #pragma unroll
   for (int r = 0; r < 4; ++r) { acc[r] = a[r]; acc[4 + r] = b[r]; }
   for (int s = 1; s < S; ++s) {
     const f32x4_t* q = (const f32x4_t*)(ws + (int64_t)s * stride + i);
-    a = q[0];
-    b = q[1];
+    a = __builtin_nontemporal_load(q);
+    b = __builtin_nontemporal_load(q + 1);
 #pragma unroll
     for (int r = 0; r < 4; ++r) { acc[r] += a[r]; acc[4 + r] += b[r]; }
   }
   u32x4_t o{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
             pack_bf16x2(acc[6], acc[7])};
-  *(u32x4_t*)(out + i) = o;
+  __builtin_nontemporal_store(o, (u32x4_t*)(out + i));
 }
 
 // The forward's tail columns: for element (t, c) of [T x tn], the
@@ -65,13 +67,13 @@ __global__ void __launch_bounds__(256) splitk_gelu_reduce(const float* __restric
   const int c = (int)(i - t * tn);
   float acc[8];
   const f32x4_t* p = (const f32x4_t*)(ws + i);
-  f32x4_t a = p[0], b = p[1];
+  f32x4_t a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
 #pragma unroll
   for (int r = 0; r < 4; ++r) { acc[r] = a[r]; acc[4 + r] = b[r]; }
   for (int sl = 1; sl < S; ++sl) {
     const f32x4_t* q = (const f32x4_t*)(ws + (int64_t)sl * n + i);
-    a = q[0];
-    b = q[1];
+    a = __builtin_nontemporal_load(q);
+    b = __builtin_nontemporal_load(q + 1);
 #pragma unroll
     for (int r = 0; r < 4; ++r) { acc[r] += a[r]; acc[4 + r] += b[r]; }
   }
@@ -106,15 +108,15 @@ __global__ void __launch_bounds__(256) splitk_reduce_f32(const float* __restrict
   const int64_t t = i / tn;
   const int c = (int)(i - t * tn);
   const f32x4_t* p = (const f32x4_t*)(ws + i);
-  f32x4_t a = p[0], b = p[1];
+  f32x4_t a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
   for (int sl = 1; sl < S; ++sl) {
     const f32x4_t* q = (const f32x4_t*)(ws + (int64_t)sl * n + i);
-    a += q[0];
-    b += q[1];
+    a += __builtin_nontemporal_load(q);
+    b += __builtin_nontemporal_load(q + 1);
   }
   f32x4_t* o = (f32x4_t*)(Z + t * ld + c);
-  o[0] = a;
-  o[1] = b;
+  __builtin_nontemporal_store(a, o);
+  __builtin_nontemporal_store(b, o + 1);
 }
 
 // db1[j] = bf16( sum_{p = 0..P-1} part[p*N + j] ), p ascending.
@@ -168,9 +170,9 @@ __global__ void __launch_bounds__(512) ce_tile_combine(const float* __restrict__
       for (int j = 0; j < kCombineChunk; ++j) {
         const bool in = p + j < p1;
         const int64_t o = (int64_t)(p + j) * T + row;
-        cm[j] = in ? pm[o] : -INFINITY;
-        cs[j] = in ? ps[o] : 0.f;
-        cz[j] = in ? pz[o] : 0.f;
+        cm[j] = in ? __builtin_nontemporal_load(pm + o) : -INFINITY;
+        cs[j] = in ? __builtin_nontemporal_load(ps + o) : 0.f;
+        cz[j] = in ? __builtin_nontemporal_load(pz + o) : 0.f;
       }
       float mx = cm[0];
 #pragma unroll

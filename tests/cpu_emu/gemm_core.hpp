@@ -44,9 +44,10 @@ inline void buf_store(V v, rsrc_t r, uint32_t off) {
   if ((int64_t)off + (int64_t)sizeof(V) <= r.bytes) std::memcpy(r.base + off, &v, sizeof(V));
 }
 inline u32x4_t buf_load16(rsrc_t r, uint32_t off) { return buf_load<u32x4_t>(r, off); }
+template <int POLICY = 0>
 inline u32x2_t buf_load8(rsrc_t r, uint32_t off) { return buf_load<u32x2_t>(r, off); }
 // the cache-policy argument of the real helpers changes nothing on the host
-constexpr int kStreamStore = 2;
+constexpr int kNonTemporal = 2;
 template <int POLICY = 0>
 inline void buf_store16(u32x4_t v, rsrc_t r, uint32_t off) { buf_store(v, r, off); }
 template <int POLICY = 0>
